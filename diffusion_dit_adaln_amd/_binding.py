@@ -1,0 +1,243 @@
+"""ctypes binding of libadaln (include/adaln.h): argument marshalling only.
+
+Torch tensors supply device pointers, strides and the current HIP stream; every
+step of the computation runs in the library's HIP kernels.  A missing library is
+an error (no CPU fallback exists).
+"""
+from __future__ import annotations
+
+import ctypes
+import os
+
+import torch
+
+_PKG = os.path.dirname(os.path.abspath(__file__))
+ABI_VERSION = 1
+
+STATUS_NAMES = {0: "ADALN_OK", 1: "ADALN_ERR_NULL", 2: "ADALN_ERR_SHAPE", 3: "ADALN_ERR_ALIGN",
+                4: "ADALN_ERR_STRIDE", 5: "ADALN_ERR_OVERLAP", 6: "ADALN_ERR_VALUE",
+                7: "ADALN_ERR_LAUNCH"}
+
+# every symbol include/adaln.h declares
+EXPORTS = ("adaln_layernorm_modulate", "adaln_rmsnorm_scale_shift",
+           "adaln_residual_gate_rmsnorm_scale_shift", "adaln_check_layernorm_modulate",
+           "adaln_check_rmsnorm_scale_shift", "adaln_check_residual_gate_rmsnorm_scale_shift",
+           "adaln_reduction_layout", "adaln_status_string", "adaln_abi_version",
+           "adaln_diag_round_bf16", "adaln_diag_finalize")
+
+
+class AdalnError(RuntimeError):
+    """A libadaln entry point returned a non-OK status."""
+
+    def __init__(self, status: int, what: str):
+        self.status = status
+        super().__init__(f"{what}: {STATUS_NAMES.get(status, status)} ({_status_text(status)})")
+
+
+_lib = None
+
+
+def library_path() -> str:
+    return os.path.join(_PKG, "libadaln.so")
+
+
+def load_library():
+    """Load the built libadaln.so from the package directory (raises if absent)."""
+    global _lib
+    if _lib is not None:
+        return _lib
+    path = library_path()
+    if not os.path.exists(path):
+        raise RuntimeError(f"libadaln is not built ({path} missing); run __graft_entry__.build()")
+    lib = ctypes.CDLL(path)
+    P, I, F, S = ctypes.c_void_p, ctypes.c_int64, ctypes.c_float, ctypes.c_int
+    sig = {
+        "adaln_layernorm_modulate": [P, P, P, P, I, I, I, I, I, F, P],
+        "adaln_rmsnorm_scale_shift": [P, P, P, P, P, I, I, I, I, I, F, P],
+        "adaln_residual_gate_rmsnorm_scale_shift": [P, P, P, P, P, P, P, P, I, I, I, I, I, I, F, P],
+        "adaln_check_layernorm_modulate": [P, P, P, P, I, I, I, I, I, F],
+        "adaln_check_rmsnorm_scale_shift": [P, P, P, P, P, I, I, I, I, I, F],
+        "adaln_check_residual_gate_rmsnorm_scale_shift": [P, P, P, P, P, P, P, P, I, I, I, I, I, I,
+                                                          F],
+        "adaln_reduction_layout": [I, ctypes.POINTER(S), ctypes.POINTER(S), ctypes.POINTER(S)],
+        "adaln_diag_round_bf16": [P, P, I, P],
+        "adaln_diag_finalize": [P, P, I, F, P],
+    }
+    for name, args in sig.items():
+        fn = getattr(lib, name)
+        fn.argtypes = args
+        fn.restype = S
+    lib.adaln_status_string.argtypes = [S]
+    lib.adaln_status_string.restype = ctypes.c_char_p
+    lib.adaln_abi_version.argtypes = []
+    lib.adaln_abi_version.restype = S
+    if lib.adaln_abi_version() != ABI_VERSION:
+        raise RuntimeError(f"libadaln ABI {lib.adaln_abi_version()} != binding ABI {ABI_VERSION}")
+    _lib = lib
+    return lib
+
+
+def _status_text(status: int) -> str:
+    try:
+        return load_library().adaln_status_string(int(status)).decode()
+    except Exception:  # pragma: no cover - library missing while formatting an error
+        return "?"
+
+
+def _check(status: int, what: str):
+    if status != 0:
+        raise AdalnError(status, what)
+
+
+# ---------------------------------------------------------------------------
+# marshalling helpers
+# ---------------------------------------------------------------------------
+def _stream(stream):
+    if stream is None:
+        return ctypes.c_void_p(torch.cuda.current_stream().cuda_stream)
+    if isinstance(stream, torch.cuda.Stream):
+        return ctypes.c_void_p(stream.cuda_stream)
+    return ctypes.c_void_p(int(stream))
+
+
+def _act(t: torch.Tensor, name: str):
+    if t.dtype != torch.bfloat16 or t.dim() != 3 or not t.is_contiguous():
+        raise ValueError(f"{name}: expected a contiguous bfloat16 [B,T,H] tensor")
+    return t
+
+
+def _vec(v: torch.Tensor, B: int, H: int, name: str):
+    """Pointer and batch stride (elements) of a per-batch vector [B,H], [1,H] or [H]."""
+    if v.dtype != torch.bfloat16:
+        raise ValueError(f"{name}: expected bfloat16")
+    if v.dim() == 1:
+        v = v.unsqueeze(0)
+    if v.dim() != 2 or v.size(1) != H or v.stride(1) != 1 or v.size(0) not in (1, B):
+        raise ValueError(f"{name}: expected [B,H], [1,H] or [H] with unit inner stride")
+    bstride = v.stride(0) if (v.size(0) == B and B > 1) else 0
+    return v.data_ptr(), bstride
+
+
+def _ptr(t):
+    return None if t is None else t.data_ptr()
+
+
+def _eps(eps: float) -> float:
+    return float(torch.tensor(eps, dtype=torch.float32).item())
+
+
+# ---------------------------------------------------------------------------
+# entry points (same names as the C ABI)
+# ---------------------------------------------------------------------------
+def adaln_layernorm_modulate(x, scale, shift, eps: float = 1e-6, out=None, stream=None):
+    """y = LayerNorm(x) * (1 + scale[b]) + shift[b] (no affine)."""
+    lib = load_library()
+    _act(x, "x")
+    B, T, H = x.shape
+    sp, sbs = _vec(scale, B, H, "scale")
+    hp, hbs = _vec(shift, B, H, "shift")
+    y = torch.empty_like(x) if out is None else _act(out, "out")
+    _check(lib.adaln_layernorm_modulate(x.data_ptr(), sp, hp, y.data_ptr(), B, T, H, sbs, hbs,
+                                        _eps(eps), _stream(stream)), "adaln_layernorm_modulate")
+    return y
+
+
+def adaln_rmsnorm_scale_shift(x, weight, scale, shift, eps: float = 1e-6, out=None, stream=None):
+    """y = RMSNorm(x) * (1 + scale[b]) + shift[b]; weight None means one."""
+    lib = load_library()
+    _act(x, "x")
+    B, T, H = x.shape
+    if weight is not None and (weight.dtype != torch.bfloat16 or weight.numel() != H
+                               or not weight.is_contiguous()):
+        raise ValueError("weight: expected a contiguous bfloat16 [H] tensor")
+    sp, sbs = _vec(scale, B, H, "scale")
+    hp, hbs = _vec(shift, B, H, "shift")
+    y = torch.empty_like(x) if out is None else _act(out, "out")
+    _check(lib.adaln_rmsnorm_scale_shift(x.data_ptr(), _ptr(weight), sp, hp, y.data_ptr(), B, T, H,
+                                         sbs, hbs, _eps(eps), _stream(stream)),
+           "adaln_rmsnorm_scale_shift")
+    return y
+
+
+def adaln_residual_gate_rmsnorm_scale_shift(res, x, gate, weight, scale, shift, eps: float = 1e-6,
+                                            out=None, r_out=None, stream=None):
+    """(r, y): r = res + gate[b] * x, y = RMSNorm(r) * (1 + scale[b]) + shift[b]."""
+    lib = load_library()
+    _act(res, "res")
+    _act(x, "x")
+    if res.shape != x.shape:
+        raise ValueError("res and x must have the same shape")
+    B, T, H = x.shape
+    if weight is not None and (weight.dtype != torch.bfloat16 or weight.numel() != H
+                               or not weight.is_contiguous()):
+        raise ValueError("weight: expected a contiguous bfloat16 [H] tensor")
+    gp, gbs = _vec(gate, B, H, "gate")
+    sp, sbs = _vec(scale, B, H, "scale")
+    hp, hbs = _vec(shift, B, H, "shift")
+    y = torch.empty_like(x) if out is None else _act(out, "out")
+    r = torch.empty_like(x) if r_out is None else _act(r_out, "r_out")
+    _check(lib.adaln_residual_gate_rmsnorm_scale_shift(
+        res.data_ptr(), x.data_ptr(), gp, _ptr(weight), sp, hp, r.data_ptr(), y.data_ptr(), B, T,
+        H, gbs, sbs, hbs, _eps(eps), _stream(stream)), "adaln_residual_gate_rmsnorm_scale_shift")
+    return r, y
+
+
+def adaln_check_layernorm_modulate(x_ptr, scale_ptr, shift_ptr, y_ptr, B, T, H, scale_bstride,
+                                   shift_bstride, eps=1e-6) -> int:
+    """Status code of the validation (raw pointers as ints; nothing is launched)."""
+    return load_library().adaln_check_layernorm_modulate(x_ptr, scale_ptr, shift_ptr, y_ptr, B, T,
+                                                         H, scale_bstride, shift_bstride, eps)
+
+
+def adaln_check_rmsnorm_scale_shift(x_ptr, weight_ptr, scale_ptr, shift_ptr, y_ptr, B, T, H,
+                                    scale_bstride, shift_bstride, eps=1e-6) -> int:
+    return load_library().adaln_check_rmsnorm_scale_shift(x_ptr, weight_ptr, scale_ptr, shift_ptr,
+                                                          y_ptr, B, T, H, scale_bstride,
+                                                          shift_bstride, eps)
+
+
+def adaln_check_residual_gate_rmsnorm_scale_shift(res_ptr, x_ptr, gate_ptr, weight_ptr, scale_ptr,
+                                                  shift_ptr, r_ptr, y_ptr, B, T, H, gate_bstride,
+                                                  scale_bstride, shift_bstride, eps=1e-6) -> int:
+    return load_library().adaln_check_residual_gate_rmsnorm_scale_shift(
+        res_ptr, x_ptr, gate_ptr, weight_ptr, scale_ptr, shift_ptr, r_ptr, y_ptr, B, T, H,
+        gate_bstride, scale_bstride, shift_bstride, eps)
+
+
+def adaln_reduction_layout(H: int):
+    """(waves per row, lanes per row, chunks per lane) of the fixed order for H."""
+    lib = load_library()
+    w, p, c = ctypes.c_int(), ctypes.c_int(), ctypes.c_int()
+    _check(lib.adaln_reduction_layout(H, ctypes.byref(w), ctypes.byref(p), ctypes.byref(c)),
+           "adaln_reduction_layout")
+    return w.value, p.value, c.value
+
+
+def adaln_status_string(status: int) -> str:
+    return load_library().adaln_status_string(int(status)).decode()
+
+
+def adaln_abi_version() -> int:
+    return load_library().adaln_abi_version()
+
+
+def adaln_diag_round_bf16(x: torch.Tensor, stream=None) -> torch.Tensor:
+    """Device bf16 rounding of a float32 tensor (the kernels' rounding step)."""
+    lib = load_library()
+    if x.dtype != torch.float32 or not x.is_contiguous():
+        raise ValueError("expected a contiguous float32 tensor")
+    out = torch.empty(x.shape, dtype=torch.bfloat16, device=x.device)
+    _check(lib.adaln_diag_round_bf16(x.data_ptr(), out.data_ptr(), x.numel(), _stream(stream)),
+           "adaln_diag_round_bf16")
+    return out
+
+
+def adaln_diag_finalize(x: torch.Tensor, eps: float = 1e-6, stream=None) -> torch.Tensor:
+    """Device rstd = RN(1/RN(sqrt(RN(x + eps)))) of a float32 tensor (the kernels' step)."""
+    lib = load_library()
+    if x.dtype != torch.float32 or not x.is_contiguous():
+        raise ValueError("expected a contiguous float32 tensor")
+    out = torch.empty_like(x)
+    _check(lib.adaln_diag_finalize(x.data_ptr(), out.data_ptr(), x.numel(), _eps(eps),
+                                   _stream(stream)), "adaln_diag_finalize")
+    return out

@@ -1,0 +1,179 @@
+"""Seeded synthetic inputs for the fused adaLN normalisation path.
+
+This module only draws random numbers and stores them as bfloat16 bit patterns
+(numpy ``uint16``).  It holds none of the method's arithmetic; the library and the
+CPU oracle both take their inputs from here.
+
+Recipe (shared by tests, the smoke check and the benchmark):
+  * every tensor has its own numpy ``PCG64`` stream seeded by
+    ``SeedSequence([seed, config_id, tensor_id])``;
+  * values are drawn as float64 standard normals, multiplied by sigma (a standard
+    deviation) and offset by mu in float64, cast to float32, then rounded to
+    bfloat16 (nearest-even) by torch's dtype conversion;
+  * outliers: ``round(frac * N)`` positions chosen without replacement are
+    multiplied by the factor in float32 before the bf16 rounding.
+
+Workload shapes follow the pages: the FLUX.1 adaLN site shapes (PR #34126 report,
+test snippet: hidden 3072, 4096 image + 512 text tokens, a CFG batch of 2), the
+ERNIE-Image shapes (PR #33854 report, tests: (1,4216,4096), (2,1140,4096),
+(1,128,2048)) and the contract docstring shapes in the sglang diffusion kernels
+guide (add-a-kernel workflow, step 4).
+"""
+from __future__ import annotations
+
+import dataclasses
+
+import numpy as np
+import torch
+
+TENSOR_IDS = {"x": 0, "scale": 1, "shift": 2, "gate": 3, "res": 4, "weight": 5, "mask": 6,
+              "tokens": 7, "class": 8}
+
+
+def _rng(seed: int, config_id: int, tensor: str) -> np.random.Generator:
+    return np.random.Generator(np.random.PCG64(np.random.SeedSequence(
+        [seed, config_id, TENSOR_IDS[tensor]])))
+
+
+def f32_to_bf16_bits(a: np.ndarray) -> np.ndarray:
+    """float32 -> bf16 bit patterns via torch's conversion (nearest-even)."""
+    a = np.ascontiguousarray(a, dtype=np.float32)
+    t = torch.from_numpy(a).to(torch.bfloat16)
+    return t.view(torch.int16).numpy().view(np.uint16).copy()
+
+
+def bf16_bits_to_f32(b: np.ndarray) -> np.ndarray:
+    """bf16 bit patterns -> float32 values (exact widening)."""
+    return (np.asarray(b, dtype=np.uint16).astype(np.uint32) << 16).view(np.float32)
+
+
+def normal_bf16(rng: np.random.Generator, shape, sigma: float = 1.0, mu: float = 0.0,
+                outlier_frac: float = 0.0, outlier_factor: float = 1.0,
+                chunk: int = 1 << 24) -> np.ndarray:
+    """bf16 bits of mu + sigma*N(0,1), drawn in float64, optional outliers."""
+    shape = tuple(int(s) for s in shape)
+    n = int(np.prod(shape)) if shape else 1
+    out = np.empty(n, np.uint16)
+    for lo in range(0, n, chunk):
+        hi = min(n, lo + chunk)
+        v = rng.standard_normal(hi - lo) * sigma + mu
+        out[lo:hi] = f32_to_bf16_bits(v.astype(np.float32))
+    if outlier_frac > 0.0:
+        k = int(round(outlier_frac * n))
+        pos = rng.choice(n, size=k, replace=False)
+        v = bf16_bits_to_f32(out[pos]) * np.float32(outlier_factor)
+        out[pos] = f32_to_bf16_bits(v)
+    return out.reshape(shape)
+
+
+@dataclasses.dataclass
+class Workload:
+    """One synthetic invocation of an entry point (arrays are bf16 bits)."""
+    op: str                      # "ln" | "rms" | "rg"
+    name: str
+    x: np.ndarray                # [B,T,H]
+    scale: np.ndarray            # [B,H] (possibly a strided view)
+    shift: np.ndarray            # [B,H]
+    weight: np.ndarray | None = None  # [H] (rms / rg)
+    gate: np.ndarray | None = None    # [B,H] (rg)
+    res: np.ndarray | None = None     # [B,T,H] (rg)
+    eps: float = 1e-6
+
+    @property
+    def shape(self):
+        return self.x.shape
+
+    def algorithmic_bytes(self) -> int:
+        """HBM bytes the path must move: read x[,res], write y[,r] (bf16)."""
+        n = int(np.prod(self.x.shape))
+        return (8 if self.op == "rg" else 4) * n
+
+
+def _vecs(seed, cid, B, H, names, sigma=0.1):
+    return {n: normal_bf16(_rng(seed, cid, n), (B, H), sigma) for n in names}
+
+
+def config0(seed: int = 0) -> Workload:
+    """LayerNorm (no affine, eps 1e-6) + modulate, x [1,128,2048] ~ N(0,1),
+    scale/shift [1,2048] ~ 0.1*N(0,1)."""
+    B, T, H = 1, 128, 2048
+    v = _vecs(seed, 0, B, H, ["scale", "shift"])
+    return Workload("ln", "ln_1x128x2048", normal_bf16(_rng(seed, 0, "x"), (B, T, H)),
+                    v["scale"], v["shift"])
+
+
+def config1(seed: int = 0) -> Workload:
+    """RMSNorm (weight 1+0.02*N, eps 1e-6) + scale/shift, x [1,4216,4096] ~ N(0,1)
+    with 0.1% of entries multiplied by 50; scale/shift [1,4096] ~ 0.1*N."""
+    B, T, H = 1, 4216, 4096
+    v = _vecs(seed, 1, B, H, ["scale", "shift"])
+    w = normal_bf16(_rng(seed, 1, "weight"), (H,), 0.02, 1.0)
+    x = normal_bf16(_rng(seed, 1, "x"), (B, T, H), outlier_frac=0.001, outlier_factor=50.0)
+    return Workload("rms", "rms_1x4216x4096", x, v["scale"], v["shift"], weight=w)
+
+
+def config2(seed: int = 0) -> Workload:
+    """Residual-gate RMSNorm + scale/shift (CFG batch): res, x [2,1140,4096] ~ N(0,1);
+    gate/scale/shift [2,4096] ~ 0.1*N; no weight."""
+    B, T, H = 2, 1140, 4096
+    v = _vecs(seed, 2, B, H, ["scale", "shift", "gate"])
+    return Workload("rg", "rg_rms_2x1140x4096", normal_bf16(_rng(seed, 2, "x"), (B, T, H)),
+                    v["scale"], v["shift"], weight=None, gate=v["gate"],
+                    res=normal_bf16(_rng(seed, 2, "res"), (B, T, H)))
+
+
+def config3(seed: int = 0, site: str = "a") -> Workload:
+    """FLUX.1-like LayerNorm + modulate: site a x [2,4608,3072] (4096 image + 512
+    text tokens, CFG batch), site b x [1,4333,3072]; scale/shift [B,3072] ~ 0.1*N."""
+    if site == "a":
+        B, T, H, cid = 2, 4608, 3072, 3
+    else:
+        B, T, H, cid = 1, 4333, 3072, 33
+    v = _vecs(seed, cid, B, H, ["scale", "shift"])
+    return Workload("ln", f"ln_{B}x{T}x{H}", normal_bf16(_rng(seed, cid, "x"), (B, T, H)),
+                    v["scale"], v["shift"])
+
+
+def flux_chunk_views(seed: int, B: int, H: int, chunks: int, cid: int = 30):
+    """scale/shift as strided views of one [B, chunks*H] embedding, like
+    ``emb.chunk(chunks, dim=1)`` in the FLUX.1 test snippet: (emb, shift, scale)
+    with shift = part 0 and scale = part 1, batch stride chunks*H."""
+    emb = normal_bf16(_rng(seed, cid, "scale"), (B, chunks * H), 1.0)
+    return emb, emb[:, 0:H], emb[:, H:2 * H]
+
+
+@dataclasses.dataclass
+class StressSets:
+    """Batch-invariance stress workload: packed row-sets of one hidden size."""
+    x: np.ndarray            # [R, H] all sets' rows, packed
+    offsets: np.ndarray      # [S+1] row offsets of the sets
+    row_class: np.ndarray    # [R] 0: N(0,1), 1: 1e-3*N(0,1), 2: 1e3*N(0,1)
+    scale: np.ndarray        # [S, H] per-set modulation
+    shift: np.ndarray        # [S, H]
+    weight: np.ndarray       # [H] (RMSNorm variant), 1 + 0.02*N
+
+
+CLASS_SIGMA = (1.0, 1e-3, 1e3)
+
+
+def config4(seed: int = 0, n_sets: int = 256, max_tokens: int = 4096, H: int = 3072,
+            cid: int = 4) -> StressSets:
+    """256 packed row-sets, token counts uniform in [1, max_tokens], hidden 3072;
+    each row is N(0,1), 1e-3*N(0,1) or 1e3*N(0,1) with equal probability."""
+    tr = _rng(seed, cid, "tokens")
+    counts = tr.integers(1, max_tokens + 1, size=n_sets)
+    offsets = np.zeros(n_sets + 1, np.int64)
+    offsets[1:] = np.cumsum(counts)
+    R = int(offsets[-1])
+    cls = _rng(seed, cid, "class").integers(0, 3, size=R).astype(np.int8)
+    xr = _rng(seed, cid, "x")
+    x = np.empty((R, H), np.uint16)
+    step = max(1, (1 << 22) // H)
+    sig = np.array(CLASS_SIGMA, np.float64)
+    for lo in range(0, R, step):
+        hi = min(R, lo + step)
+        v = xr.standard_normal((hi - lo, H)) * sig[cls[lo:hi]][:, None]
+        x[lo:hi] = f32_to_bf16_bits(v.astype(np.float32))
+    v = _vecs(seed, cid, n_sets, H, ["scale", "shift"])
+    w = normal_bf16(_rng(seed, cid, "weight"), (H,), 0.02, 1.0)
+    return StressSets(x, offsets, cls, v["scale"], v["shift"], w)

@@ -1,0 +1,158 @@
+/*
+ * adaln.h -- C ABI of libadaln: fused adaLN normalisation for AMD MI355X (gfx950).
+ *
+ * The three compute entry points fuse a row normalisation (LayerNorm without
+ * affine parameters, or RMSNorm with an optional weight) with the adaLN
+ * modulate epilogue  y = norm(x) * (1 + scale[b]) + shift[b]  that diffusion
+ * transformers run at every adaLN site, optionally preceded by the residual-gate
+ * prologue  r = res + gate[b] * x.
+ *
+ * Sources, cited by page title and section:
+ *  - FLUX.1 PR report "route the adaLN LN+modulate sites through the bit-exact
+ *    fused LayerNorm+modulate kernel" (sglang #34126): the LayerNorm+modulate
+ *    operation (source snippet of flux.py), its eager semantics (test snippet,
+ *    `_eager`: LayerNorm(hidden, eps=1e-6, elementwise_affine=False), then
+ *    norm(x) * (1 + scale[:, None]) + shift[:, None]), the site shapes and the
+ *    strided `emb.chunk` modulation views, and the kernel contract
+ *    (implementation item 4; related PRs: hidden % 4 == 0, hidden <= 8192).
+ *  - ERNIE-Image PR report "fused RMSNorm+scale/shift bit-exact kernel"
+ *    (sglang #33854): the RMSNorm+scale/shift operation and its residual-gate
+ *    variant that also returns the residual stream (implementation items 1-2).
+ *  - sglang diffusion kernels guide, "selection matrix / Norm + scale/shift":
+ *    the rounding points of the chain; "entry-point protocol": unsupported
+ *    input raises (here: returns a status), it never degrades silently.
+ *  - Batch-invariance article (vLLM), section 3 (RMSNorm): the reduction layout
+ *    depends on the hidden size only, never on the number of rows.
+ *
+ * Numerics (identical bits on every call, for every batch composition):
+ *   every binary32 operation is rounded to nearest-even with no FMA
+ *   contraction; sqrt and divide are correctly rounded; denormals are kept.
+ *   The reduction order is a function of H only:
+ *     W = 1 wave (64 lanes) per row if H < 4096, else W = 4 waves (256 lanes);
+ *     P = 64W lanes; C = ceil(H / 8P) chunks; lane t owns the columns
+ *     b*8P + 8t + v (b < C, v < 8) and visits them b-major, v-minor;
+ *     lane partials are folded by a butterfly over the lane index with distances
+ *     1, 2, ..., P/2, each step combining (partial of lane t&~k, partial of
+ *     lane t|k) in that order.
+ *   RMS statistic: s = s + RN(x*x) per lane, fold by +; rstd =
+ *     RN(1 / RN(sqrt(RN(RN(S / H) + eps)))).
+ *   LN statistic: per-lane Welford with the count's rounded reciprocal
+ *     (mean += RN(d * RN(1/n)), M2 += RN(d * RN(x - mean))), folded by the
+ *     Chan pairwise combine; var = RN(M2 / H); rstd as for RMS.
+ *   Norm output (bf16, rounded once): LN RN(RN(x - mean) * rstd);
+ *     RMS RN(RN(x * rstd) * RN(w + 0)).
+ *   Modulate: a = bf16(1 + scale); p = bf16(yn * a); y = bf16(p + shift).
+ *   Residual gate: g = bf16(gate * x); r = bf16(res + g); r feeds the norm.
+ *
+ * Conventions shared by all entry points:
+ *  - Tensors are raw bf16 bit patterns (adaln_bf16).  x, res, y, r are
+ *    contiguous row-major [B, T, H]; row index = b*T + t.
+ *  - Per-batch vectors scale / shift / gate have unit inner stride; row b starts
+ *    at ptr + b * <name>_bstride elements.  A batch stride of 0 shares one
+ *    vector across the batch; otherwise it must be >= H.  Views such as
+ *    emb.chunk(k, dim=1) of a [B, k*H] embedding are accepted without a copy.
+ *    weight is a contiguous [H] vector; NULL means a weight of one.
+ *  - Requirements: 8 <= H <= 8192, H % 8 == 0 (16-byte vectors of 8 bf16);
+ *    every pointer 16-byte aligned; batch strides >= 0 and % 8 == 0; B, T >= 0;
+ *    eps finite and >= 0.  B*T == 0 is a successful no-op (pointers unchecked).
+ *  - Outputs (y, r) may not overlap any input or each other.
+ *  - Ownership: the caller owns every buffer; the library never allocates,
+ *    frees or synchronises.  Work is enqueued on `hip_stream` (a hipStream_t;
+ *    NULL = the null stream) of the current device; pointers must be device
+ *    memory of that device.
+ *  - Errors: a non-OK status is returned before anything is launched, so the
+ *    outputs are untouched.  ADALN_ERR_LAUNCH reports a failed launch (for
+ *    example no gfx950 device).  Thread-safe and reentrant (no global state).
+ */
+#ifndef ADALN_H
+#define ADALN_H
+
+#include <stdint.h>
+
+#ifdef __cplusplus
+extern "C" {
+#endif
+
+#define ADALN_ABI_VERSION 1
+
+typedef uint16_t adaln_bf16; /* raw bfloat16 bits */
+
+typedef enum adaln_status {
+    ADALN_OK = 0,
+    ADALN_ERR_NULL = 1,    /* a required pointer is NULL */
+    ADALN_ERR_SHAPE = 2,   /* H outside [8, 8192] or H % 8 != 0, B < 0, T < 0, size overflow */
+    ADALN_ERR_ALIGN = 3,   /* a pointer is not 16-byte aligned */
+    ADALN_ERR_STRIDE = 4,  /* a batch stride is negative, not % 8, or in (0, H) */
+    ADALN_ERR_OVERLAP = 5, /* an output overlaps an input or the other output */
+    ADALN_ERR_VALUE = 6,   /* eps is negative or not finite */
+    ADALN_ERR_LAUNCH = 7   /* the HIP launch failed */
+} adaln_status;
+
+/* y = LayerNorm(x) * (1 + scale[b]) + shift[b]; LayerNorm without affine
+ * parameters, biased variance (FLUX.1 PR report, flux.py and test snippets). */
+adaln_status adaln_layernorm_modulate(const adaln_bf16* x, const adaln_bf16* scale,
+                                      const adaln_bf16* shift, adaln_bf16* y, int64_t B, int64_t T,
+                                      int64_t H, int64_t scale_bstride, int64_t shift_bstride,
+                                      float eps, void* hip_stream);
+
+/* y = RMSNorm(x) * (1 + scale[b]) + shift[b]; RMSNorm(x) = x * rstd * w, with
+ * weight NULL meaning w = 1 (ERNIE-Image PR report, kernel snippet). */
+adaln_status adaln_rmsnorm_scale_shift(const adaln_bf16* x, const adaln_bf16* weight,
+                                       const adaln_bf16* scale, const adaln_bf16* shift,
+                                       adaln_bf16* y, int64_t B, int64_t T, int64_t H,
+                                       int64_t scale_bstride, int64_t shift_bstride, float eps,
+                                       void* hip_stream);
+
+/* r = res + gate[b] * x (written to r_out), then
+ * y = RMSNorm(r) * (1 + scale[b]) + shift[b] (ERNIE-Image PR report,
+ * implementation item 2: the gated site returns the bit-identical residual). */
+adaln_status adaln_residual_gate_rmsnorm_scale_shift(
+    const adaln_bf16* res, const adaln_bf16* x, const adaln_bf16* gate, const adaln_bf16* weight,
+    const adaln_bf16* scale, const adaln_bf16* shift, adaln_bf16* r_out, adaln_bf16* y, int64_t B,
+    int64_t T, int64_t H, int64_t gate_bstride, int64_t scale_bstride, int64_t shift_bstride,
+    float eps, void* hip_stream);
+
+/* Predicates: the validation of the entry point of the same name, without a
+ * launch (the `can_use_*` predicate of the kernels guide's entry-point protocol).
+ * They never touch the GPU. */
+adaln_status adaln_check_layernorm_modulate(const adaln_bf16* x, const adaln_bf16* scale,
+                                            const adaln_bf16* shift, const adaln_bf16* y,
+                                            int64_t B, int64_t T, int64_t H,
+                                            int64_t scale_bstride, int64_t shift_bstride,
+                                            float eps);
+adaln_status adaln_check_rmsnorm_scale_shift(const adaln_bf16* x, const adaln_bf16* weight,
+                                             const adaln_bf16* scale, const adaln_bf16* shift,
+                                             const adaln_bf16* y, int64_t B, int64_t T, int64_t H,
+                                             int64_t scale_bstride, int64_t shift_bstride,
+                                             float eps);
+adaln_status adaln_check_residual_gate_rmsnorm_scale_shift(
+    const adaln_bf16* res, const adaln_bf16* x, const adaln_bf16* gate, const adaln_bf16* weight,
+    const adaln_bf16* scale, const adaln_bf16* shift, const adaln_bf16* r_out,
+    const adaln_bf16* y, int64_t B, int64_t T, int64_t H, int64_t gate_bstride,
+    int64_t scale_bstride, int64_t shift_bstride, float eps);
+
+/* The fixed reduction layout for H: waves per row, lanes per row, chunks per
+ * lane.  ADALN_ERR_SHAPE for an unsupported H; out-pointers may be NULL. */
+adaln_status adaln_reduction_layout(int64_t H, int* waves_per_row, int* lanes_per_row,
+                                    int* chunks_per_lane);
+
+/* Static English text for a status (never NULL). */
+const char* adaln_status_string(adaln_status status);
+
+/* ADALN_ABI_VERSION of the built library. */
+int adaln_abi_version(void);
+
+/* Diagnostics: run the exact device steps the kernels use, elementwise, so that
+ * tests can check them exhaustively against host IEEE arithmetic.
+ *  - adaln_diag_round_bf16: out[i] = bf16(in[i]) (nearest-even).
+ *  - adaln_diag_finalize:   out[i] = RN(1 / RN(sqrt(RN(in[i] + eps)))).
+ * n >= 0 elements of device memory, 4-byte aligned; ADALN_ERR_* as above. */
+adaln_status adaln_diag_round_bf16(const float* in, adaln_bf16* out, int64_t n, void* hip_stream);
+adaln_status adaln_diag_finalize(const float* in, float* out, int64_t n, float eps,
+                                 void* hip_stream);
+
+#ifdef __cplusplus
+}
+#endif
+
+#endif /* ADALN_H */

@@ -1,0 +1,607 @@
+"""Pins of the CPU oracle to things other than itself (no GPU needed).
+
+Each test ties a part of the oracle to an independent authority:
+  * the pages' round-to-nearest-even example (tests/golden/rne_ties.txt);
+  * torch's eager bf16 ops, which are the very chain the pages define as the
+    semantics of the modulate and residual-gate steps (FLUX PR report, test
+    snippet `_eager`; sglang kernels guide, selection matrix);
+  * the fp64 two-pass definition of LayerNorm / RMSNorm (batch-invariance article,
+    section 3.1 for RMS; plain LayerNorm without affine for LN) within a bound;
+  * closed forms, exact invariants, exhaustive enumeration of tiny rows, and
+    worked examples derived by hand in integer arithmetic for the fixed order.
+"""
+import os
+import zlib
+
+import numpy as np
+import pytest
+import torch
+
+from oracle import oracle as O
+from diffusion_dit_adaln_amd import synth
+
+GOLDEN = os.path.join(os.path.dirname(__file__), "golden")
+EPS = 1e-6
+EPS32 = float(np.float32(EPS))
+
+
+def f32(bits):
+    return np.array(bits, np.uint32).view(np.float32)
+
+
+def bits32(v):
+    return np.asarray(v, np.float32).view(np.uint32)
+
+
+def widen(b):
+    return synth.bf16_bits_to_f32(b)
+
+
+def torch_bf16(bits):
+    return torch.from_numpy(np.ascontiguousarray(bits, np.uint16).view(np.int16)).view(torch.bfloat16)
+
+
+def from_torch(t):
+    return t.contiguous().view(torch.int16).numpy().view(np.uint16)
+
+
+# --------------------------------------------------------------------------
+# bf16 rounding
+# --------------------------------------------------------------------------
+def test_rne_ties_from_page():
+    rows = []
+    with open(os.path.join(GOLDEN, "rne_ties.txt")) as fh:
+        for line in fh:
+            line = line.split("#")[0].strip()
+            if line:
+                a, b = line.split()[:2]
+                rows.append((int(a, 16), int(b, 16)))
+    inp = f32([r[0] for r in rows])
+    got = O.round_bf16(inp)
+    assert [hex(g) for g in got] == [hex(r[1]) for r in rows]
+
+
+def test_round_bf16_matches_torch_on_structured_sample():
+    hi = np.arange(1 << 16, dtype=np.uint32) << 16
+    lows = np.array([0x0000, 0x0001, 0x7FFF, 0x8000, 0x8001, 0xFFFF, 0x4000, 0xC000], np.uint32)
+    rng = np.random.default_rng(7)
+    lows = np.concatenate([lows, rng.integers(0, 1 << 16, 8).astype(np.uint32)])
+    u = (hi[:, None] | lows[None, :]).reshape(-1)
+    x = u.view(np.float32)
+    got = O.round_bf16(x)
+    ref = from_torch(torch.from_numpy(x.copy()).to(torch.bfloat16))
+    nan = np.isnan(x)
+    assert np.array_equal(got[~nan], ref[~nan])
+    # NaN stays NaN with its sign
+    g = got[nan]
+    assert np.all((g & 0x7F80) == 0x7F80) and np.all((g & 0x007F) != 0)
+    assert np.array_equal(g >> 15, (u[nan] >> 31).astype(np.uint16))
+
+
+# --------------------------------------------------------------------------
+# modulate and residual-gate steps against torch eager bf16 (the defined chain)
+# --------------------------------------------------------------------------
+def _finite_bf16_all():
+    b = np.arange(1 << 16, dtype=np.uint32).astype(np.uint16)
+    return b[np.isfinite(widen(b))]
+
+
+def test_one_plus_scale_exhaustive_vs_eager():
+    s = _finite_bf16_all()
+    zeros = np.zeros_like(s)
+    one = np.full_like(s, 0x3F80)
+    # modulate(yn=1, scale=s, shift=0) = round(round(1 + s) * 1) + 0 = round(1 + s)
+    got = O.modulate(one, s, zeros)
+    ref = from_torch((1 + torch_bf16(s)) * torch_bf16(one) + torch_bf16(zeros))
+    assert np.array_equal(got, ref)
+
+
+@pytest.mark.parametrize("seed", [0, 1])
+def test_modulate_vs_eager_chain(seed):
+    rng = np.random.default_rng(seed)
+    fin = _finite_bf16_all()
+    n = 1 << 21
+    yn = rng.choice(fin, n)
+    sc = rng.choice(fin, n)
+    sh = rng.choice(fin, n)
+    # also realistic magnitudes: |scale| ~ 0.1, yn ~ N(0,1), shift ~ 0.1
+    yn[: n // 2] = synth.normal_bf16(rng, (n // 2,), 1.0)
+    sc[: n // 2] = synth.normal_bf16(rng, (n // 2,), 0.1)
+    sh[: n // 2] = synth.normal_bf16(rng, (n // 2,), 0.1)
+    got = O.modulate(yn, sc, sh)
+    ref = from_torch(torch_bf16(yn) * (1 + torch_bf16(sc)) + torch_bf16(sh))
+    nan = np.isnan(widen(ref))
+    assert np.array_equal(got[~nan], ref[~nan])
+    assert np.all(np.isnan(widen(got[nan])))
+
+
+def test_products_and_sums_exhaustive_rows_vs_eager():
+    # every finite bf16 yn against a spread of factors (products), then every
+    # finite bf16 against a spread of addends (sums)
+    fin = _finite_bf16_all()
+    zeros = np.zeros_like(fin)
+    for sbits in [0x0000, 0x3DCD, 0xBDCD, 0x3F00, 0xBF40, 0x4049, 0x0001, 0x3F7F]:
+        s = np.full_like(fin, sbits)
+        got = O.modulate(fin, s, zeros)
+        ref = from_torch(torch_bf16(fin) * (1 + torch_bf16(s)) + torch_bf16(zeros))
+        assert np.array_equal(got, ref), hex(sbits)
+    for hbits in [0x3DCD, 0xBDCD, 0x8000, 0x4380, 0x0001, 0xC2C8]:
+        h = np.full_like(fin, hbits)
+        got = O.modulate(fin, zeros, h)
+        ref = from_torch(torch_bf16(fin) * (1 + torch_bf16(zeros)) + torch_bf16(h))
+        nan = np.isnan(widen(ref))
+        assert np.array_equal(got[~nan], ref[~nan]), hex(hbits)
+
+
+def test_gate_residual_vs_eager_chain():
+    rng = np.random.default_rng(3)
+    fin = _finite_bf16_all()
+    n = 1 << 21
+    res = rng.choice(fin, n)
+    x = rng.choice(fin, n)
+    g = rng.choice(fin, n)
+    res[: n // 2] = synth.normal_bf16(rng, (n // 2,), 1.0)
+    x[: n // 2] = synth.normal_bf16(rng, (n // 2,), 1.0)
+    g[: n // 2] = synth.normal_bf16(rng, (n // 2,), 0.1)
+    got = O.gate_residual(res, x, g)
+    ref = from_torch(torch_bf16(res) + torch_bf16(g) * torch_bf16(x))
+    nan = np.isnan(widen(ref))
+    assert np.array_equal(got[~nan], ref[~nan])
+
+
+# --------------------------------------------------------------------------
+# accuracy against the fp64 two-pass definition
+# --------------------------------------------------------------------------
+def ulp_bf16(v):
+    """bf16 spacing at |v| (2^-133 below the normal range)."""
+    v = np.abs(np.asarray(v, np.float64))
+    _, e = np.frexp(v)
+    u = np.ldexp(1.0, e - 8)
+    return np.where(v < 2.0 ** -126, 2.0 ** -133, u)
+
+
+# Bound for LayerNorm outputs: 2 bf16 ulp of the exact value, plus the fp32
+# statistics' own error carried through (x - mean) * rstd.  The mean and the
+# squared-deviation sums are evaluated in binary32 over at most 64 elements per
+# lane plus an 8-level combine, so their absolute error is a small multiple of
+# u32 = 2^-24 times (|mean| + sigma); KAPPA = 256 covers it with margin.
+KAPPA = 256.0
+U32 = 2.0 ** -24
+
+
+def ln_ref64(x_bits, eps):
+    x = widen(x_bits).astype(np.float64)
+    mu = x.mean(axis=-1, keepdims=True)
+    var = ((x - mu) ** 2).mean(axis=-1, keepdims=True)
+    inv = 1.0 / np.sqrt(var + eps)
+    ref = (x - mu) * inv
+    floor = KAPPA * U32 * (np.abs(mu) + np.sqrt(var)) * inv
+    return ref, floor, var
+
+
+def rms_ref64(x_bits, w_bits, eps):
+    x = widen(x_bits).astype(np.float64)
+    ms = (x * x).mean(axis=-1, keepdims=True)
+    w = 1.0 if w_bits is None else widen(w_bits).astype(np.float64)
+    ref = x / np.sqrt(ms + eps) * w
+    return ref, np.zeros_like(ref) + 2.0 ** -133
+
+
+def assert_within(yn_bits, ref, floor, what):
+    got = widen(yn_bits).astype(np.float64)
+    err = np.abs(got - ref)
+    tol = 2.0 * ulp_bf16(ref) + floor
+    bad = err > tol
+    assert not bad.any(), (what, int(bad.sum()), float((err / tol).max()))
+
+
+def _rows(kind, B, T, H, seed):
+    rng = np.random.default_rng(seed)
+    if kind == "normal":
+        return synth.normal_bf16(rng, (B, T, H))
+    if kind == "outliers":
+        return synth.normal_bf16(rng, (B, T, H), outlier_frac=0.001, outlier_factor=50.0)
+    if kind == "tiny":        # variance ~ eps: the eps term matters
+        return synth.normal_bf16(rng, (B, T, H), 1e-3)
+    if kind == "huge":
+        return synth.normal_bf16(rng, (B, T, H), 1e3)
+    if kind == "offset":      # LayerNorm cancellation: mean 1e3, sigma 1
+        return synth.normal_bf16(rng, (B, T, H), 1.0, 1e3)
+    if kind == "mixed":
+        cls = rng.integers(0, 3, size=(B, T, 1))
+        sig = np.array([1.0, 1e-3, 1e3])[cls]
+        v = rng.standard_normal((B, T, H)) * sig
+        return synth.f32_to_bf16_bits(v.astype(np.float32)).reshape(B, T, H)
+    raise ValueError(kind)
+
+
+SHAPES = [(1, 3, 8), (2, 5, 16), (1, 7, 24), (1, 9, 520), (2, 4, 2048), (1, 4, 3072),
+          (1, 3, 4088), (1, 3, 4096), (1, 2, 4104), (1, 2, 8192)]
+KINDS = ["normal", "outliers", "tiny", "huge", "offset", "mixed"]
+
+
+@pytest.mark.parametrize("shape", SHAPES, ids=lambda s: "x".join(map(str, s)))
+@pytest.mark.parametrize("kind", KINDS)
+def test_layernorm_accuracy_fp64(shape, kind):
+    B, T, H = shape
+    x = _rows(kind, B, T, H, zlib.crc32(repr((kind, shape)).encode()) % 1000)
+    z = np.zeros((B, H), np.uint16)
+    _, yn, st = O.layernorm_modulate(x, z, z, EPS, want_norm=True, want_stats=True)
+    ref, floor, var = ln_ref64(x, EPS32)
+    assert_within(yn, ref, floor, "ln")
+    assert np.all(st[:, 1] >= 0.0) and np.all(st[:, 2] >= 0.0)   # M2 and var never negative
+
+
+@pytest.mark.parametrize("shape", SHAPES, ids=lambda s: "x".join(map(str, s)))
+@pytest.mark.parametrize("kind", ["normal", "outliers", "tiny", "huge", "mixed"])
+@pytest.mark.parametrize("with_weight", [True, False])
+def test_rmsnorm_accuracy_fp64(shape, kind, with_weight):
+    B, T, H = shape
+    x = _rows(kind, B, T, H, zlib.crc32(repr((kind, shape, 1)).encode()) % 1000)
+    w = synth.normal_bf16(np.random.default_rng(5), (H,), 0.02, 1.0) if with_weight else None
+    z = np.zeros((B, H), np.uint16)
+    _, yn = O.rmsnorm_scale_shift(x, w, z, z, EPS, want_norm=True)
+    ref, floor = rms_ref64(x, w, EPS32)
+    assert_within(yn, ref, floor, "rms")
+
+
+def test_residual_gate_norm_input_is_r():
+    B, T, H = 2, 5, 4096
+    rng = np.random.default_rng(11)
+    res = synth.normal_bf16(rng, (B, T, H))
+    x = synth.normal_bf16(rng, (B, T, H))
+    g = synth.normal_bf16(rng, (B, H), 0.1)
+    sc = synth.normal_bf16(rng, (B, H), 0.1)
+    sh = synth.normal_bf16(rng, (B, H), 0.1)
+    r, y, yn = O.residual_gate_rmsnorm_scale_shift(res, x, g, None, sc, sh, EPS, want_norm=True)
+    ref_r = from_torch(torch_bf16(res) + torch_bf16(g)[:, None, :] * torch_bf16(x))
+    assert np.array_equal(r, ref_r)
+    ref, floor = rms_ref64(r, None, EPS32)
+    assert_within(yn, ref, floor, "rg")
+    # the RMS tail on r equals the plain RMS entry point run on r
+    y2 = O.rmsnorm_scale_shift(r, None, sc, sh, EPS)
+    assert np.array_equal(y, y2)
+
+
+# --------------------------------------------------------------------------
+# the full output is the modulate chain applied to the norm output
+# --------------------------------------------------------------------------
+@pytest.mark.parametrize("op", ["ln", "rms"])
+def test_output_composes_norm_and_modulate(op):
+    B, T, H = 2, 6, 3072
+    rng = np.random.default_rng(21)
+    x = synth.normal_bf16(rng, (B, T, H))
+    sc = synth.normal_bf16(rng, (B, H), 0.1)
+    sh = synth.normal_bf16(rng, (B, H), 0.1)
+    if op == "ln":
+        y, yn = O.layernorm_modulate(x, sc, sh, EPS, want_norm=True)
+    else:
+        w = synth.normal_bf16(rng, (H,), 0.02, 1.0)
+        y, yn = O.rmsnorm_scale_shift(x, w, sc, sh, EPS, want_norm=True)
+    ref = from_torch(torch_bf16(yn) * (1 + torch_bf16(sc)[:, None, :]) + torch_bf16(sh)[:, None, :])
+    assert np.array_equal(y, ref)
+
+
+def test_strided_chunk_views_match_contiguous():
+    B, T, H = 2, 3, 3072
+    x = synth.normal_bf16(np.random.default_rng(2), (B, T, H))
+    emb, shift, scale = synth.flux_chunk_views(0, B, H, 6)
+    y1 = O.layernorm_modulate(x, scale, shift, EPS)
+    y2 = O.layernorm_modulate(x, np.ascontiguousarray(scale), np.ascontiguousarray(shift), EPS)
+    assert np.array_equal(y1, y2)
+
+
+# --------------------------------------------------------------------------
+# closed forms
+# --------------------------------------------------------------------------
+def _nonzero_bf16(rng, shape, sigma):
+    v = synth.normal_bf16(rng, shape, sigma)
+    v[(v & 0x7FFF) == 0] = 0x3DCD
+    return v
+
+
+@pytest.mark.parametrize("H", [8, 512, 3072, 4096, 8192])
+def test_constant_rows_layernorm_give_shift(H):
+    rng = np.random.default_rng(H)
+    consts = np.array([0.0, 1.0, -3.5, 1000.0, 1e-30, -65504.0, 2.0 ** -130], np.float32)
+    x = np.repeat(synth.f32_to_bf16_bits(consts)[:, None], H, axis=1)[None]
+    T = x.shape[1]
+    sc = synth.normal_bf16(rng, (1, H), 0.1)
+    sh = _nonzero_bf16(rng, (1, H), 0.1)
+    y, yn, st = O.layernorm_modulate(x, sc, sh, EPS, want_norm=True, want_stats=True)
+    assert np.all(yn == 0)                                   # +0 exactly
+    assert np.array_equal(y, np.broadcast_to(sh, (1, T, H)))
+    assert np.all(st[:, 1] == 0.0)                           # M2 = 0
+    assert np.array_equal(st[:, 0], widen(x[0, :, 0]) + np.float32(0.0))   # mean = c (+0 for 0)
+
+
+@pytest.mark.parametrize("H", [8, 2048, 4096])
+def test_zero_rows_rmsnorm_give_shift(H):
+    rng = np.random.default_rng(H + 1)
+    x = np.zeros((1, 3, H), np.uint16)
+    w = synth.normal_bf16(rng, (H,), 0.02, 1.0)
+    sc = synth.normal_bf16(rng, (1, H), 0.1)
+    sh = _nonzero_bf16(rng, (1, H), 0.1)
+    y = O.rmsnorm_scale_shift(x, w, sc, sh, EPS)
+    assert np.array_equal(y, np.broadcast_to(sh, y.shape))
+
+
+@pytest.mark.parametrize("op", ["ln", "rms"])
+def test_scale_minus_one_gives_shift(op):
+    H = 3072
+    rng = np.random.default_rng(8)
+    x = synth.normal_bf16(rng, (1, 4, H))
+    sc = np.full((1, H), 0xBF80, np.uint16)   # -1.0
+    sh = _nonzero_bf16(rng, (1, H), 0.1)
+    if op == "ln":
+        y = O.layernorm_modulate(x, sc, sh, EPS)
+    else:
+        y = O.rmsnorm_scale_shift(x, None, sc, sh, EPS)
+    assert np.array_equal(y, np.broadcast_to(sh, y.shape))
+
+
+def _unit_rows(rng, T, H):
+    """Rows with exact mean 0 and exact mean square 1: balanced +-1 rows, and
+    rows of 10x(+-0.5) and 6x(+-1.5) per 16 columns with balanced signs."""
+    rows = []
+    for t in range(T):
+        if t % 2 == 0:
+            r = np.array([1.0, -1.0] * (H // 2), np.float32)
+        else:
+            blk = np.array([0.5] * 5 + [-0.5] * 5 + [1.5] * 3 + [-1.5] * 3, np.float32)
+            r = np.tile(blk, H // 16)
+        rows.append(rng.permutation(r))
+    return synth.f32_to_bf16_bits(np.stack(rows))[None]
+
+
+@pytest.mark.parametrize("H", [16, 1024, 3072, 4096, 8192])
+@pytest.mark.parametrize("op", ["ln", "rms"])
+def test_unit_rows_with_zero_modulation_return_x(H, op):
+    rng = np.random.default_rng(H)
+    x = _unit_rows(rng, 6, H)
+    z = np.zeros((1, H), np.uint16)
+    if op == "ln":
+        y = O.layernorm_modulate(x, z, z, EPS)
+    else:
+        y = O.rmsnorm_scale_shift(x, None, z, z, EPS)
+    assert np.array_equal(y, x)
+
+
+# --------------------------------------------------------------------------
+# exact invariants
+# --------------------------------------------------------------------------
+@pytest.mark.parametrize("H", [24, 2048, 3072, 4096, 8192])
+@pytest.mark.parametrize("op", ["ln", "rms"])
+def test_sign_symmetry(H, op):
+    rng = np.random.default_rng(H + 3)
+    x = synth.normal_bf16(rng, (1, 8, H))
+    z = np.zeros((1, H), np.uint16)
+    run = (lambda a: O.layernorm_modulate(a, z, z, EPS, want_norm=True)[1]) if op == "ln" else \
+          (lambda a: O.rmsnorm_scale_shift(a, None, z, z, EPS, want_norm=True)[1])
+    yp = run(x)
+    yq = run(x ^ np.uint16(0x8000))
+    nz = (yp & 0x7FFF) != 0
+    assert np.array_equal(yq[nz], yp[nz] ^ np.uint16(0x8000))
+    assert np.all((yq[~nz] & 0x7FFF) == 0)
+
+
+@pytest.mark.parametrize("k", [-4, -2, -1, 1, 3])
+@pytest.mark.parametrize("op", ["ln", "rms"])
+def test_power_of_two_scaling_invariance(k, op):
+    # rows with statistic >= 32 before and after scaling: eps is absorbed and
+    # every operation scales exactly, so the norm output is unchanged.
+    H = 3072
+    rng = np.random.default_rng(40 + k)
+    x = synth.normal_bf16(rng, (1, 6, H), 1e3)
+    xs = synth.f32_to_bf16_bits(widen(x) * np.float32(2.0 ** k)).reshape(x.shape)
+    assert np.array_equal(widen(xs), widen(x) * np.float32(2.0 ** k))   # scaling was exact
+    z = np.zeros((1, H), np.uint16)
+    if op == "ln":
+        _, a, sa = O.layernorm_modulate(x, z, z, EPS, want_norm=True, want_stats=True)
+        _, b, sb = O.layernorm_modulate(xs, z, z, EPS, want_norm=True, want_stats=True)
+        assert np.all(sa[:, 2] >= 32) and np.all(sb[:, 2] >= 32)
+    else:
+        _, a, sa = O.rmsnorm_scale_shift(x, None, z, z, EPS, want_norm=True, want_stats=True)
+        _, b, sb = O.rmsnorm_scale_shift(xs, None, z, z, EPS, want_norm=True, want_stats=True)
+        assert np.all(sa[:, 1] >= 32) and np.all(sb[:, 1] >= 32)
+    assert np.array_equal(a, b)
+
+
+def test_rows_independent_of_batch():
+    B, T, H = 3, 5, 3072
+    rng = np.random.default_rng(9)
+    x = synth.normal_bf16(rng, (B, T, H))
+    sc = synth.normal_bf16(rng, (B, H), 0.1)
+    sh = synth.normal_bf16(rng, (B, H), 0.1)
+    y = O.layernorm_modulate(x, sc, sh, EPS)
+    for b in range(B):
+        for t in range(T):
+            y1 = O.layernorm_modulate(np.ascontiguousarray(x[b:b + 1, t:t + 1]), sc[b:b + 1],
+                                      sh[b:b + 1], EPS)
+            assert np.array_equal(y1[0, 0], y[b, t])
+
+
+# --------------------------------------------------------------------------
+# brute force over a tiny domain
+# --------------------------------------------------------------------------
+def _all_rows(alphabet, H):
+    a = synth.f32_to_bf16_bits(np.array(alphabet, np.float32))
+    idx = np.indices((len(a),) * H).reshape(H, -1).T
+    return np.ascontiguousarray(a[idx])
+
+
+@pytest.mark.parametrize("op", ["ln", "rms"])
+def test_brute_force_h8(op):
+    rows = _all_rows([0.0, 0.5, -1.0, 2.0, -3.0, 0.0625], 8)     # 6^8 = 1.68M rows
+    x = rows[None]
+    z = np.zeros((1, 8), np.uint16)
+    if op == "ln":
+        _, yn, st = O.layernorm_modulate(x, z, z, EPS, want_norm=True, want_stats=True)
+        ref, floor, _ = ln_ref64(x, EPS32)
+        assert np.all(st[:, 1] >= 0)
+    else:
+        _, yn = O.rmsnorm_scale_shift(x, None, z, z, EPS, want_norm=True)
+        ref, floor = rms_ref64(x, None, EPS32)
+    assert_within(yn, ref, floor, op)
+
+
+# --------------------------------------------------------------------------
+# the fixed order, pinned by worked examples (integer arithmetic by hand)
+# --------------------------------------------------------------------------
+def _row_with(H, entries):
+    v = np.zeros(H, np.float32)
+    for c, val in entries.items():
+        v[c] = val
+    return synth.f32_to_bf16_bits(v)[None, None]
+
+
+def _rms_S(x):
+    H = x.shape[-1]
+    z = np.zeros((1, H), np.uint16)
+    _, st = O.rmsnorm_scale_shift(x, None, z, z, EPS, want_stats=True)
+    return float(st[0, 0])
+
+
+def test_order_within_lane_is_v_then_b():
+    # H=1024: one wave, 64 lanes, 2 chunks.  Lane 0 owns columns 0..7 then
+    # 512..519.  Squares 1, 1, then 2^24: 1+1 = 2, 2 + 2^24 = 16777218 exactly.
+    # A chunk-major (b fastest) visit would add 1 + 2^24 first, which ties to
+    # even at 2^24, and the second 1 is lost the same way: S = 2^24.
+    x = _row_with(1024, {0: 1.0, 1: 1.0, 512: 4096.0})
+    assert O.layout(1024) == (1, 64, 2)
+    assert _rms_S(x) == 16777218.0
+
+
+def test_fold_is_adjacent_pair_butterfly():
+    # H=512: 64 lanes, 1 chunk, lane t owns 8t..8t+7.  Lane partials
+    # s0 = 2^24 (x[0]=4096), s1 = 0, s2 = 1 (x[16]=1), s3 = 1 (x[24]=1).
+    # Distances 1,2,...: (s0+s1) = 2^24, (s2+s3) = 2, then 2^24+2 exactly.
+    # A sequential lane sum or a fold starting at distance 32 pairs 2^24 with a
+    # single 1 first and ends at 2^24.
+    x = _row_with(512, {0: 4096.0, 16: 1.0, 24: 1.0})
+    assert _rms_S(x) == 16777218.0
+
+
+def test_cross_wave_combine_is_pairwise():
+    # H=4096: 4 waves x 64 lanes, 2 chunks; lane 64w owns column 512w in chunk 0.
+    # Wave sums w0 = 2^24, w1 = 0, w2 = 1 (x[1024]), w3 = 1 (x[1536]):
+    # ((w0+w1) + (w2+w3)) = 2^24 + 2; a running sum over waves gives 2^24.
+    x = _row_with(4096, {0: 4096.0, 1024: 1.0, 1536: 1.0})
+    assert O.layout(4096) == (4, 256, 2)
+    assert _rms_S(x) == 16777218.0
+
+
+def test_welford_combine_operand_order():
+    # H=16: lane 0 holds eight 1.0, lane 1 eight c = 3*2^-25 (bf16 0x33C0).
+    # Per lane: (8, 1, 0) and (8, c, 0).  combine(lo=lane0, hi=lane1):
+    #   delta = RN(c - 1) = -(1 - 1.5*2^-24), a tie between 1-2^-24 (odd) and
+    #           1-2^-23 (even)            -> -(1 - 2^-23)
+    #   wb    = RN(8/16) = 1/2;  delta*wb = -(1/2 - 2^-24) exactly
+    #   mean  = RN(1 - 1/2 + 2^-24) = 1/2 + 2^-24           = 0x3F000001
+    #   M2    = RN(RN(delta^2) * RN(8 * 1/2)); delta^2 = 1 - 2^-22 + 2^-46
+    #           -> 1 - 2^-22;  times 4 = 4 - 2^-20            = 0x407FFFFC
+    #   var   = RN(M2 / 16) = 1/4 - 2^-24                      = 0x3E7FFFFC
+    # The reversed operand order gives mean RN(c + 1/2 - 2^-24) = 1/2 (a tie).
+    x = np.zeros((1, 1, 16), np.uint16)
+    x[..., :8] = 0x3F80
+    x[..., 8:] = 0x33C0
+    z = np.zeros((1, 16), np.uint16)
+    _, st = O.layernorm_modulate(x, z, z, EPS, want_stats=True)
+    assert bits32(st[0, 0]) == 0x3F000001
+    assert bits32(st[0, 1]) == 0x407FFFFC
+    assert bits32(st[0, 2]) == 0x3E7FFFFC
+
+
+def test_welford_uses_reciprocal_of_count():
+    # H=8, one lane: 0,0,0,0,0,0,c,0 with c = 65*2^-6 (1.015625).
+    #   rho_7 = RN(1/7) = 9586981 * 2^-26
+    #   n=7: mean = RN(c * rho_7) = RN(623153765 * 2^-32) = 9736778 * 2^-26
+    #        (623153765 / 64 = 9736777.58 -> 9736778)
+    #   n=8: x=0, d = -mean, step = -mean/8 exactly,
+    #        mean = RN(7/8 * 9736778 * 2^-26) = RN(8519680.75 * 2^-26)
+    #             = 8519681 * 2^-26                              = 0x3E020001
+    # A literal divide d/7 would give 9736777 at n=7 and then 8519680 * 2^-26
+    # (= 65/512, the exact mean, 0x3E020000).
+    x = _row_with(8, {6: 1.015625})
+    z = np.zeros((1, 8), np.uint16)
+    _, st = O.layernorm_modulate(x, z, z, EPS, want_stats=True)
+    assert bits32(st[0, 0]) == 0x3E020001
+
+
+def test_finalize_rounding_chain():
+    # eps32 = RN(1e-6) = 0x358637BD.  A row with mean square 1 exactly (+-1 row):
+    # v = RN(1 + eps32) = 1 + 8*2^-23 (1e-6 / 2^-23 = 8.39 -> 8),
+    # sqrt(v) = 1 + 4*2^-23 - tiny -> RN = 1 + 4*2^-23 = 0x3F800004,
+    # 1 / that = 1 - 4*2^-23 + ... -> RN: 0x3F7FFFF8.
+    assert bits32(np.float32(EPS)) == 0x358637BD
+    x = _row_with(64, {c: (1.0 if c % 2 else -1.0) for c in range(64)})
+    z = np.zeros((1, 64), np.uint16)
+    _, st = O.rmsnorm_scale_shift(x, None, z, z, EPS, want_stats=True)
+    assert float(st[0, 1]) == 1.0
+    assert bits32(st[0, 2]) == 0x3F800008
+    assert bits32(st[0, 3]) == 0x3F800004
+    assert bits32(st[0, 4]) == 0x3F7FFFF8
+
+
+def test_layout_table():
+    expect = {8: (1, 64, 1), 16: (1, 64, 1), 512: (1, 64, 1), 520: (1, 64, 2), 2048: (1, 64, 4),
+              3072: (1, 64, 6), 4088: (1, 64, 8), 4096: (4, 256, 2), 4104: (4, 256, 3),
+              6144: (4, 256, 3), 8192: (4, 256, 4)}
+    for H, v in expect.items():
+        assert O.layout(H) == v, H
+    for H in [0, 4, 12, 8200, -8, 8193]:
+        with pytest.raises(ValueError):
+            O.layout(H)
+
+
+def test_rms_output_rounded_once():
+    # A row with mean square exactly 1 (10 x +-0.5 and 6 x +-1.5 per 16 columns)
+    # has rstd = 0x3F7FFFF8 = 1 - 2^-21 (see test_finalize_rounding_chain).
+    # At a column with x = 1.5 and weight w = 1 + 2^-7 (bf16 0x3F81):
+    #   single rounding: RN(1.5 * rstd) = 1.5 - 6*2^-23 exactly, times w lands
+    #   just below 1.51171875, the midpoint of bf16 0x3FC1 and 0x3FC2 -> 0x3FC1;
+    #   rounding x*rstd to bf16 first (giving 1.5) would make 1.5*w the exact
+    #   midpoint, which ties to even -> 0x3FC2.
+    H = 16
+    row = np.array([0.5] * 5 + [-0.5] * 5 + [1.5] * 3 + [-1.5] * 3, np.float32)
+    x = synth.f32_to_bf16_bits(row)[None, None]
+    w = np.full(H, 0x3F80, np.uint16)
+    w[10] = 0x3F81
+    z = np.zeros((1, H), np.uint16)
+    y, st = O.rmsnorm_scale_shift(x, w, z, z, EPS, want_stats=True)
+    assert bits32(st[0, 4]) == 0x3F7FFFF8
+    assert x[0, 0, 10] == 0x3FC0 and y[0, 0, 10] == 0x3FC1
+
+
+def test_welford_combine_operand_order_across_waves():
+    # H=4096: wave w owns columns [512w, 512w+512) and [2048+512w, ...).  Waves
+    # 0 and 2 hold 1.0, waves 1 and 3 hold c = 3*2^-25.  Each wave folds to
+    # (1024, 1, 0) or (1024, c, 0) exactly (equal values, delta 0).
+    #   combine(w0, w1): as in test_welford_combine_operand_order with counts
+    #     1024: mean 1/2 + 2^-24, M2 = (1 - 2^-22) * 512 = 512 - 2^-13
+    #   combine(w01, w23) of two identical states: delta 0, mean unchanged,
+    #     M2 = 1024 - 2^-12 (0x447FFFFC); var = M2 / 4096 = 1/4 - 2^-24.
+    # Swapping the operands at the cross-wave level gives mean 1/2.
+    cols = np.arange(4096)
+    x = np.where(((cols % 2048) // 512) % 2 == 0, 0x3F80, 0x33C0).astype(np.uint16)[None, None]
+    z = np.zeros((1, 4096), np.uint16)
+    _, st = O.layernorm_modulate(x, z, z, EPS, want_stats=True)
+    assert bits32(st[0, 0]) == 0x3F000001
+    assert bits32(st[0, 1]) == 0x447FFFFC
+    assert bits32(st[0, 2]) == 0x3E7FFFFC
+
+
+def test_finalize_rounds_sqrt_then_divides():
+    # H=8 row [1,0,...,0]: S = 1, RN(S/8) = 1/8, v = RN(1/8 + eps32) = (2^23+67)*2^-26
+    # (eps32 / 2^-26 = 67.1).  sqrt(v) in [1/4,1/2) rounds to m*2^-25 with
+    # m = 11863331, since (m-1/2)^2 < v*2^50 < (m+1/2)^2.  Then 2^22/r =
+    # 11863235.406..., so rstd = 11863235*2^-22 = 0x403504C3.  The exact
+    # 1/sqrt(v) scaled by 2^22 lies in (11863235.5, 11863236): a single-rounded
+    # reciprocal square root would give 0x403504C4.
+    x = _row_with(8, {0: 1.0})
+    z = np.zeros((1, 8), np.uint16)
+    _, st = O.rmsnorm_scale_shift(x, None, z, z, EPS, want_stats=True)
+    assert float(st[0, 1]) == 0.125
+    assert bits32(st[0, 2]) == 0x3E000043
+    assert float(st[0, 3]) == 11863331 * 2.0 ** -25
+    assert bits32(st[0, 4]) == 0x403504C3

@@ -12,6 +12,8 @@ from ._binding import (  # noqa: F401
     adaln_check_layernorm_modulate,
     adaln_check_residual_gate_rmsnorm_scale_shift,
     adaln_check_rmsnorm_scale_shift,
+    adaln_diag_finalize,
+    adaln_diag_round_bf16,
     adaln_layernorm_modulate,
     adaln_reduction_layout,
     adaln_residual_gate_rmsnorm_scale_shift,

@@ -1,0 +1,249 @@
+// adaln_api.cpp -- the C ABI of libadaln (include/adaln.h): argument validation,
+// status codes, and the launch on the caller's stream.
+//
+// Unsupported input is rejected with a status before anything is launched, so
+// outputs are never half-written and the path never degrades silently (kernels
+// guide, "entry-point protocol": a kernel raises on unsupported input and never
+// returns a silent None).  Validation touches no GPU state, so the `adaln_check_*`
+// predicates and every rejection path run on a machine without a GPU.
+#include <hip/hip_runtime.h>
+#include <math.h>
+#include <stdint.h>
+
+#include "../../include/adaln.h"
+#include "adaln_internal.hpp"
+
+namespace {
+
+constexpr int64_t kMaxH = 8192;
+
+struct Span {
+    uintptr_t lo, hi;  // [lo, hi) in bytes; empty when lo == hi
+};
+
+bool overlaps(const Span& a, const Span& b) {
+    if (a.lo == a.hi || b.lo == b.hi) return false;
+    return a.lo < b.hi && b.lo < a.hi;
+}
+
+Span act_span(const void* p, int64_t rows, int64_t H) {
+    uintptr_t lo = (uintptr_t)p;
+    return Span{lo, lo + (uintptr_t)(rows * H * 2)};
+}
+
+Span vec_span(const void* p, int64_t B, int64_t H, int64_t bstride) {
+    uintptr_t lo = (uintptr_t)p;
+    int64_t elems = (B > 1 ? (B - 1) * bstride : 0) + H;
+    return Span{lo, lo + (uintptr_t)(elems * 2)};
+}
+
+bool aligned16(const void* p) { return ((uintptr_t)p & 15u) == 0; }
+
+// Shape checks shared by all entry points; *rows receives B*T.
+adaln_status check_shape(int64_t B, int64_t T, int64_t H, float eps, int64_t* rows) {
+    if (B < 0 || T < 0) return ADALN_ERR_SHAPE;
+    if (H < 8 || H > kMaxH || (H % 8) != 0) return ADALN_ERR_SHAPE;
+    if (T != 0 && B > INT64_MAX / T) return ADALN_ERR_SHAPE;
+    const int64_t r = B * T;
+    if (r != 0 && r > INT64_MAX / (2 * H)) return ADALN_ERR_SHAPE;  // byte size must fit
+    if (!(eps >= 0.0f) || !isfinite(eps)) return ADALN_ERR_VALUE;
+    *rows = r;
+    return ADALN_OK;
+}
+
+adaln_status check_vec(const void* p, int64_t B, int64_t H, int64_t bstride) {
+    if (!p) return ADALN_ERR_NULL;
+    if (!aligned16(p)) return ADALN_ERR_ALIGN;
+    if (B > 1) {
+        if (bstride < 0 || (bstride % 8) != 0) return ADALN_ERR_STRIDE;
+        if (bstride != 0 && bstride < H) return ADALN_ERR_STRIDE;
+        if (bstride != 0 && (B - 1) > (INT64_MAX / 2 - H) / bstride) return ADALN_ERR_SHAPE;
+    }
+    return ADALN_OK;
+}
+
+#define ADALN_TRY(expr)                  \
+    do {                                 \
+        adaln_status s_ = (expr);        \
+        if (s_ != ADALN_OK) return s_;   \
+    } while (0)
+
+// Validation of all three entry points.  res/gate/r are NULL for LN and RMS; the
+// `need_*` flags say which pointers are required.
+adaln_status validate(int op, const void* res, const void* x, const void* gate,
+                      const void* weight, const void* scale, const void* shift, const void* r,
+                      const void* y, int64_t B, int64_t T, int64_t H, int64_t gate_bs,
+                      int64_t scale_bs, int64_t shift_bs, float eps, int64_t* rows_out) {
+    int64_t rows = 0;
+    ADALN_TRY(check_shape(B, T, H, eps, &rows));
+    *rows_out = rows;
+    if (rows == 0) return ADALN_OK;
+    const bool gated = op == adaln::OP_RG;
+    if (!x || !y || (gated && (!res || !r))) return ADALN_ERR_NULL;
+    if (!aligned16(x) || !aligned16(y)) return ADALN_ERR_ALIGN;
+    if (gated && (!aligned16(res) || !aligned16(r))) return ADALN_ERR_ALIGN;
+    if (weight && !aligned16(weight)) return ADALN_ERR_ALIGN;
+    ADALN_TRY(check_vec(scale, B, H, scale_bs));
+    ADALN_TRY(check_vec(shift, B, H, shift_bs));
+    if (gated) ADALN_TRY(check_vec(gate, B, H, gate_bs));
+
+    // outputs may not overlap any input or each other
+    Span in[6];
+    int n_in = 0;
+    in[n_in++] = act_span(x, rows, H);
+    in[n_in++] = vec_span(scale, B, H, scale_bs);
+    in[n_in++] = vec_span(shift, B, H, shift_bs);
+    if (weight) in[n_in++] = Span{(uintptr_t)weight, (uintptr_t)weight + (uintptr_t)(2 * H)};
+    if (gated) {
+        in[n_in++] = act_span(res, rows, H);
+        in[n_in++] = vec_span(gate, B, H, gate_bs);
+    }
+    const Span ys = act_span(y, rows, H);
+    for (int i = 0; i < n_in; ++i)
+        if (overlaps(ys, in[i])) return ADALN_ERR_OVERLAP;
+    if (gated) {
+        const Span rs = act_span(r, rows, H);
+        if (overlaps(rs, ys)) return ADALN_ERR_OVERLAP;
+        for (int i = 0; i < n_in; ++i)
+            if (overlaps(rs, in[i])) return ADALN_ERR_OVERLAP;
+    }
+    return ADALN_OK;
+}
+
+adaln_status run(adaln::Op op, const adaln_bf16* res, const adaln_bf16* x, const adaln_bf16* gate,
+                 const adaln_bf16* weight, const adaln_bf16* scale, const adaln_bf16* shift,
+                 adaln_bf16* r, adaln_bf16* y, int64_t B, int64_t T, int64_t H, int64_t gate_bs,
+                 int64_t scale_bs, int64_t shift_bs, float eps, void* stream) {
+    int64_t rows = 0;
+    ADALN_TRY(validate(op, res, x, gate, weight, scale, shift, r, y, B, T, H, gate_bs, scale_bs,
+                       shift_bs, eps, &rows));
+    if (rows == 0) return ADALN_OK;
+    adaln::Params p{};
+    p.x = x;
+    p.res = res;
+    p.gate = gate;
+    p.weight = weight;
+    p.scale = scale;
+    p.shift = shift;
+    p.y = y;
+    p.r = r;
+    p.rows = rows;
+    p.T = T;
+    p.H = H;
+    p.gate_bs = B > 1 ? gate_bs : 0;
+    p.scale_bs = B > 1 ? scale_bs : 0;
+    p.shift_bs = B > 1 ? shift_bs : 0;
+    p.eps = eps;
+    hipError_t e = adaln::launch(op, p, (hipStream_t)stream);
+    return e == hipSuccess ? ADALN_OK : ADALN_ERR_LAUNCH;
+}
+
+}  // namespace
+
+extern "C" {
+
+adaln_status adaln_layernorm_modulate(const adaln_bf16* x, const adaln_bf16* scale,
+                                      const adaln_bf16* shift, adaln_bf16* y, int64_t B, int64_t T,
+                                      int64_t H, int64_t scale_bstride, int64_t shift_bstride,
+                                      float eps, void* hip_stream) {
+    return run(adaln::OP_LN, nullptr, x, nullptr, nullptr, scale, shift, nullptr, y, B, T, H, 0,
+               scale_bstride, shift_bstride, eps, hip_stream);
+}
+
+adaln_status adaln_rmsnorm_scale_shift(const adaln_bf16* x, const adaln_bf16* weight,
+                                       const adaln_bf16* scale, const adaln_bf16* shift,
+                                       adaln_bf16* y, int64_t B, int64_t T, int64_t H,
+                                       int64_t scale_bstride, int64_t shift_bstride, float eps,
+                                       void* hip_stream) {
+    return run(adaln::OP_RMS, nullptr, x, nullptr, weight, scale, shift, nullptr, y, B, T, H, 0,
+               scale_bstride, shift_bstride, eps, hip_stream);
+}
+
+adaln_status adaln_residual_gate_rmsnorm_scale_shift(
+    const adaln_bf16* res, const adaln_bf16* x, const adaln_bf16* gate, const adaln_bf16* weight,
+    const adaln_bf16* scale, const adaln_bf16* shift, adaln_bf16* r_out, adaln_bf16* y, int64_t B,
+    int64_t T, int64_t H, int64_t gate_bstride, int64_t scale_bstride, int64_t shift_bstride,
+    float eps, void* hip_stream) {
+    return run(adaln::OP_RG, res, x, gate, weight, scale, shift, r_out, y, B, T, H, gate_bstride,
+               scale_bstride, shift_bstride, eps, hip_stream);
+}
+
+adaln_status adaln_check_layernorm_modulate(const adaln_bf16* x, const adaln_bf16* scale,
+                                            const adaln_bf16* shift, const adaln_bf16* y,
+                                            int64_t B, int64_t T, int64_t H,
+                                            int64_t scale_bstride, int64_t shift_bstride,
+                                            float eps) {
+    int64_t rows;
+    return validate(adaln::OP_LN, nullptr, x, nullptr, nullptr, scale, shift, nullptr, y, B, T, H,
+                    0, scale_bstride, shift_bstride, eps, &rows);
+}
+
+adaln_status adaln_check_rmsnorm_scale_shift(const adaln_bf16* x, const adaln_bf16* weight,
+                                             const adaln_bf16* scale, const adaln_bf16* shift,
+                                             const adaln_bf16* y, int64_t B, int64_t T, int64_t H,
+                                             int64_t scale_bstride, int64_t shift_bstride,
+                                             float eps) {
+    int64_t rows;
+    return validate(adaln::OP_RMS, nullptr, x, nullptr, weight, scale, shift, nullptr, y, B, T, H,
+                    0, scale_bstride, shift_bstride, eps, &rows);
+}
+
+adaln_status adaln_check_residual_gate_rmsnorm_scale_shift(
+    const adaln_bf16* res, const adaln_bf16* x, const adaln_bf16* gate, const adaln_bf16* weight,
+    const adaln_bf16* scale, const adaln_bf16* shift, const adaln_bf16* r_out,
+    const adaln_bf16* y, int64_t B, int64_t T, int64_t H, int64_t gate_bstride,
+    int64_t scale_bstride, int64_t shift_bstride, float eps) {
+    int64_t rows;
+    return validate(adaln::OP_RG, res, x, gate, weight, scale, shift, r_out, y, B, T, H,
+                    gate_bstride, scale_bstride, shift_bstride, eps, &rows);
+}
+
+adaln_status adaln_reduction_layout(int64_t H, int* waves_per_row, int* lanes_per_row,
+                                    int* chunks_per_lane) {
+    if (H < 8 || H > kMaxH || (H % 8) != 0) return ADALN_ERR_SHAPE;
+    const adaln::Layout L = adaln::layout_of(H);
+    if (waves_per_row) *waves_per_row = L.waves;
+    if (lanes_per_row) *lanes_per_row = L.lanes;
+    if (chunks_per_lane) *chunks_per_lane = L.chunks;
+    return ADALN_OK;
+}
+
+const char* adaln_status_string(adaln_status status) {
+    switch (status) {
+        case ADALN_OK: return "success";
+        case ADALN_ERR_NULL: return "a required pointer is NULL";
+        case ADALN_ERR_SHAPE: return "unsupported shape: need 8 <= H <= 8192, H % 8 == 0, B, T >= 0";
+        case ADALN_ERR_ALIGN: return "a pointer is not 16-byte aligned";
+        case ADALN_ERR_STRIDE: return "a batch stride is negative, not a multiple of 8, or in (0, H)";
+        case ADALN_ERR_OVERLAP: return "an output overlaps an input or the other output";
+        case ADALN_ERR_VALUE: return "eps must be finite and >= 0";
+        case ADALN_ERR_LAUNCH: return "the HIP kernel launch failed";
+    }
+    return "unknown status";
+}
+
+int adaln_abi_version(void) { return ADALN_ABI_VERSION; }
+
+adaln_status adaln_diag_round_bf16(const float* in, adaln_bf16* out, int64_t n, void* hip_stream) {
+    if (n < 0) return ADALN_ERR_SHAPE;
+    if (n == 0) return ADALN_OK;
+    if (!in || !out) return ADALN_ERR_NULL;
+    if (((uintptr_t)in & 3u) || ((uintptr_t)out & 1u)) return ADALN_ERR_ALIGN;
+    return adaln::launch_diag_round(in, out, n, (hipStream_t)hip_stream) == hipSuccess
+               ? ADALN_OK
+               : ADALN_ERR_LAUNCH;
+}
+
+adaln_status adaln_diag_finalize(const float* in, float* out, int64_t n, float eps,
+                                 void* hip_stream) {
+    if (n < 0) return ADALN_ERR_SHAPE;
+    if (!(eps >= 0.0f) || !isfinite(eps)) return ADALN_ERR_VALUE;
+    if (n == 0) return ADALN_OK;
+    if (!in || !out) return ADALN_ERR_NULL;
+    if (((uintptr_t)in & 3u) || ((uintptr_t)out & 3u)) return ADALN_ERR_ALIGN;
+    return adaln::launch_diag_finalize(in, out, n, eps, (hipStream_t)hip_stream) == hipSuccess
+               ? ADALN_OK
+               : ADALN_ERR_LAUNCH;
+}
+
+}  // extern "C"

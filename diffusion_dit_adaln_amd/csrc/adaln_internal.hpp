@@ -1,0 +1,44 @@
+// adaln_internal.hpp -- interface between the C-ABI layer (adaln_api.cpp) and the
+// HIP launchers (adaln_kernels.hip) of libadaln.  Not installed; not part of the ABI.
+#pragma once
+
+#include <hip/hip_runtime.h>
+#include <stdint.h>
+
+namespace adaln {
+
+enum Op : int { OP_LN = 0, OP_RMS = 1, OP_RG = 2 };
+
+// Arguments of one launch, already validated by the C-ABI layer.
+struct Params {
+    const uint16_t* x;       // norm input (LN, RMS) or the gated update (RG), [rows, H]
+    const uint16_t* res;     // RG: residual stream [rows, H]
+    const uint16_t* gate;    // RG: per-batch gate, row b at gate + b*gate_bs
+    const uint16_t* weight;  // RMS / RG: [H] or NULL
+    const uint16_t* scale;   // per-batch, row b at scale + b*scale_bs
+    const uint16_t* shift;   // per-batch, row b at shift + b*shift_bs
+    uint16_t* y;             // [rows, H]
+    uint16_t* r;             // RG: [rows, H]
+    int64_t rows;            // B*T > 0
+    int64_t T;               // rows per batch entry
+    int64_t H;
+    int64_t gate_bs, scale_bs, shift_bs;
+    float eps;
+    int64_t groups;          // row groups: a wave (H < 4096) or a workgroup (H >= 4096)
+};
+
+// Reduction layout of H (the numerics contract): waves per row, lanes, chunks.
+struct Layout {
+    int waves, lanes, chunks;
+    bool ragged;  // H % (8 * lanes) != 0: the last chunk is partial
+};
+Layout layout_of(int64_t H);
+
+// Launch the fused kernel for `op`; returns the HIP error of the launch.
+hipError_t launch(Op op, const Params& p, hipStream_t stream);
+
+hipError_t launch_diag_round(const float* in, uint16_t* out, int64_t n, hipStream_t stream);
+hipError_t launch_diag_finalize(const float* in, float* out, int64_t n, float eps,
+                                hipStream_t stream);
+
+}  // namespace adaln

@@ -177,3 +177,44 @@ def config4(seed: int = 0, n_sets: int = 256, max_tokens: int = 4096, H: int = 3
     v = _vecs(seed, cid, n_sets, H, ["scale", "shift"])
     w = normal_bf16(_rng(seed, cid, "weight"), (H,), 0.02, 1.0)
     return StressSets(x, offsets, cls, v["scale"], v["shift"], w)
+
+
+@dataclasses.dataclass
+class StressSetsDevice:
+    """The batch-invariance stress workload drawn on the device (torch tensors)."""
+    x: "torch.Tensor"        # [R, H] bfloat16, packed row-sets
+    offsets: np.ndarray      # [S+1] row offsets
+    row_class: np.ndarray    # [R] 0: N(0,1), 1: 1e-3*N(0,1), 2: 1e3*N(0,1)
+    scale: "torch.Tensor"    # [S, H] bfloat16
+    shift: "torch.Tensor"    # [S, H] bfloat16
+    weight: "torch.Tensor"   # [H] bfloat16, 1 + 0.02*N
+
+
+def config4_device(seed: int = 0, n_sets: int = 256, max_tokens: int = 4096, H: int = 3072,
+                   device: str = "cuda", cid: int = 4) -> StressSetsDevice:
+    """Same recipe as config4 (set sizes and row classes from the numpy streams),
+    but the ~1.6e9 activations are drawn on the device with torch's seeded
+    generator: float32 N(0,1) times the row's sigma, rounded to bfloat16."""
+    tr = _rng(seed, cid, "tokens")
+    counts = tr.integers(1, max_tokens + 1, size=n_sets)
+    offsets = np.zeros(n_sets + 1, np.int64)
+    offsets[1:] = np.cumsum(counts)
+    R = int(offsets[-1])
+    cls = _rng(seed, cid, "class").integers(0, 3, size=R).astype(np.int8)
+    gen = torch.Generator(device=device)
+    gen.manual_seed(int(np.random.SeedSequence([seed, cid, TENSOR_IDS["x"]]).generate_state(1)[0]))
+    sig = torch.tensor(CLASS_SIGMA, dtype=torch.float32, device=device)[
+        torch.from_numpy(cls.astype(np.int64)).to(device)]
+    x = torch.empty((R, H), dtype=torch.bfloat16, device=device)
+    step = 1 << 16
+    for lo in range(0, R, step):
+        hi = min(R, lo + step)
+        v = torch.randn((hi - lo, H), generator=gen, device=device, dtype=torch.float32)
+        x[lo:hi] = (v * sig[lo:hi, None]).to(torch.bfloat16)
+    v = _vecs(seed, cid, n_sets, H, ["scale", "shift"])
+    w = normal_bf16(_rng(seed, cid, "weight"), (H,), 0.02, 1.0)
+
+    def to_dev(a):
+        return torch.from_numpy(np.ascontiguousarray(a).view(np.int16)).view(torch.bfloat16).to(device)
+
+    return StressSetsDevice(x, offsets, cls, to_dev(v["scale"]), to_dev(v["shift"]), to_dev(w))

@@ -1,0 +1,180 @@
+"""The C-ABI library loads, exports every symbol include/adaln.h declares, agrees
+with the oracle on the reduction layout, and rejects bad arguments before any GPU
+work (no compute call is made here, so these run without a GPU)."""
+import ctypes
+import os
+import re
+
+import numpy as np
+import pytest
+
+import diffusion_dit_adaln_amd as A
+from diffusion_dit_adaln_amd import _binding
+from oracle import oracle as O
+
+ROOT = os.path.dirname(os.path.dirname(os.path.abspath(__file__)))
+HEADER = os.path.join(ROOT, "include", "adaln.h")
+
+OK, NULL, SHAPE, ALIGN, STRIDE, OVERLAP, VALUE, LAUNCH = range(8)
+
+
+@pytest.fixture(scope="module")
+def lib():
+    if not os.path.exists(A.library_path()):
+        pytest.fail("libadaln.so is not built: run python __graft_entry__.py")
+    return A.load_library()
+
+
+def declared_symbols():
+    text = open(HEADER).read()
+    text = re.sub(r"/\*.*?\*/", "", text, flags=re.S)
+    return sorted(set(re.findall(r"\b(adaln_[a-z0-9_]+)\s*\(", text)))
+
+
+def test_header_symbols_are_exported(lib):
+    names = declared_symbols()
+    assert len(names) == 11, names
+    assert set(names) == set(_binding.EXPORTS)
+    for n in names:
+        assert hasattr(lib, n), n
+
+
+def test_abi_version_and_status_strings(lib):
+    assert A.adaln_abi_version() == A.ABI_VERSION == 1
+    for s in range(8):
+        assert len(A.adaln_status_string(s)) > 5
+    assert A.adaln_status_string(99) == "unknown status"
+
+
+def test_layout_matches_oracle_for_every_h(lib):
+    for H in range(8, 8193, 8):
+        assert A.adaln_reduction_layout(H) == O.layout(H), H
+    for H in [0, 4, 12, 8200, -8]:
+        with pytest.raises(A.AdalnError):
+            A.adaln_reduction_layout(H)
+
+
+# fake, well-separated, 16-byte aligned "device" addresses: validation never
+# dereferences them
+BASE = 1 << 40
+
+
+def addr(i):
+    return BASE + i * (1 << 34)
+
+
+def ln_args(**kw):
+    a = dict(x=addr(0), scale=addr(1), shift=addr(2), y=addr(3), B=2, T=5, H=3072, sbs=3072,
+             hbs=3072, eps=1e-6)
+    a.update(kw)
+    return a
+
+
+def ln_check(lib, **kw):
+    a = ln_args(**kw)
+    return lib.adaln_check_layernorm_modulate(a["x"], a["scale"], a["shift"], a["y"], a["B"],
+                                              a["T"], a["H"], a["sbs"], a["hbs"], a["eps"])
+
+
+def rg_check(lib, **kw):
+    a = dict(res=addr(0), x=addr(1), gate=addr(2), w=addr(3), scale=addr(4), shift=addr(5),
+             r=addr(6), y=addr(7), B=2, T=5, H=4096, gbs=4096, sbs=4096, hbs=4096, eps=1e-6)
+    a.update(kw)
+    return lib.adaln_check_residual_gate_rmsnorm_scale_shift(
+        a["res"], a["x"], a["gate"], a["w"], a["scale"], a["shift"], a["r"], a["y"], a["B"],
+        a["T"], a["H"], a["gbs"], a["sbs"], a["hbs"], a["eps"])
+
+
+def test_valid_arguments_pass(lib):
+    assert ln_check(lib) == OK
+    assert rg_check(lib) == OK
+    assert rg_check(lib, w=None) == OK
+    assert lib.adaln_check_rmsnorm_scale_shift(addr(0), None, addr(1), addr(2), addr(3), 1, 7,
+                                               2048, 0, 0, 1e-6) == OK
+    # FLUX chunk views: scale/shift are slices of one [B, 6H] embedding
+    assert ln_check(lib, scale=addr(1) + 2 * 3072, shift=addr(1), sbs=6 * 3072, hbs=6 * 3072) == OK
+    assert ln_check(lib, sbs=0, hbs=0) == OK           # one vector shared by the batch
+    assert ln_check(lib, B=1, sbs=5, hbs=-3) == OK     # stride unused when B == 1
+
+
+def test_empty_is_a_noop(lib):
+    assert ln_check(lib, B=0, x=None, y=None, scale=None, shift=None) == OK
+    assert ln_check(lib, T=0, x=None) == OK
+    # the compute entry point also returns before touching anything
+    assert lib.adaln_layernorm_modulate(None, None, None, None, 0, 3, 3072, 0, 0, 1e-6, None) == OK
+
+
+@pytest.mark.parametrize("H", [0, 4, 12, 8200, 8193, -8, 1 << 20])
+def test_bad_h(lib, H):
+    assert ln_check(lib, H=H) == SHAPE
+
+
+def test_bad_sizes(lib):
+    assert ln_check(lib, B=-1) == SHAPE
+    assert ln_check(lib, T=-2) == SHAPE
+    assert ln_check(lib, B=1 << 40, T=1 << 40) == SHAPE
+
+
+def test_nulls(lib):
+    assert ln_check(lib, x=None) == NULL
+    assert ln_check(lib, y=None) == NULL
+    assert ln_check(lib, scale=None) == NULL
+    assert ln_check(lib, shift=None) == NULL
+    assert rg_check(lib, res=None) == NULL
+    assert rg_check(lib, gate=None) == NULL
+    assert rg_check(lib, r=None) == NULL
+
+
+def test_alignment(lib):
+    assert ln_check(lib, x=addr(0) + 2) == ALIGN
+    assert ln_check(lib, y=addr(3) + 8) == ALIGN
+    assert ln_check(lib, scale=addr(1) + 2) == ALIGN
+    assert rg_check(lib, w=addr(3) + 4) == ALIGN
+    assert rg_check(lib, r=addr(6) + 2) == ALIGN
+
+
+def test_strides(lib):
+    assert ln_check(lib, sbs=-8) == STRIDE
+    assert ln_check(lib, sbs=3076) == STRIDE      # not a multiple of 8
+    assert ln_check(lib, hbs=1024) == STRIDE      # in (0, H)
+    assert rg_check(lib, gbs=8) == STRIDE
+
+
+def test_eps(lib):
+    assert ln_check(lib, eps=-1e-6) == VALUE
+    assert ln_check(lib, eps=float("nan")) == VALUE
+    assert ln_check(lib, eps=float("inf")) == VALUE
+
+
+def test_overlaps(lib):
+    rows_bytes = 2 * 5 * 3072 * 2
+    assert ln_check(lib, y=addr(0)) == OVERLAP                      # y == x
+    assert ln_check(lib, y=addr(0) + rows_bytes - 16) == OVERLAP    # tail of x
+    assert ln_check(lib, y=addr(0) + rows_bytes) == OK              # just after x
+    assert ln_check(lib, y=addr(1) - 16) == OVERLAP                 # runs into scale
+    assert rg_check(lib, r=addr(7)) == OVERLAP                      # r == y
+    assert rg_check(lib, r=addr(0)) == OVERLAP                      # r == res
+    assert rg_check(lib, y=addr(2)) == OVERLAP                      # y over gate
+    assert rg_check(lib, y=addr(3)) == OVERLAP                      # y over weight
+
+
+def test_compute_entry_points_reject_before_launch(lib):
+    # invalid calls return their status without any HIP call (no GPU here)
+    assert lib.adaln_layernorm_modulate(addr(0), addr(1), addr(2), addr(0), 1, 2, 3072, 0, 0,
+                                        1e-6, None) == OVERLAP
+    assert lib.adaln_rmsnorm_scale_shift(addr(0), None, addr(1), addr(2), addr(3), 1, 2, 12, 0, 0,
+                                         1e-6, None) == SHAPE
+    assert lib.adaln_residual_gate_rmsnorm_scale_shift(
+        addr(0), addr(1), None, None, addr(4), addr(5), addr(6), addr(7), 1, 2, 4096, 0, 0, 0,
+        1e-6, None) == NULL
+    assert lib.adaln_diag_round_bf16(None, None, -1, None) == SHAPE
+    assert lib.adaln_diag_finalize(addr(0), addr(1), 4, -1.0, None) == VALUE
+
+
+def test_binding_raises_adaln_error(lib):
+    torch = pytest.importorskip("torch")
+    x = torch.zeros(1, 2, 12, dtype=torch.bfloat16)
+    v = torch.zeros(12, dtype=torch.bfloat16)
+    with pytest.raises(A.AdalnError) as e:
+        A.adaln_layernorm_modulate(x, v, v, stream=0)
+    assert e.value.status == SHAPE

@@ -1,0 +1,291 @@
+"""GPU parity: the HIP path through the C ABI equals the CPU oracle bit for bit.
+
+Sizes: the five workloads at their full sizes (the oracle finishes each in
+seconds), the FLUX.1 site signatures with strided `emb.chunk` modulation views
+(FLUX PR report, test snippet), ragged and extreme hidden sizes, empty and
+single-row inputs, non-finite inputs, and exhaustive sweeps of the device's
+bf16 rounding and finalize steps.
+"""
+import numpy as np
+import pytest
+import torch
+
+import diffusion_dit_adaln_amd as A
+from diffusion_dit_adaln_amd import synth
+from oracle import oracle as O
+from tests.helpers import assert_bits_equal, dev, host, say
+
+pytestmark = pytest.mark.gpu
+EPS = 1e-6
+
+
+def run_ln(x, sc, sh, eps=EPS):
+    return host(A.adaln_layernorm_modulate(dev(x), dev(sc), dev(sh), eps))
+
+
+def run_rms(x, w, sc, sh, eps=EPS):
+    return host(A.adaln_rmsnorm_scale_shift(dev(x), None if w is None else dev(w), dev(sc), dev(sh),
+                                            eps))
+
+
+def run_rg(res, x, g, w, sc, sh, eps=EPS):
+    r, y = A.adaln_residual_gate_rmsnorm_scale_shift(dev(res), dev(x), dev(g),
+                                                     None if w is None else dev(w), dev(sc),
+                                                     dev(sh), eps)
+    return host(r), host(y)
+
+
+def check_workload(wl, what):
+    say(f"[parity] {what} {wl.op} shape={wl.x.shape}")
+    if wl.op == "ln":
+        assert_bits_equal(run_ln(wl.x, wl.scale, wl.shift), O.layernorm_modulate(
+            wl.x, wl.scale, wl.shift, wl.eps), what)
+    elif wl.op == "rms":
+        assert_bits_equal(run_rms(wl.x, wl.weight, wl.scale, wl.shift), O.rmsnorm_scale_shift(
+            wl.x, wl.weight, wl.scale, wl.shift, wl.eps), what)
+    else:
+        r, y = run_rg(wl.res, wl.x, wl.gate, wl.weight, wl.scale, wl.shift)
+        r0, y0 = O.residual_gate_rmsnorm_scale_shift(wl.res, wl.x, wl.gate, wl.weight, wl.scale,
+                                                     wl.shift, wl.eps)
+        assert_bits_equal(r, r0, what + " r")
+        assert_bits_equal(y, y0, what + " y")
+
+
+# --------------------------------------------------------------------------
+# the workloads at full size
+# --------------------------------------------------------------------------
+@pytest.mark.parametrize("cfg", ["0", "1", "2", "3a", "3b"])
+def test_workload_full_size(cfg):
+    wl = {"0": synth.config0, "1": synth.config1, "2": synth.config2,
+          "3a": lambda: synth.config3(site="a"), "3b": lambda: synth.config3(site="b")}[cfg]()
+    check_workload(wl, f"config {cfg}")
+
+
+def test_rg_with_weight():
+    wl = synth.config2()
+    wl.weight = synth.normal_bf16(np.random.default_rng(5), (4096,), 0.02, 1.0)
+    check_workload(wl, "config 2 with weight")
+
+
+# --------------------------------------------------------------------------
+# FLUX.1 site signatures with strided modulation views
+# --------------------------------------------------------------------------
+@pytest.mark.parametrize("shape,chunks", [((1, 4096, 3072), 6), ((1, 512, 3072), 6),
+                                          ((1, 4608, 3072), 3), ((2, 300, 3072), 6)])
+def test_flux_sites_chunk_views(shape, chunks):
+    B, T, H = shape
+    say(f"[parity] flux site {shape} chunk({chunks})")
+    rng = np.random.default_rng(0)
+    x = synth.normal_bf16(rng, shape, 8.0)          # randn * 8, as in the test snippet
+    emb, shift, scale = synth.flux_chunk_views(0, B, H, chunks)
+    emb_d = dev(emb)
+    shift_d = emb_d[:, 0:H]
+    scale_d = emb_d[:, H:2 * H]
+    assert scale_d.stride(0) == chunks * H
+    y = host(A.adaln_layernorm_modulate(dev(x), scale_d, shift_d, EPS))
+    assert_bits_equal(y, O.layernorm_modulate(x, scale, shift, EPS), f"flux {shape}")
+    # the RMS variant through the same strided views
+    y = host(A.adaln_rmsnorm_scale_shift(dev(x), None, scale_d, shift_d, EPS))
+    assert_bits_equal(y, O.rmsnorm_scale_shift(x, None, scale, shift, EPS), f"flux rms {shape}")
+
+
+# --------------------------------------------------------------------------
+# hidden sizes: ragged tails, both layouts, the extremes
+# --------------------------------------------------------------------------
+EDGE_H = [8, 16, 24, 64, 504, 512, 520, 1000, 1536, 2040, 2048, 2056, 3064, 3072, 3080, 4088,
+          4096, 4104, 5000, 6144, 8184, 8192]
+
+
+def mixed_rows(rng, B, T, H):
+    cls = rng.integers(0, 4, size=(B, T, 1))
+    sig = np.array([1.0, 1e-3, 1e3, 8.0])[cls]
+    mu = np.where(cls == 3, 100.0, 0.0)
+    v = rng.standard_normal((B, T, H)) * sig + mu
+    return synth.f32_to_bf16_bits(v.astype(np.float32)).reshape(B, T, H)
+
+
+@pytest.mark.parametrize("H", EDGE_H)
+def test_edge_hidden_sizes(H):
+    say(f"[parity] edge H={H}")
+    rng = np.random.default_rng(H)
+    B, T = 2, 7
+    x = mixed_rows(rng, B, T, H)
+    res = mixed_rows(rng, B, T, H)
+    w = synth.normal_bf16(rng, (H,), 0.02, 1.0)
+    g = synth.normal_bf16(rng, (B, H), 0.1)
+    sc = synth.normal_bf16(rng, (B, H), 0.1)
+    sh = synth.normal_bf16(rng, (B, H), 0.1)
+    assert_bits_equal(run_ln(x, sc, sh), O.layernorm_modulate(x, sc, sh, EPS), f"ln H={H}")
+    for ww in (w, None):
+        tag = f"H={H} weight={ww is not None}"
+        assert_bits_equal(run_rms(x, ww, sc, sh), O.rmsnorm_scale_shift(x, ww, sc, sh, EPS),
+                          "rms " + tag)
+        r, y = run_rg(res, x, g, ww, sc, sh)
+        r0, y0 = O.residual_gate_rmsnorm_scale_shift(res, x, g, ww, sc, sh, EPS)
+        assert_bits_equal(r, r0, "rg r " + tag)
+        assert_bits_equal(y, y0, "rg y " + tag)
+
+
+@pytest.mark.parametrize("eps", [0.0, 1e-5, 1e-6, 0.25])
+def test_eps_values(eps):
+    say(f"[parity] eps={eps}")
+    rng = np.random.default_rng(17)
+    for H in (3072, 4096):
+        x = mixed_rows(rng, 1, 9, H)
+        sc = synth.normal_bf16(rng, (1, H), 0.1)
+        sh = synth.normal_bf16(rng, (1, H), 0.1)
+        assert_bits_equal(run_ln(x, sc, sh, eps), O.layernorm_modulate(x, sc, sh, eps), "ln")
+        assert_bits_equal(run_rms(x, None, sc, sh, eps), O.rmsnorm_scale_shift(x, None, sc, sh, eps),
+                          "rms")
+
+
+def test_constant_and_zero_rows():
+    say("[parity] constant / zero / denormal rows")
+    H = 4096
+    consts = np.array([0.0, -0.0, 1.0, -3.5, 1e3, 2.0 ** -130, -(2.0 ** -133), 65504.0],
+                      np.float32)
+    x = np.repeat(synth.f32_to_bf16_bits(consts)[:, None], H, axis=1)[None]
+    rng = np.random.default_rng(2)
+    sc = synth.normal_bf16(rng, (1, H), 0.1)
+    sh = synth.normal_bf16(rng, (1, H), 0.1)
+    assert_bits_equal(run_ln(x, sc, sh), O.layernorm_modulate(x, sc, sh, EPS), "ln")
+    assert_bits_equal(run_rms(x, None, sc, sh), O.rmsnorm_scale_shift(x, None, sc, sh, EPS), "rms")
+
+
+def test_nonfinite_inputs_give_nan_in_the_same_places():
+    say("[parity] inf / nan inputs")
+    H = 3072
+    rng = np.random.default_rng(4)
+    x = synth.normal_bf16(rng, (1, 6, H))
+    x[0, 1, 7] = 0x7F80     # +inf
+    x[0, 2, 100] = 0xFF80   # -inf
+    x[0, 3, 2000] = 0x7FC0  # nan
+    sc = synth.normal_bf16(rng, (1, H), 0.1)
+    sh = synth.normal_bf16(rng, (1, H), 0.1)
+    for got, want in ((run_ln(x, sc, sh), O.layernorm_modulate(x, sc, sh, EPS)),
+                      (run_rms(x, None, sc, sh), O.rmsnorm_scale_shift(x, None, sc, sh, EPS))):
+        gn = np.isnan(synth.bf16_bits_to_f32(got))
+        wn = np.isnan(synth.bf16_bits_to_f32(want))
+        assert np.array_equal(gn, wn)
+        assert_bits_equal(got[~gn], want[~wn], "finite outputs")
+
+
+# --------------------------------------------------------------------------
+# shapes: empty, single rows, shared vectors
+# --------------------------------------------------------------------------
+def test_empty_inputs():
+    say("[parity] empty inputs")
+    for shape in [(0, 5, 3072), (2, 0, 4096)]:
+        x = torch.empty(shape, dtype=torch.bfloat16, device="cuda")
+        v = torch.zeros(max(shape[0], 1), shape[2], dtype=torch.bfloat16, device="cuda")
+        v = v[: shape[0]] if shape[0] else v
+        y = A.adaln_layernorm_modulate(x, v, v, EPS)
+        assert y.shape == x.shape
+
+
+def test_single_row():
+    say("[parity] single rows")
+    rng = np.random.default_rng(6)
+    for H in (8, 2048, 4096, 8192):
+        x = synth.normal_bf16(rng, (1, 1, H))
+        sc = synth.normal_bf16(rng, (1, H), 0.1)
+        sh = synth.normal_bf16(rng, (1, H), 0.1)
+        assert_bits_equal(run_ln(x, sc, sh), O.layernorm_modulate(x, sc, sh, EPS), f"ln H={H}")
+
+
+def test_shared_vectors_batch_stride_zero():
+    say("[parity] batch stride 0")
+    rng = np.random.default_rng(7)
+    B, T, H = 3, 11, 3072
+    x = synth.normal_bf16(rng, (B, T, H))
+    sc = synth.normal_bf16(rng, (1, H), 0.1)
+    sh = synth.normal_bf16(rng, (1, H), 0.1)
+    y = host(A.adaln_layernorm_modulate(dev(x), dev(sc), dev(sh), EPS))
+    assert_bits_equal(y, O.layernorm_modulate(x, sc, sh, EPS), "bstride 0")
+
+
+def test_rejected_call_leaves_outputs_untouched():
+    say("[parity] rejected call")
+    lib = A.load_library()
+    H = 3072
+    x = torch.zeros(1, 4, H, dtype=torch.bfloat16, device="cuda")
+    v = torch.zeros(1, H, dtype=torch.bfloat16, device="cuda")
+    y = torch.full((1, 4, H), 7.0, dtype=torch.bfloat16, device="cuda")
+    stream = torch.cuda.current_stream().cuda_stream
+    st = lib.adaln_layernorm_modulate(x.data_ptr() + 2, v.data_ptr(), v.data_ptr(), y.data_ptr(),
+                                      1, 3, H, 0, 0, 1e-6, stream)
+    assert st == 3  # ADALN_ERR_ALIGN
+    torch.cuda.synchronize()
+    assert bool((y == 7.0).all())
+
+
+# --------------------------------------------------------------------------
+# batch invariance on small inputs (the large stress lives in its own file)
+# --------------------------------------------------------------------------
+def test_rows_alone_equal_rows_in_batch():
+    say("[parity] rows alone vs in batch")
+    rng = np.random.default_rng(8)
+    B, T, H = 3, 17, 4096
+    x = mixed_rows(rng, B, T, H)
+    sc = synth.normal_bf16(rng, (B, H), 0.1)
+    sh = synth.normal_bf16(rng, (B, H), 0.1)
+    xd, scd, shd = dev(x), dev(sc), dev(sh)
+    y = A.adaln_layernorm_modulate(xd, scd, shd, EPS)
+    yr = A.adaln_rmsnorm_scale_shift(xd, None, scd, shd, EPS)
+    for b in range(B):
+        for t in range(0, T, 3):
+            y1 = A.adaln_layernorm_modulate(xd[b:b + 1, t:t + 1].contiguous(), scd[b], shd[b], EPS)
+            assert torch.equal(y1[0, 0].view(torch.int16), y[b, t].view(torch.int16))
+            y2 = A.adaln_rmsnorm_scale_shift(xd[b:b + 1, t:t + 1].contiguous(), None, scd[b],
+                                             shd[b], EPS)
+            assert torch.equal(y2[0, 0].view(torch.int16), yr[b, t].view(torch.int16))
+
+
+# --------------------------------------------------------------------------
+# the device's rounding and finalize steps, exhaustively
+# --------------------------------------------------------------------------
+def test_device_bf16_rounding_all_fp32_patterns():
+    # torch's float32 -> bfloat16 conversion (nearest-even) is the reference; NaN
+    # inputs must stay NaN.
+    n_chunks = 16
+    step = (1 << 32) // n_chunks
+    for k in range(n_chunks):
+        say(f"[diag] bf16 rounding chunk {k + 1}/{n_chunks}")
+        u = torch.arange(k * step, (k + 1) * step, dtype=torch.int64, device="cuda")
+        f = (u - (1 << 32) * (u >= (1 << 31)).long()).to(torch.int32).view(torch.float32)
+        got = A.adaln_diag_round_bf16(f).view(torch.int16)
+        want = f.to(torch.bfloat16).view(torch.int16)
+        nan = torch.isnan(f)
+        assert torch.equal(got[~nan], want[~nan]), f"chunk {k}"
+        gw = got[nan].to(torch.int32) & 0xFFFF
+        assert bool(((gw & 0x7F80) == 0x7F80).all() and ((gw & 0x7F) != 0).all())
+        del u, f, got, want, nan, gw
+    torch.cuda.synchronize()
+
+
+def test_device_finalize_all_nonnegative_stats():
+    # stat in [+0, +inf]: rstd = RN(1/RN(sqrt(RN(stat + eps)))).  Reference: the
+    # fp32 add, then sqrt and divide in float64 rounded once to float32 (a double
+    # rounding through binary64 equals the single fp32 rounding for sqrt and
+    # divide, since 53 >= 2*24 + 2).
+    eps = torch.tensor(1e-6, dtype=torch.float32, device="cuda")
+    top = 0x7F800000 + 1
+    n_chunks = 16
+    step = (top + n_chunks - 1) // n_chunks
+    for k in range(n_chunks):
+        say(f"[diag] finalize chunk {k + 1}/{n_chunks}")
+        lo, hi = k * step, min(top, (k + 1) * step)
+        s = torch.arange(lo, hi, dtype=torch.int32, device="cuda").view(torch.float32)
+        got = A.adaln_diag_finalize(s, 1e-6)
+        v = s + eps
+        root = v.double().sqrt().float()
+        want = (1.0 / root.double()).float()
+        assert torch.equal(got.view(torch.int32), want.view(torch.int32)), f"chunk {k}"
+    # host IEEE arithmetic on a sample, independent of torch's device math
+    rng = np.random.default_rng(1)
+    bits = rng.integers(0, 0x7F800000, size=1 << 22, dtype=np.uint32)
+    s = bits.view(np.float32)
+    got = A.adaln_diag_finalize(torch.from_numpy(s.copy()).cuda(), 1e-6).cpu().numpy()
+    v = s + np.float32(1e-6)
+    want = np.float32(1.0) / np.sqrt(v)
+    assert np.array_equal(got.view(np.uint32), want.view(np.uint32))

@@ -1,0 +1,299 @@
+"""Benchmark of the fused adaLN path on one MI355X.
+
+A step is one pass of the whole hot path (load, statistic, fold, finalize,
+normalise, modulate, store) over one batch: one launch of the fused kernel.  The
+default workload is RMSNorm + scale/shift on bf16 x [1, 4216, 4096] (ERNIE-Image
+site shape), the configuration the headline metric is quoted on.  Inputs are
+resident in HBM; the launches rotate over buffer sets totalling >= 1 GiB so
+every launch reads from HBM, not from the 256 MB Infinity Cache.
+
+Prints ONE JSON line: value = achieved HBM GB/s (algorithmic bytes: read x[,res],
+write y[,r]) over the timed steps, plus rows/s, the roofline of the fused
+kernel, the copy ceiling, the other workloads' figures, and the CPU oracle timed
+on this host as the baseline.
+"""
+from __future__ import annotations
+
+import argparse
+import ctypes
+import hashlib
+import json
+import os
+import sys
+import time
+
+import numpy as np
+
+ROOT = os.path.dirname(os.path.abspath(__file__))
+sys.path.insert(0, ROOT)
+
+PEAK_HBM_GBPS = 8000.0
+METRIC = "achieved HBM GB/s (% of MI355X peak) and rows/s for fused norm+modulate"
+KERNEL_SRC = os.path.join(ROOT, "diffusion_dit_adaln_amd", "csrc", "adaln_kernels.hip")
+
+
+def kernel_src_sha() -> str:
+    with open(KERNEL_SRC, "rb") as fh:
+        return hashlib.sha256(fh.read()).hexdigest()[:16]
+
+
+def load_counters(name: str):
+    """Per-dispatch HBM bytes from the committed rocprofv3 --pmc summary, or None
+    when the summary is missing or was taken on a different kernel source."""
+    path = os.path.join(ROOT, "profiles", f"counters_{name}.txt")
+    if not os.path.exists(path):
+        return None
+    kv = {}
+    with open(path) as fh:
+        for line in fh:
+            if "=" in line and not line.lstrip().startswith("#"):
+                k, v = line.split("=", 1)
+                kv[k.strip()] = v.strip()
+    if kv.get("kernel_src_sha") != kernel_src_sha():
+        return None
+    try:
+        return float(kv["traffic_bytes_per_dispatch"])
+    except (KeyError, ValueError):
+        return None
+
+
+# ---------------------------------------------------------------------------
+# workloads
+# ---------------------------------------------------------------------------
+def workload(cfg: str):
+    from diffusion_dit_adaln_amd import synth
+    return {"0": synth.config0, "1": synth.config1, "2": synth.config2,
+            "3a": lambda: synth.config3(site="a"), "3b": lambda: synth.config3(site="b")}[cfg]()
+
+
+class Launcher:
+    """Pre-marshalled C-ABI calls over rotating device buffer sets."""
+
+    def __init__(self, wl, rotate_bytes: int):
+        import torch
+        import diffusion_dit_adaln_amd as A
+        self.torch = torch
+        self.lib = A.load_library()
+        self.wl = wl
+        B, T, H = wl.x.shape
+        self.B, self.T, self.H = B, T, H
+
+        def dev(a):
+            return torch.from_numpy(np.ascontiguousarray(a).view(np.int16)).view(
+                torch.bfloat16).cuda()
+
+        per_set = wl.algorithmic_bytes()
+        self.nsets = max(2, -(-rotate_bytes // per_set))
+        x0 = dev(wl.x)
+        self.sets = []
+        for _ in range(self.nsets):
+            s = {"x": x0.clone(), "y": torch.empty_like(x0)}
+            if wl.op == "rg":
+                s["res"] = dev(wl.res)
+                s["r"] = torch.empty_like(x0)
+            self.sets.append(s)
+        self.scale = dev(wl.scale)
+        self.shift = dev(wl.shift)
+        self.weight = dev(wl.weight) if wl.weight is not None else None
+        self.gate = dev(wl.gate) if wl.gate is not None else None
+        self.eps = ctypes.c_float(np.float32(wl.eps))
+        bs = H if B > 1 else 0
+        self.bs = bs
+        del x0
+        torch.cuda.synchronize()
+
+    def call(self, i: int, stream) -> int:
+        s = self.sets[i % self.nsets]
+        B, T, H, bs = self.B, self.T, self.H, self.bs
+        if self.wl.op == "ln":
+            return self.lib.adaln_layernorm_modulate(
+                s["x"].data_ptr(), self.scale.data_ptr(), self.shift.data_ptr(), s["y"].data_ptr(),
+                B, T, H, bs, bs, self.eps, stream)
+        if self.wl.op == "rms":
+            return self.lib.adaln_rmsnorm_scale_shift(
+                s["x"].data_ptr(), None if self.weight is None else self.weight.data_ptr(),
+                self.scale.data_ptr(), self.shift.data_ptr(), s["y"].data_ptr(), B, T, H, bs, bs,
+                self.eps, stream)
+        return self.lib.adaln_residual_gate_rmsnorm_scale_shift(
+            s["res"].data_ptr(), s["x"].data_ptr(), self.gate.data_ptr(),
+            None if self.weight is None else self.weight.data_ptr(), self.scale.data_ptr(),
+            self.shift.data_ptr(), s["r"].data_ptr(), s["y"].data_ptr(), B, T, H, bs, bs, bs,
+            self.eps, stream)
+
+
+def time_steps(launch, steps: int, warmup: int, mode: str):
+    """Elapsed seconds of `steps` launches (warm-up excluded), timed with HIP
+    events on the launch stream, bracketed by synchronize on both sides."""
+    import torch
+    stream = torch.cuda.Stream()
+    handle = stream.cuda_stream
+    with torch.cuda.stream(stream):
+        for i in range(warmup):
+            st = launch(i, handle)
+            if st:
+                raise RuntimeError(f"launch failed with status {st}")
+    torch.cuda.synchronize()
+    start = torch.cuda.Event(enable_timing=True)
+    end = torch.cuda.Event(enable_timing=True)
+    if mode == "graph":
+        graph = torch.cuda.CUDAGraph()
+        with torch.cuda.graph(graph, stream=stream):
+            for i in range(steps):
+                launch(warmup + i, handle)
+        torch.cuda.synchronize()
+        graph.replay()  # untimed replay: graph upload
+        torch.cuda.synchronize()
+        with torch.cuda.stream(stream):
+            start.record(stream)
+            graph.replay()
+            end.record(stream)
+        torch.cuda.synchronize()
+        del graph
+    else:
+        with torch.cuda.stream(stream):
+            start.record(stream)
+            for i in range(steps):
+                launch(warmup + i, handle)
+            end.record(stream)
+        torch.cuda.synchronize()
+    return start.elapsed_time(end) / 1e3
+
+
+def copy_ceiling(nbytes_rw: int, rotate_bytes: int, steps: int, warmup: int, mode="graph"):
+    """GB/s of a plain device copy moving the same bytes (read n/2, write n/2)."""
+    import torch
+    n = nbytes_rw // 4  # bf16 elements per direction
+    nsets = max(2, -(-rotate_bytes // nbytes_rw))
+    src = [torch.empty(n, dtype=torch.bfloat16, device="cuda").fill_(1.0) for _ in range(nsets)]
+    dst = [torch.empty_like(src[0]) for _ in range(nsets)]
+
+    def launch(i, _h):
+        dst[i % nsets].copy_(src[i % nsets])
+        return 0
+
+    t = time_steps(launch, steps, warmup, mode)
+    return nbytes_rw * steps / t / 1e9
+
+
+def cpu_baseline(wl, budget_s: float):
+    from oracle import oracle as O
+    fn = {"ln": lambda: O.layernorm_modulate(wl.x, wl.scale, wl.shift, wl.eps),
+          "rms": lambda: O.rmsnorm_scale_shift(wl.x, wl.weight, wl.scale, wl.shift, wl.eps),
+          "rg": lambda: O.residual_gate_rmsnorm_scale_shift(wl.res, wl.x, wl.gate, wl.weight,
+                                                            wl.scale, wl.shift, wl.eps)}[wl.op]
+    fn()  # warm (page in the library and the arrays)
+    reps = 0
+    t0 = time.perf_counter()
+    while True:
+        fn()
+        reps += 1
+        el = time.perf_counter() - t0
+        if el >= budget_s:
+            break
+    return {"value": round(wl.algorithmic_bytes() * reps / el / 1e9, 4), "unit": "GB/s",
+            "cores": 1, "kind": "oracle",
+            "rows_per_s": round(wl.x.shape[0] * wl.x.shape[1] * reps / el, 1),
+            "sample": f"the whole workload ({wl.x.shape[0] * wl.x.shape[1]} rows) x {reps} "
+                      f"repetitions, single-threaded C oracle, {el:.1f} s"}
+
+
+def describe(wl):
+    B, T, H = wl.x.shape
+    name = {"ln": "layernorm_modulate", "rms": "rmsnorm_scale_shift",
+            "rg": "residual_gate_rmsnorm_scale_shift"}[wl.op]
+    extra = {"rms": " weight 1+0.02N", "rg": " weight none"}.get(wl.op, "")
+    return f"{name} bf16 [{B},{T},{H}]{extra}, eps 1e-6"
+
+
+def main():
+    ap = argparse.ArgumentParser(description=__doc__)
+    ap.add_argument("--gpus", type=int, default=1)
+    ap.add_argument("--steps", type=int, default=400)
+    ap.add_argument("--warmup", type=int, default=40)
+    ap.add_argument("--config", default="1", choices=["0", "1", "2", "3a", "3b"])
+    ap.add_argument("--timing", default="graph", choices=["graph", "eager"])
+    ap.add_argument("--rotate-mb", type=int, default=1024)
+    ap.add_argument("--cpu-seconds", type=float, default=10.0)
+    ap.add_argument("--no-cpu", action="store_true", help="skip the CPU oracle baseline")
+    ap.add_argument("--no-extras", action="store_true",
+                    help="only the headline workload (for profiler runs)")
+    ap.add_argument("--copy-only", action="store_true",
+                    help="only a plain device copy of the workload's byte count (counter "
+                         "calibration for profiler runs)")
+    args = ap.parse_args()
+
+    if args.gpus != 1 or int(os.environ.get("WORLD_SIZE", "1")) != 1:
+        print("bench.py: this path runs on one GPU; row-sharding it across GPUs needs no "
+              "collective and is not measured here (run with --gpus 1)", file=sys.stderr)
+        sys.exit(2)
+
+    import torch
+    if not torch.cuda.is_available():
+        print("bench.py: no GPU visible", file=sys.stderr)
+        sys.exit(2)
+
+    rotate = args.rotate_mb << 20
+    wl = workload(args.config)
+    if args.copy_only:
+        g = copy_ceiling(wl.algorithmic_bytes(), rotate, args.steps, args.warmup, args.timing)
+        print(json.dumps({"copy_GBps": round(g, 2), "bytes_per_copy": wl.algorithmic_bytes(),
+                          "read_bytes": wl.algorithmic_bytes() // 2,
+                          "write_bytes": wl.algorithmic_bytes() // 2}), flush=True)
+        return
+    L = Launcher(wl, rotate)
+    nbytes = wl.algorithmic_bytes()
+    rows = wl.x.shape[0] * wl.x.shape[1]
+
+    t = time_steps(L.call, args.steps, args.warmup, args.timing)
+    gbps = nbytes * args.steps / t / 1e9
+    ms_per_step = t / args.steps * 1e3
+    # average launch duration of the fused kernel: the same events, per launch
+    avg_launch_s = t / args.steps
+
+    name = wl.name
+    traffic = load_counters(name)
+    out = {
+        "metric": METRIC, "value": round(gbps, 2), "unit": "GB/s", "n_gpus": 1,
+        "steps": args.steps, "warmup": args.warmup, "ms_per_step": round(ms_per_step, 5),
+        "higher_is_better": True, "scaling": "weak", "vs_baseline": None, "dtype": "f32",
+        "data": "synthetic",
+        "config": {"workload": describe(wl), "io_dtype": "bf16", "rows": rows,
+                   "bytes_per_step": nbytes, "rotation_sets": L.nsets, "timing": args.timing},
+        "pct_of_peak": round(100.0 * gbps / PEAK_HBM_GBPS, 2),
+        "rows_per_s": round(rows * args.steps / t, 1),
+        "roofline": {"bound": "hbm", "achieved": round(nbytes / avg_launch_s / 1e9, 2),
+                     "peak": PEAK_HBM_GBPS, "unit": "GB/s",
+                     "frac": round(nbytes / avg_launch_s / 1e9 / PEAK_HBM_GBPS, 4),
+                     "traffic": traffic, "kernel": f"fused_norm_modulate ({wl.op})",
+                     "avg_launch_us": round(avg_launch_s * 1e6, 3)},
+    }
+    del L
+    torch.cuda.empty_cache()
+    if not args.no_extras:
+        steps = max(50, args.steps // 2)
+        out["copy_ceiling_GBps"] = round(copy_ceiling(nbytes, rotate, steps, args.warmup), 2)
+        per = {}
+        for cfg in ["0", "1", "2", "3a", "3b"]:
+            w2 = workload(cfg)
+            L2 = Launcher(w2, rotate)
+            res = {}
+            for mode in ("graph", "eager"):
+                t2 = time_steps(L2.call, steps, args.warmup, mode)
+                res[mode] = {"GBps": round(w2.algorithmic_bytes() * steps / t2 / 1e9, 2),
+                             "us_per_launch": round(t2 / steps * 1e6, 3)}
+            per[w2.name] = {"op": w2.op, "shape": list(w2.x.shape),
+                            "bytes": w2.algorithmic_bytes(), **res,
+                            "rows_per_s": round(w2.x.shape[0] * w2.x.shape[1] * steps /
+                                                time_steps(L2.call, steps, 5, "graph"), 1)}
+            del L2
+            torch.cuda.empty_cache()
+        out["per_workload"] = per
+    if not args.no_cpu:
+        cb = cpu_baseline(wl, args.cpu_seconds)
+        cb["cores"] = 1
+        out["cpu_baseline"] = cb
+    print(json.dumps(out), flush=True)
+
+
+if __name__ == "__main__":
+    main()

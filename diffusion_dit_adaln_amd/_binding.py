@@ -38,7 +38,9 @@ _lib = None
 
 
 def library_path() -> str:
-    return os.path.join(_PKG, "libadaln.so")
+    """The in-tree libadaln.so, or the build named by $ADALN_LIBRARY (used to compare
+    launch-tuning builds; the numerics of every build are the same)."""
+    return os.environ.get("ADALN_LIBRARY") or os.path.join(_PKG, "libadaln.so")
 
 
 def load_library():

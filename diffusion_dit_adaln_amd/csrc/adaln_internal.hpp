@@ -25,6 +25,7 @@ struct Params {
     int64_t gate_bs, scale_bs, shift_bs;
     float eps;
     int64_t groups;          // row groups: a wave (H < 4096) or a workgroup (H >= 4096)
+    int64_t per;             // rows per group (the last group may hold fewer)
 };
 
 // Reduction layout of H (the numerics contract): waves per row, lanes, chunks.

@@ -16,10 +16,29 @@
 //    count-weighted combine; test snippet `_eager` for the modulate chain.
 // Built with -ffp-contract=off; fp32 sqrt and divide are the correctly rounded
 // expansions (__builtin_sqrtf and '/'; HIP's __fsqrt_rn is the approximate one).
+//
+// Execution: a persistent grid.  Each group (a wave, or a 4-wave workgroup for
+// H >= 4096) owns a contiguous range of rows.  It keeps the per-column constants
+// of its current batch entry in registers (bf16(1 + scale), shift, weight, gate:
+// computed once per batch entry, not once per row) and loads row i+1 with
+// non-temporal 16-byte loads before it reduces row i, so HBM traffic never waits
+// on the reduction.
 #include <hip/hip_runtime.h>
 #include <stdint.h>
 
+#include <mutex>
+
 #include "adaln_internal.hpp"
+
+// Launch tuning (never changes the numerics): groups per resident group slot, for
+// one-wave rows and for four-wave (workgroup) rows.  Measured on MI355X: the
+// one-wave LayerNorm rows need more, shorter groups to keep every SIMD busy.
+#ifndef ADALN_GROUP_OVERSUBSCRIBE_W1
+#define ADALN_GROUP_OVERSUBSCRIBE_W1 3
+#endif
+#ifndef ADALN_GROUP_OVERSUBSCRIBE_W4
+#define ADALN_GROUP_OVERSUBSCRIBE_W4 1
+#endif
 
 namespace adaln {
 namespace {
@@ -42,10 +61,40 @@ __device__ __forceinline__ u32 pack_bf16(float lo, float hi) {
     return __builtin_bit_cast(u32, r);
 }
 
+// bf16(v) widened back to binary32 in one instruction: with a zero low slot,
+// v_cvt_pk_bf16_f32 leaves bf16(v) in the high half, and that register read as
+// binary32 is exactly the bf16 value (the low half bf16(+0) is all zero bits).
+__device__ __forceinline__ float round_bf16(float v) { return __uint_as_float(pack_bf16(0.0f, v)); }
+
+typedef unsigned int u32x4 __attribute__((ext_vector_type(4)));
+
+// Small per-batch vectors: ordinary cached loads (shared by every row of a batch).
 __device__ __forceinline__ uint4 ld16(const uint16_t* p) {
     return *reinterpret_cast<const uint4*>(p);
 }
-__device__ __forceinline__ void st16(uint16_t* p, uint4 v) { *reinterpret_cast<uint4*>(p) = v; }
+// Activations are touched once: non-temporal (nt) 16-byte buffer loads and stores
+// through a descriptor that spans exactly one group's rows.  An access at an
+// offset past the descriptor's range reads zeros and writes nothing, without
+// memory traffic; the kernel uses that to issue every load and store of its loop
+// unconditionally (refills past the last row, lanes past a ragged row end), so
+// the compiler can count outstanding memory operations exactly and never waits
+// on a prefetch it does not need yet.
+using rsrc_t = __amdgpu_buffer_rsrc_t;
+constexpr int kRsrcWord3 = 0x00020000;  // raw (untyped) buffer, gfx9-family descriptor word 3
+constexpr int kOutOfRange = 0x7FFFFFF0;  // any offset >= the descriptor's byte range
+constexpr int kNonTemporal = 2;          // cache-policy bit nt
+
+__device__ __forceinline__ rsrc_t make_rsrc(const void* base, int64_t bytes) {
+    return __builtin_amdgcn_make_buffer_rsrc(const_cast<void*>(base), 0, (int)bytes, kRsrcWord3);
+}
+__device__ __forceinline__ uint4 ld16_stream(rsrc_t r, int off) {
+    const u32x4 t = __builtin_amdgcn_raw_buffer_load_b128(r, off, 0, kNonTemporal);
+    return make_uint4(t.x, t.y, t.z, t.w);
+}
+__device__ __forceinline__ void st16_stream(rsrc_t r, int off, uint4 v) {
+    const u32x4 t = {v.x, v.y, v.z, v.w};
+    __builtin_amdgcn_raw_buffer_store_b128(t, r, off, 0, kNonTemporal);
+}
 
 __device__ __forceinline__ u32 word(const uint4& v, int j) {
     return j == 0 ? v.x : j == 1 ? v.y : j == 2 ? v.z : v.w;
@@ -80,6 +129,8 @@ struct Welford {
 };
 
 // Chan pairwise combine of (lo, hi) in that order; an empty side yields the other.
+// n = na + nb, delta = mean_b - mean_a, wb = RN(nb/n), mean = mean_a + delta*wb,
+// M2 = (M2a + M2b) + (delta*delta)*(na*wb).
 __device__ __forceinline__ Welford combine(const Welford& lo, const Welford& hi) {
     const float n = lo.n + hi.n;
     const float delta = hi.mean - lo.mean;
@@ -97,7 +148,23 @@ __device__ __forceinline__ Welford combine(const Welford& lo, const Welford& hi)
     return o;
 }
 
-// One in-row butterfly level at distance K (1, 2, 4 or 8) for Welford partials.
+// The same combine when both sides hold NA > 0 elements (every level of a row
+// whose H fills all chunks): wb = RN(NA/2NA) = 1/2 and na*wb = NA/2 exactly, so
+// the two constants below give the bits of the general formula.  m2 enters as
+// the sum M2a + M2b, which fp32 addition makes independent of operand order.
+template <int NA>
+__device__ __forceinline__ void combine_equal(float lo_mean, float hi_mean, float m2_sum,
+                                              float& mean, float& m2) {
+    const float delta = hi_mean - lo_mean;
+    const float step = delta * 0.5f;
+    mean = lo_mean + step;
+    const float dd = delta * delta;
+    const float corr = dd * (0.5f * (float)NA);
+    m2 = m2_sum + corr;
+}
+
+// One in-row butterfly level at distance K (1, 2, 4 or 8) for Welford partials
+// with runtime counts (ragged rows).
 template <int K, int CTRL>
 __device__ __forceinline__ Welford welford_level(const Welford& me, int lane) {
     Welford other{dpp<CTRL>(me.n), dpp<CTRL>(me.mean), dpp<CTRL>(me.m2)};
@@ -105,6 +172,17 @@ __device__ __forceinline__ Welford welford_level(const Welford& me, int lane) {
     Welford lo{upper ? other.n : me.n, upper ? other.mean : me.mean, upper ? other.m2 : me.m2};
     Welford hi{upper ? me.n : other.n, upper ? me.mean : other.mean, upper ? me.m2 : other.m2};
     return combine(lo, hi);
+}
+
+// The same level when both partners hold NA elements.
+template <int K, int CTRL, int NA>
+__device__ __forceinline__ void welford_level_equal(float& mean, float& m2, int lane) {
+    const float om = dpp<CTRL>(mean);
+    const float o2 = dpp<CTRL>(m2);
+    const bool upper = (lane & K) != 0;
+    const float lo = upper ? om : mean;
+    const float hi = upper ? mean : om;
+    combine_equal<NA>(lo, hi, m2 + o2, mean, m2);
 }
 
 __device__ __forceinline__ Welford readlane(const Welford& w, int lane) {
@@ -135,6 +213,21 @@ __device__ __forceinline__ Welford wave_welford(Welford w, int lane) {
     return combine(a, b);
 }
 
+// Wave butterfly when every lane holds N elements.
+template <int N>
+__device__ __forceinline__ void wave_welford_equal(float& mean, float& m2, int lane) {
+    welford_level_equal<1, DPP_XOR1, N>(mean, m2, lane);
+    welford_level_equal<2, DPP_XOR2, 2 * N>(mean, m2, lane);
+    welford_level_equal<4, DPP_HALF_MIRROR, 4 * N>(mean, m2, lane);
+    welford_level_equal<8, DPP_MIRROR, 8 * N>(mean, m2, lane);
+    float ma, qa, mb, qb;
+    combine_equal<16 * N>(readlane(mean, 0), readlane(mean, 16),
+                          readlane(m2, 0) + readlane(m2, 16), ma, qa);
+    combine_equal<16 * N>(readlane(mean, 32), readlane(mean, 48),
+                          readlane(m2, 32) + readlane(m2, 48), mb, qb);
+    combine_equal<32 * N>(ma, mb, qa + qb, mean, m2);
+}
+
 // rstd = RN(1 / RN(sqrt(RN(stat + eps)))), correctly rounded steps.
 __device__ __forceinline__ float finalize(float stat, float eps) {
     const float v = stat + eps;
@@ -145,173 +238,344 @@ __device__ __forceinline__ float finalize(float stat, float eps) {
 // ---------------------------------------------------------------------------
 // the fused row kernel
 // ---------------------------------------------------------------------------
+// Rows in flight per group (prefetch depth + 1), by lane footprint: enough bytes
+// outstanding per CU to cover HBM latency without costing occupancy.
+#ifndef ADALN_SLOTS_SMALL
+#define ADALN_SLOTS_SMALL 3  // <= 16 bf16 of x per lane
+#endif
+#ifndef ADALN_SLOTS_MID
+#define ADALN_SLOTS_MID 3    // <= 32 per lane
+#endif
+#ifndef ADALN_SLOTS_LARGE
+#define ADALN_SLOTS_LARGE 2  // more
+#endif
+// Per-column constants as fp32 (no unpacking per row) when they fit in at most
+// ADALN_KF_MAX registers per lane, else as packed bf16 pairs.
+#ifndef ADALN_KF_MAX
+#define ADALN_KF_MAX 96
+#endif
+constexpr bool consts_as_f32(int W, int C, int op, bool weight) {
+    const int nvec = 2 + (weight ? 1 : 0) + (op == OP_RG ? 1 : 0);
+    return W > 1 || 8 * C * nvec <= ADALN_KF_MAX;
+}
+constexpr int ring_slots(int W, int C, bool gated) {
+    const int per_lane = C * 8 * (gated ? 2 : 1);
+    return per_lane <= 16 ? ADALN_SLOTS_SMALL : per_lane <= 32 ? ADALN_SLOTS_MID
+                                                               : ADALN_SLOTS_LARGE;
+}
+
 // OP: Op; W: waves per row; C: chunks per lane; TAIL: the last chunk is partial;
 // WEIGHT: RMS weight present.  256 threads per workgroup.
+//
+// Per-lane constants of the current batch entry are kept as fp32 (no unpacking
+// per row) or, for wide rows on one wave, as packed bf16 pairs (every constant is
+// a bf16 value); see consts_as_f32.
 template <int OP, int W, int C, bool TAIL, bool WEIGHT>
 __global__ __launch_bounds__(256) void fused_norm_modulate(Params p) {
     constexpr int P = 64 * W;
+    constexpr bool KF = consts_as_f32(W, C, OP, WEIGHT);
+    constexpr int NK = KF ? 8 * C : 4 * C;           // constants per vector per lane
+    constexpr bool GATED = (OP == OP_RG);
+    constexpr int HFULL = C * 8 * P;                 // H when no chunk is partial
+
     const int lane = threadIdx.x & 63;
-    const int wave = threadIdx.x >> 6;
+    // readfirstlane: the wave index is uniform, and the compiler must know it so
+    // that a group's row range and buffer descriptors live in scalar registers
+    const int wave = __builtin_amdgcn_readfirstlane(threadIdx.x >> 6);
     const int64_t group = (W == 1) ? (int64_t)blockIdx.x * 4 + wave : (int64_t)blockIdx.x;
-    if (W == 1 && group >= p.groups) return;  // whole wave leaves (no barriers when W == 1)
-    const int64_t row_begin = group * p.rows / p.groups;
-    const int64_t row_end = (group + 1) * p.rows / p.groups;
+    if (group >= p.groups) return;  // a whole wave (W == 1) or workgroup (W == 4) leaves
+    const int64_t r0 = group * p.per;
+    const int64_t r1 = r0 + p.per < p.rows ? r0 + p.per : p.rows;
+    if (r0 >= r1) return;           // uniform over the group, before any barrier
     const int t = (W == 1) ? lane : wave * 64 + lane;  // lane index within the row
-    const int64_t H = p.H;
-    const float Hf = (float)H;
+    const int64_t H = TAIL ? p.H : HFULL;
 
     __shared__ float xwave[2][4][3];  // cross-wave partials, double-buffered by row parity
 
-    for (int64_t row = row_begin; row < row_end; ++row) {
-        const int64_t b = row / p.T;
-        const int64_t base = row * H;
+    int col[C];
+    bool ok[C];
+#pragma unroll
+    for (int c = 0; c < C; ++c) {
+        col[c] = c * 8 * P + 8 * t;
+        ok[c] = !TAIL || c < C - 1 || col[c] < H;
+    }
 
-        // A1 (+A2): load the row once; the gated variant forms r and stores it.
-        uint4 xb[C];
-        bool ok[C];
+    // ---- per-column constants of batch entry b --------------------------------
+    float ka[KF ? NK : 1], kh[KF ? NK : 1], kw[KF ? NK : 1], kg[KF ? NK : 1];
+    u32 pa[KF ? 1 : NK], ph[KF ? 1 : NK], pw[KF ? 1 : NK], pg[KF ? 1 : NK];
+    auto load_consts = [&](int64_t b) {
+        const uint16_t* sc_row = p.scale + b * p.scale_bs;
+        const uint16_t* sh_row = p.shift + b * p.shift_bs;
+        const uint16_t* g_row = GATED ? p.gate + b * p.gate_bs : nullptr;
 #pragma unroll
         for (int c = 0; c < C; ++c) {
-            const int col = c * 8 * P + 8 * t;
-            ok[c] = !TAIL || c < C - 1 || col < H;
-            xb[c] = make_uint4(0u, 0u, 0u, 0u);
+            uint4 sc = make_uint4(0u, 0u, 0u, 0u), sh = sc, wv = sc, gv = sc;
             if (ok[c]) {
-                uint4 v = ld16(p.x + base + col);
-                if (OP == OP_RG) {
-                    const uint4 rs = ld16(p.res + base + col);
-                    const uint4 g = ld16(p.gate + b * p.gate_bs + col);
-                    u32 rr[4];
+                sc = ld16(sc_row + col[c]);
+                sh = ld16(sh_row + col[c]);
+                if (WEIGHT) wv = ld16(p.weight + col[c]);
+                if (GATED) gv = ld16(g_row + col[c]);
+            }
 #pragma unroll
-                    for (int j = 0; j < 4; ++j) {
-                        const u32 gw = word(g, j), xw = word(v, j), rw = word(rs, j);
-                        const float g0 = bf_lo(gw) * bf_lo(xw);
-                        const float g1 = bf_hi(gw) * bf_hi(xw);
-                        const u32 gx = pack_bf16(g0, g1);
-                        const float r0 = bf_lo(rw) + bf_lo(gx);
-                        const float r1 = bf_hi(rw) + bf_hi(gx);
-                        rr[j] = pack_bf16(r0, r1);
-                    }
-                    v = make_uint4(rr[0], rr[1], rr[2], rr[3]);
-                    st16(p.r + base + col, v);
+            for (int j = 0; j < 4; ++j) {
+                const u32 s = word(sc, j);
+                const u32 a = pack_bf16(1.0f + bf_lo(s), 1.0f + bf_hi(s));  // bf16(1 + scale)
+                const u32 w = word(wv, j);
+                const float w0 = bf_lo(w) + 0.0f, w1 = bf_hi(w) + 0.0f;    // (w + 0.0): -0 -> +0
+                if (KF) {
+                    const int e = c * 8 + 2 * j;
+                    ka[e] = bf_lo(a);
+                    ka[e + 1] = bf_hi(a);
+                    kh[e] = bf_lo(word(sh, j));
+                    kh[e + 1] = bf_hi(word(sh, j));
+                    kw[e] = w0;
+                    kw[e + 1] = w1;
+                    kg[e] = bf_lo(word(gv, j));
+                    kg[e + 1] = bf_hi(word(gv, j));
+                } else {
+                    const int e = c * 4 + j;
+                    pa[e] = a;
+                    ph[e] = word(sh, j);
+                    pw[e] = pack_bf16(w0, w1);  // exact: w + 0 is a bf16 value
+                    pg[e] = word(gv, j);
                 }
-                xb[c] = v;
             }
         }
+    };
+    auto K_a = [&](int c, int v) {
+        return KF ? ka[c * 8 + v] : ((v & 1) ? bf_hi(pa[c * 4 + (v >> 1)]) : bf_lo(pa[c * 4 + (v >> 1)]));
+    };
+    auto K_h = [&](int c, int v) {
+        return KF ? kh[c * 8 + v] : ((v & 1) ? bf_hi(ph[c * 4 + (v >> 1)]) : bf_lo(ph[c * 4 + (v >> 1)]));
+    };
+    auto K_w = [&](int c, int v) {
+        return KF ? kw[c * 8 + v] : ((v & 1) ? bf_hi(pw[c * 4 + (v >> 1)]) : bf_lo(pw[c * 4 + (v >> 1)]));
+    };
+    auto K_g = [&](int c, int v) {
+        return KF ? kg[c * 8 + v] : ((v & 1) ? bf_hi(pg[c * 4 + (v >> 1)]) : bf_lo(pg[c * 4 + (v >> 1)]));
+    };
 
-        // A3: per-lane ordered statistic, b-major then v-minor.
+    // ---- the group's rows through buffer descriptors ----------------------------
+    // Byte offset of (row, chunk) inside the group's range; lanes past a ragged
+    // row end get an out-of-range offset (their loads read zero, stores drop).
+    const int64_t span = (r1 - r0) * H * 2;
+    const rsrc_t rx = make_rsrc(p.x + r0 * H, span);
+    const rsrc_t ry = make_rsrc(p.y + r0 * H, span);
+    const rsrc_t rres = GATED ? make_rsrc(p.res + r0 * H, span) : rx;
+    const rsrc_t rr_out = GATED ? make_rsrc(p.r + r0 * H, span) : ry;
+    auto offset = [&](int64_t row, int c) {
+        return ok[c] ? (int)((row - r0) * H * 2) + 2 * col[c] : kOutOfRange;
+    };
+    // Loads of a row; a row at or past r1 lies beyond the range and reads zeros.
+    auto load_row = [&](int64_t row, uint4 (&xv)[C], uint4 (&rv)[C]) {
+        const int64_t rr = row < r1 ? row : r1;  // keeps the offset arithmetic in range
+#pragma unroll
+        for (int c = 0; c < C; ++c) {
+            const int off = offset(rr, c);
+            xv[c] = ld16_stream(rx, off);
+            if (GATED) rv[c] = ld16_stream(rres, off);
+        }
+    };
+
+    int64_t b = r0 / p.T;
+    int64_t t_in = r0 - b * p.T;
+    load_consts(b);
+
+    // A ring of S row slots: slot k holds row row0 + k; after a row is finished its
+    // slot is refilled with the row S ahead, so S rows' loads stay in flight.
+    constexpr int S = ring_slots(W, C, GATED);
+    uint4 xs[S][C], rs[S][C];
+    // Prologue in the steady state's order: before slot k's loads, stand-ins for
+    // slot k-1's stores (out of range: dropped), so that at the loop head the
+    // outstanding operations after slot 0's loads are the same on the first pass
+    // as on every later one.
+#pragma unroll
+    for (int k = 0; k < S; ++k) {
+        if (k > 0) {
+#pragma unroll
+            for (int i = 0; i < (GATED ? 2 * C : C); ++i)  // distinct, so none is merged
+                st16_stream(ry, kOutOfRange - 16 * i, make_uint4(0u, 0u, 0u, 0u));
+        }
+        load_row(r0 + k, xs[k], rs[k]);
+    }
+
+    // One exit test per pass over the S slots, at the loop head: the only way back
+    // to the head runs through all S slots, so the compiler knows exactly which
+    // loads and stores are still outstanding at each slot and waits only for that
+    // slot's own data.  In the last pass a slot past r1 holds zeros (its loads were
+    // out of range) and its stores land out of range; the host makes the rows per
+    // group a multiple of S, so only the final group can have such slots.
+    for (int64_t row0 = r0; row0 < r1; row0 += S) {
+#pragma unroll
+    for (int k = 0; k < S; ++k) {
+        const int64_t row = row0 + k;
+        uint4 (&xa)[C] = xs[k];
+        uint4 (&ra)[C] = rs[k];
+        const int par = (int)((row - r0) & 1);
+
+        // A2: r = bf16(res + bf16(gate * x)), stored; r is the norm input.  The norm
+        // input is widened to binary32 once and kept for the statistic and A7.
+        float xf[C][8];
+#pragma unroll
+        for (int c = 0; c < C; ++c) {
+            u32 rr[4];
+#pragma unroll
+            for (int j = 0; j < 4; ++j) {
+                u32 xw = word(xa[c], j);
+                if (GATED) {
+                    const u32 rw = word(ra[c], j);
+                    const float g0 = round_bf16(K_g(c, 2 * j) * bf_lo(xw));
+                    const float g1 = round_bf16(K_g(c, 2 * j + 1) * bf_hi(xw));
+                    const float s0 = bf_lo(rw) + g0;
+                    const float s1 = bf_hi(rw) + g1;
+                    xw = pack_bf16(s0, s1);
+                    rr[j] = xw;
+                }
+                xf[c][2 * j] = bf_lo(xw);
+                xf[c][2 * j + 1] = bf_hi(xw);
+            }
+            if (GATED) st16_stream(rr_out, offset(row, c), make_uint4(rr[0], rr[1], rr[2], rr[3]));
+        }
+
+        // A3-A6: ordered per-lane statistic, butterfly, cross-wave pairs, finalize.
         float mean = 0.0f, rstd;
         if (OP == OP_LN) {
-            Welford w{0.0f, 0.0f, 0.0f};
+            float wm = 0.0f, w2 = 0.0f;
 #pragma unroll
             for (int c = 0; c < C; ++c) {
                 if (!ok[c]) continue;
 #pragma unroll
                 for (int v = 0; v < 8; ++v) {
-                    const u32 wd = word(xb[c], v >> 1);
-                    const float x = (v & 1) ? bf_hi(wd) : bf_lo(wd);
+                    const float x = xf[c][v];
                     const float rho = 1.0f / (float)(c * 8 + v + 1);  // RN(1/n), folded
-                    const float d = x - w.mean;
+                    const float d = x - wm;
                     const float step = d * rho;
-                    w.mean = w.mean + step;
-                    const float e = x - w.mean;
+                    wm = wm + step;
+                    const float e = x - wm;
                     const float q = d * e;
-                    w.m2 = w.m2 + q;
+                    w2 = w2 + q;
                 }
             }
-            w.n = TAIL ? (ok[C - 1] ? 8.0f * C : 8.0f * (C - 1)) : 8.0f * C;
-            // A4: wave butterfly; A5: cross-wave pairs through LDS.
-            w = wave_welford(w, lane);
-            if (W > 1) {
-                const int par = (int)((row - row_begin) & 1);
-                if (lane == 0) {
-                    xwave[par][wave][0] = w.n;
-                    xwave[par][wave][1] = w.mean;
-                    xwave[par][wave][2] = w.m2;
+            if (!TAIL) {
+                constexpr int N = 8 * C;
+                wave_welford_equal<N>(wm, w2, lane);
+                if (W > 1) {
+                    if (lane == 0) {
+                        xwave[par][wave][0] = wm;
+                        xwave[par][wave][1] = w2;
+                    }
+                    __syncthreads();
+                    float ma, qa, mb, qb;
+                    combine_equal<64 * N>(xwave[par][0][0], xwave[par][1][0],
+                                          xwave[par][0][1] + xwave[par][1][1], ma, qa);
+                    combine_equal<64 * N>(xwave[par][2][0], xwave[par][3][0],
+                                          xwave[par][2][1] + xwave[par][3][1], mb, qb);
+                    combine_equal<128 * N>(ma, mb, qa + qb, wm, w2);
                 }
-                __syncthreads();
-                Welford q[4];
+            } else {
+                Welford w{ok[C - 1] ? 8.0f * C : 8.0f * (C - 1), wm, w2};
+                w = wave_welford(w, lane);
+                if (W > 1) {
+                    if (lane == 0) {
+                        xwave[par][wave][0] = w.n;
+                        xwave[par][wave][1] = w.mean;
+                        xwave[par][wave][2] = w.m2;
+                    }
+                    __syncthreads();
+                    Welford q[4];
 #pragma unroll
-                for (int i = 0; i < 4; ++i)
-                    q[i] = Welford{xwave[par][i][0], xwave[par][i][1], xwave[par][i][2]};
-                w = combine(combine(q[0], q[1]), combine(q[2], q[3]));
+                    for (int i = 0; i < 4; ++i)
+                        q[i] = Welford{xwave[par][i][0], xwave[par][i][1], xwave[par][i][2]};
+                    w = combine(combine(q[0], q[1]), combine(q[2], q[3]));
+                }
+                wm = w.mean;
+                w2 = w.m2;
             }
-            // A6
-            mean = w.mean;
-            rstd = finalize(w.m2 / Hf, p.eps);
+            mean = wm;
+            rstd = finalize(w2 / (float)H, p.eps);
         } else {
             float s = 0.0f;
 #pragma unroll
             for (int c = 0; c < C; ++c) {
                 if (!ok[c]) continue;
 #pragma unroll
-                for (int j = 0; j < 4; ++j) {
-                    const u32 wd = word(xb[c], j);
-                    const float x0 = bf_lo(wd), x1 = bf_hi(wd);
-                    const float q0 = x0 * x0;
-                    s = s + q0;
-                    const float q1 = x1 * x1;
-                    s = s + q1;
+                for (int v = 0; v < 8; ++v) {
+                    const float q = xf[c][v] * xf[c][v];
+                    s = s + q;
                 }
             }
             s = wave_sum(s);
             if (W > 1) {
-                const int par = (int)((row - row_begin) & 1);
                 if (lane == 0) xwave[par][wave][0] = s;
                 __syncthreads();
                 const float a = xwave[par][0][0] + xwave[par][1][0];
                 const float bb = xwave[par][2][0] + xwave[par][3][0];
                 s = a + bb;
             }
-            rstd = finalize(s / Hf, p.eps);
+            rstd = finalize(s / (float)H, p.eps);
         }
 
-        // A7 + A8: normalise from registers, modulate, 16-byte stores.
-        const uint16_t* sc_row = p.scale + b * p.scale_bs;
-        const uint16_t* sh_row = p.shift + b * p.shift_bs;
+        // A7 + A8: normalise from registers, modulate, 16-byte non-temporal stores.
 #pragma unroll
         for (int c = 0; c < C; ++c) {
-            if (!ok[c]) continue;
-            const int col = c * 8 * P + 8 * t;
-            const uint4 sc = ld16(sc_row + col);
-            const uint4 sh = ld16(sh_row + col);
-            uint4 wv = make_uint4(0u, 0u, 0u, 0u);
-            if (WEIGHT) wv = ld16(p.weight + col);
             u32 out[4];
 #pragma unroll
             for (int j = 0; j < 4; ++j) {
-                const u32 xw = word(xb[c], j);
                 float n0, n1;
                 if (OP == OP_LN) {
-                    const float d0 = bf_lo(xw) - mean;
-                    const float d1 = bf_hi(xw) - mean;
+                    const float d0 = xf[c][2 * j] - mean;
+                    const float d1 = xf[c][2 * j + 1] - mean;
                     n0 = d0 * rstd;
                     n1 = d1 * rstd;
                 } else {
-                    n0 = bf_lo(xw) * rstd;
-                    n1 = bf_hi(xw) * rstd;
+                    n0 = xf[c][2 * j] * rstd;
+                    n1 = xf[c][2 * j + 1] * rstd;
                     if (WEIGHT) {
-                        const u32 ww = word(wv, j);
-                        const float w0 = bf_lo(ww) + 0.0f;  // (w + 0.0): -0 -> +0
-                        const float w1 = bf_hi(ww) + 0.0f;
-                        n0 = n0 * w0;
-                        n1 = n1 * w1;
+                        n0 = n0 * K_w(c, 2 * j);
+                        n1 = n1 * K_w(c, 2 * j + 1);
                     }
                 }
-                const u32 yn = pack_bf16(n0, n1);
-                const u32 scw = word(sc, j);
-                const u32 a = pack_bf16(1.0f + bf_lo(scw), 1.0f + bf_hi(scw));
-                const u32 pr = pack_bf16(bf_lo(yn) * bf_lo(a), bf_hi(yn) * bf_hi(a));
-                const u32 shw = word(sh, j);
-                out[j] = pack_bf16(bf_lo(pr) + bf_lo(shw), bf_hi(pr) + bf_hi(shw));
+                const float y0 = round_bf16(n0), y1 = round_bf16(n1);               // yn
+                const float p0 = round_bf16(y0 * K_a(c, 2 * j));                   // bf16(yn*a)
+                const float p1 = round_bf16(y1 * K_a(c, 2 * j + 1));
+                out[j] = pack_bf16(p0 + K_h(c, 2 * j), p1 + K_h(c, 2 * j + 1));  // bf16(p+shift)
             }
-            st16(p.y + base + col, make_uint4(out[0], out[1], out[2], out[3]));
+            st16_stream(ry, offset(row, c), make_uint4(out[0], out[1], out[2], out[3]));
         }
+
+        // refill this slot S rows ahead; switch batch entry if the next row needs it
+        load_row(row + S, xa, ra);
+        if (row + 1 < r1 && ++t_in == p.T) {  // uniform over the group
+            t_in = 0;
+            ++b;
+            load_consts(b);
+        }
+    }
+    }
+    // Never true (rows > 0): gives the ring registers a use after the loop, so the
+    // compiler cannot sink a refill load below the exit test into the next pass.
+    // Even if executed, the stores land out of range and are dropped.
+    if (p.rows < 0) {
+#pragma unroll
+        for (int k = 0; k < S; ++k)
+#pragma unroll
+            for (int c = 0; c < C; ++c) {
+                st16_stream(ry, kOutOfRange, xs[k][c]);
+                if (GATED) st16_stream(ry, kOutOfRange, rs[k][c]);
+            }
     }
 }
 
 __global__ __launch_bounds__(256) void diag_round(const float* in, uint16_t* out, int64_t n) {
     for (int64_t i = (int64_t)blockIdx.x * blockDim.x + threadIdx.x; i < n;
          i += (int64_t)gridDim.x * blockDim.x)
-        out[i] = (uint16_t)(pack_bf16(in[i], 0.0f) & 0xFFFFu);
+    {
+        // both conversion slots of v_cvt_pk_bf16_f32 are used by the kernels; a
+        // disagreement between them is reported as the quiet NaN 0x7FC1
+        const u32 lo = pack_bf16(in[i], 0.0f) & 0xFFFFu;
+        const u32 hi = __float_as_uint(round_bf16(in[i])) >> 16;
+        out[i] = (uint16_t)(lo == hi ? lo : 0x7FC1u);
+    }
 }
 
 __global__ __launch_bounds__(256) void diag_finalize(const float* in, float* out, int64_t n,
@@ -361,6 +625,40 @@ KernelFn pick(const Layout& L, bool weight) {
     return nullptr;
 }
 
+// Resident workgroups per CU for a kernel on the current device (cached).
+struct OccEntry {
+    KernelFn fn;
+    int device;
+    int blocks_per_cu;
+    int cus;
+};
+
+bool occupancy(KernelFn fn, int* blocks_per_cu, int* cus) {
+    static std::mutex mu;
+    static OccEntry cache[256];
+    static int n_cache = 0;
+    int dev = 0;
+    if (hipGetDevice(&dev) != hipSuccess) return false;
+    std::lock_guard<std::mutex> lock(mu);
+    for (int i = 0; i < n_cache; ++i)
+        if (cache[i].fn == fn && cache[i].device == dev) {
+            *blocks_per_cu = cache[i].blocks_per_cu;
+            *cus = cache[i].cus;
+            return true;
+        }
+    int nb = 0, ncu = 0;
+    if (hipOccupancyMaxActiveBlocksPerMultiprocessor(&nb, reinterpret_cast<const void*>(fn), 256,
+                                                     0) != hipSuccess)
+        return false;
+    if (hipDeviceGetAttribute(&ncu, hipDeviceAttributeMultiprocessorCount, dev) != hipSuccess)
+        return false;
+    if (nb < 1) nb = 1;
+    if (n_cache < 256) cache[n_cache++] = OccEntry{fn, dev, nb, ncu};
+    *blocks_per_cu = nb;
+    *cus = ncu;
+    return true;
+}
+
 }  // namespace
 
 Layout layout_of(int64_t H) {
@@ -379,11 +677,30 @@ hipError_t launch(Op op, const Params& p_in, hipStream_t stream) {
                 : op == OP_RMS ? pick<OP_RMS>(L, weight)
                                : pick<OP_RG>(L, weight);
     if (!fn) return hipErrorInvalidValue;
+    int blocks_per_cu = 0, cus = 0;
+    if (!occupancy(fn, &blocks_per_cu, &cus)) {
+        (void)hipGetLastError();
+        return hipErrorInvalidDeviceFunction;
+    }
     Params p = p_in;
-    // One row per group; very large inputs give each group a contiguous range.
-    const int64_t max_groups = int64_t(1) << 30;
-    p.groups = p.rows < max_groups ? p.rows : max_groups;
-    const int64_t blocks = L.waves == 1 ? (p.groups + 3) / 4 : p.groups;
+    // As many row groups as can be resident at once; each group walks `per`
+    // contiguous rows, a multiple of the kernel's ring depth S, so that only the
+    // last group can end with idle ring slots.
+    const int S = ring_slots(L.waves, L.chunks, op == OP_RG);
+    const int64_t slots = (int64_t)cus * blocks_per_cu *
+                          (L.waves == 1 ? 4 * ADALN_GROUP_OVERSUBSCRIBE_W1
+                                        : ADALN_GROUP_OVERSUBSCRIBE_W4);
+    const int64_t groups0 = p.rows < slots ? p.rows : slots;
+    int64_t per = (p.rows + groups0 - 1) / groups0;
+    per = (per + S - 1) / S * S;
+    // A group's buffer descriptors address its rows with 32-bit byte offsets and the
+    // last pass reaches S rows past its range: keep (per + S) rows below 2^31 bytes.
+    const int64_t max_per = ((int64_t(0x7FFFFFFF) - 64) / (2 * p.H) - S) / S * S;
+    if (per > max_per) per = max_per;
+    p.per = per;
+    p.groups = (p.rows + per - 1) / per;
+    const int64_t groups = p.groups;
+    const int64_t blocks = L.waves == 1 ? (groups + 3) / 4 : groups;
     hipLaunchKernelGGL(fn, dim3((unsigned)blocks), dim3(256), 0, stream, p);
     return hipGetLastError();
 }

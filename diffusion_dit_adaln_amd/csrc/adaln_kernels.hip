@@ -1,8 +1,8 @@
 // adaln_kernels.hip -- gfx950 kernels of libadaln: LayerNorm / RMSNorm fused with
 // the adaLN modulate epilogue, optionally preceded by the residual-gate prologue.
 //
-// One row is owned by one wave (H < 4096) or by one workgroup of 4 waves
-// (H >= 4096).  The row is read from HBM once with 16-byte loads and kept in
+// One row is owned by one wave (H < 2048) or by one workgroup of two waves
+// (H < 4096) or four waves.  The row is read from HBM once with 16-byte loads and kept in
 // registers; the statistic is reduced in the fixed order of the numerics contract
 // (include/adaln.h), which depends on H only, so the bits of a row never depend on
 // the batch it is launched in or on the grid.  Sources, by page title and section:
@@ -17,8 +17,8 @@
 // Built with -ffp-contract=off; fp32 sqrt and divide are the correctly rounded
 // expansions (__builtin_sqrtf and '/'; HIP's __fsqrt_rn is the approximate one).
 //
-// Execution: a persistent grid.  Each group (a wave, or a 4-wave workgroup for
-// H >= 4096) owns a contiguous range of rows.  It keeps the per-column constants
+// Execution: a persistent grid.  Each group (a wave, or a workgroup of W waves)
+// owns a contiguous range of rows.  It keeps the per-column constants
 // of its current batch entry in registers (bf16(1 + scale), shift, weight, gate:
 // computed once per batch entry, not once per row) and loads row i+1 with
 // non-temporal 16-byte loads before it reduces row i, so HBM traffic never waits
@@ -35,6 +35,9 @@
 // one-wave LayerNorm rows need more, shorter groups to keep every SIMD busy.
 #ifndef ADALN_GROUP_OVERSUBSCRIBE_W1
 #define ADALN_GROUP_OVERSUBSCRIBE_W1 3
+#endif
+#ifndef ADALN_GROUP_OVERSUBSCRIBE_W2
+#define ADALN_GROUP_OVERSUBSCRIBE_W2 2
 #endif
 #ifndef ADALN_GROUP_OVERSUBSCRIBE_W4
 #define ADALN_GROUP_OVERSUBSCRIBE_W4 1
@@ -258,7 +261,11 @@ constexpr bool consts_as_f32(int W, int C, int op, bool weight) {
     const int nvec = 2 + (weight ? 1 : 0) + (op == OP_RG ? 1 : 0);
     return W > 1 || 8 * C * nvec <= ADALN_KF_MAX;
 }
+#ifndef ADALN_SLOTS_W2
+#define ADALN_SLOTS_W2 2     // two-wave rows without the gate (2048 <= H < 4096)
+#endif
 constexpr int ring_slots(int W, int C, bool gated) {
+    if (W == 2 && !gated) return ADALN_SLOTS_W2;
     const int per_lane = C * 8 * (gated ? 2 : 1);
     return per_lane <= 16 ? ADALN_SLOTS_SMALL : per_lane <= 32 ? ADALN_SLOTS_MID
                                                                : ADALN_SLOTS_LARGE;
@@ -283,7 +290,7 @@ __global__ __launch_bounds__(256) void fused_norm_modulate(Params p) {
     // that a group's row range and buffer descriptors live in scalar registers
     const int wave = __builtin_amdgcn_readfirstlane(threadIdx.x >> 6);
     const int64_t group = (W == 1) ? (int64_t)blockIdx.x * 4 + wave : (int64_t)blockIdx.x;
-    if (group >= p.groups) return;  // a whole wave (W == 1) or workgroup (W == 4) leaves
+    if (group >= p.groups) return;  // a whole wave (W == 1) or workgroup (W > 1) leaves
     const int64_t r0 = group * p.per;
     const int64_t r1 = r0 + p.per < p.rows ? r0 + p.per : p.rows;
     if (r0 >= r1) return;           // uniform over the group, before any barrier
@@ -465,12 +472,17 @@ __global__ __launch_bounds__(256) void fused_norm_modulate(Params p) {
                         xwave[par][wave][1] = w2;
                     }
                     __syncthreads();
-                    float ma, qa, mb, qb;
-                    combine_equal<64 * N>(xwave[par][0][0], xwave[par][1][0],
-                                          xwave[par][0][1] + xwave[par][1][1], ma, qa);
-                    combine_equal<64 * N>(xwave[par][2][0], xwave[par][3][0],
-                                          xwave[par][2][1] + xwave[par][3][1], mb, qb);
-                    combine_equal<128 * N>(ma, mb, qa + qb, wm, w2);
+                    if (W == 2) {
+                        combine_equal<64 * N>(xwave[par][0][0], xwave[par][1][0],
+                                              xwave[par][0][1] + xwave[par][1][1], wm, w2);
+                    } else {
+                        float ma, qa, mb, qb;
+                        combine_equal<64 * N>(xwave[par][0][0], xwave[par][1][0],
+                                              xwave[par][0][1] + xwave[par][1][1], ma, qa);
+                        combine_equal<64 * N>(xwave[par][2][0], xwave[par][3][0],
+                                              xwave[par][2][1] + xwave[par][3][1], mb, qb);
+                        combine_equal<128 * N>(ma, mb, qa + qb, wm, w2);
+                    }
                 }
             } else {
                 Welford w{ok[C - 1] ? 8.0f * C : 8.0f * (C - 1), wm, w2};
@@ -482,11 +494,14 @@ __global__ __launch_bounds__(256) void fused_norm_modulate(Params p) {
                         xwave[par][wave][2] = w.m2;
                     }
                     __syncthreads();
-                    Welford q[4];
+                    Welford q[W];
 #pragma unroll
-                    for (int i = 0; i < 4; ++i)
+                    for (int i = 0; i < W; ++i)
                         q[i] = Welford{xwave[par][i][0], xwave[par][i][1], xwave[par][i][2]};
-                    w = combine(combine(q[0], q[1]), combine(q[2], q[3]));
+                    if (W == 2)
+                        w = combine(q[0], q[W - 1]);
+                    else
+                        w = combine(combine(q[0], q[1 % W]), combine(q[2 % W], q[3 % W]));
                 }
                 wm = w.mean;
                 w2 = w.m2;
@@ -508,9 +523,13 @@ __global__ __launch_bounds__(256) void fused_norm_modulate(Params p) {
             if (W > 1) {
                 if (lane == 0) xwave[par][wave][0] = s;
                 __syncthreads();
-                const float a = xwave[par][0][0] + xwave[par][1][0];
-                const float bb = xwave[par][2][0] + xwave[par][3][0];
-                s = a + bb;
+                if (W == 2) {
+                    s = xwave[par][0][0] + xwave[par][1][0];
+                } else {
+                    const float a = xwave[par][0][0] + xwave[par][1][0];
+                    const float bb = xwave[par][2][0] + xwave[par][3][0];
+                    s = a + bb;
+                }
             }
             rstd = finalize(s / (float)H, p.eps);
         }
@@ -604,16 +623,20 @@ KernelFn pick_tail(bool tail, bool weight) {
 
 template <int OP>
 KernelFn pick(const Layout& L, bool weight) {
+    // H < 2048: one wave, C = 1..4; 2048 <= H < 4096: two waves, C = 2..4;
+    // H >= 4096: four waves, C = 2..4.
     if (L.waves == 1) {
         switch (L.chunks) {
             case 1: return pick_tail<OP, 1, 1>(L.ragged, weight);
             case 2: return pick_tail<OP, 1, 2>(L.ragged, weight);
             case 3: return pick_tail<OP, 1, 3>(L.ragged, weight);
             case 4: return pick_tail<OP, 1, 4>(L.ragged, weight);
-            case 5: return pick_tail<OP, 1, 5>(L.ragged, weight);
-            case 6: return pick_tail<OP, 1, 6>(L.ragged, weight);
-            case 7: return pick_tail<OP, 1, 7>(L.ragged, weight);
-            case 8: return pick_tail<OP, 1, 8>(L.ragged, weight);
+        }
+    } else if (L.waves == 2) {
+        switch (L.chunks) {
+            case 2: return pick_tail<OP, 2, 2>(L.ragged, weight);
+            case 3: return pick_tail<OP, 2, 3>(L.ragged, weight);
+            case 4: return pick_tail<OP, 2, 4>(L.ragged, weight);
         }
     } else {
         switch (L.chunks) {
@@ -633,7 +656,7 @@ struct OccEntry {
     int cus;
 };
 
-bool occupancy(KernelFn fn, int* blocks_per_cu, int* cus) {
+bool occupancy(KernelFn fn, int block, int* blocks_per_cu, int* cus) {
     static std::mutex mu;
     static OccEntry cache[256];
     static int n_cache = 0;
@@ -647,7 +670,7 @@ bool occupancy(KernelFn fn, int* blocks_per_cu, int* cus) {
             return true;
         }
     int nb = 0, ncu = 0;
-    if (hipOccupancyMaxActiveBlocksPerMultiprocessor(&nb, reinterpret_cast<const void*>(fn), 256,
+    if (hipOccupancyMaxActiveBlocksPerMultiprocessor(&nb, reinterpret_cast<const void*>(fn), block,
                                                      0) != hipSuccess)
         return false;
     if (hipDeviceGetAttribute(&ncu, hipDeviceAttributeMultiprocessorCount, dev) != hipSuccess)
@@ -663,7 +686,7 @@ bool occupancy(KernelFn fn, int* blocks_per_cu, int* cus) {
 
 Layout layout_of(int64_t H) {
     Layout L;
-    L.waves = H < 4096 ? 1 : 4;
+    L.waves = H < 2048 ? 1 : H < 4096 ? 2 : 4;
     L.lanes = 64 * L.waves;
     L.chunks = (int)((H + 8 * L.lanes - 1) / (8 * L.lanes));
     L.ragged = (H % (8 * L.lanes)) != 0;
@@ -677,8 +700,11 @@ hipError_t launch(Op op, const Params& p_in, hipStream_t stream) {
                 : op == OP_RMS ? pick<OP_RMS>(L, weight)
                                : pick<OP_RG>(L, weight);
     if (!fn) return hipErrorInvalidValue;
+    // one-wave rows: four independent waves per workgroup; else one row group per
+    // workgroup of W waves
+    const int block = L.waves == 1 ? 256 : 64 * L.waves;
     int blocks_per_cu = 0, cus = 0;
-    if (!occupancy(fn, &blocks_per_cu, &cus)) {
+    if (!occupancy(fn, block, &blocks_per_cu, &cus)) {
         (void)hipGetLastError();
         return hipErrorInvalidDeviceFunction;
     }
@@ -688,8 +714,9 @@ hipError_t launch(Op op, const Params& p_in, hipStream_t stream) {
     // last group can end with idle ring slots.
     const int S = ring_slots(L.waves, L.chunks, op == OP_RG);
     const int64_t slots = (int64_t)cus * blocks_per_cu *
-                          (L.waves == 1 ? 4 * ADALN_GROUP_OVERSUBSCRIBE_W1
-                                        : ADALN_GROUP_OVERSUBSCRIBE_W4);
+                          (L.waves == 1   ? 4 * ADALN_GROUP_OVERSUBSCRIBE_W1
+                           : L.waves == 2 ? ADALN_GROUP_OVERSUBSCRIBE_W2
+                                          : ADALN_GROUP_OVERSUBSCRIBE_W4);
     const int64_t groups0 = p.rows < slots ? p.rows : slots;
     int64_t per = (p.rows + groups0 - 1) / groups0;
     per = (per + S - 1) / S * S;
@@ -701,7 +728,7 @@ hipError_t launch(Op op, const Params& p_in, hipStream_t stream) {
     p.groups = (p.rows + per - 1) / per;
     const int64_t groups = p.groups;
     const int64_t blocks = L.waves == 1 ? (groups + 3) / 4 : groups;
-    hipLaunchKernelGGL(fn, dim3((unsigned)blocks), dim3(256), 0, stream, p);
+    hipLaunchKernelGGL(fn, dim3((unsigned)blocks), dim3(block), 0, stream, p);
     return hipGetLastError();
 }
 

@@ -28,7 +28,7 @@
  *   every binary32 operation is rounded to nearest-even with no FMA
  *   contraction; sqrt and divide are correctly rounded; denormals are kept.
  *   The reduction order is a function of H only:
- *     W = 1 wave (64 lanes) per row if H < 4096, else W = 4 waves (256 lanes);
+ *     W = 1 wave (64 lanes) per row if H < 2048, 2 waves if H < 4096, else 4;
  *     P = 64W lanes; C = ceil(H / 8P) chunks; lane t owns the columns
  *     b*8P + 8t + v (b < C, v < 8) and visits them b-major, v-minor;
  *     lane partials are folded by a butterfly over the lane index with distances
@@ -73,7 +73,7 @@
 extern "C" {
 #endif
 
-#define ADALN_ABI_VERSION 1
+#define ADALN_ABI_VERSION 2 /* 2: two waves per row for 2048 <= H < 4096 */
 
 typedef uint16_t adaln_bf16; /* raw bfloat16 bits */
 

@@ -28,14 +28,14 @@
  *    1979 for the pairwise combine).
  *
  * The fixed order (a function of H only):
- *   W = 1 wave of 64 lanes per row if H < 4096, else W = 4 waves (256 lanes).
+ *   W waves of 64 lanes per row: W = 1 if H < 2048, W = 2 if H < 4096, else W = 4.
  *   P = 64*W lanes, C = ceil(H / (8*P)) chunks.  Lane t owns the columns
  *   b*8P + 8t + v (b < C, v < 8, column < H) and visits them b-major, v-minor.
  *   Lane partials are folded by a butterfly over the lane index with distances
  *   1, 2, 4, ..., P/2: at distance k every lane combines the partial of lane
  *   (t & ~k) with the partial of lane (t | k) in that order, so all lanes end
  *   with identical bits.  Distances 64 and 128 are the cross-wave combine
- *   ((w0 (+) w1) (+) (w2 (+) w3)).
+ *   (w0 (+) w1) for two waves, ((w0 (+) w1) (+) (w2 (+) w3)) for four.
  *
  * Every arithmetic step below is one IEEE-754 binary32 operation rounded to
  * nearest-even.  The file must be compiled with -ffp-contract=off and without
@@ -104,7 +104,7 @@ static int valid_h(int64_t H) { return H >= 8 && H <= ORACLE_MAX_H && (H % 8) ==
 
 int oracle_layout(int64_t H, int* waves, int* lanes, int* chunks) {
     if (!valid_h(H)) return -1;
-    int W = (H < 4096) ? 1 : 4;
+    int W = (H < 2048) ? 1 : (H < 4096) ? 2 : 4;
     int P = 64 * W;
     int C = (int)((H + 8 * P - 1) / (8 * P));
     if (waves) *waves = W;

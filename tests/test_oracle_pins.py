@@ -544,9 +544,10 @@ def test_finalize_rounding_chain():
 
 
 def test_layout_table():
-    expect = {8: (1, 64, 1), 16: (1, 64, 1), 512: (1, 64, 1), 520: (1, 64, 2), 2048: (1, 64, 4),
-              3072: (1, 64, 6), 4088: (1, 64, 8), 4096: (4, 256, 2), 4104: (4, 256, 3),
-              6144: (4, 256, 3), 8192: (4, 256, 4)}
+    expect = {8: (1, 64, 1), 16: (1, 64, 1), 512: (1, 64, 1), 520: (1, 64, 2), 1024: (1, 64, 2),
+              2040: (1, 64, 4), 2048: (2, 128, 2), 2056: (2, 128, 3), 3072: (2, 128, 3),
+              4088: (2, 128, 4), 4096: (4, 256, 2), 4104: (4, 256, 3), 6144: (4, 256, 3),
+              8192: (4, 256, 4)}
     for H, v in expect.items():
         assert O.layout(H) == v, H
     for H in [0, 4, 12, 8200, -8, 8193]:
@@ -605,3 +606,19 @@ def test_finalize_rounds_sqrt_then_divides():
     assert bits32(st[0, 2]) == 0x3E000043
     assert float(st[0, 3]) == 11863331 * 2.0 ** -25
     assert bits32(st[0, 4]) == 0x403504C3
+
+
+def test_welford_combine_operand_order_two_waves():
+    # H=2048: two waves x 64 lanes, 2 chunks; wave w owns [512w, 512w+512) and
+    # [1024+512w, ...).  Wave 0 holds 1.0, wave 1 holds c = 3*2^-25; each folds to
+    # (1024, value, 0).  combine(w0, w1) as in test_welford_combine_operand_order:
+    # mean 1/2 + 2^-24, M2 = (1 - 2^-22) * 512 = 512 - 2^-13 (0x43FFFFFC),
+    # var = M2 / 2048 = 1/4 - 2^-24.  The reversed operands give mean 1/2.
+    cols = np.arange(2048)
+    x = np.where(((cols % 1024) // 512) == 0, 0x3F80, 0x33C0).astype(np.uint16)[None, None]
+    assert O.layout(2048) == (2, 128, 2)
+    z = np.zeros((1, 2048), np.uint16)
+    _, st = O.layernorm_modulate(x, z, z, EPS, want_stats=True)
+    assert bits32(st[0, 0]) == 0x3F000001
+    assert bits32(st[0, 1]) == 0x43FFFFFC
+    assert bits32(st[0, 2]) == 0x3E7FFFFC

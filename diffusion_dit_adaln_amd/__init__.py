@@ -10,12 +10,15 @@ from ._binding import (  # noqa: F401
     AdalnError,
     adaln_abi_version,
     adaln_check_layernorm_modulate,
+    adaln_check_residual_gate_layernorm_modulate,
     adaln_check_residual_gate_rmsnorm_scale_shift,
     adaln_check_rmsnorm_scale_shift,
     adaln_diag_finalize,
     adaln_diag_round_bf16,
+    adaln_diag_stream_copy,
     adaln_layernorm_modulate,
     adaln_reduction_layout,
+    adaln_residual_gate_layernorm_modulate,
     adaln_residual_gate_rmsnorm_scale_shift,
     adaln_rmsnorm_scale_shift,
     adaln_status_string,

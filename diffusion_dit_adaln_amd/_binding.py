@@ -12,7 +12,7 @@ import os
 import torch
 
 _PKG = os.path.dirname(os.path.abspath(__file__))
-ABI_VERSION = 2
+ABI_VERSION = 3
 
 STATUS_NAMES = {0: "ADALN_OK", 1: "ADALN_ERR_NULL", 2: "ADALN_ERR_SHAPE", 3: "ADALN_ERR_ALIGN",
                 4: "ADALN_ERR_STRIDE", 5: "ADALN_ERR_OVERLAP", 6: "ADALN_ERR_VALUE",
@@ -20,10 +20,12 @@ STATUS_NAMES = {0: "ADALN_OK", 1: "ADALN_ERR_NULL", 2: "ADALN_ERR_SHAPE", 3: "AD
 
 # every symbol include/adaln.h declares
 EXPORTS = ("adaln_layernorm_modulate", "adaln_rmsnorm_scale_shift",
-           "adaln_residual_gate_rmsnorm_scale_shift", "adaln_check_layernorm_modulate",
-           "adaln_check_rmsnorm_scale_shift", "adaln_check_residual_gate_rmsnorm_scale_shift",
-           "adaln_reduction_layout", "adaln_status_string", "adaln_abi_version",
-           "adaln_diag_round_bf16", "adaln_diag_finalize")
+           "adaln_residual_gate_rmsnorm_scale_shift", "adaln_residual_gate_layernorm_modulate",
+           "adaln_check_layernorm_modulate", "adaln_check_rmsnorm_scale_shift",
+           "adaln_check_residual_gate_rmsnorm_scale_shift",
+           "adaln_check_residual_gate_layernorm_modulate", "adaln_reduction_layout",
+           "adaln_status_string", "adaln_abi_version", "adaln_diag_round_bf16",
+           "adaln_diag_finalize", "adaln_diag_stream_copy")
 
 
 class AdalnError(RuntimeError):
@@ -57,13 +59,16 @@ def load_library():
         "adaln_layernorm_modulate": [P, P, P, P, I, I, I, I, I, F, P],
         "adaln_rmsnorm_scale_shift": [P, P, P, P, P, I, I, I, I, I, F, P],
         "adaln_residual_gate_rmsnorm_scale_shift": [P, P, P, P, P, P, P, P, I, I, I, I, I, I, F, P],
+        "adaln_residual_gate_layernorm_modulate": [P, P, P, P, P, P, P, I, I, I, I, I, I, F, P],
         "adaln_check_layernorm_modulate": [P, P, P, P, I, I, I, I, I, F],
         "adaln_check_rmsnorm_scale_shift": [P, P, P, P, P, I, I, I, I, I, F],
         "adaln_check_residual_gate_rmsnorm_scale_shift": [P, P, P, P, P, P, P, P, I, I, I, I, I, I,
                                                           F],
+        "adaln_check_residual_gate_layernorm_modulate": [P, P, P, P, P, P, P, I, I, I, I, I, I, F],
         "adaln_reduction_layout": [I, ctypes.POINTER(S), ctypes.POINTER(S), ctypes.POINTER(S)],
         "adaln_diag_round_bf16": [P, P, I, P],
         "adaln_diag_finalize": [P, P, I, F, P],
+        "adaln_diag_stream_copy": [P, P, I, P],
     }
     for name, args in sig.items():
         fn = getattr(lib, name)
@@ -184,6 +189,26 @@ def adaln_residual_gate_rmsnorm_scale_shift(res, x, gate, weight, scale, shift, 
     return r, y
 
 
+def adaln_residual_gate_layernorm_modulate(res, x, gate, scale, shift, eps: float = 1e-6,
+                                           out=None, r_out=None, stream=None):
+    """(r, y): r = res + gate[b] * x, y = LayerNorm(r) * (1 + scale[b]) + shift[b]."""
+    lib = load_library()
+    _act(res, "res")
+    _act(x, "x")
+    if res.shape != x.shape:
+        raise ValueError("res and x must have the same shape")
+    B, T, H = x.shape
+    gp, gbs = _vec(gate, B, H, "gate")
+    sp, sbs = _vec(scale, B, H, "scale")
+    hp, hbs = _vec(shift, B, H, "shift")
+    y = torch.empty_like(x) if out is None else _act(out, "out")
+    r = torch.empty_like(x) if r_out is None else _act(r_out, "r_out")
+    _check(lib.adaln_residual_gate_layernorm_modulate(
+        res.data_ptr(), x.data_ptr(), gp, sp, hp, r.data_ptr(), y.data_ptr(), B, T, H, gbs, sbs,
+        hbs, _eps(eps), _stream(stream)), "adaln_residual_gate_layernorm_modulate")
+    return r, y
+
+
 def adaln_check_layernorm_modulate(x_ptr, scale_ptr, shift_ptr, y_ptr, B, T, H, scale_bstride,
                                    shift_bstride, eps=1e-6) -> int:
     """Status code of the validation (raw pointers as ints; nothing is launched)."""
@@ -204,6 +229,14 @@ def adaln_check_residual_gate_rmsnorm_scale_shift(res_ptr, x_ptr, gate_ptr, weig
     return load_library().adaln_check_residual_gate_rmsnorm_scale_shift(
         res_ptr, x_ptr, gate_ptr, weight_ptr, scale_ptr, shift_ptr, r_ptr, y_ptr, B, T, H,
         gate_bstride, scale_bstride, shift_bstride, eps)
+
+
+def adaln_check_residual_gate_layernorm_modulate(res_ptr, x_ptr, gate_ptr, scale_ptr, shift_ptr,
+                                                 r_ptr, y_ptr, B, T, H, gate_bstride,
+                                                 scale_bstride, shift_bstride, eps=1e-6) -> int:
+    return load_library().adaln_check_residual_gate_layernorm_modulate(
+        res_ptr, x_ptr, gate_ptr, scale_ptr, shift_ptr, r_ptr, y_ptr, B, T, H, gate_bstride,
+        scale_bstride, shift_bstride, eps)
 
 
 def adaln_reduction_layout(H: int):
@@ -243,3 +276,16 @@ def adaln_diag_finalize(x: torch.Tensor, eps: float = 1e-6, stream=None) -> torc
     _check(lib.adaln_diag_finalize(x.data_ptr(), out.data_ptr(), x.numel(), _eps(eps),
                                    _stream(stream)), "adaln_diag_finalize")
     return out
+
+
+def adaln_diag_stream_copy(src: torch.Tensor, dst: torch.Tensor, stream=None) -> torch.Tensor:
+    """Copy src into dst (same byte size, contiguous) with the library's streaming copy."""
+    lib = load_library()
+    if not (src.is_contiguous() and dst.is_contiguous()):
+        raise ValueError("expected contiguous tensors")
+    nbytes = src.numel() * src.element_size()
+    if dst.numel() * dst.element_size() != nbytes:
+        raise ValueError("src and dst sizes differ")
+    _check(lib.adaln_diag_stream_copy(src.data_ptr(), dst.data_ptr(), nbytes, _stream(stream)),
+           "adaln_diag_stream_copy")
+    return dst

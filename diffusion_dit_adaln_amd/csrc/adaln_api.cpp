@@ -68,8 +68,8 @@ adaln_status check_vec(const void* p, int64_t B, int64_t H, int64_t bstride) {
         if (s_ != ADALN_OK) return s_;   \
     } while (0)
 
-// Validation of all three entry points.  res/gate/r are NULL for LN and RMS; the
-// `need_*` flags say which pointers are required.
+// Validation of the compute entry points.  res/gate/r are required by the gated
+// ops (RG, RGLN) and ignored by LN and RMS.
 adaln_status validate(int op, const void* res, const void* x, const void* gate,
                       const void* weight, const void* scale, const void* shift, const void* r,
                       const void* y, int64_t B, int64_t T, int64_t H, int64_t gate_bs,
@@ -78,7 +78,7 @@ adaln_status validate(int op, const void* res, const void* x, const void* gate,
     ADALN_TRY(check_shape(B, T, H, eps, &rows));
     *rows_out = rows;
     if (rows == 0) return ADALN_OK;
-    const bool gated = op == adaln::OP_RG;
+    const bool gated = adaln::op_gated(op);
     if (!x || !y || (gated && (!res || !r))) return ADALN_ERR_NULL;
     if (!aligned16(x) || !aligned16(y)) return ADALN_ERR_ALIGN;
     if (gated && (!aligned16(res) || !aligned16(r))) return ADALN_ERR_ALIGN;
@@ -168,6 +168,15 @@ adaln_status adaln_residual_gate_rmsnorm_scale_shift(
                scale_bstride, shift_bstride, eps, hip_stream);
 }
 
+adaln_status adaln_residual_gate_layernorm_modulate(
+    const adaln_bf16* res, const adaln_bf16* x, const adaln_bf16* gate, const adaln_bf16* scale,
+    const adaln_bf16* shift, adaln_bf16* r_out, adaln_bf16* y, int64_t B, int64_t T, int64_t H,
+    int64_t gate_bstride, int64_t scale_bstride, int64_t shift_bstride, float eps,
+    void* hip_stream) {
+    return run(adaln::OP_RGLN, res, x, gate, nullptr, scale, shift, r_out, y, B, T, H,
+               gate_bstride, scale_bstride, shift_bstride, eps, hip_stream);
+}
+
 adaln_status adaln_check_layernorm_modulate(const adaln_bf16* x, const adaln_bf16* scale,
                                             const adaln_bf16* shift, const adaln_bf16* y,
                                             int64_t B, int64_t T, int64_t H,
@@ -195,6 +204,15 @@ adaln_status adaln_check_residual_gate_rmsnorm_scale_shift(
     int64_t scale_bstride, int64_t shift_bstride, float eps) {
     int64_t rows;
     return validate(adaln::OP_RG, res, x, gate, weight, scale, shift, r_out, y, B, T, H,
+                    gate_bstride, scale_bstride, shift_bstride, eps, &rows);
+}
+
+adaln_status adaln_check_residual_gate_layernorm_modulate(
+    const adaln_bf16* res, const adaln_bf16* x, const adaln_bf16* gate, const adaln_bf16* scale,
+    const adaln_bf16* shift, const adaln_bf16* r_out, const adaln_bf16* y, int64_t B, int64_t T,
+    int64_t H, int64_t gate_bstride, int64_t scale_bstride, int64_t shift_bstride, float eps) {
+    int64_t rows;
+    return validate(adaln::OP_RGLN, res, x, gate, nullptr, scale, shift, r_out, y, B, T, H,
                     gate_bstride, scale_bstride, shift_bstride, eps, &rows);
 }
 
@@ -242,6 +260,20 @@ adaln_status adaln_diag_finalize(const float* in, float* out, int64_t n, float e
     if (!in || !out) return ADALN_ERR_NULL;
     if (((uintptr_t)in & 3u) || ((uintptr_t)out & 3u)) return ADALN_ERR_ALIGN;
     return adaln::launch_diag_finalize(in, out, n, eps, (hipStream_t)hip_stream) == hipSuccess
+               ? ADALN_OK
+               : ADALN_ERR_LAUNCH;
+}
+
+adaln_status adaln_diag_stream_copy(const void* src, void* dst, int64_t bytes,
+                                    void* hip_stream) {
+    if (bytes < 0 || (bytes % 16) != 0) return ADALN_ERR_SHAPE;
+    if (bytes == 0) return ADALN_OK;
+    if (!src || !dst) return ADALN_ERR_NULL;
+    if (!aligned16(src) || !aligned16(dst)) return ADALN_ERR_ALIGN;
+    const Span a{(uintptr_t)src, (uintptr_t)src + (uintptr_t)bytes};
+    const Span b{(uintptr_t)dst, (uintptr_t)dst + (uintptr_t)bytes};
+    if (overlaps(a, b)) return ADALN_ERR_OVERLAP;
+    return adaln::launch_diag_copy(src, dst, bytes / 16, (hipStream_t)hip_stream) == hipSuccess
                ? ADALN_OK
                : ADALN_ERR_LAUNCH;
 }

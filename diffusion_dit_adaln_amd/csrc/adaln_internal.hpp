@@ -7,24 +7,28 @@
 
 namespace adaln {
 
-enum Op : int { OP_LN = 0, OP_RMS = 1, OP_RG = 2 };
+// LN: LayerNorm + modulate; RMS: RMSNorm + scale/shift; RG: residual gate then
+// RMSNorm + scale/shift; RGLN: residual gate then LayerNorm + modulate.
+enum Op : int { OP_LN = 0, OP_RMS = 1, OP_RG = 2, OP_RGLN = 3 };
+constexpr bool op_gated(int op) { return op == OP_RG || op == OP_RGLN; }
+constexpr bool op_layernorm(int op) { return op == OP_LN || op == OP_RGLN; }
 
 // Arguments of one launch, already validated by the C-ABI layer.
 struct Params {
-    const uint16_t* x;       // norm input (LN, RMS) or the gated update (RG), [rows, H]
-    const uint16_t* res;     // RG: residual stream [rows, H]
-    const uint16_t* gate;    // RG: per-batch gate, row b at gate + b*gate_bs
+    const uint16_t* x;       // norm input (LN, RMS) or the gated update (RG, RGLN), [rows, H]
+    const uint16_t* res;     // RG, RGLN: residual stream [rows, H]
+    const uint16_t* gate;    // RG, RGLN: per-batch gate, row b at gate + b*gate_bs
     const uint16_t* weight;  // RMS / RG: [H] or NULL
     const uint16_t* scale;   // per-batch, row b at scale + b*scale_bs
     const uint16_t* shift;   // per-batch, row b at shift + b*shift_bs
     uint16_t* y;             // [rows, H]
-    uint16_t* r;             // RG: [rows, H]
+    uint16_t* r;             // RG, RGLN: [rows, H]
     int64_t rows;            // B*T > 0
     int64_t T;               // rows per batch entry
     int64_t H;
     int64_t gate_bs, scale_bs, shift_bs;
     float eps;
-    int64_t groups;          // row groups: a wave (H < 4096) or a workgroup (H >= 4096)
+    int64_t groups;          // row groups: a wave (H < 2048) or a workgroup of 2 or 4 waves
     int64_t per;             // rows per group (the last group may hold fewer)
 };
 
@@ -41,5 +45,6 @@ hipError_t launch(Op op, const Params& p, hipStream_t stream);
 hipError_t launch_diag_round(const float* in, uint16_t* out, int64_t n, hipStream_t stream);
 hipError_t launch_diag_finalize(const float* in, float* out, int64_t n, float eps,
                                 hipStream_t stream);
+hipError_t launch_diag_copy(const void* src, void* dst, int64_t n16, hipStream_t stream);
 
 }  // namespace adaln

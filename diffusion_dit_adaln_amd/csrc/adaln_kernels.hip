@@ -258,7 +258,7 @@ __device__ __forceinline__ float finalize(float stat, float eps) {
 #define ADALN_KF_MAX 96
 #endif
 constexpr bool consts_as_f32(int W, int C, int op, bool weight) {
-    const int nvec = 2 + (weight ? 1 : 0) + (op == OP_RG ? 1 : 0);
+    const int nvec = 2 + (weight ? 1 : 0) + (op_gated(op) ? 1 : 0);
     return W > 1 || 8 * C * nvec <= ADALN_KF_MAX;
 }
 #ifndef ADALN_SLOTS_W2
@@ -282,7 +282,8 @@ __global__ __launch_bounds__(256) void fused_norm_modulate(Params p) {
     constexpr int P = 64 * W;
     constexpr bool KF = consts_as_f32(W, C, OP, WEIGHT);
     constexpr int NK = KF ? 8 * C : 4 * C;           // constants per vector per lane
-    constexpr bool GATED = (OP == OP_RG);
+    constexpr bool GATED = op_gated(OP);
+    constexpr bool LNSTAT = op_layernorm(OP);
     constexpr int HFULL = C * 8 * P;                 // H when no chunk is partial
 
     const int lane = threadIdx.x & 63;
@@ -420,8 +421,9 @@ __global__ __launch_bounds__(256) void fused_norm_modulate(Params p) {
         uint4 (&ra)[C] = rs[k];
         const int par = (int)((row - r0) & 1);
 
-        // A2: r = bf16(res + bf16(gate * x)), stored; r is the norm input.  The norm
-        // input is widened to binary32 once and kept for the statistic and A7.
+        // Residual gate (gated ops): r = bf16(res + bf16(gate * x)), stored; r is the
+        // norm input.  The norm input is widened to binary32 once and kept for the
+        // statistic and the normalisation.
         float xf[C][8];
 #pragma unroll
         for (int c = 0; c < C; ++c) {
@@ -444,9 +446,9 @@ __global__ __launch_bounds__(256) void fused_norm_modulate(Params p) {
             if (GATED) st16_stream(rr_out, offset(row, c), make_uint4(rr[0], rr[1], rr[2], rr[3]));
         }
 
-        // A3-A6: ordered per-lane statistic, butterfly, cross-wave pairs, finalize.
+        // Statistic: ordered per-lane chain, butterfly, cross-wave pairs, finalize.
         float mean = 0.0f, rstd;
-        if (OP == OP_LN) {
+        if (LNSTAT) {
             float wm = 0.0f, w2 = 0.0f;
 #pragma unroll
             for (int c = 0; c < C; ++c) {
@@ -534,14 +536,14 @@ __global__ __launch_bounds__(256) void fused_norm_modulate(Params p) {
             rstd = finalize(s / (float)H, p.eps);
         }
 
-        // A7 + A8: normalise from registers, modulate, 16-byte non-temporal stores.
+        // Normalise from registers, modulate, 16-byte non-temporal stores.
 #pragma unroll
         for (int c = 0; c < C; ++c) {
             u32 out[4];
 #pragma unroll
             for (int j = 0; j < 4; ++j) {
                 float n0, n1;
-                if (OP == OP_LN) {
+                if (LNSTAT) {
                     const float d0 = xf[c][2 * j] - mean;
                     const float d1 = xf[c][2 * j + 1] - mean;
                     n0 = d0 * rstd;
@@ -604,6 +606,33 @@ __global__ __launch_bounds__(256) void diag_finalize(const float* in, float* out
         out[i] = finalize(in[i], eps);
 }
 
+// A plain streaming copy with the fused kernel's memory access style (16-byte
+// non-temporal loads and stores): the attainable read+write rate of the device,
+// the ceiling the fused kernel is compared with.  Each thread moves kCopyPer
+// 16-byte vectors, all loads issued before the first store.
+constexpr int kCopyPer = 8;
+__global__ __launch_bounds__(256) void diag_copy(const u32x4* __restrict__ src,
+                                                 u32x4* __restrict__ dst, int64_t n16) {
+    const int64_t base = (int64_t)blockIdx.x * 256 * kCopyPer + threadIdx.x;
+    uint4 v[kCopyPer];
+#pragma unroll
+    for (int k = 0; k < kCopyPer; ++k) {
+        const int64_t i = base + (int64_t)k * 256;
+        if (i < n16) {
+            const u32x4 t = __builtin_nontemporal_load(src + i);
+            v[k] = make_uint4(t.x, t.y, t.z, t.w);
+        }
+    }
+#pragma unroll
+    for (int k = 0; k < kCopyPer; ++k) {
+        const int64_t i = base + (int64_t)k * 256;
+        if (i < n16) {
+            const u32x4 t = {v[k].x, v[k].y, v[k].z, v[k].w};
+            __builtin_nontemporal_store(t, dst + i);
+        }
+    }
+}
+
 // ---------------------------------------------------------------------------
 // host-side dispatch
 // ---------------------------------------------------------------------------
@@ -611,9 +640,12 @@ using KernelFn = void (*)(Params);
 
 template <int OP, int W, int C, bool TAIL>
 KernelFn pick_weight(bool weight) {
-    if (OP == OP_LN) return fused_norm_modulate<OP, W, C, TAIL, false>;
-    return weight ? fused_norm_modulate<OP, W, C, TAIL, true>
-                  : fused_norm_modulate<OP, W, C, TAIL, false>;
+    if constexpr (op_layernorm(OP)) {
+        return fused_norm_modulate<OP, W, C, TAIL, false>;  // LayerNorm has no weight
+    } else {
+        return weight ? fused_norm_modulate<OP, W, C, TAIL, true>
+                      : fused_norm_modulate<OP, W, C, TAIL, false>;
+    }
 }
 
 template <int OP, int W, int C>
@@ -696,9 +728,11 @@ Layout layout_of(int64_t H) {
 hipError_t launch(Op op, const Params& p_in, hipStream_t stream) {
     const Layout L = layout_of(p_in.H);
     const bool weight = p_in.weight != nullptr;
-    KernelFn fn = op == OP_LN ? pick<OP_LN>(L, false)
-                : op == OP_RMS ? pick<OP_RMS>(L, weight)
-                               : pick<OP_RG>(L, weight);
+    KernelFn fn = op == OP_LN    ? pick<OP_LN>(L, false)
+                : op == OP_RMS   ? pick<OP_RMS>(L, weight)
+                : op == OP_RG    ? pick<OP_RG>(L, weight)
+                : op == OP_RGLN  ? pick<OP_RGLN>(L, false)
+                                 : nullptr;
     if (!fn) return hipErrorInvalidValue;
     // one-wave rows: four independent waves per workgroup; else one row group per
     // workgroup of W waves
@@ -712,7 +746,7 @@ hipError_t launch(Op op, const Params& p_in, hipStream_t stream) {
     // As many row groups as can be resident at once; each group walks `per`
     // contiguous rows, a multiple of the kernel's ring depth S, so that only the
     // last group can end with idle ring slots.
-    const int S = ring_slots(L.waves, L.chunks, op == OP_RG);
+    const int S = ring_slots(L.waves, L.chunks, op_gated(op));
     const int64_t slots = (int64_t)cus * blocks_per_cu *
                           (L.waves == 1   ? 4 * ADALN_GROUP_OVERSUBSCRIBE_W1
                            : L.waves == 2 ? ADALN_GROUP_OVERSUBSCRIBE_W2
@@ -743,6 +777,15 @@ hipError_t launch_diag_finalize(const float* in, float* out, int64_t n, float ep
     const int64_t blocks = n / 256 + 1 < 65536 ? n / 256 + 1 : 65536;
     hipLaunchKernelGGL(diag_finalize, dim3((unsigned)blocks), dim3(256), 0, stream, in, out, n,
                        eps);
+    return hipGetLastError();
+}
+
+hipError_t launch_diag_copy(const void* src, void* dst, int64_t n16, hipStream_t stream) {
+    const int64_t per_block = 256 * kCopyPer;
+    const int64_t blocks = (n16 + per_block - 1) / per_block;
+    if (blocks > 0x7FFFFFFF) return hipErrorInvalidValue;
+    hipLaunchKernelGGL(diag_copy, dim3((unsigned)blocks), dim3(256), 0, stream,
+                       static_cast<const u32x4*>(src), static_cast<u32x4*>(dst), n16);
     return hipGetLastError();
 }
 

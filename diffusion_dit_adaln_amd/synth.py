@@ -69,14 +69,14 @@ def normal_bf16(rng: np.random.Generator, shape, sigma: float = 1.0, mu: float =
 @dataclasses.dataclass
 class Workload:
     """One synthetic invocation of an entry point (arrays are bf16 bits)."""
-    op: str                      # "ln" | "rms" | "rg"
+    op: str                      # "ln" | "rms" | "rg" | "rgln"
     name: str
     x: np.ndarray                # [B,T,H]
     scale: np.ndarray            # [B,H] (possibly a strided view)
     shift: np.ndarray            # [B,H]
     weight: np.ndarray | None = None  # [H] (rms / rg)
-    gate: np.ndarray | None = None    # [B,H] (rg)
-    res: np.ndarray | None = None     # [B,T,H] (rg)
+    gate: np.ndarray | None = None    # [B,H] (rg, rgln)
+    res: np.ndarray | None = None     # [B,T,H] (rg, rgln)
     eps: float = 1e-6
 
     @property
@@ -86,7 +86,7 @@ class Workload:
     def algorithmic_bytes(self) -> int:
         """HBM bytes the path must move: read x[,res], write y[,r] (bf16)."""
         n = int(np.prod(self.x.shape))
-        return (8 if self.op == "rg" else 4) * n
+        return (8 if self.op in ("rg", "rgln") else 4) * n
 
 
 def _vecs(seed, cid, B, H, names, sigma=0.1):
@@ -132,6 +132,17 @@ def config3(seed: int = 0, site: str = "a") -> Workload:
     v = _vecs(seed, cid, B, H, ["scale", "shift"])
     return Workload("ln", f"ln_{B}x{T}x{H}", normal_bf16(_rng(seed, cid, "x"), (B, T, H)),
                     v["scale"], v["shift"])
+
+
+def config5(seed: int = 0) -> Workload:
+    """Residual-gate LayerNorm + modulate at the FLUX.1 dual-stream image-token site
+    (hidden 3072, 4096 image tokens, CFG batch of 2): res, x [2,4096,3072] ~ N(0,1);
+    gate/scale/shift [2,3072] ~ 0.1*N."""
+    B, T, H = 2, 4096, 3072
+    v = _vecs(seed, 5, B, H, ["scale", "shift", "gate"])
+    return Workload("rgln", "rg_ln_2x4096x3072", normal_bf16(_rng(seed, 5, "x"), (B, T, H)),
+                    v["scale"], v["shift"], gate=v["gate"],
+                    res=normal_bf16(_rng(seed, 5, "res"), (B, T, H)))
 
 
 def flux_chunk_views(seed: int, B: int, H: int, chunks: int, cid: int = 30):

@@ -1,11 +1,11 @@
 /*
  * adaln.h -- C ABI of libadaln: fused adaLN normalisation for AMD MI355X (gfx950).
  *
- * The three compute entry points fuse a row normalisation (LayerNorm without
+ * The four compute entry points fuse a row normalisation (LayerNorm without
  * affine parameters, or RMSNorm with an optional weight) with the adaLN
  * modulate epilogue  y = norm(x) * (1 + scale[b]) + shift[b]  that diffusion
  * transformers run at every adaLN site, optionally preceded by the residual-gate
- * prologue  r = res + gate[b] * x.
+ * prologue  r = res + gate[b] * x (for both norms).
  *
  * Sources, cited by page title and section:
  *  - FLUX.1 PR report "route the adaLN LN+modulate sites through the bit-exact
@@ -19,8 +19,13 @@
  *    (sglang #33854): the RMSNorm+scale/shift operation and its residual-gate
  *    variant that also returns the residual stream (implementation items 1-2).
  *  - sglang diffusion kernels guide, "selection matrix / Norm + scale/shift":
- *    the rounding points of the chain; "entry-point protocol": unsupported
- *    input raises (here: returns a status), it never degrades silently.
+ *    the rounding points of the chain and of the residual variant; "directory
+ *    layout / kernel registry": the scale_residual_norm_scale_shift operator
+ *    (residual gate + norm + scale/shift) that the LayerNorm gated entry point
+ *    provides; "entry-point protocol": unsupported input raises (here: returns
+ *    a status), it never degrades silently.
+ *  - FLUX.1 PR report, related PRs: the FLUX.1 bit-exact residual-gate fast path
+ *    (#33819) beside the LN+modulate sites.
  *  - Batch-invariance article (vLLM), section 3 (RMSNorm): the reduction layout
  *    depends on the hidden size only, never on the number of rows.
  *
@@ -73,7 +78,8 @@
 extern "C" {
 #endif
 
-#define ADALN_ABI_VERSION 2 /* 2: two waves per row for 2048 <= H < 4096 */
+#define ADALN_ABI_VERSION 3 /* 2: two waves per row for 2048 <= H < 4096;
+                              3: residual-gate LayerNorm, stream copy */
 
 typedef uint16_t adaln_bf16; /* raw bfloat16 bits */
 
@@ -112,6 +118,16 @@ adaln_status adaln_residual_gate_rmsnorm_scale_shift(
     int64_t T, int64_t H, int64_t gate_bstride, int64_t scale_bstride, int64_t shift_bstride,
     float eps, void* hip_stream);
 
+/* r = res + gate[b] * x (written to r_out), then
+ * y = LayerNorm(r) * (1 + scale[b]) + shift[b] with the LayerNorm of
+ * adaln_layernorm_modulate (kernels guide: the residual variant feeds the rounded
+ * r to the same norm; scale_residual_norm_scale_shift in the kernel registry). */
+adaln_status adaln_residual_gate_layernorm_modulate(
+    const adaln_bf16* res, const adaln_bf16* x, const adaln_bf16* gate, const adaln_bf16* scale,
+    const adaln_bf16* shift, adaln_bf16* r_out, adaln_bf16* y, int64_t B, int64_t T, int64_t H,
+    int64_t gate_bstride, int64_t scale_bstride, int64_t shift_bstride, float eps,
+    void* hip_stream);
+
 /* Predicates: the validation of the entry point of the same name, without a
  * launch (the `can_use_*` predicate of the kernels guide's entry-point protocol).
  * They never touch the GPU. */
@@ -130,6 +146,11 @@ adaln_status adaln_check_residual_gate_rmsnorm_scale_shift(
     const adaln_bf16* scale, const adaln_bf16* shift, const adaln_bf16* r_out,
     const adaln_bf16* y, int64_t B, int64_t T, int64_t H, int64_t gate_bstride,
     int64_t scale_bstride, int64_t shift_bstride, float eps);
+
+adaln_status adaln_check_residual_gate_layernorm_modulate(
+    const adaln_bf16* res, const adaln_bf16* x, const adaln_bf16* gate, const adaln_bf16* scale,
+    const adaln_bf16* shift, const adaln_bf16* r_out, const adaln_bf16* y, int64_t B, int64_t T,
+    int64_t H, int64_t gate_bstride, int64_t scale_bstride, int64_t shift_bstride, float eps);
 
 /* The fixed reduction layout for H: waves per row, lanes per row, chunks per
  * lane.  ADALN_ERR_SHAPE for an unsupported H; out-pointers may be NULL. */
@@ -150,6 +171,13 @@ int adaln_abi_version(void);
 adaln_status adaln_diag_round_bf16(const float* in, adaln_bf16* out, int64_t n, void* hip_stream);
 adaln_status adaln_diag_finalize(const float* in, float* out, int64_t n, float eps,
                                  void* hip_stream);
+
+/* Measurement aid: copy `bytes` bytes of device memory from src to dst with the
+ * fused kernels' access style (16-byte non-temporal loads and stores), so that the
+ * attainable streaming rate of the device can be timed beside the fused kernels.
+ * bytes >= 0 and % 16 == 0 (else ADALN_ERR_SHAPE); both pointers 16-byte aligned
+ * (ADALN_ERR_ALIGN); the ranges may not overlap (ADALN_ERR_OVERLAP). */
+adaln_status adaln_diag_stream_copy(const void* src, void* dst, int64_t bytes, void* hip_stream);
 
 #ifdef __cplusplus
 }

@@ -288,6 +288,23 @@ static int check_common(int64_t B, int64_t T, int64_t H) {
  * yn_out (nullable): the bf16 norm output before modulate, [B,T,H].
  * stats_out (nullable): STATS_PER_ROW floats per row, see ln_stat.
  * Returns 0, -1 for bad arguments, or the number of rows whose lanes disagreed. */
+/* Shared LN tail: statistic of the fp32 row xr, then normalise and modulate. */
+static int ln_row(const float* xr, const uint16_t* sc, const uint16_t* sh, int64_t H, float eps,
+                  uint16_t* yrow, uint16_t* ynrow, float* strow) {
+    float st[STATS_PER_ROW];
+    int bad = ln_stat(xr, H, eps, st);
+    float mean = st[0], rstd = st[5];
+    for (int64_t c = 0; c < H; c++) {
+        float d = xr[c] - mean;
+        float p = d * rstd;
+        uint16_t yn = to_bf16(p);
+        if (ynrow) ynrow[c] = yn;
+        yrow[c] = modulate(yn, sc[c], sh[c]);
+    }
+    if (strow) memcpy(strow, st, sizeof st);
+    return bad;
+}
+
 int oracle_layernorm_modulate(const uint16_t* x, const uint16_t* scale, const uint16_t* shift,
                               uint16_t* y, int64_t B, int64_t T, int64_t H, int64_t scale_bstride,
                               int64_t shift_bstride, float eps, uint16_t* yn_out, float* stats_out) {
@@ -299,19 +316,9 @@ int oracle_layernorm_modulate(const uint16_t* x, const uint16_t* scale, const ui
         int64_t b = row / T;
         const uint16_t* xp = x + row * H;
         for (int64_t c = 0; c < H; c++) xr[c] = widen(xp[c]);
-        float st[STATS_PER_ROW];
-        bad += ln_stat(xr, H, eps, st);
-        float mean = st[0], rstd = st[5];
-        const uint16_t* sc = scale + b * scale_bstride;
-        const uint16_t* sh = shift + b * shift_bstride;
-        for (int64_t c = 0; c < H; c++) {
-            float d = xr[c] - mean;
-            float p = d * rstd;
-            uint16_t yn = to_bf16(p);
-            if (yn_out) yn_out[row * H + c] = yn;
-            y[row * H + c] = modulate(yn, sc[c], sh[c]);
-        }
-        if (stats_out) memcpy(stats_out + row * STATS_PER_ROW, st, sizeof st);
+        bad += ln_row(xr, scale + b * scale_bstride, shift + b * shift_bstride, H, eps, y + row * H,
+                      yn_out ? yn_out + row * H : NULL,
+                      stats_out ? stats_out + row * STATS_PER_ROW : NULL);
     }
     fp_leave(env);
     return bad;
@@ -382,6 +389,39 @@ int oracle_residual_gate_rmsnorm_scale_shift(const uint16_t* res, const uint16_t
         bad += rms_row(xr, weight, scale + b * scale_bstride, shift + b * shift_bstride, H, eps,
                        y + row * H, yn_out ? yn_out + row * H : NULL,
                        stats_out ? stats_out + row * STATS_PER_ROW : NULL);
+    }
+    fp_leave(env);
+    return bad;
+}
+
+/* The LayerNorm member of the residual-gate family (the operator the kernels
+ * guide registers as scale_residual_norm_scale_shift, and the FLUX.1 residual-gate
+ * fast path the FLUX PR report relates to): r = res + gate[b]*x with the same two
+ * roundings as above, returned; y = LN(r)*(1+scale[b])+shift[b] with the LN of
+ * oracle_layernorm_modulate. */
+int oracle_residual_gate_layernorm_modulate(const uint16_t* res, const uint16_t* x,
+                                            const uint16_t* gate, const uint16_t* scale,
+                                            const uint16_t* shift, uint16_t* r_out, uint16_t* y,
+                                            int64_t B, int64_t T, int64_t H, int64_t gate_bstride,
+                                            int64_t scale_bstride, int64_t shift_bstride, float eps,
+                                            uint16_t* yn_out, float* stats_out) {
+    if (check_common(B, T, H)) return -1;
+    unsigned int env = fp_enter();
+    float xr[ORACLE_MAX_H];
+    int bad = 0;
+    for (int64_t row = 0; row < B * T; row++) {
+        int64_t b = row / T;
+        const uint16_t* rp = res + row * H;
+        const uint16_t* up = x + row * H;
+        const uint16_t* gp = gate + b * gate_bstride;
+        for (int64_t c = 0; c < H; c++) {
+            uint16_t r = gate_residual(rp[c], up[c], gp[c]);
+            r_out[row * H + c] = r;
+            xr[c] = widen(r);
+        }
+        bad += ln_row(xr, scale + b * scale_bstride, shift + b * shift_bstride, H, eps, y + row * H,
+                      yn_out ? yn_out + row * H : NULL,
+                      stats_out ? stats_out + row * STATS_PER_ROW : NULL);
     }
     fp_leave(env);
     return bad;

@@ -57,6 +57,9 @@ def _load():
     lib.oracle_residual_gate_rmsnorm_scale_shift.argtypes = [P, P, P, P, P, P, P, P, I, I, I, I, I,
                                                              I, F, P, P]
     lib.oracle_residual_gate_rmsnorm_scale_shift.restype = ctypes.c_int
+    lib.oracle_residual_gate_layernorm_modulate.argtypes = [P, P, P, P, P, P, P, I, I, I, I, I, I,
+                                                            F, P, P]
+    lib.oracle_residual_gate_layernorm_modulate.restype = ctypes.c_int
     lib.oracle_round_bf16.argtypes = [P, P, I]
     lib.oracle_round_bf16.restype = None
     lib.oracle_modulate.argtypes = [P, P, P, P, I]
@@ -164,6 +167,30 @@ def residual_gate_rmsnorm_scale_shift(res, x, gate, weight, scale, shift, eps=1e
     _check(rc, "residual_gate_rmsnorm_scale_shift")
     out = (r,) + _ret(y, yn, st, want_norm, want_stats, tup=True)
     return out
+
+
+def residual_gate_layernorm_modulate(res, x, gate, scale, shift, eps=1e-6, want_norm=False,
+                                     want_stats=False):
+    """r = res + gate[b]*x (two roundings); y = LN(r)*(1+scale[b])+shift[b].
+    Returns (r, y[, yn][, stats]); stats are the LN statistics of r."""
+    lib = _load()
+    res = _act(res, "res")
+    x = _act(x, "x")
+    if res.shape != x.shape:
+        raise ValueError("res and x shapes differ")
+    B, T, H = x.shape
+    g, gbs = _vec(gate, B, H, "gate")
+    sc, sbs = _vec(scale, B, H, "scale")
+    sh, hbs = _vec(shift, B, H, "shift")
+    r = np.empty_like(x)
+    y = np.empty_like(x)
+    yn = np.empty_like(x) if want_norm else None
+    st = np.empty((B * T, STATS_PER_ROW), np.float32) if want_stats else None
+    rc = lib.oracle_residual_gate_layernorm_modulate(
+        _ptr(res), _ptr(x), _ptr(g), _ptr(sc), _ptr(sh), _ptr(r), _ptr(y), B, T, H, gbs, sbs, hbs,
+        float(np.float32(eps)), _ptr(yn), _ptr(st))
+    _check(rc, "residual_gate_layernorm_modulate")
+    return (r,) + _ret(y, yn, st, want_norm, want_stats, tup=True)
 
 
 def _ret(y, yn, st, want_norm, want_stats, tup=False):

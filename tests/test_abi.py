@@ -33,14 +33,14 @@ def declared_symbols():
 
 def test_header_symbols_are_exported(lib):
     names = declared_symbols()
-    assert len(names) == 11, names
+    assert len(names) == 14, names
     assert set(names) == set(_binding.EXPORTS)
     for n in names:
         assert hasattr(lib, n), n
 
 
 def test_abi_version_and_status_strings(lib):
-    assert A.adaln_abi_version() == A.ABI_VERSION == 2
+    assert A.adaln_abi_version() == A.ABI_VERSION == 3
     for s in range(8):
         assert len(A.adaln_status_string(s)) > 5
     assert A.adaln_status_string(99) == "unknown status"
@@ -85,10 +85,21 @@ def rg_check(lib, **kw):
         a["T"], a["H"], a["gbs"], a["sbs"], a["hbs"], a["eps"])
 
 
+def rgln_check(lib, **kw):
+    a = dict(res=addr(0), x=addr(1), gate=addr(2), scale=addr(4), shift=addr(5), r=addr(6),
+             y=addr(7), B=2, T=5, H=3072, gbs=3072, sbs=3072, hbs=3072, eps=1e-6)
+    a.update(kw)
+    return lib.adaln_check_residual_gate_layernorm_modulate(
+        a["res"], a["x"], a["gate"], a["scale"], a["shift"], a["r"], a["y"], a["B"], a["T"],
+        a["H"], a["gbs"], a["sbs"], a["hbs"], a["eps"])
+
+
 def test_valid_arguments_pass(lib):
     assert ln_check(lib) == OK
     assert rg_check(lib) == OK
     assert rg_check(lib, w=None) == OK
+    assert rgln_check(lib) == OK
+    assert rgln_check(lib, gbs=6 * 3072, sbs=6 * 3072, hbs=6 * 3072) == OK
     assert lib.adaln_check_rmsnorm_scale_shift(addr(0), None, addr(1), addr(2), addr(3), 1, 7,
                                                2048, 0, 0, 1e-6) == OK
     # FLUX chunk views: scale/shift are slices of one [B, 6H] embedding
@@ -123,6 +134,10 @@ def test_nulls(lib):
     assert rg_check(lib, res=None) == NULL
     assert rg_check(lib, gate=None) == NULL
     assert rg_check(lib, r=None) == NULL
+    assert rgln_check(lib, res=None) == NULL
+    assert rgln_check(lib, gate=None) == NULL
+    assert rgln_check(lib, r=None) == NULL
+    assert rgln_check(lib, scale=None) == NULL
 
 
 def test_alignment(lib):
@@ -131,6 +146,8 @@ def test_alignment(lib):
     assert ln_check(lib, scale=addr(1) + 2) == ALIGN
     assert rg_check(lib, w=addr(3) + 4) == ALIGN
     assert rg_check(lib, r=addr(6) + 2) == ALIGN
+    assert rgln_check(lib, res=addr(0) + 8) == ALIGN
+    assert rgln_check(lib, gate=addr(2) + 2) == ALIGN
 
 
 def test_strides(lib):
@@ -138,6 +155,9 @@ def test_strides(lib):
     assert ln_check(lib, sbs=3076) == STRIDE      # not a multiple of 8
     assert ln_check(lib, hbs=1024) == STRIDE      # in (0, H)
     assert rg_check(lib, gbs=8) == STRIDE
+    assert rgln_check(lib, gbs=3072 + 4) == STRIDE
+    assert rgln_check(lib, H=3068) == SHAPE
+    assert rgln_check(lib, eps=-1.0) == VALUE
 
 
 def test_eps(lib):
@@ -156,6 +176,9 @@ def test_overlaps(lib):
     assert rg_check(lib, r=addr(0)) == OVERLAP                      # r == res
     assert rg_check(lib, y=addr(2)) == OVERLAP                      # y over gate
     assert rg_check(lib, y=addr(3)) == OVERLAP                      # y over weight
+    assert rgln_check(lib, r=addr(7)) == OVERLAP                    # r == y
+    assert rgln_check(lib, y=addr(1)) == OVERLAP                    # y over x
+    assert rgln_check(lib, r=addr(2)) == OVERLAP                    # r over gate
 
 
 def test_compute_entry_points_reject_before_launch(lib):
@@ -167,7 +190,18 @@ def test_compute_entry_points_reject_before_launch(lib):
     assert lib.adaln_residual_gate_rmsnorm_scale_shift(
         addr(0), addr(1), None, None, addr(4), addr(5), addr(6), addr(7), 1, 2, 4096, 0, 0, 0,
         1e-6, None) == NULL
+    assert lib.adaln_residual_gate_layernorm_modulate(
+        addr(0), addr(1), addr(2), addr(4), addr(5), addr(6), addr(6), 1, 2, 3072, 0, 0, 0,
+        1e-6, None) == OVERLAP
+    assert lib.adaln_residual_gate_layernorm_modulate(
+        None, None, None, None, None, None, None, 0, 2, 3072, 0, 0, 0, 1e-6, None) == OK
     assert lib.adaln_diag_round_bf16(None, None, -1, None) == SHAPE
+    assert lib.adaln_diag_stream_copy(addr(0), addr(1), 24, None) == SHAPE
+    assert lib.adaln_diag_stream_copy(addr(0), addr(1), -16, None) == SHAPE
+    assert lib.adaln_diag_stream_copy(addr(0) + 8, addr(1), 32, None) == ALIGN
+    assert lib.adaln_diag_stream_copy(None, addr(1), 32, None) == NULL
+    assert lib.adaln_diag_stream_copy(addr(0), addr(0) + 16, 32, None) == OVERLAP
+    assert lib.adaln_diag_stream_copy(None, None, 0, None) == OK
     assert lib.adaln_diag_finalize(addr(0), addr(1), 4, -1.0, None) == VALUE
 
 

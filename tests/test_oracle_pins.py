@@ -263,6 +263,60 @@ def test_residual_gate_norm_input_is_r():
     assert np.array_equal(y, y2)
 
 
+@pytest.mark.parametrize("shape", [(2, 5, 3072), (1, 3, 4096), (1, 4, 2056), (1, 3, 520),
+                                   (1, 2, 8192)], ids=lambda s: "x".join(map(str, s)))
+@pytest.mark.parametrize("kind", ["normal", "offset", "mixed", "tiny"])
+def test_residual_gate_layernorm_pins(shape, kind):
+    # r against torch's eager bf16 chain res + gate * x; the norm output against the
+    # fp64 two-pass LayerNorm of r; y against the eager modulate of that output
+    B, T, H = shape
+    seed = zlib.crc32(repr((kind, shape, "rgln")).encode()) % 1000
+    res = _rows(kind, B, T, H, seed)
+    x = _rows("normal", B, T, H, seed + 1)
+    rng = np.random.default_rng(seed + 2)
+    g = synth.normal_bf16(rng, (B, H), 0.1)
+    sc = synth.normal_bf16(rng, (B, H), 0.1)
+    sh = synth.normal_bf16(rng, (B, H), 0.1)
+    r, y, yn, st = O.residual_gate_layernorm_modulate(res, x, g, sc, sh, EPS, want_norm=True,
+                                                      want_stats=True)
+    ref_r = from_torch(torch_bf16(res) + torch_bf16(g)[:, None, :] * torch_bf16(x))
+    assert np.array_equal(r, ref_r)
+    ref, floor, _ = ln_ref64(r, EPS32)
+    assert_within(yn, ref, floor, "rgln")
+    assert np.all(st[:, 1] >= 0.0)
+    ref_y = from_torch(torch_bf16(yn) * (1 + torch_bf16(sc)[:, None, :]) + torch_bf16(sh)[:, None, :])
+    assert np.array_equal(y, ref_y)
+
+
+def test_residual_gate_layernorm_special_gates():
+    B, T, H = 2, 4, 3072
+    rng = np.random.default_rng(13)
+    res = _nonzero_bf16(rng, (B, T, H), 1.0)
+    x = _nonzero_bf16(rng, (B, T, H), 1.0)
+    sc = synth.normal_bf16(rng, (B, H), 0.1)
+    sh = synth.normal_bf16(rng, (B, H), 0.1)
+    # gate 0: gate*x is a signed zero and res + (+-0) = res for nonzero res, so the
+    # op reduces to LayerNorm+modulate of res
+    zero = np.zeros((B, H), np.uint16)
+    r, y = O.residual_gate_layernorm_modulate(res, x, zero, sc, sh, EPS)
+    assert np.array_equal(r, res)
+    assert np.array_equal(y, O.layernorm_modulate(res, sc, sh, EPS))
+    # gate 1 and a zero residual: r = x
+    one = np.full((B, H), 0x3F80, np.uint16)
+    r, y = O.residual_gate_layernorm_modulate(np.zeros_like(res), x, one, sc, sh, EPS)
+    assert np.array_equal(r, x)
+    assert np.array_equal(y, O.layernorm_modulate(x, sc, sh, EPS))
+    # a constant residual row with a zero gate gives exactly the shift (LN closed form)
+    c = np.full((B, T, H), 0x4040, np.uint16)   # 3.0
+    _, y = O.residual_gate_layernorm_modulate(c, x, zero, sc, sh, EPS)
+    assert np.array_equal(y, np.broadcast_to(sh[:, None, :], y.shape))
+    # the gate of batch entry b multiplies only that entry's rows
+    g = np.stack([zero[0], one[0]])
+    r, _ = O.residual_gate_layernorm_modulate(np.zeros_like(res), x, g, sc, sh, EPS)
+    assert np.array_equal(r[1], x[1])
+    assert not np.any(r[0] & 0x7FFF)
+
+
 # --------------------------------------------------------------------------
 # the full output is the modulate chain applied to the norm output
 # --------------------------------------------------------------------------

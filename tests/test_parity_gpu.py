@@ -35,6 +35,18 @@ def run_rg(res, x, g, w, sc, sh, eps=EPS):
     return host(r), host(y)
 
 
+def run_rgln(res, x, g, sc, sh, eps=EPS):
+    r, y = A.adaln_residual_gate_layernorm_modulate(dev(res), dev(x), dev(g), dev(sc), dev(sh), eps)
+    return host(r), host(y)
+
+
+def check_rgln(res, x, g, sc, sh, what, eps=EPS):
+    r, y = run_rgln(res, x, g, sc, sh, eps)
+    r0, y0 = O.residual_gate_layernorm_modulate(res, x, g, sc, sh, eps)
+    assert_bits_equal(r, r0, what + " r")
+    assert_bits_equal(y, y0, what + " y")
+
+
 def check_workload(wl, what):
     say(f"[parity] {what} {wl.op} shape={wl.x.shape}")
     if wl.op == "ln":
@@ -43,6 +55,8 @@ def check_workload(wl, what):
     elif wl.op == "rms":
         assert_bits_equal(run_rms(wl.x, wl.weight, wl.scale, wl.shift), O.rmsnorm_scale_shift(
             wl.x, wl.weight, wl.scale, wl.shift, wl.eps), what)
+    elif wl.op == "rgln":
+        check_rgln(wl.res, wl.x, wl.gate, wl.scale, wl.shift, what, wl.eps)
     else:
         r, y = run_rg(wl.res, wl.x, wl.gate, wl.weight, wl.scale, wl.shift)
         r0, y0 = O.residual_gate_rmsnorm_scale_shift(wl.res, wl.x, wl.gate, wl.weight, wl.scale,
@@ -54,10 +68,11 @@ def check_workload(wl, what):
 # --------------------------------------------------------------------------
 # the workloads at full size
 # --------------------------------------------------------------------------
-@pytest.mark.parametrize("cfg", ["0", "1", "2", "3a", "3b"])
+@pytest.mark.parametrize("cfg", ["0", "1", "2", "3a", "3b", "5"])
 def test_workload_full_size(cfg):
     wl = {"0": synth.config0, "1": synth.config1, "2": synth.config2,
-          "3a": lambda: synth.config3(site="a"), "3b": lambda: synth.config3(site="b")}[cfg]()
+          "3a": lambda: synth.config3(site="a"), "3b": lambda: synth.config3(site="b"),
+          "5": synth.config5}[cfg]()
     check_workload(wl, f"config {cfg}")
 
 
@@ -87,6 +102,14 @@ def test_flux_sites_chunk_views(shape, chunks):
     # the RMS variant through the same strided views
     y = host(A.adaln_rmsnorm_scale_shift(dev(x), None, scale_d, shift_d, EPS))
     assert_bits_equal(y, O.rmsnorm_scale_shift(x, None, scale, shift, EPS), f"flux rms {shape}")
+    # the residual-gate LayerNorm with its gate a third slice of the same embedding
+    res = synth.normal_bf16(rng, shape, 8.0)
+    gate = emb[:, 2 * H:3 * H]
+    r, y = A.adaln_residual_gate_layernorm_modulate(dev(res), dev(x), emb_d[:, 2 * H:3 * H],
+                                                    scale_d, shift_d, EPS)
+    r0, y0 = O.residual_gate_layernorm_modulate(res, x, gate, scale, shift, EPS)
+    assert_bits_equal(host(r), r0, f"flux rgln r {shape}")
+    assert_bits_equal(host(y), y0, f"flux rgln y {shape}")
 
 
 # --------------------------------------------------------------------------
@@ -124,6 +147,7 @@ def test_edge_hidden_sizes(H):
         r0, y0 = O.residual_gate_rmsnorm_scale_shift(res, x, g, ww, sc, sh, EPS)
         assert_bits_equal(r, r0, "rg r " + tag)
         assert_bits_equal(y, y0, "rg y " + tag)
+    check_rgln(res, x, g, sc, sh, f"rgln H={H}")
 
 
 @pytest.mark.parametrize("eps", [0.0, 1e-5, 1e-6, 0.25])
@@ -137,6 +161,9 @@ def test_eps_values(eps):
         assert_bits_equal(run_ln(x, sc, sh, eps), O.layernorm_modulate(x, sc, sh, eps), "ln")
         assert_bits_equal(run_rms(x, None, sc, sh, eps), O.rmsnorm_scale_shift(x, None, sc, sh, eps),
                           "rms")
+        res = mixed_rows(rng, 1, 9, H)
+        g = synth.normal_bf16(rng, (1, H), 0.1)
+        check_rgln(res, x, g, sc, sh, f"rgln eps={eps}", eps)
 
 
 def test_constant_and_zero_rows():
@@ -150,6 +177,10 @@ def test_constant_and_zero_rows():
     sh = synth.normal_bf16(rng, (1, H), 0.1)
     assert_bits_equal(run_ln(x, sc, sh), O.layernorm_modulate(x, sc, sh, EPS), "ln")
     assert_bits_equal(run_rms(x, None, sc, sh), O.rmsnorm_scale_shift(x, None, sc, sh, EPS), "rms")
+    # residual gate with a zero gate: r is the constant residual row, y the shift
+    upd = synth.normal_bf16(rng, x.shape)
+    zero = np.zeros((1, H), np.uint16)
+    check_rgln(x, upd, zero, sc, sh, "rgln zero gate")
 
 
 def test_nonfinite_inputs_give_nan_in_the_same_places():
@@ -162,8 +193,14 @@ def test_nonfinite_inputs_give_nan_in_the_same_places():
     x[0, 3, 2000] = 0x7FC0  # nan
     sc = synth.normal_bf16(rng, (1, H), 0.1)
     sh = synth.normal_bf16(rng, (1, H), 0.1)
+    res = synth.normal_bf16(rng, (1, 6, H))
+    res[0, 4, 9] = 0x7F80
+    g = synth.normal_bf16(rng, (1, H), 0.1)
+    rg_r, rg_y = run_rgln(res, x, g, sc, sh)
+    rg_r0, rg_y0 = O.residual_gate_layernorm_modulate(res, x, g, sc, sh, EPS)
     for got, want in ((run_ln(x, sc, sh), O.layernorm_modulate(x, sc, sh, EPS)),
-                      (run_rms(x, None, sc, sh), O.rmsnorm_scale_shift(x, None, sc, sh, EPS))):
+                      (run_rms(x, None, sc, sh), O.rmsnorm_scale_shift(x, None, sc, sh, EPS)),
+                      (rg_r, rg_r0), (rg_y, rg_y0)):
         gn = np.isnan(synth.bf16_bits_to_f32(got))
         wn = np.isnan(synth.bf16_bits_to_f32(want))
         assert np.array_equal(gn, wn)
@@ -232,13 +269,42 @@ def test_rows_alone_equal_rows_in_batch():
     xd, scd, shd = dev(x), dev(sc), dev(sh)
     y = A.adaln_layernorm_modulate(xd, scd, shd, EPS)
     yr = A.adaln_rmsnorm_scale_shift(xd, None, scd, shd, EPS)
+    resd = dev(mixed_rows(rng, B, T, H))
+    gd = dev(synth.normal_bf16(rng, (B, H), 0.1))
+    rg_r, rg_y = A.adaln_residual_gate_layernorm_modulate(resd, xd, gd, scd, shd, EPS)
     for b in range(B):
         for t in range(0, T, 3):
+            r1, y1 = A.adaln_residual_gate_layernorm_modulate(
+                resd[b:b + 1, t:t + 1].contiguous(), xd[b:b + 1, t:t + 1].contiguous(), gd[b],
+                scd[b], shd[b], EPS)
+            assert torch.equal(r1[0, 0].view(torch.int16), rg_r[b, t].view(torch.int16))
+            assert torch.equal(y1[0, 0].view(torch.int16), rg_y[b, t].view(torch.int16))
             y1 = A.adaln_layernorm_modulate(xd[b:b + 1, t:t + 1].contiguous(), scd[b], shd[b], EPS)
             assert torch.equal(y1[0, 0].view(torch.int16), y[b, t].view(torch.int16))
             y2 = A.adaln_rmsnorm_scale_shift(xd[b:b + 1, t:t + 1].contiguous(), None, scd[b],
                                              shd[b], EPS)
             assert torch.equal(y2[0, 0].view(torch.int16), yr[b, t].view(torch.int16))
+
+
+# --------------------------------------------------------------------------
+# the streaming copy used as the bench's ceiling
+# --------------------------------------------------------------------------
+def test_stream_copy_is_exact():
+    say("[diag] stream copy")
+    g = torch.Generator(device="cuda")
+    g.manual_seed(0)
+    for n16 in (1, 255, 2048, 2049, 123457, 4216 * 512):
+        src = torch.randint(-(1 << 31), (1 << 31) - 1, (n16 * 4,), dtype=torch.int32,
+                            device="cuda", generator=g)
+        full = torch.full((n16 * 4 + 64,), 7, dtype=torch.int32, device="cuda")
+        dst = full[: n16 * 4]
+        A.adaln_diag_stream_copy(src, dst)
+        assert torch.equal(src, dst), n16
+        assert bool((full[n16 * 4:] == 7).all()), "wrote past the end"
+    lib = A.load_library()
+    assert lib.adaln_diag_stream_copy(None, None, 0, None) == 0
+    assert lib.adaln_diag_stream_copy(src.data_ptr(), dst.data_ptr(), 24, None) == 2  # SHAPE
+    assert lib.adaln_diag_stream_copy(src.data_ptr(), src.data_ptr() + 16, 64, None) == 5
 
 
 # --------------------------------------------------------------------------

@@ -29,7 +29,9 @@ struct Params {
     int64_t gate_bs, scale_bs, shift_bs;
     float eps;
     int64_t groups;          // row groups: a wave (H < 2048) or a workgroup of 2 or 4 waves
-    int64_t per;             // rows per group (the last group may hold fewer)
+    int64_t group_stride;    // group g's first row is g * group_stride
+    int64_t step;            // rows between a group's consecutive rows
+    int64_t span;            // a group's rows lie below first row + span (and below rows)
 };
 
 // Reduction layout of H (the numerics contract): waves per row, lanes, chunks.

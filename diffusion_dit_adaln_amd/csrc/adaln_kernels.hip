@@ -17,12 +17,14 @@
 // Built with -ffp-contract=off; fp32 sqrt and divide are the correctly rounded
 // expansions (__builtin_sqrtf and '/'; HIP's __fsqrt_rn is the approximate one).
 //
-// Execution: a persistent grid.  Each group (a wave, or a workgroup of W waves)
-// owns a contiguous range of rows.  It keeps the per-column constants
+// Execution: a persistent grid of row groups (a wave, or a workgroup of W waves),
+// at most as many as can be resident at once.  A group owns either a contiguous
+// range of rows or every G-th row (interleaved; then the groups together stream a
+// contiguous band of the tensor at any moment).  It keeps the per-column constants
 // of its current batch entry in registers (bf16(1 + scale), shift, weight, gate:
-// computed once per batch entry, not once per row) and loads row i+1 with
-// non-temporal 16-byte loads before it reduces row i, so HBM traffic never waits
-// on the reduction.
+// computed once per batch entry, not once per row) and keeps its next rows' loads
+// in flight (non-temporal 16-byte loads) while it reduces the current one, so HBM
+// traffic never waits on the reduction.
 #include <hip/hip_runtime.h>
 #include <stdint.h>
 
@@ -30,9 +32,9 @@
 
 #include "adaln_internal.hpp"
 
-// Launch tuning (never changes the numerics): groups per resident group slot, for
-// one-wave rows and for four-wave (workgroup) rows.  Measured on MI355X: the
-// one-wave LayerNorm rows need more, shorter groups to keep every SIMD busy.
+// Launch tuning (never changes the numerics): for contiguous row ranges, groups per
+// resident group slot for one-, two- and four-wave rows.  Measured on MI355X: the
+// narrower rows need more, shorter groups to keep every SIMD busy.
 #ifndef ADALN_GROUP_OVERSUBSCRIBE_W1
 #define ADALN_GROUP_OVERSUBSCRIBE_W1 3
 #endif
@@ -42,11 +44,32 @@
 #ifndef ADALN_GROUP_OVERSUBSCRIBE_W4
 #define ADALN_GROUP_OVERSUBSCRIBE_W4 1
 #endif
+// Row assignment per op (never changes the numerics): interleaved (group g takes
+// rows g, g + G, ...) or contiguous ranges.  Measured on MI355X: the LayerNorm ops
+// gain from the interleaved assignment (more groups, shorter chains), the RMS ops
+// stream slightly faster over contiguous ranges.
+#ifndef ADALN_INTERLEAVE_LN
+#define ADALN_INTERLEAVE_LN 1
+#endif
+#ifndef ADALN_INTERLEAVE_RMS
+#define ADALN_INTERLEAVE_RMS 0
+#endif
+#ifndef ADALN_INTERLEAVE_RG
+#define ADALN_INTERLEAVE_RG 0
+#endif
+#ifndef ADALN_INTERLEAVE_RGLN
+#define ADALN_INTERLEAVE_RGLN 1
+#endif
 
 namespace adaln {
 namespace {
 
 using u32 = uint32_t;
+
+constexpr bool interleaved(int op) {
+    return (op == OP_LN && ADALN_INTERLEAVE_LN) || (op == OP_RMS && ADALN_INTERLEAVE_RMS) ||
+           (op == OP_RG && ADALN_INTERLEAVE_RG) || (op == OP_RGLN && ADALN_INTERLEAVE_RGLN);
+}
 
 // ---------------------------------------------------------------------------
 // bf16 <-> binary32
@@ -277,7 +300,7 @@ constexpr int ring_slots(int W, int C, bool gated) {
 // Per-lane constants of the current batch entry are kept as fp32 (no unpacking
 // per row) or, for wide rows on one wave, as packed bf16 pairs (every constant is
 // a bf16 value); see consts_as_f32.
-template <int OP, int W, int C, bool TAIL, bool WEIGHT>
+template <int OP, int W, int C, bool TAIL, bool WEIGHT, bool IL>
 __global__ __launch_bounds__(256) void fused_norm_modulate(Params p) {
     constexpr int P = 64 * W;
     constexpr bool KF = consts_as_f32(W, C, OP, WEIGHT);
@@ -291,10 +314,14 @@ __global__ __launch_bounds__(256) void fused_norm_modulate(Params p) {
     // that a group's row range and buffer descriptors live in scalar registers
     const int wave = __builtin_amdgcn_readfirstlane(threadIdx.x >> 6);
     const int64_t group = (W == 1) ? (int64_t)blockIdx.x * 4 + wave : (int64_t)blockIdx.x;
-    if (group >= p.groups) return;  // a whole wave (W == 1) or workgroup (W > 1) leaves
-    const int64_t r0 = group * p.per;
-    const int64_t r1 = r0 + p.per < p.rows ? r0 + p.per : p.rows;
-    if (r0 >= r1) return;           // uniform over the group, before any barrier
+    // a whole wave (W == 1) or workgroup (W > 1) leaves, before any barrier
+    if (group >= p.groups) return;
+    // Group g owns the rows r_begin, r_begin + step, ... below r_end: a contiguous
+    // range (step 1) or every G-th row (step G, the interleaved assignment).
+    const int64_t r_begin = group * p.group_stride;
+    const int64_t r_end = r_begin + p.span < p.rows ? r_begin + p.span : p.rows;
+    if (r_begin >= r_end) return;
+    const int64_t step = IL ? p.step : 1;
     const int t = (W == 1) ? lane : wave * 64 + lane;  // lane index within the row
     const int64_t H = TAIL ? p.H : HFULL;
 
@@ -363,34 +390,51 @@ __global__ __launch_bounds__(256) void fused_norm_modulate(Params p) {
         return KF ? kg[c * 8 + v] : ((v & 1) ? bf_hi(pg[c * 4 + (v >> 1)]) : bf_lo(pg[c * 4 + (v >> 1)]));
     };
 
-    // ---- the group's rows through buffer descriptors ----------------------------
-    // Byte offset of (row, chunk) inside the group's range; lanes past a ragged
-    // row end get an out-of-range offset (their loads read zero, stores drop).
-    const int64_t span = (r1 - r0) * H * 2;
-    const rsrc_t rx = make_rsrc(p.x + r0 * H, span);
-    const rsrc_t ry = make_rsrc(p.y + r0 * H, span);
-    const rsrc_t rres = GATED ? make_rsrc(p.res + r0 * H, span) : rx;
-    const rsrc_t rr_out = GATED ? make_rsrc(p.r + r0 * H, span) : ry;
-    auto offset = [&](int64_t row, int c) {
-        return ok[c] ? (int)((row - r0) * H * 2) + 2 * col[c] : kOutOfRange;
+    // ---- addressing through buffer descriptors ---------------------------------
+    // Interleaved rows (IL): one descriptor per row spanning exactly its 2H bytes,
+    // an empty one for a row past the end, and a lane offset that is the same for
+    // every row.  Contiguous rows: one descriptor per tensor over the group's range
+    // and a per-row offset; a row past the range lands beyond it.  Either way lanes
+    // past a ragged row end get an out-of-range offset, and an access out of range
+    // reads zero or is dropped.
+    int voff[C];
+#pragma unroll
+    for (int c = 0; c < C; ++c) voff[c] = ok[c] ? 2 * col[c] : kOutOfRange;
+    const int64_t span_bytes = IL ? 0 : (r_end - r_begin) * H * 2;
+    auto range_rsrc = [&](const uint16_t* base) {
+        return make_rsrc(IL ? base : base + r_begin * H, span_bytes);
     };
-    // Loads of a row; a row at or past r1 lies beyond the range and reads zeros.
+    const rsrc_t gx = range_rsrc(p.x), gy = range_rsrc(p.y);
+    const rsrc_t gres = GATED ? range_rsrc(p.res) : gx;
+    const rsrc_t gr = GATED ? range_rsrc(p.r) : gy;
+    auto rsrc_of = [&](const uint16_t* base, const rsrc_t& range, int64_t row) {
+        if (!IL) return range;
+        return row < r_end ? make_rsrc(base + row * H, H * 2) : make_rsrc(base, 0);
+    };
+    auto off_of = [&](int64_t row, int c) {
+        if (IL) return voff[c];
+        const int64_t rr = row < r_end ? row : r_end;  // keeps the offset arithmetic in range
+        return ok[c] ? (int)((rr - r_begin) * H * 2) + 2 * col[c] : kOutOfRange;
+    };
     auto load_row = [&](int64_t row, uint4 (&xv)[C], uint4 (&rv)[C]) {
-        const int64_t rr = row < r1 ? row : r1;  // keeps the offset arithmetic in range
+        const rsrc_t rx = rsrc_of(p.x, gx, row);
+        const rsrc_t rres = GATED ? rsrc_of(p.res, gres, row) : rx;
 #pragma unroll
         for (int c = 0; c < C; ++c) {
-            const int off = offset(rr, c);
+            const int off = off_of(row, c);
             xv[c] = ld16_stream(rx, off);
             if (GATED) rv[c] = ld16_stream(rres, off);
         }
     };
+    const rsrc_t r_none = make_rsrc(p.y, 0);  // an empty range: every store dropped
 
-    int64_t b = r0 / p.T;
-    int64_t t_in = r0 - b * p.T;
+    int64_t b = r_begin / p.T;
+    int64_t t_in = r_begin - b * p.T;
     load_consts(b);
 
-    // A ring of S row slots: slot k holds row row0 + k; after a row is finished its
-    // slot is refilled with the row S ahead, so S rows' loads stay in flight.
+    // A ring of S row slots: slot k holds the group's row row0 + k*G; after a row is
+    // finished its slot is refilled with the group's row S ahead, so S rows' loads
+    // stay in flight.
     constexpr int S = ring_slots(W, C, GATED);
     uint4 xs[S][C], rs[S][C];
     // Prologue in the steady state's order: before slot k's loads, stand-ins for
@@ -402,24 +446,26 @@ __global__ __launch_bounds__(256) void fused_norm_modulate(Params p) {
         if (k > 0) {
 #pragma unroll
             for (int i = 0; i < (GATED ? 2 * C : C); ++i)  // distinct, so none is merged
-                st16_stream(ry, kOutOfRange - 16 * i, make_uint4(0u, 0u, 0u, 0u));
+                st16_stream(r_none, kOutOfRange - 16 * i, make_uint4(0u, 0u, 0u, 0u));
         }
-        load_row(r0 + k, xs[k], rs[k]);
+        load_row(r_begin + k * step, xs[k], rs[k]);
     }
 
     // One exit test per pass over the S slots, at the loop head: the only way back
     // to the head runs through all S slots, so the compiler knows exactly which
     // loads and stores are still outstanding at each slot and waits only for that
-    // slot's own data.  In the last pass a slot past r1 holds zeros (its loads were
-    // out of range) and its stores land out of range; the host makes the rows per
-    // group a multiple of S, so only the final group can have such slots.
-    for (int64_t row0 = r0; row0 < r1; row0 += S) {
+    // slot's own data.  In the last pass a slot past the group's last row holds
+    // zeros (its loads were out of range) and its stores are dropped.
+    int seq = 0;  // index of the current row among the group's rows
+    for (int64_t row0 = r_begin; row0 < r_end; row0 += S * step) {
 #pragma unroll
     for (int k = 0; k < S; ++k) {
-        const int64_t row = row0 + k;
+        const int64_t row = row0 + k * step;
         uint4 (&xa)[C] = xs[k];
         uint4 (&ra)[C] = rs[k];
-        const int par = (int)((row - r0) & 1);
+        const int par = seq & 1;  // alternates over the group's consecutive rows
+        const rsrc_t ry = rsrc_of(p.y, gy, row);
+        const rsrc_t rr_out = GATED ? rsrc_of(p.r, gr, row) : ry;
 
         // Residual gate (gated ops): r = bf16(res + bf16(gate * x)), stored; r is the
         // norm input.  The norm input is widened to binary32 once and kept for the
@@ -443,8 +489,22 @@ __global__ __launch_bounds__(256) void fused_norm_modulate(Params p) {
                 xf[c][2 * j] = bf_lo(xw);
                 xf[c][2 * j + 1] = bf_hi(xw);
             }
-            if (GATED) st16_stream(rr_out, offset(row, c), make_uint4(rr[0], rr[1], rr[2], rr[3]));
+            if (GATED) st16_stream(rr_out, off_of(row, c), make_uint4(rr[0], rr[1], rr[2], rr[3]));
         }
+
+        // Interleaved rows: the statistic and the normalisation run only for a real
+        // row (a uniform branch with no HBM access inside) and the y stores follow
+        // it, issued either way, so every pass issues the same memory operations in
+        // the same order.  Contiguous rows (only the last group can have an idle
+        // slot): no branch, and each chunk's store leaves as soon as it is ready.
+        u32 yw_out[C][4];
+        if (IL) {
+#pragma unroll
+            for (int c = 0; c < C; ++c)
+#pragma unroll
+                for (int j = 0; j < 4; ++j) yw_out[c][j] = 0u;
+        }
+        if (!IL || row < r_end) {
 
         // Statistic: ordered per-lane chain, butterfly, cross-wave pairs, finalize.
         float mean = 0.0f, rstd;
@@ -536,10 +596,10 @@ __global__ __launch_bounds__(256) void fused_norm_modulate(Params p) {
             rstd = finalize(s / (float)H, p.eps);
         }
 
-        // Normalise from registers, modulate, 16-byte non-temporal stores.
+        // Normalise from registers, modulate.
 #pragma unroll
         for (int c = 0; c < C; ++c) {
-            u32 out[4];
+            u32 (&out)[4] = yw_out[c];
 #pragma unroll
             for (int j = 0; j < 4; ++j) {
                 float n0, n1;
@@ -561,15 +621,34 @@ __global__ __launch_bounds__(256) void fused_norm_modulate(Params p) {
                 const float p1 = round_bf16(y1 * K_a(c, 2 * j + 1));
                 out[j] = pack_bf16(p0 + K_h(c, 2 * j), p1 + K_h(c, 2 * j + 1));  // bf16(p+shift)
             }
-            st16_stream(ry, offset(row, c), make_uint4(out[0], out[1], out[2], out[3]));
+            if (!IL) st16_stream(ry, off_of(row, c), make_uint4(out[0], out[1], out[2], out[3]));
+        }
+        }  // row < r_end
+
+        // 16-byte non-temporal stores of y (interleaved rows)
+        if (IL) {
+#pragma unroll
+            for (int c = 0; c < C; ++c)
+                st16_stream(ry, off_of(row, c), make_uint4(yw_out[c][0], yw_out[c][1],
+                                                           yw_out[c][2], yw_out[c][3]));
         }
 
         // refill this slot S rows ahead; switch batch entry if the next row needs it
-        load_row(row + S, xa, ra);
-        if (row + 1 < r1 && ++t_in == p.T) {  // uniform over the group
-            t_in = 0;
-            ++b;
-            load_consts(b);
+        load_row(row + S * step, xa, ra);
+        ++seq;
+        const int64_t next = row + step;
+        if (next < r_end) {  // uniform over the group
+            t_in += step;
+            if (t_in >= p.T) {
+                if (IL) {
+                    b = next / p.T;
+                    t_in = next - b * p.T;
+                } else {  // consecutive rows: the next batch entry
+                    ++b;
+                    t_in = 0;
+                }
+                load_consts(b);
+            }
         }
     }
     }
@@ -581,8 +660,8 @@ __global__ __launch_bounds__(256) void fused_norm_modulate(Params p) {
         for (int k = 0; k < S; ++k)
 #pragma unroll
             for (int c = 0; c < C; ++c) {
-                st16_stream(ry, kOutOfRange, xs[k][c]);
-                if (GATED) st16_stream(ry, kOutOfRange, rs[k][c]);
+                st16_stream(r_none, kOutOfRange, xs[k][c]);
+                if (GATED) st16_stream(r_none, kOutOfRange, rs[k][c]);
             }
     }
 }
@@ -640,11 +719,12 @@ using KernelFn = void (*)(Params);
 
 template <int OP, int W, int C, bool TAIL>
 KernelFn pick_weight(bool weight) {
+    constexpr bool IL = interleaved(OP);
     if constexpr (op_layernorm(OP)) {
-        return fused_norm_modulate<OP, W, C, TAIL, false>;  // LayerNorm has no weight
+        return fused_norm_modulate<OP, W, C, TAIL, false, IL>;  // LayerNorm has no weight
     } else {
-        return weight ? fused_norm_modulate<OP, W, C, TAIL, true>
-                      : fused_norm_modulate<OP, W, C, TAIL, false>;
+        return weight ? fused_norm_modulate<OP, W, C, TAIL, true, IL>
+                      : fused_norm_modulate<OP, W, C, TAIL, false, IL>;
     }
 }
 
@@ -743,23 +823,33 @@ hipError_t launch(Op op, const Params& p_in, hipStream_t stream) {
         return hipErrorInvalidDeviceFunction;
     }
     Params p = p_in;
-    // As many row groups as can be resident at once; each group walks `per`
-    // contiguous rows, a multiple of the kernel's ring depth S, so that only the
-    // last group can end with idle ring slots.
     const int S = ring_slots(L.waves, L.chunks, op_gated(op));
-    const int64_t slots = (int64_t)cus * blocks_per_cu *
-                          (L.waves == 1   ? 4 * ADALN_GROUP_OVERSUBSCRIBE_W1
-                           : L.waves == 2 ? ADALN_GROUP_OVERSUBSCRIBE_W2
-                                          : ADALN_GROUP_OVERSUBSCRIBE_W4);
-    const int64_t groups0 = p.rows < slots ? p.rows : slots;
-    int64_t per = (p.rows + groups0 - 1) / groups0;
-    per = (per + S - 1) / S * S;
-    // A group's buffer descriptors address its rows with 32-bit byte offsets and the
-    // last pass reaches S rows past its range: keep (per + S) rows below 2^31 bytes.
-    const int64_t max_per = ((int64_t(0x7FFFFFFF) - 64) / (2 * p.H) - S) / S * S;
-    if (per > max_per) per = max_per;
-    p.per = per;
-    p.groups = (p.rows + per - 1) / per;
+    const int64_t resident = (int64_t)cus * blocks_per_cu * (L.waves == 1 ? 4 : 1);
+    if (interleaved(op)) {
+        // one group per resident group slot (at most one per row); a group's ring
+        // slots past its last row skip their arithmetic
+        p.groups = p.rows < resident ? p.rows : resident;
+        p.group_stride = 1;
+        p.step = p.groups;
+        p.span = p.rows;
+    } else {
+        // `per` contiguous rows per group, a multiple of S so that only the last
+        // group can end with idle ring slots; the group's descriptors address its
+        // rows with 32-bit byte offsets and the last pass reaches S rows past its
+        // range, so (per + S) rows stay below 2^31 bytes
+        const int64_t slots = resident * (L.waves == 1   ? ADALN_GROUP_OVERSUBSCRIBE_W1
+                                          : L.waves == 2 ? ADALN_GROUP_OVERSUBSCRIBE_W2
+                                                         : ADALN_GROUP_OVERSUBSCRIBE_W4);
+        const int64_t groups0 = p.rows < slots ? p.rows : slots;
+        int64_t per = (p.rows + groups0 - 1) / groups0;
+        per = (per + S - 1) / S * S;
+        const int64_t max_per = ((int64_t(0x7FFFFFFF) - 64) / (2 * p.H) - S) / S * S;
+        if (per > max_per) per = max_per;
+        p.groups = (p.rows + per - 1) / per;
+        p.group_stride = per;
+        p.step = 1;
+        p.span = per;
+    }
     const int64_t groups = p.groups;
     const int64_t blocks = L.waves == 1 ? (groups + 3) / 4 : groups;
     hipLaunchKernelGGL(fn, dim3((unsigned)blocks), dim3(block), 0, stream, p);

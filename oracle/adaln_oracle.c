@@ -273,6 +273,49 @@ static uint16_t gate_residual(uint16_t res, uint16_t upd, uint16_t gate) {
 }
 
 /* ------------------------------------------------------------------------ */
+/* static FP8 quantisation (OCP E4M3, "e4m3fn")                              */
+/* ------------------------------------------------------------------------ */
+/* The format: 1 sign bit, 4 exponent bits with bias 7, 3 mantissa bits; exponent
+ * field 0 holds the subnormals m * 2^-9; there is no infinity; S.1111.111 is NaN,
+ * so the largest finite value is 1.75 * 2^8 = 448.  Rounding to nearest-even from
+ * the definition: the spacing of representable values around |v| is 2^(E-3) for
+ * |v| in [2^E, 2^(E+1)) with E >= -6, and 2^-9 below 2^-6. */
+static uint8_t to_e4m3fn(float v) {
+    uint8_t sign = signbit(v) ? 0x80 : 0x00;
+    if (isnan(v)) return sign | 0x7F;
+    double a = fabs((double)v);
+    if (a == 0.0) return sign;
+    int e2;
+    (void)frexp(a, &e2);        /* a = f * 2^e2, f in [0.5, 1): floor(log2 a) = e2 - 1 */
+    int E = e2 - 1;
+    if (E < -6) E = -6;         /* subnormal range shares the spacing of [2^-6, 2^-5) */
+    double units = ldexp(a, 3 - E);    /* a / spacing, exact (power-of-two scaling) */
+    double r = nearbyint(units);       /* round half to even (default rounding mode) */
+    /* r in [8, 16] for the normal range (16: carry into the next binade), in [0, 8]
+     * below 2^-6 (8: the smallest normal); the encoding is continuous across both */
+    int code;
+    if (r >= 8.0) {
+        int e = E, m = (int)r - 8;
+        if (r == 16.0) { e = E + 1; m = 0; }
+        code = ((e + 7) << 3) | m;
+    } else {
+        code = (int)r;  /* exponent field 0: m * 2^-9 */
+    }
+    if (code >= 0x7F) return sign | 0x7F;  /* beyond 448: NaN (the caller clamps first) */
+    return sign | (uint8_t)code;
+}
+
+/* q = e4m3fn(clamp(RN(f(y) * inv), -448, 448)); NaN stays NaN. */
+static uint8_t quant_fp8(uint16_t y, float inv) {
+    float v = widen(y) * inv;
+    if (!isnan(v)) {
+        if (v > 448.0f) v = 448.0f;
+        if (v < -448.0f) v = -448.0f;
+    }
+    return to_e4m3fn(v);
+}
+
+/* ------------------------------------------------------------------------ */
 /* entry points                                                              */
 /* ------------------------------------------------------------------------ */
 #define STATS_PER_ROW 6
@@ -427,6 +470,37 @@ int oracle_residual_gate_layernorm_modulate(const uint16_t* res, const uint16_t*
     return bad;
 }
 
+/* LayerNorm + modulate + static FP8 quantisation (kernels guide, data movement and
+ * quantised layout producers: fused_layernorm_modulate_fp8_quant_raw folds FLUX.2's
+ * LayerNorm, adaLN modulate and static FP8 quantisation into one kernel):
+ * y = LN(x)*(1+scale[b])+shift[b] exactly as oracle_layernorm_modulate (bf16), then
+ * q = e4m3fn(clamp(RN(f(y) * RN(1/qscale)), -448, 448)), one byte per element.
+ * y_out (nullable) receives the bf16 y. */
+int oracle_layernorm_modulate_fp8(const uint16_t* x, const uint16_t* scale, const uint16_t* shift,
+                                  float qscale, uint8_t* q, int64_t B, int64_t T, int64_t H,
+                                  int64_t scale_bstride, int64_t shift_bstride, float eps,
+                                  uint16_t* y_out, float* stats_out) {
+    if (check_common(B, T, H)) return -1;
+    unsigned int env = fp_enter();
+    float xr[ORACLE_MAX_H];
+    uint16_t yr[ORACLE_MAX_H];
+    const float inv = 1.0f / qscale;  /* correctly rounded */
+    int bad = 0;
+    for (int64_t row = 0; row < B * T; row++) {
+        int64_t b = row / T;
+        const uint16_t* xp = x + row * H;
+        for (int64_t c = 0; c < H; c++) xr[c] = widen(xp[c]);
+        bad += ln_row(xr, scale + b * scale_bstride, shift + b * shift_bstride, H, eps, yr, NULL,
+                      stats_out ? stats_out + row * STATS_PER_ROW : NULL);
+        for (int64_t c = 0; c < H; c++) {
+            q[row * H + c] = quant_fp8(yr[c], inv);
+            if (y_out) y_out[row * H + c] = yr[c];
+        }
+    }
+    fp_leave(env);
+    return bad;
+}
+
 /* ------------------------------------------------------------------------ */
 /* elementwise helpers exposed for the pins                                  */
 /* ------------------------------------------------------------------------ */
@@ -447,6 +521,19 @@ void oracle_gate_residual(const uint16_t* res, const uint16_t* x, const uint16_t
                           uint16_t* out, int64_t n) {
     unsigned int env = fp_enter();
     for (int64_t i = 0; i < n; i++) out[i] = gate_residual(res[i], x[i], gate[i]);
+    fp_leave(env);
+}
+
+void oracle_to_e4m3fn(const float* in, uint8_t* out, int64_t n) {
+    unsigned int env = fp_enter();
+    for (int64_t i = 0; i < n; i++) out[i] = to_e4m3fn(in[i]);
+    fp_leave(env);
+}
+
+void oracle_quant_fp8(const uint16_t* y, uint8_t* q, int64_t n, float qscale) {
+    unsigned int env = fp_enter();
+    const float inv = 1.0f / qscale;
+    for (int64_t i = 0; i < n; i++) q[i] = quant_fp8(y[i], inv);
     fp_leave(env);
 }
 

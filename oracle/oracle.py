@@ -60,6 +60,12 @@ def _load():
     lib.oracle_residual_gate_layernorm_modulate.argtypes = [P, P, P, P, P, P, P, I, I, I, I, I, I,
                                                             F, P, P]
     lib.oracle_residual_gate_layernorm_modulate.restype = ctypes.c_int
+    lib.oracle_layernorm_modulate_fp8.argtypes = [P, P, P, F, P, I, I, I, I, I, F, P, P]
+    lib.oracle_layernorm_modulate_fp8.restype = ctypes.c_int
+    lib.oracle_to_e4m3fn.argtypes = [P, P, I]
+    lib.oracle_to_e4m3fn.restype = None
+    lib.oracle_quant_fp8.argtypes = [P, P, I, F]
+    lib.oracle_quant_fp8.restype = None
     lib.oracle_round_bf16.argtypes = [P, P, I]
     lib.oracle_round_bf16.restype = None
     lib.oracle_modulate.argtypes = [P, P, P, P, I]
@@ -191,6 +197,42 @@ def residual_gate_layernorm_modulate(res, x, gate, scale, shift, eps=1e-6, want_
         float(np.float32(eps)), _ptr(yn), _ptr(st))
     _check(rc, "residual_gate_layernorm_modulate")
     return (r,) + _ret(y, yn, st, want_norm, want_stats, tup=True)
+
+
+def layernorm_modulate_fp8(x, scale, shift, qscale, eps=1e-6, want_y=False, want_stats=False):
+    """q = e4m3fn(clamp(RN(f(y) * RN(1/qscale)), -448, 448)) of the LayerNorm+modulate
+    output y; uint8 codes [B,T,H].  Returns q[, y][, stats]."""
+    lib = _load()
+    x = _act(x, "x")
+    B, T, H = x.shape
+    sc, sbs = _vec(scale, B, H, "scale")
+    sh, hbs = _vec(shift, B, H, "shift")
+    q = np.empty(x.shape, np.uint8)
+    y = np.empty_like(x) if want_y else None
+    st = np.empty((B * T, STATS_PER_ROW), np.float32) if want_stats else None
+    rc = lib.oracle_layernorm_modulate_fp8(_ptr(x), _ptr(sc), _ptr(sh), float(np.float32(qscale)),
+                                           _ptr(q), B, T, H, sbs, hbs, float(np.float32(eps)),
+                                           _ptr(y), _ptr(st))
+    _check(rc, "layernorm_modulate_fp8")
+    return _ret(q, y, st, want_y, want_stats)
+
+
+def to_e4m3fn(a):
+    """Elementwise binary32 -> OCP E4M3 (e4m3fn) codes, nearest-even, no clamping."""
+    lib = _load()
+    a = np.ascontiguousarray(a, dtype=np.float32)
+    out = np.empty(a.shape, np.uint8)
+    lib.oracle_to_e4m3fn(_ptr(a), _ptr(out), a.size)
+    return out
+
+
+def quant_fp8(y, qscale):
+    """Elementwise static quantisation of bf16 bits y with scale qscale."""
+    lib = _load()
+    y = np.ascontiguousarray(y, dtype=np.uint16)
+    out = np.empty(y.shape, np.uint8)
+    lib.oracle_quant_fp8(_ptr(y), _ptr(out), y.size, float(np.float32(qscale)))
+    return out
 
 
 def _ret(y, yn, st, want_norm, want_stats, tup=False):

@@ -318,6 +318,83 @@ def test_residual_gate_layernorm_special_gates():
 
 
 # --------------------------------------------------------------------------
+# static FP8 (OCP E4M3, e4m3fn) quantisation: torch's float8_e4m3fn conversion is an
+# independent implementation of the format's round-to-nearest-even
+# --------------------------------------------------------------------------
+def torch_e4m3fn(v):
+    return torch.from_numpy(np.ascontiguousarray(v, np.float32)).to(
+        torch.float8_e4m3fn).view(torch.uint8).numpy()
+
+
+def e4m3fn_values():
+    """Every finite e4m3fn value (codes 0x00..0x7E and their negatives), via torch."""
+    codes = np.array([c for c in range(256) if (c & 0x7F) != 0x7F], np.uint8)
+    return codes, torch.from_numpy(codes).view(torch.float8_e4m3fn).float().numpy()
+
+
+def assert_fp8_equal(got, want, what):
+    gn = (got & 0x7F) == 0x7F
+    wn = (want & 0x7F) == 0x7F
+    assert np.array_equal(gn, wn), what                 # NaN in the same places
+    assert np.array_equal(got[~gn], want[~wn]), what
+
+
+def test_e4m3fn_codes_round_trip():
+    codes, vals = e4m3fn_values()
+    assert float(vals.max()) == 448.0 and float(vals[vals > 0].min()) == 2.0 ** -9
+    assert np.array_equal(O.to_e4m3fn(vals), codes)
+
+
+def test_e4m3fn_rounding_vs_torch():
+    _, vals = e4m3fn_values()
+    pos = np.unique(np.abs(vals.astype(np.float64)))
+    mids = (pos[:-1] + pos[1:]) / 2.0                       # ties: exact in fp32
+    mids32 = mids.astype(np.float32)
+    assert np.array_equal(mids32.astype(np.float64), mids)
+    b = mids32.view(np.uint32)
+    near = np.concatenate([b - 1, b, b + 1]).view(np.float32)  # ties and one fp32 ulp either side
+    rng = np.random.default_rng(31)
+    rand = rng.uniform(-448.0, 448.0, 1 << 21).astype(np.float32)
+    tiny = rng.uniform(-2.0 ** -5, 2.0 ** -5, 1 << 20).astype(np.float32)   # subnormal range
+    logu = (np.exp2(rng.uniform(-12.0, 9.0, 1 << 20)) * rng.choice([-1.0, 1.0], 1 << 20))
+    logu = np.clip(logu, -448.0, 448.0).astype(np.float32)
+    special = np.array([0.0, -0.0, 448.0, -448.0, 464.0, -464.0, 2.0 ** -10, -(2.0 ** -10),
+                        float("nan")], np.float32)
+    for v in (near, -near, rand, tiny, logu, special):
+        assert_fp8_equal(O.to_e4m3fn(v), torch_e4m3fn(v), "e4m3fn rounding")
+
+
+@pytest.mark.parametrize("qscale", [1.0, 0.0173, 3.7, 2.0 ** -7, 1e-3, 300.0])
+def test_quant_fp8_all_bf16_vs_eager(qscale):
+    # the eager static quantisation chain: (y.float() * (1 / scale)).clamp(-448, 448)
+    # then float8_e4m3fn, over every bf16 bit pattern
+    y = np.arange(1 << 16, dtype=np.uint32).astype(np.uint16)
+    inv = torch.tensor(1.0, dtype=torch.float32) / torch.tensor(qscale, dtype=torch.float32)
+    ref = (torch_bf16(y).float() * inv).clamp(-448.0, 448.0).to(
+        torch.float8_e4m3fn).view(torch.uint8).numpy()
+    assert_fp8_equal(O.quant_fp8(y, qscale), ref, f"quant qscale={qscale}")
+
+
+def test_layernorm_modulate_fp8_quantises_the_ln_output():
+    B, T, H = 2, 6, 3072
+    rng = np.random.default_rng(41)
+    x = _rows("mixed", B, T, H, 41)
+    sc = synth.normal_bf16(rng, (B, H), 0.1)
+    sh = synth.normal_bf16(rng, (B, H), 0.1)
+    qs = 0.0173
+    q, y = O.layernorm_modulate_fp8(x, sc, sh, qs, EPS, want_y=True)
+    assert np.array_equal(y, O.layernorm_modulate(x, sc, sh, EPS))
+    assert np.array_equal(q, O.quant_fp8(y, qs))
+    # dequantised, q is y to within half the e4m3fn spacing (saturating at 448)
+    deq = torch.from_numpy(q).view(torch.float8_e4m3fn).float().numpy().astype(np.float64) * qs
+    yv = widen(y).astype(np.float64)
+    t = np.clip(yv / qs, -448.0, 448.0)
+    _, e2 = np.frexp(np.abs(t))
+    spacing = np.ldexp(1.0, np.maximum(e2 - 1, -6) - 3)
+    assert np.all(np.abs(deq / qs - t) <= spacing / 2 * (1 + 1e-6))
+
+
+# --------------------------------------------------------------------------
 # the full output is the modulate chain applied to the norm output
 # --------------------------------------------------------------------------
 @pytest.mark.parametrize("op", ["ln", "rms"])

@@ -64,7 +64,7 @@ def workload(cfg: str):
     from diffusion_dit_adaln_amd import synth
     return {"0": synth.config0, "1": synth.config1, "2": synth.config2,
             "3a": lambda: synth.config3(site="a"), "3b": lambda: synth.config3(site="b"),
-            "5": synth.config5}[cfg]()
+            "5": synth.config5, "6": synth.config6}[cfg]()
 
 
 class Launcher:
@@ -88,7 +88,10 @@ class Launcher:
         x0 = dev(wl.x)
         self.sets = []
         for _ in range(self.nsets):
-            s = {"x": x0.clone(), "y": torch.empty_like(x0)}
+            if wl.op == "lnq":
+                s = {"x": x0.clone(), "y": torch.empty(x0.shape, dtype=torch.uint8, device="cuda")}
+            else:
+                s = {"x": x0.clone(), "y": torch.empty_like(x0)}
             if wl.op in ("rg", "rgln"):
                 s["res"] = dev(wl.res)
                 s["r"] = torch.empty_like(x0)
@@ -97,6 +100,8 @@ class Launcher:
         self.shift = dev(wl.shift)
         self.weight = dev(wl.weight) if wl.weight is not None else None
         self.gate = dev(wl.gate) if wl.gate is not None else None
+        self.qscale = (torch.tensor([wl.qscale], dtype=torch.float32, device="cuda")
+                       if wl.qscale is not None else None)
         self.eps = ctypes.c_float(np.float32(wl.eps))
         bs = H if B > 1 else 0
         self.bs = bs
@@ -115,6 +120,10 @@ class Launcher:
                 s["x"].data_ptr(), None if self.weight is None else self.weight.data_ptr(),
                 self.scale.data_ptr(), self.shift.data_ptr(), s["y"].data_ptr(), B, T, H, bs, bs,
                 self.eps, stream)
+        if self.wl.op == "lnq":
+            return self.lib.adaln_layernorm_modulate_fp8_quant(
+                s["x"].data_ptr(), self.scale.data_ptr(), self.shift.data_ptr(),
+                self.qscale.data_ptr(), s["y"].data_ptr(), B, T, H, bs, bs, self.eps, stream)
         if self.wl.op == "rgln":
             return self.lib.adaln_residual_gate_layernorm_modulate(
                 s["res"].data_ptr(), s["x"].data_ptr(), self.gate.data_ptr(),
@@ -204,7 +213,9 @@ def cpu_baseline(wl, budget_s: float):
           "rg": lambda: O.residual_gate_rmsnorm_scale_shift(wl.res, wl.x, wl.gate, wl.weight,
                                                             wl.scale, wl.shift, wl.eps),
           "rgln": lambda: O.residual_gate_layernorm_modulate(wl.res, wl.x, wl.gate, wl.scale,
-                                                             wl.shift, wl.eps)}[wl.op]
+                                                             wl.shift, wl.eps),
+          "lnq": lambda: O.layernorm_modulate_fp8(wl.x, wl.scale, wl.shift, wl.qscale,
+                                                  wl.eps)}[wl.op]
     fn()  # warm (page in the library and the arrays)
     reps = 0
     t0 = time.perf_counter()
@@ -225,8 +236,10 @@ def describe(wl):
     B, T, H = wl.x.shape
     name = {"ln": "layernorm_modulate", "rms": "rmsnorm_scale_shift",
             "rg": "residual_gate_rmsnorm_scale_shift",
-            "rgln": "residual_gate_layernorm_modulate"}[wl.op]
-    extra = {"rms": " weight 1+0.02N", "rg": " weight none"}.get(wl.op, "")
+            "rgln": "residual_gate_layernorm_modulate",
+            "lnq": "layernorm_modulate_fp8_quant"}[wl.op]
+    extra = {"rms": " weight 1+0.02N", "rg": " weight none",
+             "lnq": f" -> E4M3, static scale {wl.qscale}"}.get(wl.op, "")
     return f"{name} bf16 [{B},{T},{H}]{extra}, eps 1e-6"
 
 
@@ -235,7 +248,7 @@ def main():
     ap.add_argument("--gpus", type=int, default=1)
     ap.add_argument("--steps", type=int, default=400)
     ap.add_argument("--warmup", type=int, default=40)
-    ap.add_argument("--config", default="1", choices=["0", "1", "2", "3a", "3b", "5"])
+    ap.add_argument("--config", default="1", choices=["0", "1", "2", "3a", "3b", "5", "6"])
     ap.add_argument("--timing", default="graph", choices=["graph", "eager"])
     ap.add_argument("--rotate-mb", type=int, default=1024)
     ap.add_argument("--cpu-seconds", type=float, default=10.0)
@@ -303,7 +316,7 @@ def main():
             lambda: copy_ceiling(nbytes, rotate, steps, args.warmup, kind="torch")), 2)
         out["frac_of_copy_ceiling"] = round(gbps / out["copy_ceiling_GBps"], 4)
         per = {}
-        for cfg in ["0", "1", "2", "3a", "3b", "5"]:
+        for cfg in ["0", "1", "2", "3a", "3b", "5", "6"]:
             w2 = workload(cfg)
             L2 = Launcher(w2, rotate)
             nb2 = w2.algorithmic_bytes()

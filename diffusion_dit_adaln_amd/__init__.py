@@ -10,13 +10,16 @@ from ._binding import (  # noqa: F401
     AdalnError,
     adaln_abi_version,
     adaln_check_layernorm_modulate,
+    adaln_check_layernorm_modulate_fp8_quant,
     adaln_check_residual_gate_layernorm_modulate,
     adaln_check_residual_gate_rmsnorm_scale_shift,
     adaln_check_rmsnorm_scale_shift,
     adaln_diag_finalize,
+    adaln_diag_quant_fp8,
     adaln_diag_round_bf16,
     adaln_diag_stream_copy,
     adaln_layernorm_modulate,
+    adaln_layernorm_modulate_fp8_quant,
     adaln_reduction_layout,
     adaln_residual_gate_layernorm_modulate,
     adaln_residual_gate_rmsnorm_scale_shift,

@@ -12,7 +12,7 @@ import os
 import torch
 
 _PKG = os.path.dirname(os.path.abspath(__file__))
-ABI_VERSION = 3
+ABI_VERSION = 4
 
 STATUS_NAMES = {0: "ADALN_OK", 1: "ADALN_ERR_NULL", 2: "ADALN_ERR_SHAPE", 3: "ADALN_ERR_ALIGN",
                 4: "ADALN_ERR_STRIDE", 5: "ADALN_ERR_OVERLAP", 6: "ADALN_ERR_VALUE",
@@ -21,11 +21,12 @@ STATUS_NAMES = {0: "ADALN_OK", 1: "ADALN_ERR_NULL", 2: "ADALN_ERR_SHAPE", 3: "AD
 # every symbol include/adaln.h declares
 EXPORTS = ("adaln_layernorm_modulate", "adaln_rmsnorm_scale_shift",
            "adaln_residual_gate_rmsnorm_scale_shift", "adaln_residual_gate_layernorm_modulate",
-           "adaln_check_layernorm_modulate", "adaln_check_rmsnorm_scale_shift",
-           "adaln_check_residual_gate_rmsnorm_scale_shift",
-           "adaln_check_residual_gate_layernorm_modulate", "adaln_reduction_layout",
+           "adaln_layernorm_modulate_fp8_quant", "adaln_check_layernorm_modulate",
+           "adaln_check_rmsnorm_scale_shift", "adaln_check_residual_gate_rmsnorm_scale_shift",
+           "adaln_check_residual_gate_layernorm_modulate",
+           "adaln_check_layernorm_modulate_fp8_quant", "adaln_reduction_layout",
            "adaln_status_string", "adaln_abi_version", "adaln_diag_round_bf16",
-           "adaln_diag_finalize", "adaln_diag_stream_copy")
+           "adaln_diag_finalize", "adaln_diag_quant_fp8", "adaln_diag_stream_copy")
 
 
 class AdalnError(RuntimeError):
@@ -60,6 +61,8 @@ def load_library():
         "adaln_rmsnorm_scale_shift": [P, P, P, P, P, I, I, I, I, I, F, P],
         "adaln_residual_gate_rmsnorm_scale_shift": [P, P, P, P, P, P, P, P, I, I, I, I, I, I, F, P],
         "adaln_residual_gate_layernorm_modulate": [P, P, P, P, P, P, P, I, I, I, I, I, I, F, P],
+        "adaln_layernorm_modulate_fp8_quant": [P, P, P, P, P, I, I, I, I, I, F, P],
+        "adaln_check_layernorm_modulate_fp8_quant": [P, P, P, P, P, I, I, I, I, I, F],
         "adaln_check_layernorm_modulate": [P, P, P, P, I, I, I, I, I, F],
         "adaln_check_rmsnorm_scale_shift": [P, P, P, P, P, I, I, I, I, I, F],
         "adaln_check_residual_gate_rmsnorm_scale_shift": [P, P, P, P, P, P, P, P, I, I, I, I, I, I,
@@ -69,6 +72,7 @@ def load_library():
         "adaln_diag_round_bf16": [P, P, I, P],
         "adaln_diag_finalize": [P, P, I, F, P],
         "adaln_diag_stream_copy": [P, P, I, P],
+        "adaln_diag_quant_fp8": [P, P, I, P, P],
     }
     for name, args in sig.items():
         fn = getattr(lib, name)
@@ -209,6 +213,31 @@ def adaln_residual_gate_layernorm_modulate(res, x, gate, scale, shift, eps: floa
     return r, y
 
 
+def adaln_layernorm_modulate_fp8_quant(x, scale, shift, qscale, eps: float = 1e-6, out=None,
+                                       stream=None):
+    """q (uint8 E4M3 codes [B,T,H]) = static FP8 quantisation of
+    LayerNorm(x) * (1 + scale[b]) + shift[b]; qscale is a one-element float32 device
+    tensor (the per-tensor input scale).  View q as torch.float8_e4m3fn if wanted."""
+    lib = load_library()
+    _act(x, "x")
+    B, T, H = x.shape
+    if qscale.dtype != torch.float32 or qscale.numel() != 1 or not qscale.is_cuda:
+        raise ValueError("qscale: expected a one-element float32 device tensor")
+    sp, sbs = _vec(scale, B, H, "scale")
+    hp, hbs = _vec(shift, B, H, "shift")
+    if out is None:
+        q = torch.empty(x.shape, dtype=torch.uint8, device=x.device)
+    else:
+        if out.dtype != torch.uint8 or out.shape != x.shape or not out.is_contiguous():
+            raise ValueError("out: expected a contiguous uint8 [B,T,H] tensor")
+        q = out
+    _check(lib.adaln_layernorm_modulate_fp8_quant(x.data_ptr(), sp, hp, qscale.data_ptr(),
+                                                  q.data_ptr(), B, T, H, sbs, hbs, _eps(eps),
+                                                  _stream(stream)),
+           "adaln_layernorm_modulate_fp8_quant")
+    return q
+
+
 def adaln_check_layernorm_modulate(x_ptr, scale_ptr, shift_ptr, y_ptr, B, T, H, scale_bstride,
                                    shift_bstride, eps=1e-6) -> int:
     """Status code of the validation (raw pointers as ints; nothing is launched)."""
@@ -237,6 +266,12 @@ def adaln_check_residual_gate_layernorm_modulate(res_ptr, x_ptr, gate_ptr, scale
     return load_library().adaln_check_residual_gate_layernorm_modulate(
         res_ptr, x_ptr, gate_ptr, scale_ptr, shift_ptr, r_ptr, y_ptr, B, T, H, gate_bstride,
         scale_bstride, shift_bstride, eps)
+
+
+def adaln_check_layernorm_modulate_fp8_quant(x_ptr, scale_ptr, shift_ptr, qscale_ptr, q_ptr, B, T,
+                                             H, scale_bstride, shift_bstride, eps=1e-6) -> int:
+    return load_library().adaln_check_layernorm_modulate_fp8_quant(
+        x_ptr, scale_ptr, shift_ptr, qscale_ptr, q_ptr, B, T, H, scale_bstride, shift_bstride, eps)
 
 
 def adaln_reduction_layout(H: int):
@@ -289,3 +324,14 @@ def adaln_diag_stream_copy(src: torch.Tensor, dst: torch.Tensor, stream=None) ->
     _check(lib.adaln_diag_stream_copy(src.data_ptr(), dst.data_ptr(), nbytes, _stream(stream)),
            "adaln_diag_stream_copy")
     return dst
+
+
+def adaln_diag_quant_fp8(v: torch.Tensor, qscale: torch.Tensor, stream=None) -> torch.Tensor:
+    """The FP8 kernel's quantisation step on a float32 tensor (numel % 4 == 0)."""
+    lib = load_library()
+    if v.dtype != torch.float32 or not v.is_contiguous():
+        raise ValueError("expected a contiguous float32 tensor")
+    out = torch.empty(v.shape, dtype=torch.uint8, device=v.device)
+    _check(lib.adaln_diag_quant_fp8(v.data_ptr(), out.data_ptr(), v.numel(), qscale.data_ptr(),
+                                    _stream(stream)), "adaln_diag_quant_fp8")
+    return out

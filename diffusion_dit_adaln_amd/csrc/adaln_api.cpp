@@ -69,18 +69,22 @@ adaln_status check_vec(const void* p, int64_t B, int64_t H, int64_t bstride) {
     } while (0)
 
 // Validation of the compute entry points.  res/gate/r are required by the gated
-// ops (RG, RGLN) and ignored by LN and RMS.
+// ops (RG, RGLN) and ignored by the others; y is the bf16 output, or for LNQ the
+// one-byte E4M3 output, whose scale qscale (one float) is then an input.
 adaln_status validate(int op, const void* res, const void* x, const void* gate,
                       const void* weight, const void* scale, const void* shift, const void* r,
                       const void* y, int64_t B, int64_t T, int64_t H, int64_t gate_bs,
-                      int64_t scale_bs, int64_t shift_bs, float eps, int64_t* rows_out) {
+                      int64_t scale_bs, int64_t shift_bs, float eps, int64_t* rows_out,
+                      const void* qscale = nullptr) {
     int64_t rows = 0;
     ADALN_TRY(check_shape(B, T, H, eps, &rows));
     *rows_out = rows;
     if (rows == 0) return ADALN_OK;
     const bool gated = adaln::op_gated(op);
-    if (!x || !y || (gated && (!res || !r))) return ADALN_ERR_NULL;
+    const bool fp8 = adaln::op_fp8(op);
+    if (!x || !y || (gated && (!res || !r)) || (fp8 && !qscale)) return ADALN_ERR_NULL;
     if (!aligned16(x) || !aligned16(y)) return ADALN_ERR_ALIGN;
+    if (fp8 && ((uintptr_t)qscale & 3u)) return ADALN_ERR_ALIGN;
     if (gated && (!aligned16(res) || !aligned16(r))) return ADALN_ERR_ALIGN;
     if (weight && !aligned16(weight)) return ADALN_ERR_ALIGN;
     ADALN_TRY(check_vec(scale, B, H, scale_bs));
@@ -88,7 +92,7 @@ adaln_status validate(int op, const void* res, const void* x, const void* gate,
     if (gated) ADALN_TRY(check_vec(gate, B, H, gate_bs));
 
     // outputs may not overlap any input or each other
-    Span in[6];
+    Span in[7];
     int n_in = 0;
     in[n_in++] = act_span(x, rows, H);
     in[n_in++] = vec_span(scale, B, H, scale_bs);
@@ -98,7 +102,9 @@ adaln_status validate(int op, const void* res, const void* x, const void* gate,
         in[n_in++] = act_span(res, rows, H);
         in[n_in++] = vec_span(gate, B, H, gate_bs);
     }
-    const Span ys = act_span(y, rows, H);
+    if (fp8) in[n_in++] = Span{(uintptr_t)qscale, (uintptr_t)qscale + 4};
+    const Span ys = fp8 ? Span{(uintptr_t)y, (uintptr_t)y + (uintptr_t)(rows * H)}
+                        : act_span(y, rows, H);
     for (int i = 0; i < n_in; ++i)
         if (overlaps(ys, in[i])) return ADALN_ERR_OVERLAP;
     if (gated) {
@@ -112,11 +118,12 @@ adaln_status validate(int op, const void* res, const void* x, const void* gate,
 
 adaln_status run(adaln::Op op, const adaln_bf16* res, const adaln_bf16* x, const adaln_bf16* gate,
                  const adaln_bf16* weight, const adaln_bf16* scale, const adaln_bf16* shift,
-                 adaln_bf16* r, adaln_bf16* y, int64_t B, int64_t T, int64_t H, int64_t gate_bs,
-                 int64_t scale_bs, int64_t shift_bs, float eps, void* stream) {
+                 adaln_bf16* r, void* y, int64_t B, int64_t T, int64_t H, int64_t gate_bs,
+                 int64_t scale_bs, int64_t shift_bs, float eps, void* stream,
+                 const float* qscale = nullptr) {
     int64_t rows = 0;
     ADALN_TRY(validate(op, res, x, gate, weight, scale, shift, r, y, B, T, H, gate_bs, scale_bs,
-                       shift_bs, eps, &rows));
+                       shift_bs, eps, &rows, qscale));
     if (rows == 0) return ADALN_OK;
     adaln::Params p{};
     p.x = x;
@@ -125,7 +132,12 @@ adaln_status run(adaln::Op op, const adaln_bf16* res, const adaln_bf16* x, const
     p.weight = weight;
     p.scale = scale;
     p.shift = shift;
-    p.y = y;
+    if (adaln::op_fp8(op)) {
+        p.q = static_cast<uint8_t*>(y);
+        p.qscale = qscale;
+    } else {
+        p.y = static_cast<uint16_t*>(y);
+    }
     p.r = r;
     p.rows = rows;
     p.T = T;
@@ -177,6 +189,15 @@ adaln_status adaln_residual_gate_layernorm_modulate(
                gate_bstride, scale_bstride, shift_bstride, eps, hip_stream);
 }
 
+adaln_status adaln_layernorm_modulate_fp8_quant(const adaln_bf16* x, const adaln_bf16* scale,
+                                                const adaln_bf16* shift, const float* qscale,
+                                                uint8_t* q, int64_t B, int64_t T, int64_t H,
+                                                int64_t scale_bstride, int64_t shift_bstride,
+                                                float eps, void* hip_stream) {
+    return run(adaln::OP_LNQ, nullptr, x, nullptr, nullptr, scale, shift, nullptr, q, B, T, H, 0,
+               scale_bstride, shift_bstride, eps, hip_stream, qscale);
+}
+
 adaln_status adaln_check_layernorm_modulate(const adaln_bf16* x, const adaln_bf16* scale,
                                             const adaln_bf16* shift, const adaln_bf16* y,
                                             int64_t B, int64_t T, int64_t H,
@@ -214,6 +235,16 @@ adaln_status adaln_check_residual_gate_layernorm_modulate(
     int64_t rows;
     return validate(adaln::OP_RGLN, res, x, gate, nullptr, scale, shift, r_out, y, B, T, H,
                     gate_bstride, scale_bstride, shift_bstride, eps, &rows);
+}
+
+adaln_status adaln_check_layernorm_modulate_fp8_quant(const adaln_bf16* x, const adaln_bf16* scale,
+                                                      const adaln_bf16* shift, const float* qscale,
+                                                      const uint8_t* q, int64_t B, int64_t T,
+                                                      int64_t H, int64_t scale_bstride,
+                                                      int64_t shift_bstride, float eps) {
+    int64_t rows;
+    return validate(adaln::OP_LNQ, nullptr, x, nullptr, nullptr, scale, shift, nullptr, q, B, T, H,
+                    0, scale_bstride, shift_bstride, eps, &rows, qscale);
 }
 
 adaln_status adaln_reduction_layout(int64_t H, int* waves_per_row, int* lanes_per_row,
@@ -260,6 +291,21 @@ adaln_status adaln_diag_finalize(const float* in, float* out, int64_t n, float e
     if (!in || !out) return ADALN_ERR_NULL;
     if (((uintptr_t)in & 3u) || ((uintptr_t)out & 3u)) return ADALN_ERR_ALIGN;
     return adaln::launch_diag_finalize(in, out, n, eps, (hipStream_t)hip_stream) == hipSuccess
+               ? ADALN_OK
+               : ADALN_ERR_LAUNCH;
+}
+
+adaln_status adaln_diag_quant_fp8(const float* in, uint8_t* out, int64_t n, const float* qscale,
+                                  void* hip_stream) {
+    if (n < 0 || (n % 4) != 0) return ADALN_ERR_SHAPE;
+    if (n == 0) return ADALN_OK;
+    if (!in || !out || !qscale) return ADALN_ERR_NULL;
+    if (!aligned16(in) || ((uintptr_t)out & 3u) || ((uintptr_t)qscale & 3u)) return ADALN_ERR_ALIGN;
+    const Span o{(uintptr_t)out, (uintptr_t)out + (uintptr_t)n};
+    if (overlaps(o, Span{(uintptr_t)in, (uintptr_t)in + (uintptr_t)(4 * n)}) ||
+        overlaps(o, Span{(uintptr_t)qscale, (uintptr_t)qscale + 4}))
+        return ADALN_ERR_OVERLAP;
+    return adaln::launch_diag_quant(in, out, n, qscale, (hipStream_t)hip_stream) == hipSuccess
                ? ADALN_OK
                : ADALN_ERR_LAUNCH;
 }

@@ -8,10 +8,12 @@
 namespace adaln {
 
 // LN: LayerNorm + modulate; RMS: RMSNorm + scale/shift; RG: residual gate then
-// RMSNorm + scale/shift; RGLN: residual gate then LayerNorm + modulate.
-enum Op : int { OP_LN = 0, OP_RMS = 1, OP_RG = 2, OP_RGLN = 3 };
+// RMSNorm + scale/shift; RGLN: residual gate then LayerNorm + modulate; LNQ:
+// LayerNorm + modulate + static FP8 (E4M3) quantisation of the output.
+enum Op : int { OP_LN = 0, OP_RMS = 1, OP_RG = 2, OP_RGLN = 3, OP_LNQ = 4 };
 constexpr bool op_gated(int op) { return op == OP_RG || op == OP_RGLN; }
-constexpr bool op_layernorm(int op) { return op == OP_LN || op == OP_RGLN; }
+constexpr bool op_layernorm(int op) { return op == OP_LN || op == OP_RGLN || op == OP_LNQ; }
+constexpr bool op_fp8(int op) { return op == OP_LNQ; }
 
 // Arguments of one launch, already validated by the C-ABI layer.
 struct Params {
@@ -21,7 +23,9 @@ struct Params {
     const uint16_t* weight;  // RMS / RG: [H] or NULL
     const uint16_t* scale;   // per-batch, row b at scale + b*scale_bs
     const uint16_t* shift;   // per-batch, row b at shift + b*shift_bs
-    uint16_t* y;             // [rows, H]
+    uint16_t* y;             // [rows, H] (not LNQ)
+    uint8_t* q;              // LNQ: E4M3 codes [rows, H]
+    const float* qscale;     // LNQ: the static quantisation scale (one float, device)
     uint16_t* r;             // RG, RGLN: [rows, H]
     int64_t rows;            // B*T > 0
     int64_t T;               // rows per batch entry
@@ -48,5 +52,7 @@ hipError_t launch_diag_round(const float* in, uint16_t* out, int64_t n, hipStrea
 hipError_t launch_diag_finalize(const float* in, float* out, int64_t n, float eps,
                                 hipStream_t stream);
 hipError_t launch_diag_copy(const void* src, void* dst, int64_t n16, hipStream_t stream);
+hipError_t launch_diag_quant(const float* in, uint8_t* out, int64_t n, const float* qscale,
+                             hipStream_t stream);
 
 }  // namespace adaln

@@ -67,8 +67,9 @@ namespace {
 using u32 = uint32_t;
 
 constexpr bool interleaved(int op) {
-    return (op == OP_LN && ADALN_INTERLEAVE_LN) || (op == OP_RMS && ADALN_INTERLEAVE_RMS) ||
-           (op == OP_RG && ADALN_INTERLEAVE_RG) || (op == OP_RGLN && ADALN_INTERLEAVE_RGLN);
+    return ((op == OP_LN || op == OP_LNQ) && ADALN_INTERLEAVE_LN) ||
+           (op == OP_RMS && ADALN_INTERLEAVE_RMS) || (op == OP_RG && ADALN_INTERLEAVE_RG) ||
+           (op == OP_RGLN && ADALN_INTERLEAVE_RGLN);
 }
 
 // ---------------------------------------------------------------------------
@@ -120,6 +121,24 @@ __device__ __forceinline__ uint4 ld16_stream(rsrc_t r, int off) {
 __device__ __forceinline__ void st16_stream(rsrc_t r, int off, uint4 v) {
     const u32x4 t = {v.x, v.y, v.z, v.w};
     __builtin_amdgcn_raw_buffer_store_b128(t, r, off, 0, kNonTemporal);
+}
+
+typedef unsigned int u32x2 __attribute__((ext_vector_type(2)));
+__device__ __forceinline__ void st8_stream(rsrc_t r, int off, u32 lo, u32 hi) {
+    const u32x2 t = {lo, hi};
+    __builtin_amdgcn_raw_buffer_store_b64(t, r, off, 0, kNonTemporal);
+}
+
+// Static FP8 quantisation of four values already multiplied by 1/scale: clamp to
+// [-448, 448] with IEEE-754-2019 maximum/minimum (v_maximum3/v_minimum3: a NaN stays
+// NaN), then v_cvt_pk_fp8_f32, which rounds to nearest-even into the OCP E4M3 format
+// on gfx950.  Byte k of the result is value k.
+__device__ __forceinline__ float clamp448(float v) {
+    return __builtin_elementwise_minimum(__builtin_elementwise_maximum(v, -448.0f), 448.0f);
+}
+__device__ __forceinline__ u32 quant4(float a, float b, float c, float d) {
+    const u32 lo = __builtin_amdgcn_cvt_pk_fp8_f32(clamp448(a), clamp448(b), 0, false);
+    return __builtin_amdgcn_cvt_pk_fp8_f32(clamp448(c), clamp448(d), lo, true);
 }
 
 __device__ __forceinline__ u32 word(const uint4& v, int j) {
@@ -306,6 +325,7 @@ __global__ __launch_bounds__(256) void fused_norm_modulate(Params p) {
     constexpr bool KF = consts_as_f32(W, C, OP, WEIGHT);
     constexpr int NK = KF ? 8 * C : 4 * C;           // constants per vector per lane
     constexpr bool GATED = op_gated(OP);
+    constexpr bool FP8 = op_fp8(OP);
     constexpr bool LNSTAT = op_layernorm(OP);
     constexpr int HFULL = C * 8 * P;                 // H when no chunk is partial
 
@@ -397,36 +417,44 @@ __global__ __launch_bounds__(256) void fused_norm_modulate(Params p) {
     // and a per-row offset; a row past the range lands beyond it.  Either way lanes
     // past a ragged row end get an out-of-range offset, and an access out of range
     // reads zero or is dropped.
-    int voff[C];
-#pragma unroll
-    for (int c = 0; c < C; ++c) voff[c] = ok[c] ? 2 * col[c] : kOutOfRange;
-    const int64_t span_bytes = IL ? 0 : (r_end - r_begin) * H * 2;
-    auto range_rsrc = [&](const uint16_t* base) {
-        return make_rsrc(IL ? base : base + r_begin * H, span_bytes);
+    // ES: bytes per element of a tensor (2 for bf16, 1 for the FP8 output)
+    auto range_rsrc = [&](const void* base, int ES) {
+        return make_rsrc(IL ? base : static_cast<const char*>(base) + r_begin * H * ES,
+                         IL ? 0 : (r_end - r_begin) * H * ES);
     };
-    const rsrc_t gx = range_rsrc(p.x), gy = range_rsrc(p.y);
-    const rsrc_t gres = GATED ? range_rsrc(p.res) : gx;
-    const rsrc_t gr = GATED ? range_rsrc(p.r) : gy;
-    auto rsrc_of = [&](const uint16_t* base, const rsrc_t& range, int64_t row) {
+    auto rsrc_of = [&](const void* base, const rsrc_t& range, int64_t row, int ES) {
         if (!IL) return range;
-        return row < r_end ? make_rsrc(base + row * H, H * 2) : make_rsrc(base, 0);
+        return row < r_end ? make_rsrc(static_cast<const char*>(base) + row * H * ES, H * ES)
+                           : make_rsrc(base, 0);
     };
-    auto off_of = [&](int64_t row, int c) {
-        if (IL) return voff[c];
+    auto off_of = [&](int64_t row, int c, int ES) {
+        if (IL) return ok[c] ? ES * col[c] : kOutOfRange;
         const int64_t rr = row < r_end ? row : r_end;  // keeps the offset arithmetic in range
-        return ok[c] ? (int)((rr - r_begin) * H * 2) + 2 * col[c] : kOutOfRange;
+        return ok[c] ? (int)((rr - r_begin) * H * ES) + ES * col[c] : kOutOfRange;
     };
+    constexpr int OES = FP8 ? 1 : 2;  // output bytes per element
+    const rsrc_t gx = range_rsrc(p.x, 2);
+    const rsrc_t gy = FP8 ? range_rsrc(p.q, 1) : range_rsrc(p.y, 2);
+    const rsrc_t gres = GATED ? range_rsrc(p.res, 2) : gx;
+    const rsrc_t gr = GATED ? range_rsrc(p.r, 2) : gy;
     auto load_row = [&](int64_t row, uint4 (&xv)[C], uint4 (&rv)[C]) {
-        const rsrc_t rx = rsrc_of(p.x, gx, row);
-        const rsrc_t rres = GATED ? rsrc_of(p.res, gres, row) : rx;
+        const rsrc_t rx = rsrc_of(p.x, gx, row, 2);
+        const rsrc_t rres = GATED ? rsrc_of(p.res, gres, row, 2) : rx;
 #pragma unroll
         for (int c = 0; c < C; ++c) {
-            const int off = off_of(row, c);
+            const int off = off_of(row, c, 2);
             xv[c] = ld16_stream(rx, off);
             if (GATED) rv[c] = ld16_stream(rres, off);
         }
     };
-    const rsrc_t r_none = make_rsrc(p.y, 0);  // an empty range: every store dropped
+    const rsrc_t r_none = make_rsrc(p.x, 0);  // an empty range: every store dropped
+    // LNQ: the reciprocal of the static quantisation scale, correctly rounded
+    const float inv_qscale = FP8 ? 1.0f / *p.qscale : 0.0f;
+
+    auto store_out = [&](const rsrc_t& r, int off, const u32 (&w)[4]) {
+        if (FP8) st8_stream(r, off, w[0], w[1]);
+        else st16_stream(r, off, make_uint4(w[0], w[1], w[2], w[3]));
+    };
 
     int64_t b = r_begin / p.T;
     int64_t t_in = r_begin - b * p.T;
@@ -464,8 +492,8 @@ __global__ __launch_bounds__(256) void fused_norm_modulate(Params p) {
         uint4 (&xa)[C] = xs[k];
         uint4 (&ra)[C] = rs[k];
         const int par = seq & 1;  // alternates over the group's consecutive rows
-        const rsrc_t ry = rsrc_of(p.y, gy, row);
-        const rsrc_t rr_out = GATED ? rsrc_of(p.r, gr, row) : ry;
+        const rsrc_t ry = FP8 ? rsrc_of(p.q, gy, row, 1) : rsrc_of(p.y, gy, row, 2);
+        const rsrc_t rr_out = GATED ? rsrc_of(p.r, gr, row, 2) : ry;
 
         // Residual gate (gated ops): r = bf16(res + bf16(gate * x)), stored; r is the
         // norm input.  The norm input is widened to binary32 once and kept for the
@@ -489,7 +517,7 @@ __global__ __launch_bounds__(256) void fused_norm_modulate(Params p) {
                 xf[c][2 * j] = bf_lo(xw);
                 xf[c][2 * j + 1] = bf_hi(xw);
             }
-            if (GATED) st16_stream(rr_out, off_of(row, c), make_uint4(rr[0], rr[1], rr[2], rr[3]));
+            if (GATED) st16_stream(rr_out, off_of(row, c, 2), make_uint4(rr[0], rr[1], rr[2], rr[3]));
         }
 
         // Interleaved rows: the statistic and the normalisation run only for a real
@@ -600,6 +628,7 @@ __global__ __launch_bounds__(256) void fused_norm_modulate(Params p) {
 #pragma unroll
         for (int c = 0; c < C; ++c) {
             u32 (&out)[4] = yw_out[c];
+            float qv[8];
 #pragma unroll
             for (int j = 0; j < 4; ++j) {
                 float n0, n1;
@@ -619,18 +648,26 @@ __global__ __launch_bounds__(256) void fused_norm_modulate(Params p) {
                 const float y0 = round_bf16(n0), y1 = round_bf16(n1);               // yn
                 const float p0 = round_bf16(y0 * K_a(c, 2 * j));                   // bf16(yn*a)
                 const float p1 = round_bf16(y1 * K_a(c, 2 * j + 1));
-                out[j] = pack_bf16(p0 + K_h(c, 2 * j), p1 + K_h(c, 2 * j + 1));  // bf16(p+shift)
+                if (!FP8) {
+                    out[j] = pack_bf16(p0 + K_h(c, 2 * j), p1 + K_h(c, 2 * j + 1));  // bf16(p+shift)
+                } else {
+                    // y = bf16(p + shift) as binary32, times 1/scale
+                    qv[2 * j] = round_bf16(p0 + K_h(c, 2 * j)) * inv_qscale;
+                    qv[2 * j + 1] = round_bf16(p1 + K_h(c, 2 * j + 1)) * inv_qscale;
+                }
             }
-            if (!IL) st16_stream(ry, off_of(row, c), make_uint4(out[0], out[1], out[2], out[3]));
+            if (FP8) {
+                out[0] = quant4(qv[0], qv[1], qv[2], qv[3]);
+                out[1] = quant4(qv[4], qv[5], qv[6], qv[7]);
+            }
+            if (!IL) store_out(ry, off_of(row, c, OES), out);
         }
         }  // row < r_end
 
-        // 16-byte non-temporal stores of y (interleaved rows)
+        // non-temporal stores of y (16 bytes) or q (8 bytes) per chunk (interleaved rows)
         if (IL) {
 #pragma unroll
-            for (int c = 0; c < C; ++c)
-                st16_stream(ry, off_of(row, c), make_uint4(yw_out[c][0], yw_out[c][1],
-                                                           yw_out[c][2], yw_out[c][3]));
+            for (int c = 0; c < C; ++c) store_out(ry, off_of(row, c, OES), yw_out[c]);
         }
 
         // refill this slot S rows ahead; switch batch entry if the next row needs it
@@ -709,6 +746,19 @@ __global__ __launch_bounds__(256) void diag_copy(const u32x4* __restrict__ src,
             const u32x4 t = {v[k].x, v[k].y, v[k].z, v[k].w};
             __builtin_nontemporal_store(t, dst + i);
         }
+    }
+}
+
+// The fused LNQ kernel's quantisation step on binary32 inputs: out = E4M3 of
+// clamp(in * RN(1/qscale)), four values per thread.
+__global__ __launch_bounds__(256) void diag_quant(const float4* __restrict__ in,
+                                                  u32* __restrict__ out, int64_t n4,
+                                                  const float* qscale) {
+    const float inv = 1.0f / *qscale;
+    for (int64_t i = (int64_t)blockIdx.x * blockDim.x + threadIdx.x; i < n4;
+         i += (int64_t)gridDim.x * blockDim.x) {
+        const float4 v = in[i];
+        out[i] = quant4(v.x * inv, v.y * inv, v.z * inv, v.w * inv);
     }
 }
 
@@ -812,6 +862,7 @@ hipError_t launch(Op op, const Params& p_in, hipStream_t stream) {
                 : op == OP_RMS   ? pick<OP_RMS>(L, weight)
                 : op == OP_RG    ? pick<OP_RG>(L, weight)
                 : op == OP_RGLN  ? pick<OP_RGLN>(L, false)
+                : op == OP_LNQ   ? pick<OP_LNQ>(L, false)
                                  : nullptr;
     if (!fn) return hipErrorInvalidValue;
     // one-wave rows: four independent waves per workgroup; else one row group per
@@ -867,6 +918,16 @@ hipError_t launch_diag_finalize(const float* in, float* out, int64_t n, float ep
     const int64_t blocks = n / 256 + 1 < 65536 ? n / 256 + 1 : 65536;
     hipLaunchKernelGGL(diag_finalize, dim3((unsigned)blocks), dim3(256), 0, stream, in, out, n,
                        eps);
+    return hipGetLastError();
+}
+
+hipError_t launch_diag_quant(const float* in, uint8_t* out, int64_t n, const float* qscale,
+                             hipStream_t stream) {
+    const int64_t n4 = n / 4;
+    const int64_t blocks = n4 / 256 + 1 < 65536 ? n4 / 256 + 1 : 65536;
+    hipLaunchKernelGGL(diag_quant, dim3((unsigned)blocks), dim3(256), 0, stream,
+                       reinterpret_cast<const float4*>(in), reinterpret_cast<u32*>(out), n4,
+                       qscale);
     return hipGetLastError();
 }
 

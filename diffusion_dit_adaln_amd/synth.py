@@ -69,7 +69,7 @@ def normal_bf16(rng: np.random.Generator, shape, sigma: float = 1.0, mu: float =
 @dataclasses.dataclass
 class Workload:
     """One synthetic invocation of an entry point (arrays are bf16 bits)."""
-    op: str                      # "ln" | "rms" | "rg" | "rgln"
+    op: str                      # "ln" | "rms" | "rg" | "rgln" | "lnq"
     name: str
     x: np.ndarray                # [B,T,H]
     scale: np.ndarray            # [B,H] (possibly a strided view)
@@ -78,6 +78,7 @@ class Workload:
     gate: np.ndarray | None = None    # [B,H] (rg, rgln)
     res: np.ndarray | None = None     # [B,T,H] (rg, rgln)
     eps: float = 1e-6
+    qscale: float | None = None       # lnq: static FP8 quantisation scale
 
     @property
     def shape(self):
@@ -86,6 +87,8 @@ class Workload:
     def algorithmic_bytes(self) -> int:
         """HBM bytes the path must move: read x[,res], write y[,r] (bf16)."""
         n = int(np.prod(self.x.shape))
+        if self.op == "lnq":
+            return 3 * n  # read x (bf16), write q (one byte)
         return (8 if self.op in ("rg", "rgln") else 4) * n
 
 
@@ -143,6 +146,16 @@ def config5(seed: int = 0) -> Workload:
     return Workload("rgln", "rg_ln_2x4096x3072", normal_bf16(_rng(seed, 5, "x"), (B, T, H)),
                     v["scale"], v["shift"], gate=v["gate"],
                     res=normal_bf16(_rng(seed, 5, "res"), (B, T, H)))
+
+
+def config6(seed: int = 0) -> Workload:
+    """LayerNorm + modulate + static FP8 quantisation at the FLUX site shape
+    x [2,4608,3072] ~ N(0,1); scale/shift [2,3072] ~ 0.1*N; static scale 0.0125
+    (about amax/448 of the modulated activations)."""
+    B, T, H = 2, 4608, 3072
+    v = _vecs(seed, 6, B, H, ["scale", "shift"])
+    return Workload("lnq", "ln_fp8_2x4608x3072", normal_bf16(_rng(seed, 6, "x"), (B, T, H)),
+                    v["scale"], v["shift"], qscale=0.0125)
 
 
 def flux_chunk_views(seed: int, B: int, H: int, chunks: int, cid: int = 30):

@@ -1,11 +1,12 @@
 /*
  * adaln.h -- C ABI of libadaln: fused adaLN normalisation for AMD MI355X (gfx950).
  *
- * The four compute entry points fuse a row normalisation (LayerNorm without
+ * The five compute entry points fuse a row normalisation (LayerNorm without
  * affine parameters, or RMSNorm with an optional weight) with the adaLN
  * modulate epilogue  y = norm(x) * (1 + scale[b]) + shift[b]  that diffusion
  * transformers run at every adaLN site, optionally preceded by the residual-gate
- * prologue  r = res + gate[b] * x (for both norms).
+ * prologue  r = res + gate[b] * x (for both norms), or followed, for the
+ * LayerNorm, by a static FP8 quantisation of y.
  *
  * Sources, cited by page title and section:
  *  - FLUX.1 PR report "route the adaLN LN+modulate sites through the bit-exact
@@ -26,6 +27,11 @@
  *    a status), it never degrades silently.
  *  - FLUX.1 PR report, related PRs: the FLUX.1 bit-exact residual-gate fast path
  *    (#33819) beside the LN+modulate sites.
+ *  - kernels guide, "data movement and quantised layout producers":
+ *    fused_layernorm_modulate_fp8_quant_raw folds FLUX.2's LayerNorm, adaLN
+ *    modulate and static FP8 quantisation into one kernel; Qwen PR report
+ *    (modelopt_quant.py snippet): ModelOpt FP8 checkpoints use E4M3 (e4m3fn) with
+ *    a per-tensor static input scale.
  *  - Batch-invariance article (vLLM), section 3 (RMSNorm): the reduction layout
  *    depends on the hidden size only, never on the number of rows.
  *
@@ -48,6 +54,9 @@
  *     RMS RN(RN(x * rstd) * RN(w + 0)).
  *   Modulate: a = bf16(1 + scale); p = bf16(yn * a); y = bf16(p + shift).
  *   Residual gate: g = bf16(gate * x); r = bf16(res + g); r feeds the norm.
+ *   FP8 quantisation: inv = RN(1 / qscale); q = E4M3(clamp(RN(y * inv), -448, 448))
+ *     with nearest-even rounding into the OCP E4M3 format (bias 7, subnormals, no
+ *     infinity, largest finite 448); a NaN y gives a NaN code.
  *
  * Conventions shared by all entry points:
  *  - Tensors are raw bf16 bit patterns (adaln_bf16).  x, res, y, r are
@@ -60,14 +69,15 @@
  *  - Requirements: 8 <= H <= 8192, H % 8 == 0 (16-byte vectors of 8 bf16);
  *    every pointer 16-byte aligned; batch strides >= 0 and % 8 == 0; B, T >= 0;
  *    eps finite and >= 0.  B*T == 0 is a successful no-op (pointers unchecked).
- *  - Outputs (y, r) may not overlap any input or each other.
+ *  - Outputs (y, r, q) may not overlap any input or each other.
  *  - Ownership: the caller owns every buffer; the library never allocates,
  *    frees or synchronises.  Work is enqueued on `hip_stream` (a hipStream_t;
  *    NULL = the null stream) of the current device; pointers must be device
  *    memory of that device.
  *  - Errors: a non-OK status is returned before anything is launched, so the
  *    outputs are untouched.  ADALN_ERR_LAUNCH reports a failed launch (for
- *    example no gfx950 device).  Thread-safe and reentrant (no global state).
+ *    example no gfx950 device).  Thread-safe and reentrant: the only global state
+ *    is a mutex-guarded cache of occupancy queries per kernel and device.
  */
 #ifndef ADALN_H
 #define ADALN_H
@@ -78,8 +88,9 @@
 extern "C" {
 #endif
 
-#define ADALN_ABI_VERSION 3 /* 2: two waves per row for 2048 <= H < 4096;
-                              3: residual-gate LayerNorm, stream copy */
+#define ADALN_ABI_VERSION 4 /* 2: two waves per row for 2048 <= H < 4096;
+                              3: residual-gate LayerNorm, stream copy;
+                              4: LayerNorm + modulate + FP8 quantisation */
 
 typedef uint16_t adaln_bf16; /* raw bfloat16 bits */
 
@@ -128,6 +139,19 @@ adaln_status adaln_residual_gate_layernorm_modulate(
     int64_t gate_bstride, int64_t scale_bstride, int64_t shift_bstride, float eps,
     void* hip_stream);
 
+/* q = E4M3(clamp(RN(y * RN(1 / *qscale)), -448, 448)) with y the output of
+ * adaln_layernorm_modulate (bf16, never written to memory): one byte per element,
+ * q contiguous [B, T, H], 16-byte aligned.  qscale points to one float in device
+ * memory (the static per-tensor input scale of an FP8 checkpoint), 4-byte aligned;
+ * it is read on the device, so its value is not validated: a zero, negative or
+ * non-finite scale gives whatever the formula gives.  (kernels guide:
+ * fused_layernorm_modulate_fp8_quant_raw) */
+adaln_status adaln_layernorm_modulate_fp8_quant(const adaln_bf16* x, const adaln_bf16* scale,
+                                                const adaln_bf16* shift, const float* qscale,
+                                                uint8_t* q, int64_t B, int64_t T, int64_t H,
+                                                int64_t scale_bstride, int64_t shift_bstride,
+                                                float eps, void* hip_stream);
+
 /* Predicates: the validation of the entry point of the same name, without a
  * launch (the `can_use_*` predicate of the kernels guide's entry-point protocol).
  * They never touch the GPU. */
@@ -152,6 +176,12 @@ adaln_status adaln_check_residual_gate_layernorm_modulate(
     const adaln_bf16* shift, const adaln_bf16* r_out, const adaln_bf16* y, int64_t B, int64_t T,
     int64_t H, int64_t gate_bstride, int64_t scale_bstride, int64_t shift_bstride, float eps);
 
+adaln_status adaln_check_layernorm_modulate_fp8_quant(const adaln_bf16* x, const adaln_bf16* scale,
+                                                      const adaln_bf16* shift, const float* qscale,
+                                                      const uint8_t* q, int64_t B, int64_t T,
+                                                      int64_t H, int64_t scale_bstride,
+                                                      int64_t shift_bstride, float eps);
+
 /* The fixed reduction layout for H: waves per row, lanes per row, chunks per
  * lane.  ADALN_ERR_SHAPE for an unsupported H; out-pointers may be NULL. */
 adaln_status adaln_reduction_layout(int64_t H, int* waves_per_row, int* lanes_per_row,
@@ -171,6 +201,13 @@ int adaln_abi_version(void);
 adaln_status adaln_diag_round_bf16(const float* in, adaln_bf16* out, int64_t n, void* hip_stream);
 adaln_status adaln_diag_finalize(const float* in, float* out, int64_t n, float eps,
                                  void* hip_stream);
+
+/* Diagnostic: the FP8 kernel's quantisation step on binary32 inputs,
+ * out[i] = E4M3(clamp(RN(in[i] * RN(1 / *qscale)), -448, 448)).  n >= 0 and
+ * n % 4 == 0 (ADALN_ERR_SHAPE); in 16-byte aligned, out and qscale 4-byte aligned;
+ * device memory. */
+adaln_status adaln_diag_quant_fp8(const float* in, uint8_t* out, int64_t n, const float* qscale,
+                                  void* hip_stream);
 
 /* Measurement aid: copy `bytes` bytes of device memory from src to dst with the
  * fused kernels' access style (16-byte non-temporal loads and stores), so that the

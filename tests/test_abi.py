@@ -33,14 +33,14 @@ def declared_symbols():
 
 def test_header_symbols_are_exported(lib):
     names = declared_symbols()
-    assert len(names) == 14, names
+    assert len(names) == 17, names
     assert set(names) == set(_binding.EXPORTS)
     for n in names:
         assert hasattr(lib, n), n
 
 
 def test_abi_version_and_status_strings(lib):
-    assert A.adaln_abi_version() == A.ABI_VERSION == 3
+    assert A.adaln_abi_version() == A.ABI_VERSION == 4
     for s in range(8):
         assert len(A.adaln_status_string(s)) > 5
     assert A.adaln_status_string(99) == "unknown status"
@@ -92,6 +92,37 @@ def rgln_check(lib, **kw):
     return lib.adaln_check_residual_gate_layernorm_modulate(
         a["res"], a["x"], a["gate"], a["scale"], a["shift"], a["r"], a["y"], a["B"], a["T"],
         a["H"], a["gbs"], a["sbs"], a["hbs"], a["eps"])
+
+
+def lnq_check(lib, **kw):
+    a = dict(x=addr(0), scale=addr(1), shift=addr(2), qs=addr(3), q=addr(4), B=2, T=5, H=3072,
+             sbs=3072, hbs=3072, eps=1e-6)
+    a.update(kw)
+    return lib.adaln_check_layernorm_modulate_fp8_quant(a["x"], a["scale"], a["shift"], a["qs"],
+                                                        a["q"], a["B"], a["T"], a["H"], a["sbs"],
+                                                        a["hbs"], a["eps"])
+
+
+def test_fp8_quant_checks(lib):
+    assert lnq_check(lib) == OK
+    assert lnq_check(lib, qs=None) == NULL
+    assert lnq_check(lib, q=None) == NULL
+    assert lnq_check(lib, qs=addr(3) + 2) == ALIGN
+    assert lnq_check(lib, qs=addr(3) + 4) == OK          # 4-byte alignment suffices
+    assert lnq_check(lib, q=addr(4) + 8) == ALIGN
+    assert lnq_check(lib, H=12) == SHAPE
+    rows_bytes = 2 * 5 * 3072                            # one byte per element
+    assert lnq_check(lib, q=addr(0) + 2 * rows_bytes) == OK      # just after x (2 bytes/elem)
+    assert lnq_check(lib, q=addr(0) + 2 * rows_bytes - 16) == OVERLAP
+    assert lnq_check(lib, qs=addr(4) + rows_bytes - 4) == OVERLAP  # scale inside q
+    assert lnq_check(lib, qs=addr(4) + rows_bytes) == OK
+    assert lnq_check(lib, B=0, x=None, q=None, qs=None) == OK
+    assert lib.adaln_layernorm_modulate_fp8_quant(addr(0), addr(1), addr(2), None, addr(4), 1, 2,
+                                                  3072, 0, 0, 1e-6, None) == NULL
+    assert lib.adaln_diag_quant_fp8(addr(0), addr(1), 6, addr(2), None) == SHAPE
+    assert lib.adaln_diag_quant_fp8(addr(0) + 4, addr(1), 8, addr(2), None) == ALIGN
+    assert lib.adaln_diag_quant_fp8(addr(0), addr(0) + 8, 8, addr(2), None) == OVERLAP
+    assert lib.adaln_diag_quant_fp8(None, None, 0, None, None) == OK
 
 
 def test_valid_arguments_pass(lib):

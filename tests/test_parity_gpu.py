@@ -47,6 +47,25 @@ def check_rgln(res, x, g, sc, sh, what, eps=EPS):
     assert_bits_equal(y, y0, what + " y")
 
 
+def run_lnq(x, sc, sh, qscale, eps=EPS):
+    qs = torch.tensor([qscale], dtype=torch.float32, device="cuda")
+    return A.adaln_layernorm_modulate_fp8_quant(dev(x), dev(sc), dev(sh), qs, eps).cpu().numpy()
+
+
+def assert_fp8_equal(got, want, what):
+    """E4M3 codes equal, NaN (S.1111.111) in the same places (any NaN code)."""
+    gn = (got & 0x7F) == 0x7F
+    wn = (want & 0x7F) == 0x7F
+    assert np.array_equal(gn, wn), what + ": NaN positions differ"
+    bad = np.flatnonzero(got[~gn] != want[~wn])
+    assert bad.size == 0, f"{what}: {bad.size} codes differ, first at {bad[:5]}"
+
+
+def check_lnq(x, sc, sh, qscale, what, eps=EPS):
+    assert_fp8_equal(run_lnq(x, sc, sh, qscale, eps),
+                     O.layernorm_modulate_fp8(x, sc, sh, qscale, eps), what)
+
+
 def check_workload(wl, what):
     say(f"[parity] {what} {wl.op} shape={wl.x.shape}")
     if wl.op == "ln":
@@ -55,6 +74,8 @@ def check_workload(wl, what):
     elif wl.op == "rms":
         assert_bits_equal(run_rms(wl.x, wl.weight, wl.scale, wl.shift), O.rmsnorm_scale_shift(
             wl.x, wl.weight, wl.scale, wl.shift, wl.eps), what)
+    elif wl.op == "lnq":
+        check_lnq(wl.x, wl.scale, wl.shift, wl.qscale, what, wl.eps)
     elif wl.op == "rgln":
         check_rgln(wl.res, wl.x, wl.gate, wl.scale, wl.shift, what, wl.eps)
     else:
@@ -68,11 +89,11 @@ def check_workload(wl, what):
 # --------------------------------------------------------------------------
 # the workloads at full size
 # --------------------------------------------------------------------------
-@pytest.mark.parametrize("cfg", ["0", "1", "2", "3a", "3b", "5"])
+@pytest.mark.parametrize("cfg", ["0", "1", "2", "3a", "3b", "5", "6"])
 def test_workload_full_size(cfg):
     wl = {"0": synth.config0, "1": synth.config1, "2": synth.config2,
           "3a": lambda: synth.config3(site="a"), "3b": lambda: synth.config3(site="b"),
-          "5": synth.config5}[cfg]()
+          "5": synth.config5, "6": synth.config6}[cfg]()
     check_workload(wl, f"config {cfg}")
 
 
@@ -110,6 +131,10 @@ def test_flux_sites_chunk_views(shape, chunks):
     r0, y0 = O.residual_gate_layernorm_modulate(res, x, gate, scale, shift, EPS)
     assert_bits_equal(host(r), r0, f"flux rgln r {shape}")
     assert_bits_equal(host(y), y0, f"flux rgln y {shape}")
+    # the FP8 variant through the same strided views
+    qs = torch.tensor([0.0125], dtype=torch.float32, device="cuda")
+    q = A.adaln_layernorm_modulate_fp8_quant(dev(x), scale_d, shift_d, qs, EPS).cpu().numpy()
+    assert_fp8_equal(q, O.layernorm_modulate_fp8(x, scale, shift, 0.0125, EPS), f"flux lnq {shape}")
 
 
 # --------------------------------------------------------------------------
@@ -148,6 +173,8 @@ def test_edge_hidden_sizes(H):
         assert_bits_equal(r, r0, "rg r " + tag)
         assert_bits_equal(y, y0, "rg y " + tag)
     check_rgln(res, x, g, sc, sh, f"rgln H={H}")
+    for qs in (0.0125, 1.0):
+        check_lnq(x, sc, sh, qs, f"lnq H={H} qscale={qs}")
 
 
 @pytest.mark.parametrize("eps", [0.0, 1e-5, 1e-6, 0.25])
@@ -164,6 +191,7 @@ def test_eps_values(eps):
         res = mixed_rows(rng, 1, 9, H)
         g = synth.normal_bf16(rng, (1, H), 0.1)
         check_rgln(res, x, g, sc, sh, f"rgln eps={eps}", eps)
+        check_lnq(x, sc, sh, 0.02, f"lnq eps={eps}", eps)
 
 
 def test_constant_and_zero_rows():
@@ -181,6 +209,8 @@ def test_constant_and_zero_rows():
     upd = synth.normal_bf16(rng, x.shape)
     zero = np.zeros((1, H), np.uint16)
     check_rgln(x, upd, zero, sc, sh, "rgln zero gate")
+    for qs in (0.0125, 1e-3, 2.0 ** -12):   # the last saturates most outputs at +-448
+        check_lnq(x, sc, sh, qs, f"lnq constant rows qscale={qs}")
 
 
 def test_nonfinite_inputs_give_nan_in_the_same_places():
@@ -198,6 +228,8 @@ def test_nonfinite_inputs_give_nan_in_the_same_places():
     g = synth.normal_bf16(rng, (1, H), 0.1)
     rg_r, rg_y = run_rgln(res, x, g, sc, sh)
     rg_r0, rg_y0 = O.residual_gate_layernorm_modulate(res, x, g, sc, sh, EPS)
+    assert_fp8_equal(run_lnq(x, sc, sh, 0.0125), O.layernorm_modulate_fp8(x, sc, sh, 0.0125, EPS),
+                     "lnq non-finite")
     for got, want in ((run_ln(x, sc, sh), O.layernorm_modulate(x, sc, sh, EPS)),
                       (run_rms(x, None, sc, sh), O.rmsnorm_scale_shift(x, None, sc, sh, EPS)),
                       (rg_r, rg_r0), (rg_y, rg_y0)):
@@ -272,8 +304,13 @@ def test_rows_alone_equal_rows_in_batch():
     resd = dev(mixed_rows(rng, B, T, H))
     gd = dev(synth.normal_bf16(rng, (B, H), 0.1))
     rg_r, rg_y = A.adaln_residual_gate_layernorm_modulate(resd, xd, gd, scd, shd, EPS)
+    qs = torch.tensor([0.0125], dtype=torch.float32, device="cuda")
+    q = A.adaln_layernorm_modulate_fp8_quant(xd, scd, shd, qs, EPS)
     for b in range(B):
         for t in range(0, T, 3):
+            q1 = A.adaln_layernorm_modulate_fp8_quant(xd[b:b + 1, t:t + 1].contiguous(), scd[b],
+                                                      shd[b], qs, EPS)
+            assert torch.equal(q1[0, 0], q[b, t])
             r1, y1 = A.adaln_residual_gate_layernorm_modulate(
                 resd[b:b + 1, t:t + 1].contiguous(), xd[b:b + 1, t:t + 1].contiguous(), gd[b],
                 scd[b], shd[b], EPS)
@@ -284,6 +321,42 @@ def test_rows_alone_equal_rows_in_batch():
             y2 = A.adaln_rmsnorm_scale_shift(xd[b:b + 1, t:t + 1].contiguous(), None, scd[b],
                                              shd[b], EPS)
             assert torch.equal(y2[0, 0].view(torch.int16), yr[b, t].view(torch.int16))
+
+
+# --------------------------------------------------------------------------
+# the FP8 kernel's quantisation step, exhaustively over binary32
+# --------------------------------------------------------------------------
+def test_device_fp8_quant_all_fp32_patterns():
+    # qscale 1: the clamp and the E4M3 conversion of every fp32 pattern, against
+    # torch's float8_e4m3fn conversion of the clamped value (the eager chain)
+    qs = torch.ones(1, dtype=torch.float32, device="cuda")
+    n_chunks = 16
+    step = (1 << 32) // n_chunks
+    for k in range(n_chunks):
+        say(f"[diag] fp8 quant chunk {k + 1}/{n_chunks}")
+        u = torch.arange(k * step, (k + 1) * step, dtype=torch.int64, device="cuda")
+        f = (u - (1 << 32) * (u >= (1 << 31)).long()).to(torch.int32).view(torch.float32)
+        got = A.adaln_diag_quant_fp8(f, qs)
+        want = f.clamp(-448.0, 448.0).to(torch.float8_e4m3fn).view(torch.uint8)
+        gn = (got & 0x7F) == 0x7F
+        wn = (want & 0x7F) == 0x7F
+        assert torch.equal(gn, wn), f"chunk {k}: NaN positions"
+        assert torch.equal(got[~gn], want[~wn]), f"chunk {k}"
+        del u, f, got, want, gn, wn
+    torch.cuda.synchronize()
+
+
+@pytest.mark.parametrize("qscale", [0.0125, 3.0, 2.0 ** -20, 1e30])
+def test_device_fp8_quant_scaled_vs_oracle(qscale):
+    rng = np.random.default_rng(9)
+    bits = rng.integers(0, 1 << 32, size=1 << 22, dtype=np.uint64).astype(np.uint32)
+    v = bits.view(np.float32)
+    qs = torch.tensor([qscale], dtype=torch.float32, device="cuda")
+    got = A.adaln_diag_quant_fp8(torch.from_numpy(v.copy()).cuda(), qs).cpu().numpy()
+    inv = np.float32(1.0) / np.float32(qscale)
+    with np.errstate(over="ignore", invalid="ignore"):
+        t = np.clip(v * inv, np.float32(-448.0), np.float32(448.0))
+    assert_fp8_equal(got, O.to_e4m3fn(t), f"quant qscale={qscale}")
 
 
 # --------------------------------------------------------------------------

@@ -158,6 +158,55 @@ def config6(seed: int = 0) -> Workload:
                     v["scale"], v["shift"], qscale=0.0125)
 
 
+def rope_cache(tokens: int, head_dim: int, base: float = 10000.0) -> np.ndarray:
+    """float32 [tokens, head_dim]: row t = cos(t*theta_i) for i < head_dim/2, then
+    sin(t*theta_i), theta_i = base^(-2i/head_dim); angles and cos/sin in float64, then
+    cast to float32.  (An input of the QK-norm + RoPE op, like the cos/sin cache a
+    model precomputes.)"""
+    i = np.arange(head_dim // 2, dtype=np.float64)
+    theta = base ** (-2.0 * i / head_dim)
+    ang = np.arange(tokens, dtype=np.float64)[:, None] * theta[None, :]
+    return np.concatenate([np.cos(ang), np.sin(ang)], axis=1).astype(np.float32)
+
+
+@dataclasses.dataclass
+class QKWorkload:
+    """Per-head QK RMSNorm + RoPE input: q, k are views of one packed QKV buffer."""
+    name: str
+    qkv: np.ndarray          # [tokens, 3, heads, head_dim] bf16 bits (q, k, v)
+    q_weight: np.ndarray     # [head_dim]
+    k_weight: np.ndarray     # [head_dim]
+    cos_sin: np.ndarray      # float32 [tokens, head_dim]
+    eps: float = 1e-6
+    op: str = "qk"
+
+    @property
+    def q(self):
+        return self.qkv[:, 0]
+
+    @property
+    def k(self):
+        return self.qkv[:, 1]
+
+    def algorithmic_bytes(self) -> int:
+        """Read q and k, write q_out and k_out (bf16), read the cos/sin cache once."""
+        T, _, Hd, D = self.qkv.shape
+        return 8 * T * Hd * D + 4 * T * D
+
+
+def config7(seed: int = 0) -> QKWorkload:
+    """Qwen-Image-like attention input (Qwen PR report: batch 1, head_dim 128, Q/K as
+    views of the packed QKV projection): 4096 image + 512 text tokens, 24 heads of 128
+    (hidden 3072); qkv ~ N(0,1); RMSNorm weights 1 + 0.02*N; RoPE cache of positions
+    0..4607 with base 10000."""
+    T, Hd, D = 4608, 24, 128
+    qkv = normal_bf16(_rng(seed, 7, "x"), (T, 3, Hd, D))
+    return QKWorkload("qk_rmsnorm_rope_4608x24x128", qkv,
+                      normal_bf16(_rng(seed, 7, "weight"), (D,), 0.02, 1.0),
+                      normal_bf16(_rng(seed, 7, "scale"), (D,), 0.02, 1.0),
+                      rope_cache(T, D))
+
+
 def flux_chunk_views(seed: int, B: int, H: int, chunks: int, cid: int = 30):
     """scale/shift as strided views of one [B, chunks*H] embedding, like
     ``emb.chunk(chunks, dim=1)`` in the FLUX.1 test snippet: (emb, shift, scale)

@@ -501,6 +501,75 @@ int oracle_layernorm_modulate_fp8(const uint16_t* x, const uint16_t* scale, cons
     return bad;
 }
 
+/* Per-head QK RMSNorm + interleaved RoPE (kernels guide, RoPE / QK-norm: the
+ * QK-norm chain fused into the rotary embedding; Qwen PR report, implementation
+ * item 3 and the qwen_image.py snippet: per-head RMSNorm of Q and K with their
+ * weights, then interleaved (non-NeoX) RoPE from an fp32 cos/sin cache,
+ * head_dim 128).  Per head vector x (head_dim values):
+ *   yn[c] = bf16(RN(RN(x[c] * rstd) * RN(w[c] + 0))), with rstd the RMS statistic
+ *           of this library for H = head_dim (same fixed order);
+ *   for i < head_dim/2, with a = f(yn[2i]), b = f(yn[2i+1]), c = cs[i],
+ *   s = cs[head_dim/2 + i] (cs: the token's cache row, cos half then sin half):
+ *     out[2i]   = bf16(RN(RN(a*c) - RN(b*s)))
+ *     out[2i+1] = bf16(RN(RN(b*c) + RN(a*s)))
+ * q: token t, head h at q + t*q_tstride + h*head_dim; k likewise; outputs are
+ * contiguous [tokens, heads, head_dim].  weight NULL means one.  yn_q/yn_k
+ * (nullable) receive the normalised values before the rotation. */
+#define ORACLE_MAX_HEAD_DIM 256
+static int qk_head(const uint16_t* x, const uint16_t* w, const float* cs, int64_t D, float eps,
+                   uint16_t* out, uint16_t* yn_out) {
+    float xr[ORACLE_MAX_HEAD_DIM] = {0};
+    uint16_t yn[ORACLE_MAX_HEAD_DIM] = {0};
+    for (int64_t c = 0; c < D; c++) xr[c] = widen(x[c]);
+    float st[STATS_PER_ROW];
+    int bad = rms_stat(xr, D, eps, st);
+    const float rstd = st[4];
+    for (int64_t c = 0; c < D; c++) {
+        float n = xr[c] * rstd;
+        float wf = w ? (widen(w[c]) + 0.0f) : 1.0f;
+        float p = n * wf;
+        yn[c] = to_bf16(p);
+        if (yn_out) yn_out[c] = yn[c];
+    }
+    for (int64_t i = 0; i < D / 2; i++) {
+        float a = widen(yn[2 * i]), b = widen(yn[2 * i + 1]);
+        float co = cs[i], si = cs[D / 2 + i];
+        float ac = a * co, bs = b * si, bc = b * co, as = a * si;
+        float o1 = ac - bs;
+        float o2 = bc + as;
+        out[2 * i] = to_bf16(o1);
+        out[2 * i + 1] = to_bf16(o2);
+    }
+    return bad;
+}
+
+int oracle_qk_rmsnorm_rope(const uint16_t* q, const uint16_t* k, const uint16_t* q_weight,
+                           const uint16_t* k_weight, const float* cos_sin, uint16_t* q_out,
+                           uint16_t* k_out, int64_t tokens, int64_t heads_q, int64_t heads_k,
+                           int64_t head_dim, int64_t q_tstride, int64_t k_tstride, float eps,
+                           uint16_t* yn_q, uint16_t* yn_k) {
+    if (tokens < 0 || heads_q < 0 || heads_k < 0 || !valid_h(head_dim) ||
+        head_dim > ORACLE_MAX_HEAD_DIM)
+        return -1;
+    unsigned int env = fp_enter();
+    int bad = 0;
+    for (int64_t t = 0; t < tokens; t++) {
+        const float* cs = cos_sin + t * head_dim;
+        for (int64_t h = 0; h < heads_q; h++) {
+            int64_t o = (t * heads_q + h) * head_dim;
+            bad += qk_head(q + t * q_tstride + h * head_dim, q_weight, cs, head_dim, eps,
+                           q_out + o, yn_q ? yn_q + o : NULL);
+        }
+        for (int64_t h = 0; h < heads_k; h++) {
+            int64_t o = (t * heads_k + h) * head_dim;
+            bad += qk_head(k + t * k_tstride + h * head_dim, k_weight, cs, head_dim, eps,
+                           k_out + o, yn_k ? yn_k + o : NULL);
+        }
+    }
+    fp_leave(env);
+    return bad;
+}
+
 /* ------------------------------------------------------------------------ */
 /* elementwise helpers exposed for the pins                                  */
 /* ------------------------------------------------------------------------ */

@@ -66,6 +66,8 @@ def _load():
     lib.oracle_to_e4m3fn.restype = None
     lib.oracle_quant_fp8.argtypes = [P, P, I, F]
     lib.oracle_quant_fp8.restype = None
+    lib.oracle_qk_rmsnorm_rope.argtypes = [P, P, P, P, P, P, P, I, I, I, I, I, I, F, P, P]
+    lib.oracle_qk_rmsnorm_rope.restype = ctypes.c_int
     lib.oracle_round_bf16.argtypes = [P, P, I]
     lib.oracle_round_bf16.restype = None
     lib.oracle_modulate.argtypes = [P, P, P, P, I]
@@ -233,6 +235,43 @@ def quant_fp8(y, qscale):
     out = np.empty(y.shape, np.uint8)
     lib.oracle_quant_fp8(_ptr(y), _ptr(out), y.size, float(np.float32(qscale)))
     return out
+
+
+def _heads(a, name, tokens=None):
+    """A [tokens, heads, head_dim] uint16 view with unit head_dim stride and head stride
+    head_dim (token stride free); returns (array, heads, token stride in elements)."""
+    a = np.asarray(a)
+    if a.dtype != np.uint16 or a.ndim != 3 or a.strides[2] != 2 or a.strides[1] != 2 * a.shape[2]:
+        raise ValueError(f"{name}: expected [tokens, heads, head_dim] with contiguous heads")
+    if tokens is not None and a.shape[0] != tokens:
+        raise ValueError(f"{name}: token count differs")
+    return a, a.shape[1], a.strides[0] // 2
+
+
+def qk_rmsnorm_rope(q, k, q_weight, k_weight, cos_sin, eps=1e-6, want_norm=False):
+    """Per-head RMSNorm of q and k, then interleaved RoPE; returns (q_out, k_out[, yn_q,
+    yn_k]).  q, k: [tokens, heads, head_dim] (token stride free, e.g. views of a packed
+    QKV row); cos_sin: float32 [tokens, head_dim] (cos half, then sin half)."""
+    lib = _load()
+    q, hq, qts = _heads(q, "q")
+    T, _, D = q.shape
+    k, hk, kts = _heads(k, "k", T)
+    if k.shape[2] != D:
+        raise ValueError("q and k head_dim differ")
+    cs = np.ascontiguousarray(cos_sin, dtype=np.float32).reshape(T, D)
+    qw = None if q_weight is None else np.ascontiguousarray(q_weight, np.uint16).reshape(D)
+    kw = None if k_weight is None else np.ascontiguousarray(k_weight, np.uint16).reshape(D)
+    qo = np.empty((T, hq, D), np.uint16)
+    ko = np.empty((T, hk, D), np.uint16)
+    ynq = np.empty_like(qo) if want_norm else None
+    ynk = np.empty_like(ko) if want_norm else None
+    base_q = q.ctypes.data
+    base_k = k.ctypes.data
+    rc = lib.oracle_qk_rmsnorm_rope(base_q, base_k, _ptr(qw), _ptr(kw), _ptr(cs), _ptr(qo),
+                                    _ptr(ko), T, hq, hk, D, qts, kts, float(np.float32(eps)),
+                                    _ptr(ynq), _ptr(ynk))
+    _check(rc, "qk_rmsnorm_rope")
+    return (qo, ko, ynq, ynk) if want_norm else (qo, ko)
 
 
 def _ret(y, yn, st, want_norm, want_stats, tup=False):

@@ -395,6 +395,95 @@ def test_layernorm_modulate_fp8_quantises_the_ln_output():
 
 
 # --------------------------------------------------------------------------
+# per-head QK RMSNorm + interleaved RoPE
+# --------------------------------------------------------------------------
+def _qk_inputs(T, Hd, D=128, seed=0, sigma=1.0, angles=None):
+    rng = np.random.default_rng(seed)
+    qkv = synth.normal_bf16(rng, (T, 3, Hd, D), sigma)
+    wq = synth.normal_bf16(rng, (D,), 0.02, 1.0)
+    wk = synth.normal_bf16(rng, (D,), 0.02, 1.0)
+    cs = synth.rope_cache(T, D) if angles is None else angles
+    return qkv, wq, wk, cs
+
+
+def test_qk_norm_is_rms_of_each_head():
+    T, Hd = 7, 5
+    qkv, wq, wk, cs = _qk_inputs(T, Hd, seed=1, sigma=3.0)
+    qo, ko, ynq, ynk = O.qk_rmsnorm_rope(qkv[:, 0], qkv[:, 1], wq, wk, cs, EPS, want_norm=True)
+    for x, w, yn in ((qkv[:, 0], wq, ynq), (qkv[:, 1], wk, ynk)):
+        rows = np.ascontiguousarray(x).reshape(1, T * Hd, 128)
+        ref, floor = rms_ref64(rows, w, EPS32)
+        assert_within(yn.reshape(1, T * Hd, 128), ref, floor, "qk norm")
+
+
+@pytest.mark.parametrize("angles", ["cache", "random"])
+def test_rope_vs_eager_fp32_chain(angles):
+    # the rotation as torch float32 eager ops on the bf16 normalised values, each
+    # product and sum rounded on its own, one rounding to bf16 at the end; 2^21
+    # elements per tensor, so that a fused multiply-add (one rounding fewer) shows
+    T, Hd = 2048, 8
+    rng = np.random.default_rng(12)
+    cs = None
+    if angles == "random":
+        ang = rng.uniform(-np.pi, np.pi, (T, 64))
+        cs = np.concatenate([np.cos(ang), np.sin(ang)], 1).astype(np.float32)
+    qkv, wq, wk, cs = _qk_inputs(T, Hd, seed=2, angles=cs)
+    qo, ko, ynq, ynk = O.qk_rmsnorm_rope(qkv[:, 0], qkv[:, 1], wq, wk, cs, EPS, want_norm=True)
+    c = torch.from_numpy(cs[:, None, :64])
+    s_ = torch.from_numpy(cs[:, None, 64:])
+    for yn, out in ((ynq, qo), (ynk, ko)):
+        y = torch_bf16(yn).float()
+        a, b = y[..., 0::2], y[..., 1::2]
+        o1 = (a * c - b * s_).to(torch.bfloat16)
+        o2 = (b * c + a * s_).to(torch.bfloat16)
+        ref = torch.stack([o1, o2], dim=-1).reshape(y.shape)
+        assert np.array_equal(out, from_torch(ref))
+
+
+def test_rope_closed_forms():
+    T, Hd = 4, 3
+    qkv, wq, wk, _ = _qk_inputs(T, Hd, seed=3)
+    one, zero = np.ones((T, 64), np.float32), np.zeros((T, 64), np.float32)
+    ident = np.concatenate([one, zero], 1)
+    qo, ko, ynq, ynk = O.qk_rmsnorm_rope(qkv[:, 0], qkv[:, 1], wq, wk, ident, EPS, want_norm=True)
+    assert np.array_equal(qo, ynq) and np.array_equal(ko, ynk)        # angle 0
+    quarter = np.concatenate([zero, one], 1)                            # angle pi/2
+    qo, _, ynq, _ = O.qk_rmsnorm_rope(qkv[:, 0], qkv[:, 1], wq, wk, quarter, EPS, want_norm=True)
+    assert np.array_equal(qo[..., 0::2], ynq[..., 1::2] ^ 0x8000)        # -b
+    assert np.array_equal(qo[..., 1::2], ynq[..., 0::2])                 # a
+    half = np.concatenate([-one, zero], 1)                              # angle pi
+    qo, _, ynq, _ = O.qk_rmsnorm_rope(qkv[:, 0], qkv[:, 1], wq, wk, half, EPS, want_norm=True)
+    assert np.array_equal(qo, ynq ^ 0x8000)
+
+
+def test_rope_accuracy_fp64():
+    T, Hd = 64, 4
+    qkv, wq, wk, cs = _qk_inputs(T, Hd, seed=4, sigma=10.0)
+    qo, _, ynq, _ = O.qk_rmsnorm_rope(qkv[:, 0], qkv[:, 1], wq, wk, cs, EPS, want_norm=True)
+    y = widen(ynq).astype(np.float64)
+    a, b = y[..., 0::2], y[..., 1::2]
+    c = cs[:, None, :64].astype(np.float64)
+    s_ = cs[:, None, 64:].astype(np.float64)
+    exact = np.stack([a * c - b * s_, b * c + a * s_], -1).reshape(y.shape)
+    got = widen(qo).astype(np.float64)
+    mag = np.repeat(np.abs(a) + np.abs(b), 2, axis=-1)
+    tol = ulp_bf16(exact) / 2 + 3 * 2.0 ** -24 * mag
+    assert np.all(np.abs(got - exact) <= tol)
+
+
+def test_qk_strided_views_match_contiguous():
+    T, Hd = 9, 4
+    qkv, wq, wk, cs = _qk_inputs(T, Hd, seed=5)
+    a = O.qk_rmsnorm_rope(qkv[:, 0], qkv[:, 1], wq, wk, cs, EPS)
+    b = O.qk_rmsnorm_rope(np.ascontiguousarray(qkv[:, 0]), np.ascontiguousarray(qkv[:, 1]), wq,
+                          wk, cs, EPS)
+    assert np.array_equal(a[0], b[0]) and np.array_equal(a[1], b[1])
+    # q and k differ only in their inputs and weights: swapping them swaps the outputs
+    c = O.qk_rmsnorm_rope(qkv[:, 1], qkv[:, 0], wk, wq, cs, EPS)
+    assert np.array_equal(a[0], c[1]) and np.array_equal(a[1], c[0])
+
+
+# --------------------------------------------------------------------------
 # the full output is the modulate chain applied to the norm output
 # --------------------------------------------------------------------------
 @pytest.mark.parametrize("op", ["ln", "rms"])

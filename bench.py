@@ -64,7 +64,7 @@ def workload(cfg: str):
     from diffusion_dit_adaln_amd import synth
     return {"0": synth.config0, "1": synth.config1, "2": synth.config2,
             "3a": lambda: synth.config3(site="a"), "3b": lambda: synth.config3(site="b"),
-            "5": synth.config5, "6": synth.config6}[cfg]()
+            "5": synth.config5, "6": synth.config6, "7": synth.config7}[cfg]()
 
 
 class Launcher:
@@ -134,6 +134,50 @@ class Launcher:
             None if self.weight is None else self.weight.data_ptr(), self.scale.data_ptr(),
             self.shift.data_ptr(), s["r"].data_ptr(), s["y"].data_ptr(), B, T, H, bs, bs, bs,
             self.eps, stream)
+
+
+class QKLauncher:
+    """Pre-marshalled QK RMSNorm + RoPE calls over rotating packed-QKV buffer sets."""
+
+    def __init__(self, wl, rotate_bytes: int):
+        import torch
+        import diffusion_dit_adaln_amd as A
+        self.lib = A.load_library()
+        self.wl = wl
+        T, _, Hd, D = wl.qkv.shape
+        self.T, self.Hd = T, Hd
+
+        def dev(a):
+            return torch.from_numpy(np.ascontiguousarray(a).view(np.int16)).view(
+                torch.bfloat16).cuda()
+
+        self.nsets = max(2, -(-rotate_bytes // wl.algorithmic_bytes()))
+        q0 = dev(wl.qkv)
+        self.sets = [{"qkv": q0.clone(), "qo": torch.empty((T, Hd, D), dtype=torch.bfloat16,
+                                                            device="cuda"),
+                      "ko": torch.empty((T, Hd, D), dtype=torch.bfloat16, device="cuda")}
+                     for _ in range(self.nsets)]
+        self.wq = dev(wl.q_weight)
+        self.wk = dev(wl.k_weight)
+        self.cs = torch.from_numpy(wl.cos_sin).cuda()
+        self.eps = ctypes.c_float(np.float32(wl.eps))
+        self.ts = 3 * Hd * D
+        del q0
+        torch.cuda.synchronize()
+
+    def call(self, i: int, stream) -> int:
+        s = self.sets[i % self.nsets]
+        base = s["qkv"].data_ptr()
+        row = self.Hd * 128 * 2
+        return self.lib.adaln_qk_rmsnorm_rope(base, base + row, self.wq.data_ptr(),
+                                              self.wk.data_ptr(), self.cs.data_ptr(),
+                                              s["qo"].data_ptr(), s["ko"].data_ptr(), self.T,
+                                              self.Hd, self.Hd, 128, self.ts, self.ts, self.eps,
+                                              stream)
+
+
+def launcher_for(wl, rotate_bytes):
+    return QKLauncher(wl, rotate_bytes) if wl.op == "qk" else Launcher(wl, rotate_bytes)
 
 
 def time_steps(launch, steps: int, warmup: int, mode: str):
@@ -316,9 +360,9 @@ def main():
             lambda: copy_ceiling(nbytes, rotate, steps, args.warmup, kind="torch")), 2)
         out["frac_of_copy_ceiling"] = round(gbps / out["copy_ceiling_GBps"], 4)
         per = {}
-        for cfg in ["0", "1", "2", "3a", "3b", "5", "6"]:
+        for cfg in ["0", "1", "2", "3a", "3b", "5", "6", "7"]:
             w2 = workload(cfg)
-            L2 = Launcher(w2, rotate)
+            L2 = launcher_for(w2, rotate)
             nb2 = w2.algorithmic_bytes()
             res = {}
             for mode in ("graph", "eager"):
@@ -328,9 +372,10 @@ def main():
             del L2
             torch.cuda.empty_cache()
             cc = median3(lambda: copy_ceiling(nb2, rotate, steps, args.warmup))
-            per[w2.name] = {"op": w2.op, "shape": list(w2.x.shape), "bytes": nb2, **res,
-                            "rows_per_s": round(w2.x.shape[0] * w2.x.shape[1] /
-                                                res["graph"]["us_per_launch"] * 1e6, 1),
+            shape = list(w2.qkv.shape) if w2.op == "qk" else list(w2.x.shape)
+            rows2 = (shape[0] * 2 * shape[2]) if w2.op == "qk" else shape[0] * shape[1]
+            per[w2.name] = {"op": w2.op, "shape": shape, "bytes": nb2, **res,
+                            "rows_per_s": round(rows2 / res["graph"]["us_per_launch"] * 1e6, 1),
                             "copy_ceiling_GBps": round(cc, 2),
                             "frac_of_copy_ceiling": round(res["graph"]["GBps"] / cc, 4)}
             torch.cuda.empty_cache()

@@ -11,6 +11,7 @@ from ._binding import (  # noqa: F401
     adaln_abi_version,
     adaln_check_layernorm_modulate,
     adaln_check_layernorm_modulate_fp8_quant,
+    adaln_check_qk_rmsnorm_rope,
     adaln_check_residual_gate_layernorm_modulate,
     adaln_check_residual_gate_rmsnorm_scale_shift,
     adaln_check_rmsnorm_scale_shift,
@@ -20,6 +21,7 @@ from ._binding import (  # noqa: F401
     adaln_diag_stream_copy,
     adaln_layernorm_modulate,
     adaln_layernorm_modulate_fp8_quant,
+    adaln_qk_rmsnorm_rope,
     adaln_reduction_layout,
     adaln_residual_gate_layernorm_modulate,
     adaln_residual_gate_rmsnorm_scale_shift,

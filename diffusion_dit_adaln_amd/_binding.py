@@ -12,7 +12,7 @@ import os
 import torch
 
 _PKG = os.path.dirname(os.path.abspath(__file__))
-ABI_VERSION = 4
+ABI_VERSION = 5
 
 STATUS_NAMES = {0: "ADALN_OK", 1: "ADALN_ERR_NULL", 2: "ADALN_ERR_SHAPE", 3: "ADALN_ERR_ALIGN",
                 4: "ADALN_ERR_STRIDE", 5: "ADALN_ERR_OVERLAP", 6: "ADALN_ERR_VALUE",
@@ -21,7 +21,8 @@ STATUS_NAMES = {0: "ADALN_OK", 1: "ADALN_ERR_NULL", 2: "ADALN_ERR_SHAPE", 3: "AD
 # every symbol include/adaln.h declares
 EXPORTS = ("adaln_layernorm_modulate", "adaln_rmsnorm_scale_shift",
            "adaln_residual_gate_rmsnorm_scale_shift", "adaln_residual_gate_layernorm_modulate",
-           "adaln_layernorm_modulate_fp8_quant", "adaln_check_layernorm_modulate",
+           "adaln_layernorm_modulate_fp8_quant", "adaln_qk_rmsnorm_rope",
+           "adaln_check_layernorm_modulate", "adaln_check_qk_rmsnorm_rope",
            "adaln_check_rmsnorm_scale_shift", "adaln_check_residual_gate_rmsnorm_scale_shift",
            "adaln_check_residual_gate_layernorm_modulate",
            "adaln_check_layernorm_modulate_fp8_quant", "adaln_reduction_layout",
@@ -63,6 +64,8 @@ def load_library():
         "adaln_residual_gate_layernorm_modulate": [P, P, P, P, P, P, P, I, I, I, I, I, I, F, P],
         "adaln_layernorm_modulate_fp8_quant": [P, P, P, P, P, I, I, I, I, I, F, P],
         "adaln_check_layernorm_modulate_fp8_quant": [P, P, P, P, P, I, I, I, I, I, F],
+        "adaln_qk_rmsnorm_rope": [P, P, P, P, P, P, P, I, I, I, I, I, I, F, P],
+        "adaln_check_qk_rmsnorm_rope": [P, P, P, P, P, P, P, I, I, I, I, I, I, F],
         "adaln_check_layernorm_modulate": [P, P, P, P, I, I, I, I, I, F],
         "adaln_check_rmsnorm_scale_shift": [P, P, P, P, P, I, I, I, I, I, F],
         "adaln_check_residual_gate_rmsnorm_scale_shift": [P, P, P, P, P, P, P, P, I, I, I, I, I, I,
@@ -238,6 +241,41 @@ def adaln_layernorm_modulate_fp8_quant(x, scale, shift, qscale, eps: float = 1e-
     return q
 
 
+def _heads_view(t: torch.Tensor, name: str):
+    if (t.dtype != torch.bfloat16 or t.dim() != 3 or t.size(2) != 128 or t.stride(2) != 1
+            or t.stride(1) != 128):
+        raise ValueError(f"{name}: expected bfloat16 [tokens, heads, 128] with contiguous heads")
+    return t.stride(0)
+
+
+def adaln_qk_rmsnorm_rope(q, k, q_weight, k_weight, cos_sin, eps: float = 1e-6, q_out=None,
+                          k_out=None, stream=None):
+    """(q_out, k_out): per-head RMSNorm of q and k ([tokens, heads, 128], e.g. views
+    of a packed QKV row) with their weights, then interleaved RoPE from cos_sin
+    (float32 [tokens, 128]: cos of the 64 pairs, then sin)."""
+    lib = load_library()
+    qts = _heads_view(q, "q")
+    kts = _heads_view(k, "k")
+    T = q.size(0)
+    if k.size(0) != T:
+        raise ValueError("q and k token counts differ")
+    if cos_sin.dtype != torch.float32 or cos_sin.shape != (T, 128) or not cos_sin.is_contiguous():
+        raise ValueError("cos_sin: expected a contiguous float32 [tokens, 128] tensor")
+    for w, name in ((q_weight, "q_weight"), (k_weight, "k_weight")):
+        if w is not None and (w.dtype != torch.bfloat16 or w.numel() != 128 or
+                              not w.is_contiguous()):
+            raise ValueError(f"{name}: expected a contiguous bfloat16 [128] tensor")
+    qo = torch.empty((T, q.size(1), 128), dtype=torch.bfloat16, device=q.device) \
+        if q_out is None else q_out
+    ko = torch.empty((T, k.size(1), 128), dtype=torch.bfloat16, device=k.device) \
+        if k_out is None else k_out
+    _check(lib.adaln_qk_rmsnorm_rope(q.data_ptr(), k.data_ptr(), _ptr(q_weight), _ptr(k_weight),
+                                     cos_sin.data_ptr(), qo.data_ptr(), ko.data_ptr(), T,
+                                     q.size(1), k.size(1), 128, qts, kts, _eps(eps),
+                                     _stream(stream)), "adaln_qk_rmsnorm_rope")
+    return qo, ko
+
+
 def adaln_check_layernorm_modulate(x_ptr, scale_ptr, shift_ptr, y_ptr, B, T, H, scale_bstride,
                                    shift_bstride, eps=1e-6) -> int:
     """Status code of the validation (raw pointers as ints; nothing is launched)."""
@@ -272,6 +310,14 @@ def adaln_check_layernorm_modulate_fp8_quant(x_ptr, scale_ptr, shift_ptr, qscale
                                              H, scale_bstride, shift_bstride, eps=1e-6) -> int:
     return load_library().adaln_check_layernorm_modulate_fp8_quant(
         x_ptr, scale_ptr, shift_ptr, qscale_ptr, q_ptr, B, T, H, scale_bstride, shift_bstride, eps)
+
+
+def adaln_check_qk_rmsnorm_rope(q_ptr, k_ptr, q_weight_ptr, k_weight_ptr, cos_sin_ptr, q_out_ptr,
+                                k_out_ptr, tokens, heads_q, heads_k, head_dim, q_token_stride,
+                                k_token_stride, eps=1e-6) -> int:
+    return load_library().adaln_check_qk_rmsnorm_rope(
+        q_ptr, k_ptr, q_weight_ptr, k_weight_ptr, cos_sin_ptr, q_out_ptr, k_out_ptr, tokens,
+        heads_q, heads_k, head_dim, q_token_stride, k_token_stride, eps)
 
 
 def adaln_reduction_layout(H: int):

@@ -150,9 +150,103 @@ adaln_status run(adaln::Op op, const adaln_bf16* res, const adaln_bf16* x, const
     return e == hipSuccess ? ADALN_OK : ADALN_ERR_LAUNCH;
 }
 
+// Validation of the QK RMSNorm + RoPE entry point.
+adaln_status validate_qk(const void* q, const void* k, const void* q_weight, const void* k_weight,
+                         const void* cos_sin, const void* q_out, const void* k_out, int64_t tokens,
+                         int64_t heads_q, int64_t heads_k, int64_t head_dim, int64_t q_tstride,
+                         int64_t k_tstride, float eps, bool* empty) {
+    *empty = true;
+    if (head_dim != 128) return ADALN_ERR_SHAPE;
+    if (tokens < 0 || heads_q < 0 || heads_k < 0) return ADALN_ERR_SHAPE;
+    if (!(eps >= 0.0f) || !isfinite(eps)) return ADALN_ERR_VALUE;
+    const int64_t lim = INT64_MAX / 4 / 128;
+    if (heads_q > lim || heads_k > lim) return ADALN_ERR_SHAPE;
+    if (tokens != 0 && (heads_q + heads_k > lim / tokens)) return ADALN_ERR_SHAPE;
+    if (tokens == 0 || heads_q + heads_k == 0) return ADALN_OK;
+    *empty = false;
+    if (!cos_sin) return ADALN_ERR_NULL;
+    if ((heads_q > 0 && (!q || !q_out)) || (heads_k > 0 && (!k || !k_out))) return ADALN_ERR_NULL;
+    const void* ptrs[] = {heads_q > 0 ? q : nullptr, heads_k > 0 ? k : nullptr, q_weight,
+                          k_weight, cos_sin, heads_q > 0 ? q_out : nullptr,
+                          heads_k > 0 ? k_out : nullptr};
+    for (const void* ptr : ptrs)
+        if (ptr && !aligned16(ptr)) return ADALN_ERR_ALIGN;
+    // token strides (elements): rows of heads*128 values, 16-byte aligned
+    if (tokens > 1) {
+        if (heads_q > 0 && (q_tstride < heads_q * 128 || (q_tstride % 8) != 0 ||
+                            q_tstride > INT64_MAX / 2 / tokens))
+            return ADALN_ERR_STRIDE;
+        if (heads_k > 0 && (k_tstride < heads_k * 128 || (k_tstride % 8) != 0 ||
+                            k_tstride > INT64_MAX / 2 / tokens))
+            return ADALN_ERR_STRIDE;
+    }
+    auto strided = [&](const void* p, int64_t tstride, int64_t heads) {
+        const int64_t elems = (tokens > 1 ? (tokens - 1) * tstride : 0) + heads * 128;
+        return Span{(uintptr_t)p, (uintptr_t)p + (uintptr_t)(2 * elems)};
+    };
+    Span in[5];
+    int n_in = 0;
+    if (heads_q > 0) in[n_in++] = strided(q, q_tstride, heads_q);
+    if (heads_k > 0) in[n_in++] = strided(k, k_tstride, heads_k);
+    in[n_in++] = Span{(uintptr_t)cos_sin, (uintptr_t)cos_sin + (uintptr_t)(tokens * 128 * 4)};
+    if (q_weight) in[n_in++] = Span{(uintptr_t)q_weight, (uintptr_t)q_weight + 256};
+    if (k_weight) in[n_in++] = Span{(uintptr_t)k_weight, (uintptr_t)k_weight + 256};
+    Span outs[2];
+    int n_out = 0;
+    if (heads_q > 0) outs[n_out++] = act_span(q_out, tokens, heads_q * 128);
+    if (heads_k > 0) outs[n_out++] = act_span(k_out, tokens, heads_k * 128);
+    for (int o = 0; o < n_out; ++o) {
+        for (int i = 0; i < n_in; ++i)
+            if (overlaps(outs[o], in[i])) return ADALN_ERR_OVERLAP;
+        for (int o2 = o + 1; o2 < n_out; ++o2)
+            if (overlaps(outs[o], outs[o2])) return ADALN_ERR_OVERLAP;
+    }
+    return ADALN_OK;
+}
+
 }  // namespace
 
 extern "C" {
+
+adaln_status adaln_qk_rmsnorm_rope(const adaln_bf16* q, const adaln_bf16* k,
+                                   const adaln_bf16* q_weight, const adaln_bf16* k_weight,
+                                   const float* cos_sin, adaln_bf16* q_out, adaln_bf16* k_out,
+                                   int64_t tokens, int64_t heads_q, int64_t heads_k,
+                                   int64_t head_dim, int64_t q_token_stride,
+                                   int64_t k_token_stride, float eps, void* hip_stream) {
+    bool empty = true;
+    ADALN_TRY(validate_qk(q, k, q_weight, k_weight, cos_sin, q_out, k_out, tokens, heads_q,
+                          heads_k, head_dim, q_token_stride, k_token_stride, eps, &empty));
+    if (empty) return ADALN_OK;
+    adaln::QKParams p{};
+    p.q = q;
+    p.k = k;
+    p.q_weight = q_weight;
+    p.k_weight = k_weight;
+    p.cos_sin = cos_sin;
+    p.q_out = q_out;
+    p.k_out = k_out;
+    p.tokens = tokens;
+    p.heads_q = heads_q;
+    p.heads_k = heads_k;
+    p.q_tstride = q_token_stride;
+    p.k_tstride = k_token_stride;
+    p.eps = eps;
+    hipError_t e = adaln::launch_qk(p, (hipStream_t)hip_stream);
+    return e == hipSuccess ? ADALN_OK : ADALN_ERR_LAUNCH;
+}
+
+adaln_status adaln_check_qk_rmsnorm_rope(const adaln_bf16* q, const adaln_bf16* k,
+                                         const adaln_bf16* q_weight, const adaln_bf16* k_weight,
+                                         const float* cos_sin, const adaln_bf16* q_out,
+                                         const adaln_bf16* k_out, int64_t tokens,
+                                         int64_t heads_q, int64_t heads_k, int64_t head_dim,
+                                         int64_t q_token_stride, int64_t k_token_stride,
+                                         float eps) {
+    bool empty = true;
+    return validate_qk(q, k, q_weight, k_weight, cos_sin, q_out, k_out, tokens, heads_q, heads_k,
+                       head_dim, q_token_stride, k_token_stride, eps, &empty);
+}
 
 adaln_status adaln_layernorm_modulate(const adaln_bf16* x, const adaln_bf16* scale,
                                       const adaln_bf16* shift, adaln_bf16* y, int64_t B, int64_t T,
@@ -261,7 +355,8 @@ const char* adaln_status_string(adaln_status status) {
     switch (status) {
         case ADALN_OK: return "success";
         case ADALN_ERR_NULL: return "a required pointer is NULL";
-        case ADALN_ERR_SHAPE: return "unsupported shape: need 8 <= H <= 8192, H % 8 == 0, B, T >= 0";
+        case ADALN_ERR_SHAPE:
+            return "unsupported shape: need 8 <= H <= 8192, H % 8 == 0, B, T >= 0 (QK: head_dim 128)";
         case ADALN_ERR_ALIGN: return "a pointer is not 16-byte aligned";
         case ADALN_ERR_STRIDE: return "a batch stride is negative, not a multiple of 8, or in (0, H)";
         case ADALN_ERR_OVERLAP: return "an output overlaps an input or the other output";

@@ -45,6 +45,26 @@ struct Layout {
 };
 Layout layout_of(int64_t H);
 
+// Per-head QK RMSNorm + interleaved RoPE (head_dim 128), validated by the C-ABI layer.
+struct QKParams {
+    const uint16_t* q;         // token t, head h at q + t*q_tstride + h*128
+    const uint16_t* k;         // likewise with k_tstride
+    const uint16_t* q_weight;  // [128] or NULL (one)
+    const uint16_t* k_weight;  // [128] or NULL
+    const float* cos_sin;      // [tokens, 128]: cos of pairs 0..63, then sin
+    uint16_t* q_out;           // [tokens, heads_q, 128]
+    uint16_t* k_out;           // [tokens, heads_k, 128]
+    int64_t tokens, heads_q, heads_k, q_tstride, k_tstride;
+    float eps;
+    // set by launch_qk
+    int64_t q_tasks, tasks_per_token, tasks, waves, sg_div, sg_mod;
+};
+hipError_t launch_qk(const QKParams& p, hipStream_t stream);
+
+// Resident workgroups of `block` threads per CU for a kernel on the current device,
+// and the CU count (cached per kernel and device, thread-safe).
+bool occupancy(const void* fn, int block, int* blocks_per_cu, int* cus);
+
 // Launch the fused kernel for `op`; returns the HIP error of the launch.
 hipError_t launch(Op op, const Params& p, hipStream_t stream);
 

@@ -30,6 +30,7 @@
 
 #include <mutex>
 
+#include "adaln_device.hpp"
 #include "adaln_internal.hpp"
 
 // Launch tuning (never changes the numerics): for contiguous row ranges, groups per
@@ -64,106 +65,10 @@
 namespace adaln {
 namespace {
 
-using u32 = uint32_t;
-
 constexpr bool interleaved(int op) {
     return ((op == OP_LN || op == OP_LNQ) && ADALN_INTERLEAVE_LN) ||
            (op == OP_RMS && ADALN_INTERLEAVE_RMS) || (op == OP_RG && ADALN_INTERLEAVE_RG) ||
            (op == OP_RGLN && ADALN_INTERLEAVE_RGLN);
-}
-
-// ---------------------------------------------------------------------------
-// bf16 <-> binary32
-// ---------------------------------------------------------------------------
-__device__ __forceinline__ float bf_lo(u32 p) { return __uint_as_float(p << 16); }
-__device__ __forceinline__ float bf_hi(u32 p) { return __uint_as_float(p & 0xFFFF0000u); }
-
-typedef float f32x2 __attribute__((ext_vector_type(2)));
-typedef __bf16 bf16x2 __attribute__((ext_vector_type(2)));
-
-// Round two binary32 values to bf16, nearest-even (v_cvt_pk_bf16_f32), lo in bits 0..15.
-__device__ __forceinline__ u32 pack_bf16(float lo, float hi) {
-    f32x2 v = {lo, hi};
-    bf16x2 r = __builtin_convertvector(v, bf16x2);
-    return __builtin_bit_cast(u32, r);
-}
-
-// bf16(v) widened back to binary32 in one instruction: with a zero low slot,
-// v_cvt_pk_bf16_f32 leaves bf16(v) in the high half, and that register read as
-// binary32 is exactly the bf16 value (the low half bf16(+0) is all zero bits).
-__device__ __forceinline__ float round_bf16(float v) { return __uint_as_float(pack_bf16(0.0f, v)); }
-
-typedef unsigned int u32x4 __attribute__((ext_vector_type(4)));
-
-// Small per-batch vectors: ordinary cached loads (shared by every row of a batch).
-__device__ __forceinline__ uint4 ld16(const uint16_t* p) {
-    return *reinterpret_cast<const uint4*>(p);
-}
-// Activations are touched once: non-temporal (nt) 16-byte buffer loads and stores
-// through a descriptor that spans exactly one group's rows.  An access at an
-// offset past the descriptor's range reads zeros and writes nothing, without
-// memory traffic; the kernel uses that to issue every load and store of its loop
-// unconditionally (refills past the last row, lanes past a ragged row end), so
-// the compiler can count outstanding memory operations exactly and never waits
-// on a prefetch it does not need yet.
-using rsrc_t = __amdgpu_buffer_rsrc_t;
-constexpr int kRsrcWord3 = 0x00020000;  // raw (untyped) buffer, gfx9-family descriptor word 3
-constexpr int kOutOfRange = 0x7FFFFFF0;  // any offset >= the descriptor's byte range
-constexpr int kNonTemporal = 2;          // cache-policy bit nt
-
-__device__ __forceinline__ rsrc_t make_rsrc(const void* base, int64_t bytes) {
-    return __builtin_amdgcn_make_buffer_rsrc(const_cast<void*>(base), 0, (int)bytes, kRsrcWord3);
-}
-__device__ __forceinline__ uint4 ld16_stream(rsrc_t r, int off) {
-    const u32x4 t = __builtin_amdgcn_raw_buffer_load_b128(r, off, 0, kNonTemporal);
-    return make_uint4(t.x, t.y, t.z, t.w);
-}
-__device__ __forceinline__ void st16_stream(rsrc_t r, int off, uint4 v) {
-    const u32x4 t = {v.x, v.y, v.z, v.w};
-    __builtin_amdgcn_raw_buffer_store_b128(t, r, off, 0, kNonTemporal);
-}
-
-typedef unsigned int u32x2 __attribute__((ext_vector_type(2)));
-__device__ __forceinline__ void st8_stream(rsrc_t r, int off, u32 lo, u32 hi) {
-    const u32x2 t = {lo, hi};
-    __builtin_amdgcn_raw_buffer_store_b64(t, r, off, 0, kNonTemporal);
-}
-
-// Static FP8 quantisation of four values already multiplied by 1/scale: clamp to
-// [-448, 448] with IEEE-754-2019 maximum/minimum (v_maximum3/v_minimum3: a NaN stays
-// NaN), then v_cvt_pk_fp8_f32, which rounds to nearest-even into the OCP E4M3 format
-// on gfx950.  Byte k of the result is value k.
-__device__ __forceinline__ float clamp448(float v) {
-    return __builtin_elementwise_minimum(__builtin_elementwise_maximum(v, -448.0f), 448.0f);
-}
-__device__ __forceinline__ u32 quant4(float a, float b, float c, float d) {
-    const u32 lo = __builtin_amdgcn_cvt_pk_fp8_f32(clamp448(a), clamp448(b), 0, false);
-    return __builtin_amdgcn_cvt_pk_fp8_f32(clamp448(c), clamp448(d), lo, true);
-}
-
-__device__ __forceinline__ u32 word(const uint4& v, int j) {
-    return j == 0 ? v.x : j == 1 ? v.y : j == 2 ? v.z : v.w;
-}
-
-// ---------------------------------------------------------------------------
-// cross-lane moves for the butterfly
-// ---------------------------------------------------------------------------
-// DPP controls: quad_perm [1,0,3,2] reads lane t^1; quad_perm [2,3,0,1] reads
-// t^2; row_half_mirror reads 7-i within 8 lanes and row_mirror 15-i within 16.
-// After the earlier levels all lanes of a group hold equal bits, so the mirrors
-// deliver the partner group's value exactly as t^4 and t^8 would.
-constexpr int DPP_XOR1 = 0xB1;
-constexpr int DPP_XOR2 = 0x4E;
-constexpr int DPP_HALF_MIRROR = 0x141;
-constexpr int DPP_MIRROR = 0x140;
-
-template <int CTRL>
-__device__ __forceinline__ float dpp(float v) {
-    return __builtin_bit_cast(
-        float, __builtin_amdgcn_mov_dpp(__builtin_bit_cast(int, v), CTRL, 0xF, 0xF, false));
-}
-__device__ __forceinline__ float readlane(float v, int lane) {
-    return __builtin_bit_cast(float, __builtin_amdgcn_readlane(__builtin_bit_cast(int, v), lane));
 }
 
 // ---------------------------------------------------------------------------
@@ -273,12 +178,6 @@ __device__ __forceinline__ void wave_welford_equal(float& mean, float& m2, int l
     combine_equal<32 * N>(ma, mb, qa + qb, mean, m2);
 }
 
-// rstd = RN(1 / RN(sqrt(RN(stat + eps)))), correctly rounded steps.
-__device__ __forceinline__ float finalize(float stat, float eps) {
-    const float v = stat + eps;
-    const float root = __builtin_sqrtf(v);
-    return 1.0f / root;
-}
 
 // ---------------------------------------------------------------------------
 // the fused row kernel
@@ -810,15 +709,17 @@ KernelFn pick(const Layout& L, bool weight) {
     return nullptr;
 }
 
+}  // namespace
+
 // Resident workgroups per CU for a kernel on the current device (cached).
 struct OccEntry {
-    KernelFn fn;
+    const void* fn;
     int device;
     int blocks_per_cu;
     int cus;
 };
 
-bool occupancy(KernelFn fn, int block, int* blocks_per_cu, int* cus) {
+bool occupancy(const void* fn, int block, int* blocks_per_cu, int* cus) {
     static std::mutex mu;
     static OccEntry cache[256];
     static int n_cache = 0;
@@ -832,7 +733,7 @@ bool occupancy(KernelFn fn, int block, int* blocks_per_cu, int* cus) {
             return true;
         }
     int nb = 0, ncu = 0;
-    if (hipOccupancyMaxActiveBlocksPerMultiprocessor(&nb, reinterpret_cast<const void*>(fn), block,
+    if (hipOccupancyMaxActiveBlocksPerMultiprocessor(&nb, fn, block,
                                                      0) != hipSuccess)
         return false;
     if (hipDeviceGetAttribute(&ncu, hipDeviceAttributeMultiprocessorCount, dev) != hipSuccess)
@@ -843,8 +744,6 @@ bool occupancy(KernelFn fn, int block, int* blocks_per_cu, int* cus) {
     *cus = ncu;
     return true;
 }
-
-}  // namespace
 
 Layout layout_of(int64_t H) {
     Layout L;
@@ -869,7 +768,7 @@ hipError_t launch(Op op, const Params& p_in, hipStream_t stream) {
     // workgroup of W waves
     const int block = L.waves == 1 ? 256 : 64 * L.waves;
     int blocks_per_cu = 0, cus = 0;
-    if (!occupancy(fn, block, &blocks_per_cu, &cus)) {
+    if (!occupancy(reinterpret_cast<const void*>(fn), block, &blocks_per_cu, &cus)) {
         (void)hipGetLastError();
         return hipErrorInvalidDeviceFunction;
     }

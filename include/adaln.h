@@ -1,12 +1,13 @@
 /*
  * adaln.h -- C ABI of libadaln: fused adaLN normalisation for AMD MI355X (gfx950).
  *
- * The five compute entry points fuse a row normalisation (LayerNorm without
+ * Five compute entry points fuse a row normalisation (LayerNorm without
  * affine parameters, or RMSNorm with an optional weight) with the adaLN
  * modulate epilogue  y = norm(x) * (1 + scale[b]) + shift[b]  that diffusion
  * transformers run at every adaLN site, optionally preceded by the residual-gate
  * prologue  r = res + gate[b] * x (for both norms), or followed, for the
- * LayerNorm, by a static FP8 quantisation of y.
+ * LayerNorm, by a static FP8 quantisation of y.  A sixth normalises the attention
+ * heads of Q and K and applies the rotary embedding (adaln_qk_rmsnorm_rope).
  *
  * Sources, cited by page title and section:
  *  - FLUX.1 PR report "route the adaLN LN+modulate sites through the bit-exact
@@ -88,9 +89,10 @@
 extern "C" {
 #endif
 
-#define ADALN_ABI_VERSION 4 /* 2: two waves per row for 2048 <= H < 4096;
+#define ADALN_ABI_VERSION 5 /* 2: two waves per row for 2048 <= H < 4096;
                               3: residual-gate LayerNorm, stream copy;
-                              4: LayerNorm + modulate + FP8 quantisation */
+                              4: LayerNorm + modulate + FP8 quantisation;
+                              5: per-head QK RMSNorm + RoPE */
 
 typedef uint16_t adaln_bf16; /* raw bfloat16 bits */
 
@@ -152,6 +154,27 @@ adaln_status adaln_layernorm_modulate_fp8_quant(const adaln_bf16* x, const adaln
                                                 int64_t scale_bstride, int64_t shift_bstride,
                                                 float eps, void* hip_stream);
 
+/* Per-head QK RMSNorm + interleaved (non-NeoX) rotary embedding, head_dim 128
+ * (kernels guide, RoPE / QK-norm; Qwen PR report, implementation item 3 and the
+ * qwen_image.py snippet: Q/K RMSNorm with their weights, then RoPE from an fp32
+ * cos/sin cache, Q/K as strided views of the packed QKV projection).  Per head
+ * vector x of Q (weight q_weight) or K (weight k_weight):
+ *   yn = bf16(RN(RN(x * rstd) * RN(w + 0))), rstd the RMS statistic above with H = 128;
+ *   out[2i]   = bf16(RN(RN(a*c) - RN(b*s))), out[2i+1] = bf16(RN(RN(b*c) + RN(a*s)))
+ *   with a = yn[2i], b = yn[2i+1], c = cos_sin[t][i], s = cos_sin[t][64 + i].
+ * Layout: Q head h of token t at q + t*q_token_stride + h*128 (elements; heads
+ * contiguous, token stride >= heads_q*128 and % 8 == 0 when tokens > 1); K likewise;
+ * cos_sin fp32 [tokens, 128] contiguous (cos of the 64 pairs, then their sin);
+ * q_out [tokens, heads_q, 128] and k_out [tokens, heads_k, 128] contiguous; weights
+ * [128] bf16 or NULL (one).  head_dim other than 128 is ADALN_ERR_SHAPE; heads_q or
+ * heads_k may be 0 (that tensor's pointers are then unused). */
+adaln_status adaln_qk_rmsnorm_rope(const adaln_bf16* q, const adaln_bf16* k,
+                                   const adaln_bf16* q_weight, const adaln_bf16* k_weight,
+                                   const float* cos_sin, adaln_bf16* q_out, adaln_bf16* k_out,
+                                   int64_t tokens, int64_t heads_q, int64_t heads_k,
+                                   int64_t head_dim, int64_t q_token_stride,
+                                   int64_t k_token_stride, float eps, void* hip_stream);
+
 /* Predicates: the validation of the entry point of the same name, without a
  * launch (the `can_use_*` predicate of the kernels guide's entry-point protocol).
  * They never touch the GPU. */
@@ -181,6 +204,14 @@ adaln_status adaln_check_layernorm_modulate_fp8_quant(const adaln_bf16* x, const
                                                       const uint8_t* q, int64_t B, int64_t T,
                                                       int64_t H, int64_t scale_bstride,
                                                       int64_t shift_bstride, float eps);
+
+adaln_status adaln_check_qk_rmsnorm_rope(const adaln_bf16* q, const adaln_bf16* k,
+                                         const adaln_bf16* q_weight, const adaln_bf16* k_weight,
+                                         const float* cos_sin, const adaln_bf16* q_out,
+                                         const adaln_bf16* k_out, int64_t tokens,
+                                         int64_t heads_q, int64_t heads_k, int64_t head_dim,
+                                         int64_t q_token_stride, int64_t k_token_stride,
+                                         float eps);
 
 /* The fixed reduction layout for H: waves per row, lanes per row, chunks per
  * lane.  ADALN_ERR_SHAPE for an unsupported H; out-pointers may be NULL. */

@@ -33,14 +33,14 @@ def declared_symbols():
 
 def test_header_symbols_are_exported(lib):
     names = declared_symbols()
-    assert len(names) == 17, names
+    assert len(names) == 19, names
     assert set(names) == set(_binding.EXPORTS)
     for n in names:
         assert hasattr(lib, n), n
 
 
 def test_abi_version_and_status_strings(lib):
-    assert A.adaln_abi_version() == A.ABI_VERSION == 4
+    assert A.adaln_abi_version() == A.ABI_VERSION == 5
     for s in range(8):
         assert len(A.adaln_status_string(s)) > 5
     assert A.adaln_status_string(99) == "unknown status"
@@ -123,6 +123,38 @@ def test_fp8_quant_checks(lib):
     assert lib.adaln_diag_quant_fp8(addr(0) + 4, addr(1), 8, addr(2), None) == ALIGN
     assert lib.adaln_diag_quant_fp8(addr(0), addr(0) + 8, 8, addr(2), None) == OVERLAP
     assert lib.adaln_diag_quant_fp8(None, None, 0, None, None) == OK
+
+
+def qk_check(lib, **kw):
+    a = dict(q=addr(0), k=addr(0) + 3072 * 2, wq=addr(1), wk=addr(2), cs=addr(3), qo=addr(4),
+             ko=addr(5), T=7, hq=24, hk=24, D=128, qts=3 * 3072, kts=3 * 3072, eps=1e-6)
+    a.update(kw)
+    return lib.adaln_check_qk_rmsnorm_rope(a["q"], a["k"], a["wq"], a["wk"], a["cs"], a["qo"],
+                                           a["ko"], a["T"], a["hq"], a["hk"], a["D"], a["qts"],
+                                           a["kts"], a["eps"])
+
+
+def test_qk_checks(lib):
+    assert qk_check(lib) == OK                          # packed QKV views
+    assert qk_check(lib, wq=None, wk=None) == OK
+    assert qk_check(lib, D=64) == SHAPE
+    assert qk_check(lib, hq=-1) == SHAPE
+    assert qk_check(lib, T=0, q=None, k=None, cs=None, qo=None, ko=None) == OK
+    assert qk_check(lib, hk=0, k=None, ko=None) == OK
+    assert qk_check(lib, cs=None) == NULL
+    assert qk_check(lib, ko=None) == NULL
+    assert qk_check(lib, q=addr(0) + 8) == ALIGN
+    assert qk_check(lib, cs=addr(3) + 4) == ALIGN
+    assert qk_check(lib, qts=3072 * 2 - 8) == OK         # any stride >= heads_q*128, % 8
+    assert qk_check(lib, qts=3000) == STRIDE             # < heads_q*128
+    assert qk_check(lib, kts=3 * 3072 + 4) == STRIDE     # not % 8
+    assert qk_check(lib, T=1, qts=0, kts=0) == OK        # stride unused for one token
+    assert qk_check(lib, eps=float("nan")) == VALUE
+    assert qk_check(lib, qo=addr(0)) == OVERLAP          # output over the packed input
+    assert qk_check(lib, ko=addr(4) + 16) == OVERLAP     # q_out and k_out overlap
+    assert qk_check(lib, qo=addr(3) - 16) == OVERLAP     # runs into the cache
+    assert lib.adaln_qk_rmsnorm_rope(addr(0), addr(1), None, None, addr(3), addr(4), addr(5), 7,
+                                     24, 24, 96, 3072, 3072, 1e-6, None) == SHAPE
 
 
 def test_valid_arguments_pass(lib):

@@ -324,6 +324,84 @@ def test_rows_alone_equal_rows_in_batch():
 
 
 # --------------------------------------------------------------------------
+# per-head QK RMSNorm + RoPE
+# --------------------------------------------------------------------------
+def check_qk(qkv, wq, wk, cs, what, eps=EPS, hk=None):
+    """qkv: [tokens, 3, heads, 128] bf16 bits; q, k are its strided views."""
+    T = qkv.shape[0]
+    d = dev(qkv)
+    q_d, k_d = d[:, 0], d[:, 1]
+    q, k = qkv[:, 0], qkv[:, 1]
+    if hk is not None:            # fewer K heads than Q heads
+        k_d, k = k_d[:, :hk], k[:, :hk]
+    qo, ko = A.adaln_qk_rmsnorm_rope(q_d, k_d, None if wq is None else dev(wq),
+                                     None if wk is None else dev(wk),
+                                     torch.from_numpy(cs).cuda(), eps)
+    qo0, ko0 = O.qk_rmsnorm_rope(q, k, wq, wk, cs, eps)
+    assert_bits_equal(host(qo), qo0, what + " q")
+    assert_bits_equal(host(ko), ko0, what + " k")
+
+
+def test_qk_workload_full_size():
+    wl = synth.config7()
+    say(f"[parity] qk {wl.qkv.shape}")
+    check_qk(wl.qkv, wl.q_weight, wl.k_weight, wl.cos_sin, "qk full size")
+
+
+@pytest.mark.parametrize("T,heads", [(1, 1), (3, 2), (5, 3), (17, 5), (64, 24), (129, 48)])
+def test_qk_shapes(T, heads):
+    say(f"[parity] qk T={T} heads={heads}")
+    rng = np.random.default_rng(T * 100 + heads)
+    qkv = mixed_rows(rng, T, 3 * heads, 128).reshape(T, 3, heads, 128)
+    wq = synth.normal_bf16(rng, (128,), 0.02, 1.0)
+    wk = synth.normal_bf16(rng, (128,), 0.02, 1.0)
+    ang = rng.uniform(-np.pi, np.pi, (T, 64))
+    cs = np.concatenate([np.cos(ang), np.sin(ang)], 1).astype(np.float32)
+    check_qk(qkv, wq, wk, cs, f"qk T={T} heads={heads}")
+    check_qk(qkv, None, wk, cs, f"qk T={T} heads={heads} no q weight")
+    if heads > 1:
+        check_qk(qkv, wq, wk, cs, f"qk T={T} heads={heads} fewer k heads", hk=heads - 1)
+
+
+@pytest.mark.parametrize("eps", [0.0, 1e-5, 0.25])
+def test_qk_eps_and_special_rows(eps):
+    say(f"[parity] qk eps={eps}")
+    T, heads = 9, 4
+    rng = np.random.default_rng(77)
+    qkv = synth.normal_bf16(rng, (T, 3, heads, 128))
+    consts = synth.f32_to_bf16_bits(np.array([0.0, -0.0, 1.0, 2.0 ** -130, 1e3, 65504.0],
+                                             np.float32))
+    for i, c in enumerate(consts):
+        qkv[i, 0, 0, :] = c                    # constant and zero heads
+    qkv[6, 1, 2, 5] = 0x7F80                   # inf
+    qkv[7, 0, 3, 9] = 0x7FC0                   # nan
+    cs = synth.rope_cache(T, 128)
+    T_, d = qkv.shape[0], dev(qkv)
+    qo, ko = A.adaln_qk_rmsnorm_rope(d[:, 0], d[:, 1], None, None, torch.from_numpy(cs).cuda(), eps)
+    qo0, ko0 = O.qk_rmsnorm_rope(qkv[:, 0], qkv[:, 1], None, None, cs, eps)
+    for got, want in ((host(qo), qo0), (host(ko), ko0)):
+        gn = np.isnan(synth.bf16_bits_to_f32(got))
+        wn = np.isnan(synth.bf16_bits_to_f32(want))
+        assert np.array_equal(gn, wn)
+        assert_bits_equal(got[~gn], want[~wn], f"qk eps={eps}")
+
+
+def test_qk_heads_alone_equal_heads_in_batch():
+    say("[parity] qk tokens alone vs in batch")
+    rng = np.random.default_rng(5)
+    T, heads = 40, 6
+    qkv = synth.normal_bf16(rng, (T, 3, heads, 128))
+    cs = torch.from_numpy(synth.rope_cache(T, 128)).cuda()
+    d = dev(qkv)
+    qo, ko = A.adaln_qk_rmsnorm_rope(d[:, 0], d[:, 1], None, None, cs, EPS)
+    for t in range(0, T, 7):
+        q1, k1 = A.adaln_qk_rmsnorm_rope(d[t:t + 1, 0], d[t:t + 1, 1], None, None,
+                                         cs[t:t + 1].contiguous(), EPS)
+        assert torch.equal(q1[0].view(torch.int16), qo[t].view(torch.int16))
+        assert torch.equal(k1[0].view(torch.int16), ko[t].view(torch.int16))
+
+
+# --------------------------------------------------------------------------
 # the FP8 kernel's quantisation step, exhaustively over binary32
 # --------------------------------------------------------------------------
 def test_device_fp8_quant_all_fp32_patterns():

@@ -570,6 +570,28 @@ int oracle_qk_rmsnorm_rope(const uint16_t* q, const uint16_t* k, const uint16_t*
     return bad;
 }
 
+/* Residual gating on the channel-first layout (kernels guide, norm variants /
+ * residual gating: the transposed dense path reads `update` in its logical
+ * row-major order while the residual and the output stay in their [B, hidden,
+ * tokens] layout, with no .contiguous() copy):
+ *   out[b][h][t] = bf16(res[b][h][t] + bf16(gate[b][h] * update[b][t][h]))
+ * res, out: [B, H, T] contiguous; update: [B, T, H] contiguous; gate row b at
+ * gate + b*gate_bstride.  out may be res itself. */
+int oracle_residual_gate_channel_first(const uint16_t* res, const uint16_t* update,
+                                       const uint16_t* gate, uint16_t* out, int64_t B, int64_t T,
+                                       int64_t H, int64_t gate_bstride) {
+    if (B < 0 || T < 0 || H < 0) return -1;
+    unsigned int env = fp_enter();
+    for (int64_t b = 0; b < B; b++)
+        for (int64_t h = 0; h < H; h++)
+            for (int64_t t = 0; t < T; t++) {
+                int64_t i = (b * H + h) * T + t;
+                out[i] = gate_residual(res[i], update[(b * T + t) * H + h], gate[b * gate_bstride + h]);
+            }
+    fp_leave(env);
+    return 0;
+}
+
 /* ------------------------------------------------------------------------ */
 /* elementwise helpers exposed for the pins                                  */
 /* ------------------------------------------------------------------------ */

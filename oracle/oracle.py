@@ -68,6 +68,8 @@ def _load():
     lib.oracle_quant_fp8.restype = None
     lib.oracle_qk_rmsnorm_rope.argtypes = [P, P, P, P, P, P, P, I, I, I, I, I, I, F, P, P]
     lib.oracle_qk_rmsnorm_rope.restype = ctypes.c_int
+    lib.oracle_residual_gate_channel_first.argtypes = [P, P, P, P, I, I, I, I]
+    lib.oracle_residual_gate_channel_first.restype = ctypes.c_int
     lib.oracle_round_bf16.argtypes = [P, P, I]
     lib.oracle_round_bf16.restype = None
     lib.oracle_modulate.argtypes = [P, P, P, P, I]
@@ -272,6 +274,23 @@ def qk_rmsnorm_rope(q, k, q_weight, k_weight, cos_sin, eps=1e-6, want_norm=False
                                     _ptr(ynq), _ptr(ynk))
     _check(rc, "qk_rmsnorm_rope")
     return (qo, ko, ynq, ynk) if want_norm else (qo, ko)
+
+
+def residual_gate_channel_first(res, update, gate):
+    """out[b,h,t] = round(res[b,h,t] + round(gate[b,h] * update[b,t,h])); res and out
+    [B,H,T] (channel-first), update [B,T,H]."""
+    lib = _load()
+    res = np.ascontiguousarray(res, np.uint16)
+    update = np.ascontiguousarray(update, np.uint16)
+    B, H, T = res.shape
+    if update.shape != (B, T, H):
+        raise ValueError("update must be [B, T, H] for res [B, H, T]")
+    g, gbs = _vec(gate, B, H, "gate")
+    out = np.empty_like(res)
+    rc = lib.oracle_residual_gate_channel_first(_ptr(res), _ptr(update), _ptr(g), _ptr(out), B, T,
+                                                H, gbs)
+    _check(rc, "residual_gate_channel_first")
+    return out
 
 
 def _ret(y, yn, st, want_norm, want_stats, tup=False):

@@ -484,6 +484,40 @@ def test_qk_strided_views_match_contiguous():
 
 
 # --------------------------------------------------------------------------
+# residual gating on the channel-first [B, hidden, tokens] layout
+# --------------------------------------------------------------------------
+@pytest.mark.parametrize("shape", [(1, 8, 8), (2, 24, 40), (3, 72, 136), (2, 3072, 64)])
+def test_residual_gate_channel_first_vs_eager(shape):
+    # torch eager bf16: res + gate[:, :, None] * update.transpose(1, 2), on the
+    # channel-first residual
+    B, H, T = shape
+    rng = np.random.default_rng(B * 1000 + H + T)
+    res = synth.normal_bf16(rng, (B, H, T))
+    upd = synth.normal_bf16(rng, (B, T, H))
+    gate = synth.normal_bf16(rng, (B, H), 0.1)
+    got = O.residual_gate_channel_first(res, upd, gate)
+    ref = torch_bf16(res) + torch_bf16(gate)[:, :, None] * torch_bf16(upd).transpose(1, 2)
+    assert np.array_equal(got, from_torch(ref))
+    # the same values as the row-major residual gate on the transposed residual
+    r_rm = O.gate_residual(np.ascontiguousarray(res.transpose(0, 2, 1)), upd,
+                           np.broadcast_to(gate[:, None, :], upd.shape))
+    assert np.array_equal(got, r_rm.transpose(0, 2, 1))
+
+
+def test_residual_gate_channel_first_gate_zero_and_stride():
+    B, H, T = 2, 16, 24
+    rng = np.random.default_rng(3)
+    res = _nonzero_bf16(rng, (B, H, T), 1.0)
+    upd = synth.normal_bf16(rng, (B, T, H))
+    emb = synth.normal_bf16(rng, (B, 3 * H), 0.1)
+    emb[:, H:2 * H] = 0
+    assert np.array_equal(O.residual_gate_channel_first(res, upd, emb[:, H:2 * H]), res)
+    g = emb[:, 2 * H:]
+    assert np.array_equal(O.residual_gate_channel_first(res, upd, g),
+                          O.residual_gate_channel_first(res, upd, np.ascontiguousarray(g)))
+
+
+# --------------------------------------------------------------------------
 # the full output is the modulate chain applied to the norm output
 # --------------------------------------------------------------------------
 @pytest.mark.parametrize("op", ["ln", "rms"])

@@ -64,7 +64,8 @@ def workload(cfg: str):
     from diffusion_dit_adaln_amd import synth
     return {"0": synth.config0, "1": synth.config1, "2": synth.config2,
             "3a": lambda: synth.config3(site="a"), "3b": lambda: synth.config3(site="b"),
-            "5": synth.config5, "6": synth.config6, "7": synth.config7}[cfg]()
+            "5": synth.config5, "6": synth.config6, "7": synth.config7,
+            "8": synth.config8}[cfg]()
 
 
 class Launcher:
@@ -176,8 +177,41 @@ class QKLauncher:
                                               stream)
 
 
+class CFLauncher:
+    """Pre-marshalled channel-first residual-gate calls over rotating buffer sets."""
+
+    def __init__(self, wl, rotate_bytes: int):
+        import torch
+        import diffusion_dit_adaln_amd as A
+        self.lib = A.load_library()
+        self.wl = wl
+        self.B, self.H, self.T = wl.res.shape
+
+        def dev(a):
+            return torch.from_numpy(np.ascontiguousarray(a).view(np.int16)).view(
+                torch.bfloat16).cuda()
+
+        self.nsets = max(2, -(-rotate_bytes // wl.algorithmic_bytes()))
+        r0, u0 = dev(wl.res), dev(wl.update)
+        self.sets = [{"res": r0.clone(), "upd": u0.clone(), "out": torch.empty_like(r0)}
+                     for _ in range(self.nsets)]
+        self.gate = dev(wl.gate)
+        del r0, u0
+        torch.cuda.synchronize()
+
+    def call(self, i: int, stream) -> int:
+        s = self.sets[i % self.nsets]
+        return self.lib.adaln_residual_gate_channel_first(
+            s["res"].data_ptr(), s["upd"].data_ptr(), self.gate.data_ptr(), s["out"].data_ptr(),
+            self.B, self.T, self.H, self.H if self.B > 1 else 0, stream)
+
+
 def launcher_for(wl, rotate_bytes):
-    return QKLauncher(wl, rotate_bytes) if wl.op == "qk" else Launcher(wl, rotate_bytes)
+    if wl.op == "qk":
+        return QKLauncher(wl, rotate_bytes)
+    if wl.op == "cf":
+        return CFLauncher(wl, rotate_bytes)
+    return Launcher(wl, rotate_bytes)
 
 
 def time_steps(launch, steps: int, warmup: int, mode: str):
@@ -360,7 +394,7 @@ def main():
             lambda: copy_ceiling(nbytes, rotate, steps, args.warmup, kind="torch")), 2)
         out["frac_of_copy_ceiling"] = round(gbps / out["copy_ceiling_GBps"], 4)
         per = {}
-        for cfg in ["0", "1", "2", "3a", "3b", "5", "6", "7"]:
+        for cfg in ["0", "1", "2", "3a", "3b", "5", "6", "7", "8"]:
             w2 = workload(cfg)
             L2 = launcher_for(w2, rotate)
             nb2 = w2.algorithmic_bytes()
@@ -372,8 +406,11 @@ def main():
             del L2
             torch.cuda.empty_cache()
             cc = median3(lambda: copy_ceiling(nb2, rotate, steps, args.warmup))
-            shape = list(w2.qkv.shape) if w2.op == "qk" else list(w2.x.shape)
-            rows2 = (shape[0] * 2 * shape[2]) if w2.op == "qk" else shape[0] * shape[1]
+            shape = list({"qk": lambda: w2.qkv.shape, "cf": lambda: w2.res.shape}.get(
+                w2.op, lambda: w2.x.shape)())
+            # rows: head vectors (qk), tokens (cf: B*T), else B*T
+            rows2 = {"qk": shape[0] * 2 * shape[2], "cf": shape[0] * shape[2]}.get(
+                w2.op, shape[0] * shape[1])
             per[w2.name] = {"op": w2.op, "shape": shape, "bytes": nb2, **res,
                             "rows_per_s": round(rows2 / res["graph"]["us_per_launch"] * 1e6, 1),
                             "copy_ceiling_GBps": round(cc, 2),

@@ -12,6 +12,7 @@ from ._binding import (  # noqa: F401
     adaln_check_layernorm_modulate,
     adaln_check_layernorm_modulate_fp8_quant,
     adaln_check_qk_rmsnorm_rope,
+    adaln_check_residual_gate_channel_first,
     adaln_check_residual_gate_layernorm_modulate,
     adaln_check_residual_gate_rmsnorm_scale_shift,
     adaln_check_rmsnorm_scale_shift,
@@ -23,6 +24,7 @@ from ._binding import (  # noqa: F401
     adaln_layernorm_modulate_fp8_quant,
     adaln_qk_rmsnorm_rope,
     adaln_reduction_layout,
+    adaln_residual_gate_channel_first,
     adaln_residual_gate_layernorm_modulate,
     adaln_residual_gate_rmsnorm_scale_shift,
     adaln_rmsnorm_scale_shift,

@@ -12,7 +12,7 @@ import os
 import torch
 
 _PKG = os.path.dirname(os.path.abspath(__file__))
-ABI_VERSION = 5
+ABI_VERSION = 6
 
 STATUS_NAMES = {0: "ADALN_OK", 1: "ADALN_ERR_NULL", 2: "ADALN_ERR_SHAPE", 3: "ADALN_ERR_ALIGN",
                 4: "ADALN_ERR_STRIDE", 5: "ADALN_ERR_OVERLAP", 6: "ADALN_ERR_VALUE",
@@ -22,7 +22,8 @@ STATUS_NAMES = {0: "ADALN_OK", 1: "ADALN_ERR_NULL", 2: "ADALN_ERR_SHAPE", 3: "AD
 EXPORTS = ("adaln_layernorm_modulate", "adaln_rmsnorm_scale_shift",
            "adaln_residual_gate_rmsnorm_scale_shift", "adaln_residual_gate_layernorm_modulate",
            "adaln_layernorm_modulate_fp8_quant", "adaln_qk_rmsnorm_rope",
-           "adaln_check_layernorm_modulate", "adaln_check_qk_rmsnorm_rope",
+           "adaln_residual_gate_channel_first", "adaln_check_layernorm_modulate",
+           "adaln_check_qk_rmsnorm_rope", "adaln_check_residual_gate_channel_first",
            "adaln_check_rmsnorm_scale_shift", "adaln_check_residual_gate_rmsnorm_scale_shift",
            "adaln_check_residual_gate_layernorm_modulate",
            "adaln_check_layernorm_modulate_fp8_quant", "adaln_reduction_layout",
@@ -66,6 +67,8 @@ def load_library():
         "adaln_check_layernorm_modulate_fp8_quant": [P, P, P, P, P, I, I, I, I, I, F],
         "adaln_qk_rmsnorm_rope": [P, P, P, P, P, P, P, I, I, I, I, I, I, F, P],
         "adaln_check_qk_rmsnorm_rope": [P, P, P, P, P, P, P, I, I, I, I, I, I, F],
+        "adaln_residual_gate_channel_first": [P, P, P, P, I, I, I, I, P],
+        "adaln_check_residual_gate_channel_first": [P, P, P, P, I, I, I, I],
         "adaln_check_layernorm_modulate": [P, P, P, P, I, I, I, I, I, F],
         "adaln_check_rmsnorm_scale_shift": [P, P, P, P, P, I, I, I, I, I, F],
         "adaln_check_residual_gate_rmsnorm_scale_shift": [P, P, P, P, P, P, P, P, I, I, I, I, I, I,
@@ -276,6 +279,27 @@ def adaln_qk_rmsnorm_rope(q, k, q_weight, k_weight, cos_sin, eps: float = 1e-6, 
     return qo, ko
 
 
+def adaln_residual_gate_channel_first(res, update, gate, out=None, stream=None):
+    """out[b,h,t] = res[b,h,t] + gate[b,h] * update[b,t,h] (two bf16 roundings); res and
+    out contiguous [B,H,T] (channel-first), update contiguous [B,T,H].  out=res updates
+    the residual in place."""
+    lib = load_library()
+    if res.dtype != torch.bfloat16 or res.dim() != 3 or not res.is_contiguous():
+        raise ValueError("res: expected a contiguous bfloat16 [B,H,T] tensor")
+    B, H, T = res.shape
+    if (update.dtype != torch.bfloat16 or tuple(update.shape) != (B, T, H)
+            or not update.is_contiguous()):
+        raise ValueError("update: expected a contiguous bfloat16 [B,T,H] tensor")
+    gp, gbs = _vec(gate, B, H, "gate")
+    o = torch.empty_like(res) if out is None else out
+    if o.shape != res.shape or o.dtype != torch.bfloat16 or not o.is_contiguous():
+        raise ValueError("out: expected a contiguous bfloat16 [B,H,T] tensor")
+    _check(lib.adaln_residual_gate_channel_first(res.data_ptr(), update.data_ptr(), gp,
+                                                 o.data_ptr(), B, T, H, gbs, _stream(stream)),
+           "adaln_residual_gate_channel_first")
+    return o
+
+
 def adaln_check_layernorm_modulate(x_ptr, scale_ptr, shift_ptr, y_ptr, B, T, H, scale_bstride,
                                    shift_bstride, eps=1e-6) -> int:
     """Status code of the validation (raw pointers as ints; nothing is launched)."""
@@ -318,6 +342,12 @@ def adaln_check_qk_rmsnorm_rope(q_ptr, k_ptr, q_weight_ptr, k_weight_ptr, cos_si
     return load_library().adaln_check_qk_rmsnorm_rope(
         q_ptr, k_ptr, q_weight_ptr, k_weight_ptr, cos_sin_ptr, q_out_ptr, k_out_ptr, tokens,
         heads_q, heads_k, head_dim, q_token_stride, k_token_stride, eps)
+
+
+def adaln_check_residual_gate_channel_first(res_ptr, update_ptr, gate_ptr, out_ptr, B, T, H,
+                                            gate_bstride) -> int:
+    return load_library().adaln_check_residual_gate_channel_first(res_ptr, update_ptr, gate_ptr,
+                                                                  out_ptr, B, T, H, gate_bstride)
 
 
 def adaln_reduction_layout(H: int):

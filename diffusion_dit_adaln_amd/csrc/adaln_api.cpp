@@ -204,9 +204,49 @@ adaln_status validate_qk(const void* q, const void* k, const void* q_weight, con
     return ADALN_OK;
 }
 
+// Validation of the channel-first residual gate.
+adaln_status validate_cf(const void* res, const void* update, const void* gate, const void* out,
+                         int64_t B, int64_t T, int64_t H, int64_t gate_bs, bool* empty) {
+    *empty = true;
+    if (B < 0 || T < 0 || H < 0 || (T % 8) != 0 || (H % 8) != 0) return ADALN_ERR_SHAPE;
+    if (B == 0 || T == 0 || H == 0) return ADALN_OK;
+    if (B > INT64_MAX / T || B * T > INT64_MAX / 2 / H) return ADALN_ERR_SHAPE;
+    *empty = false;
+    if (!res || !update || !out) return ADALN_ERR_NULL;
+    if (!aligned16(res) || !aligned16(update) || !aligned16(out)) return ADALN_ERR_ALIGN;
+    ADALN_TRY(check_vec(gate, B, H, gate_bs));
+    const Span os = act_span(out, B * T, H);
+    // out may be res itself (an in-place residual update), never a partial overlap
+    if (out != res && overlaps(os, act_span(res, B * T, H))) return ADALN_ERR_OVERLAP;
+    if (overlaps(os, act_span(update, B * T, H)) || overlaps(os, vec_span(gate, B, H, gate_bs)))
+        return ADALN_ERR_OVERLAP;
+    return ADALN_OK;
+}
+
 }  // namespace
 
 extern "C" {
+
+adaln_status adaln_residual_gate_channel_first(const adaln_bf16* res, const adaln_bf16* update,
+                                               const adaln_bf16* gate, adaln_bf16* out, int64_t B,
+                                               int64_t T, int64_t H, int64_t gate_bstride,
+                                               void* hip_stream) {
+    bool empty = true;
+    ADALN_TRY(validate_cf(res, update, gate, out, B, T, H, gate_bstride, &empty));
+    if (empty) return ADALN_OK;
+    adaln::CFParams p{res, update, gate, out, B, T, H, B > 1 ? gate_bstride : 0};
+    hipError_t e = adaln::launch_cf(p, (hipStream_t)hip_stream);
+    return e == hipSuccess ? ADALN_OK : ADALN_ERR_LAUNCH;
+}
+
+adaln_status adaln_check_residual_gate_channel_first(const adaln_bf16* res,
+                                                     const adaln_bf16* update,
+                                                     const adaln_bf16* gate, const adaln_bf16* out,
+                                                     int64_t B, int64_t T, int64_t H,
+                                                     int64_t gate_bstride) {
+    bool empty = true;
+    return validate_cf(res, update, gate, out, B, T, H, gate_bstride, &empty);
+}
 
 adaln_status adaln_qk_rmsnorm_rope(const adaln_bf16* q, const adaln_bf16* k,
                                    const adaln_bf16* q_weight, const adaln_bf16* k_weight,

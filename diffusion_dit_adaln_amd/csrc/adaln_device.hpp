@@ -63,6 +63,16 @@ __device__ __forceinline__ void st16_stream(rsrc_t r, int off, uint4 v) {
     __builtin_amdgcn_raw_buffer_store_b128(t, r, off, 0, kNonTemporal);
 }
 
+// Non-temporal 16-byte accesses through plain pointers (callers check bounds).
+__device__ __forceinline__ uint4 ld16_nt(const uint16_t* p) {
+    const u32x4 t = __builtin_nontemporal_load(reinterpret_cast<const u32x4*>(p));
+    return make_uint4(t.x, t.y, t.z, t.w);
+}
+__device__ __forceinline__ void st16_nt(uint16_t* p, uint4 v) {
+    const u32x4 t = {v.x, v.y, v.z, v.w};
+    __builtin_nontemporal_store(t, reinterpret_cast<u32x4*>(p));
+}
+
 typedef unsigned int u32x2 __attribute__((ext_vector_type(2)));
 __device__ __forceinline__ void st8_stream(rsrc_t r, int off, u32 lo, u32 hi) {
     const u32x2 t = {lo, hi};

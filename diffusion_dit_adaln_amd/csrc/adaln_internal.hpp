@@ -61,6 +61,16 @@ struct QKParams {
 };
 hipError_t launch_qk(const QKParams& p, hipStream_t stream);
 
+// Residual gating on the channel-first layout, validated by the C-ABI layer.
+struct CFParams {
+    const uint16_t* res;     // [B, H, T]
+    const uint16_t* update;  // [B, T, H]
+    const uint16_t* gate;    // row b at gate + b*gate_bs
+    uint16_t* out;           // [B, H, T] (may be res)
+    int64_t B, T, H, gate_bs;
+};
+hipError_t launch_cf(const CFParams& p, hipStream_t stream);
+
 // Resident workgroups of `block` threads per CU for a kernel on the current device,
 // and the CU count (cached per kernel and device, thread-safe).
 bool occupancy(const void* fn, int block, int* blocks_per_cu, int* cus);

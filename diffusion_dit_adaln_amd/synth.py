@@ -207,6 +207,30 @@ def config7(seed: int = 0) -> QKWorkload:
                       rope_cache(T, D))
 
 
+@dataclasses.dataclass
+class CFWorkload:
+    """Residual gating on a channel-first residual: res [B,H,T], update [B,T,H]."""
+    name: str
+    res: np.ndarray          # [B, H, T] bf16 bits
+    update: np.ndarray       # [B, T, H]
+    gate: np.ndarray         # [B, H]
+    op: str = "cf"
+
+    def algorithmic_bytes(self) -> int:
+        """Read res and update, write out (bf16)."""
+        return 6 * int(np.prod(self.res.shape))
+
+
+def config8(seed: int = 0) -> CFWorkload:
+    """Channel-first residual gating at the FLUX site size: hidden 3072, 4608 tokens,
+    CFG batch 2; res, update ~ N(0,1); gate ~ 0.1*N."""
+    B, H, T = 2, 3072, 4608
+    return CFWorkload("rg_channel_first_2x3072x4608",
+                      normal_bf16(_rng(seed, 8, "res"), (B, H, T)),
+                      normal_bf16(_rng(seed, 8, "x"), (B, T, H)),
+                      normal_bf16(_rng(seed, 8, "gate"), (B, H), 0.1))
+
+
 def flux_chunk_views(seed: int, B: int, H: int, chunks: int, cid: int = 30):
     """scale/shift as strided views of one [B, chunks*H] embedding, like
     ``emb.chunk(chunks, dim=1)`` in the FLUX.1 test snippet: (emb, shift, scale)

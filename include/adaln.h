@@ -7,7 +7,8 @@
  * transformers run at every adaLN site, optionally preceded by the residual-gate
  * prologue  r = res + gate[b] * x (for both norms), or followed, for the
  * LayerNorm, by a static FP8 quantisation of y.  A sixth normalises the attention
- * heads of Q and K and applies the rotary embedding (adaln_qk_rmsnorm_rope).
+ * heads of Q and K and applies the rotary embedding (adaln_qk_rmsnorm_rope); a
+ * seventh applies the residual gate to a channel-first residual stream.
  *
  * Sources, cited by page title and section:
  *  - FLUX.1 PR report "route the adaLN LN+modulate sites through the bit-exact
@@ -89,10 +90,11 @@
 extern "C" {
 #endif
 
-#define ADALN_ABI_VERSION 5 /* 2: two waves per row for 2048 <= H < 4096;
+#define ADALN_ABI_VERSION 6 /* 2: two waves per row for 2048 <= H < 4096;
                               3: residual-gate LayerNorm, stream copy;
                               4: LayerNorm + modulate + FP8 quantisation;
-                              5: per-head QK RMSNorm + RoPE */
+                              5: per-head QK RMSNorm + RoPE;
+                              6: channel-first residual gating */
 
 typedef uint16_t adaln_bf16; /* raw bfloat16 bits */
 
@@ -175,6 +177,20 @@ adaln_status adaln_qk_rmsnorm_rope(const adaln_bf16* q, const adaln_bf16* k,
                                    int64_t head_dim, int64_t q_token_stride,
                                    int64_t k_token_stride, float eps, void* hip_stream);
 
+/* Residual gating on the channel-first layout (kernels guide, norm variants /
+ * residual gating: the transposed dense path keeps the residual and the output in
+ * their [B, hidden, tokens] layout and reads the update in its row-major order,
+ * with no .contiguous() copy):
+ *   out[b][h][t] = bf16(res[b][h][t] + bf16(gate[b][h] * update[b][t][h]))
+ * res, out: contiguous [B, H, T]; update: contiguous [B, T, H]; gate row b at
+ * gate + b*gate_bstride (0 shares one vector; else >= H and % 8 == 0).  T % 8 == 0
+ * and H % 8 == 0 (ADALN_ERR_SHAPE otherwise); pointers 16-byte aligned.  out may be
+ * res itself (in-place update); any other overlap is ADALN_ERR_OVERLAP. */
+adaln_status adaln_residual_gate_channel_first(const adaln_bf16* res, const adaln_bf16* update,
+                                               const adaln_bf16* gate, adaln_bf16* out, int64_t B,
+                                               int64_t T, int64_t H, int64_t gate_bstride,
+                                               void* hip_stream);
+
 /* Predicates: the validation of the entry point of the same name, without a
  * launch (the `can_use_*` predicate of the kernels guide's entry-point protocol).
  * They never touch the GPU. */
@@ -212,6 +228,12 @@ adaln_status adaln_check_qk_rmsnorm_rope(const adaln_bf16* q, const adaln_bf16* 
                                          int64_t heads_q, int64_t heads_k, int64_t head_dim,
                                          int64_t q_token_stride, int64_t k_token_stride,
                                          float eps);
+
+adaln_status adaln_check_residual_gate_channel_first(const adaln_bf16* res,
+                                                     const adaln_bf16* update,
+                                                     const adaln_bf16* gate, const adaln_bf16* out,
+                                                     int64_t B, int64_t T, int64_t H,
+                                                     int64_t gate_bstride);
 
 /* The fixed reduction layout for H: waves per row, lanes per row, chunks per
  * lane.  ADALN_ERR_SHAPE for an unsupported H; out-pointers may be NULL. */

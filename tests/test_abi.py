@@ -33,14 +33,14 @@ def declared_symbols():
 
 def test_header_symbols_are_exported(lib):
     names = declared_symbols()
-    assert len(names) == 19, names
+    assert len(names) == 21, names
     assert set(names) == set(_binding.EXPORTS)
     for n in names:
         assert hasattr(lib, n), n
 
 
 def test_abi_version_and_status_strings(lib):
-    assert A.adaln_abi_version() == A.ABI_VERSION == 5
+    assert A.adaln_abi_version() == A.ABI_VERSION == 6
     for s in range(8):
         assert len(A.adaln_status_string(s)) > 5
     assert A.adaln_status_string(99) == "unknown status"
@@ -155,6 +155,31 @@ def test_qk_checks(lib):
     assert qk_check(lib, qo=addr(3) - 16) == OVERLAP     # runs into the cache
     assert lib.adaln_qk_rmsnorm_rope(addr(0), addr(1), None, None, addr(3), addr(4), addr(5), 7,
                                      24, 24, 96, 3072, 3072, 1e-6, None) == SHAPE
+
+
+def cf_check(lib, **kw):
+    a = dict(res=addr(0), upd=addr(1), gate=addr(2), out=addr(3), B=2, T=4608, H=3072,
+             gbs=3072)
+    a.update(kw)
+    return lib.adaln_check_residual_gate_channel_first(a["res"], a["upd"], a["gate"], a["out"],
+                                                       a["B"], a["T"], a["H"], a["gbs"])
+
+
+def test_channel_first_checks(lib):
+    assert cf_check(lib) == OK
+    assert cf_check(lib, out=addr(0)) == OK              # in place
+    assert cf_check(lib, out=addr(0) + 16) == OVERLAP    # partial overlap with res
+    assert cf_check(lib, out=addr(1)) == OVERLAP         # over update
+    assert cf_check(lib, T=4604) == SHAPE
+    assert cf_check(lib, H=12) == SHAPE
+    assert cf_check(lib, B=0, res=None, upd=None, gate=None, out=None) == OK
+    assert cf_check(lib, upd=None) == NULL
+    assert cf_check(lib, gate=None) == NULL
+    assert cf_check(lib, res=addr(0) + 2) == ALIGN
+    assert cf_check(lib, gbs=100) == STRIDE
+    assert cf_check(lib, gbs=0) == OK
+    assert lib.adaln_residual_gate_channel_first(addr(0), addr(1), addr(2), addr(1), 2, 4608,
+                                                 3072, 3072, None) == OVERLAP
 
 
 def test_valid_arguments_pass(lib):

@@ -402,6 +402,40 @@ def test_qk_heads_alone_equal_heads_in_batch():
 
 
 # --------------------------------------------------------------------------
+# residual gating on the channel-first layout
+# --------------------------------------------------------------------------
+def test_channel_first_full_size():
+    wl = synth.config8()
+    say(f"[parity] channel-first {wl.res.shape}")
+    got = A.adaln_residual_gate_channel_first(dev(wl.res), dev(wl.update), dev(wl.gate))
+    assert_bits_equal(host(got), O.residual_gate_channel_first(wl.res, wl.update, wl.gate),
+                      "channel-first full size")
+
+
+@pytest.mark.parametrize("B,H,T", [(1, 8, 8), (2, 72, 40), (3, 136, 200), (1, 64, 64),
+                                   (2, 3072, 72), (1, 520, 4104)])
+def test_channel_first_shapes(B, H, T):
+    say(f"[parity] channel-first B={B} H={H} T={T}")
+    rng = np.random.default_rng(B * 7 + H + T)
+    res = mixed_rows(rng, B, H, T)
+    upd = mixed_rows(rng, B, T, H)
+    emb = synth.normal_bf16(rng, (B, 3 * H), 0.1)
+    gate = emb[:, H:2 * H]                        # a strided chunk view
+    want = O.residual_gate_channel_first(res, upd, gate)
+    ed = dev(emb)
+    got = A.adaln_residual_gate_channel_first(dev(res), dev(upd), ed[:, H:2 * H])
+    assert_bits_equal(host(got), want, f"cf B={B} H={H} T={T}")
+    # in place on the residual
+    rd = dev(res)
+    A.adaln_residual_gate_channel_first(rd, dev(upd), ed[:, H:2 * H], out=rd)
+    assert_bits_equal(host(rd), want, f"cf in place B={B} H={H} T={T}")
+    # one gate vector for the batch
+    g1 = synth.normal_bf16(rng, (1, H), 0.1)
+    got = A.adaln_residual_gate_channel_first(dev(res), dev(upd), dev(g1))
+    assert_bits_equal(host(got), O.residual_gate_channel_first(res, upd, g1), "cf shared gate")
+
+
+# --------------------------------------------------------------------------
 # the FP8 kernel's quantisation step, exhaustively over binary32
 # --------------------------------------------------------------------------
 def test_device_fp8_quant_all_fp32_patterns():

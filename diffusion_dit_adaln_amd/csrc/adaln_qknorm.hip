@@ -14,9 +14,11 @@
 // to bf16.
 //
 // Work: a task is four consecutive heads of Q or of K of one token.  Waves walk
-// the tasks interleaved (wave w takes tasks w, w + G, ...) with a ring of S tasks
-// in flight; the loads and stores of a pass are unconditional (descriptor ranges
-// drop what lies past the end), so each slot waits only for its own data.
+// the tasks interleaved (wave w takes tasks w, w + G, ...) with the next task's
+// loads issued before the current one's arithmetic ends (a ring of S slots); the
+// loads and stores of a pass are unconditional (descriptor ranges drop what lies
+// past the end, and a slot without a task skips its arithmetic), so each slot
+// waits only for its own data.
 #include <hip/hip_runtime.h>
 #include <stdint.h>
 
@@ -26,7 +28,16 @@
 namespace adaln {
 namespace {
 
-constexpr int kQKSlots = 3;  // tasks in flight per wave
+// Tasks in flight per wave (launch tuning; never changes the bits).  Measured on
+// MI355X: one task per wave, with seven waves per SIMD covering the latency, beats
+// deeper rings (1: 4.72 TB/s, 2: 4.57, 3: 4.55, 4: 4.40 on [4608, 24+24, 128]).
+#ifndef ADALN_QK_SLOTS
+#define ADALN_QK_SLOTS 1
+#endif
+constexpr int kQKSlots = ADALN_QK_SLOTS;
+#ifndef ADALN_QK_OVERSUB
+#define ADALN_QK_OVERSUB 1  // waves per resident wave slot
+#endif
 
 __global__ __launch_bounds__(256) void qk_rmsnorm_rope(QKParams p) {
     constexpr int D = 128;
@@ -115,6 +126,10 @@ __global__ __launch_bounds__(256) void qk_rmsnorm_rope(QKParams p) {
             Slot& sl = ring[k];
             const Task t = task_at(tok[k], jj[k]);
 
+            // the arithmetic only for a real task (uniform branch, no memory operation
+            // inside); the store below is issued either way
+            u32 out[4] = {0u, 0u, 0u, 0u};
+            if (id < p.tasks) {
             float x[8];
 #pragma unroll
             for (int j = 0; j < 4; ++j) {
@@ -138,7 +153,6 @@ __global__ __launch_bounds__(256) void qk_rmsnorm_rope(QKParams p) {
                                  __uint_as_float(sl.c.z), __uint_as_float(sl.c.w)};
             const float s4[4] = {__uint_as_float(sl.s.x), __uint_as_float(sl.s.y),
                                  __uint_as_float(sl.s.z), __uint_as_float(sl.s.w)};
-            u32 out[4];
 #pragma unroll
             for (int j = 0; j < 4; ++j) {
                 const float w0 = t.is_q ? wq[2 * j] : wk[2 * j];
@@ -150,6 +164,7 @@ __global__ __launch_bounds__(256) void qk_rmsnorm_rope(QKParams p) {
                 const float o2 = bc + as;
                 out[j] = pack_bf16(o1, o2);
             }
+            }  // id < tasks
             st16_stream(out_rsrc(id, t), head_off(t), make_uint4(out[0], out[1], out[2], out[3]));
 
             // the slot's task S*G ahead
@@ -184,7 +199,7 @@ hipError_t launch_qk(const QKParams& p_in, hipStream_t stream) {
     int blocks_per_cu = 0, cus = 0;
     if (!occupancy(reinterpret_cast<const void*>(qk_rmsnorm_rope), 256, &blocks_per_cu, &cus))
         return hipErrorInvalidDeviceFunction;
-    const int64_t slots = (int64_t)blocks_per_cu * cus * 4;
+    const int64_t slots = (int64_t)blocks_per_cu * cus * 4 * ADALN_QK_OVERSUB;
     p.waves = p.tasks < slots ? p.tasks : slots;
     const int64_t sg = (int64_t)kQKSlots * p.waves;
     p.sg_div = sg / p.tasks_per_token;

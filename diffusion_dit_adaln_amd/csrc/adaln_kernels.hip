@@ -52,6 +52,11 @@
 #ifndef ADALN_INTERLEAVE_LN
 #define ADALN_INTERLEAVE_LN 1
 #endif
+// Interleaved ops switch to a one-slot ring when each resident group would get at
+// least this many rows.
+#ifndef ADALN_SHALLOW_ROWS_PER_GROUP
+#define ADALN_SHALLOW_ROWS_PER_GROUP 3
+#endif
 #ifndef ADALN_INTERLEAVE_RMS
 #define ADALN_INTERLEAVE_RMS 0
 #endif
@@ -218,7 +223,7 @@ constexpr int ring_slots(int W, int C, bool gated) {
 // Per-lane constants of the current batch entry are kept as fp32 (no unpacking
 // per row) or, for wide rows on one wave, as packed bf16 pairs (every constant is
 // a bf16 value); see consts_as_f32.
-template <int OP, int W, int C, bool TAIL, bool WEIGHT, bool IL>
+template <int OP, int W, int C, bool TAIL, bool WEIGHT, bool IL, bool SHALLOW>
 __global__ __launch_bounds__(256) void fused_norm_modulate(Params p) {
     constexpr int P = 64 * W;
     constexpr bool KF = consts_as_f32(W, C, OP, WEIGHT);
@@ -362,7 +367,7 @@ __global__ __launch_bounds__(256) void fused_norm_modulate(Params p) {
     // A ring of S row slots: slot k holds the group's row row0 + k*G; after a row is
     // finished its slot is refilled with the group's row S ahead, so S rows' loads
     // stay in flight.
-    constexpr int S = ring_slots(W, C, GATED);
+    constexpr int S = SHALLOW ? 1 : ring_slots(W, C, GATED);
     uint4 xs[S][C], rs[S][C];
     // Prologue in the steady state's order: before slot k's loads, stand-ins for
     // slot k-1's stores (out of range: dropped), so that at the loop head the
@@ -666,44 +671,51 @@ __global__ __launch_bounds__(256) void diag_quant(const float4* __restrict__ in,
 // ---------------------------------------------------------------------------
 using KernelFn = void (*)(Params);
 
-template <int OP, int W, int C, bool TAIL>
+template <int OP, int W, int C, bool TAIL, bool SHALLOW>
 KernelFn pick_weight(bool weight) {
     constexpr bool IL = interleaved(OP);
     if constexpr (op_layernorm(OP)) {
-        return fused_norm_modulate<OP, W, C, TAIL, false, IL>;  // LayerNorm has no weight
+        return fused_norm_modulate<OP, W, C, TAIL, false, IL, SHALLOW>;  // no weight
     } else {
-        return weight ? fused_norm_modulate<OP, W, C, TAIL, true, IL>
-                      : fused_norm_modulate<OP, W, C, TAIL, false, IL>;
+        return weight ? fused_norm_modulate<OP, W, C, TAIL, true, IL, SHALLOW>
+                      : fused_norm_modulate<OP, W, C, TAIL, false, IL, SHALLOW>;
     }
 }
 
+// shallow: the one-slot ring, instantiated for the interleaved ops only
 template <int OP, int W, int C>
-KernelFn pick_tail(bool tail, bool weight) {
-    return tail ? pick_weight<OP, W, C, true>(weight) : pick_weight<OP, W, C, false>(weight);
+KernelFn pick_tail(bool tail, bool weight, bool shallow) {
+    if constexpr (interleaved(OP)) {
+        if (shallow)
+            return tail ? pick_weight<OP, W, C, true, true>(weight)
+                        : pick_weight<OP, W, C, false, true>(weight);
+    }
+    return tail ? pick_weight<OP, W, C, true, false>(weight)
+                : pick_weight<OP, W, C, false, false>(weight);
 }
 
 template <int OP>
-KernelFn pick(const Layout& L, bool weight) {
+KernelFn pick(const Layout& L, bool weight, bool shallow) {
     // H < 2048: one wave, C = 1..4; 2048 <= H < 4096: two waves, C = 2..4;
     // H >= 4096: four waves, C = 2..4.
     if (L.waves == 1) {
         switch (L.chunks) {
-            case 1: return pick_tail<OP, 1, 1>(L.ragged, weight);
-            case 2: return pick_tail<OP, 1, 2>(L.ragged, weight);
-            case 3: return pick_tail<OP, 1, 3>(L.ragged, weight);
-            case 4: return pick_tail<OP, 1, 4>(L.ragged, weight);
+            case 1: return pick_tail<OP, 1, 1>(L.ragged, weight, shallow);
+            case 2: return pick_tail<OP, 1, 2>(L.ragged, weight, shallow);
+            case 3: return pick_tail<OP, 1, 3>(L.ragged, weight, shallow);
+            case 4: return pick_tail<OP, 1, 4>(L.ragged, weight, shallow);
         }
     } else if (L.waves == 2) {
         switch (L.chunks) {
-            case 2: return pick_tail<OP, 2, 2>(L.ragged, weight);
-            case 3: return pick_tail<OP, 2, 3>(L.ragged, weight);
-            case 4: return pick_tail<OP, 2, 4>(L.ragged, weight);
+            case 2: return pick_tail<OP, 2, 2>(L.ragged, weight, shallow);
+            case 3: return pick_tail<OP, 2, 3>(L.ragged, weight, shallow);
+            case 4: return pick_tail<OP, 2, 4>(L.ragged, weight, shallow);
         }
     } else {
         switch (L.chunks) {
-            case 2: return pick_tail<OP, 4, 2>(L.ragged, weight);
-            case 3: return pick_tail<OP, 4, 3>(L.ragged, weight);
-            case 4: return pick_tail<OP, 4, 4>(L.ragged, weight);
+            case 2: return pick_tail<OP, 4, 2>(L.ragged, weight, shallow);
+            case 3: return pick_tail<OP, 4, 3>(L.ragged, weight, shallow);
+            case 4: return pick_tail<OP, 4, 4>(L.ragged, weight, shallow);
         }
     }
     return nullptr;
@@ -757,12 +769,15 @@ Layout layout_of(int64_t H) {
 hipError_t launch(Op op, const Params& p_in, hipStream_t stream) {
     const Layout L = layout_of(p_in.H);
     const bool weight = p_in.weight != nullptr;
-    KernelFn fn = op == OP_LN    ? pick<OP_LN>(L, false)
-                : op == OP_RMS   ? pick<OP_RMS>(L, weight)
-                : op == OP_RG    ? pick<OP_RG>(L, weight)
-                : op == OP_RGLN  ? pick<OP_RGLN>(L, false)
-                : op == OP_LNQ   ? pick<OP_LNQ>(L, false)
-                                 : nullptr;
+    auto pick_op = [&](bool shallow) -> KernelFn {
+        return op == OP_LN     ? pick<OP_LN>(L, false, shallow)
+               : op == OP_RMS  ? pick<OP_RMS>(L, weight, shallow)
+               : op == OP_RG   ? pick<OP_RG>(L, weight, shallow)
+               : op == OP_RGLN ? pick<OP_RGLN>(L, false, shallow)
+               : op == OP_LNQ  ? pick<OP_LNQ>(L, false, shallow)
+                               : nullptr;
+    };
+    KernelFn fn = pick_op(false);
     if (!fn) return hipErrorInvalidValue;
     // one-wave rows: four independent waves per workgroup; else one row group per
     // workgroup of W waves
@@ -773,8 +788,21 @@ hipError_t launch(Op op, const Params& p_in, hipStream_t stream) {
         return hipErrorInvalidDeviceFunction;
     }
     Params p = p_in;
-    const int S = ring_slots(L.waves, L.chunks, op_gated(op));
-    const int64_t resident = (int64_t)cus * blocks_per_cu * (L.waves == 1 ? 4 : 1);
+    int64_t resident = (int64_t)cus * blocks_per_cu * (L.waves == 1 ? 4 : 1);
+    // Interleaved ops with many rows per group: the one-slot ring (more resident
+    // groups, the latency covered by the other groups) streams faster; with few
+    // rows per group the deeper ring does (tuning; the bits never depend on it).
+    bool shallow = false;
+    if (interleaved(op) && p.rows >= ADALN_SHALLOW_ROWS_PER_GROUP * resident) {
+        KernelFn f1 = pick_op(true);
+        int bpc1 = 0;
+        if (f1 && occupancy(reinterpret_cast<const void*>(f1), block, &bpc1, &cus)) {
+            fn = f1;
+            shallow = true;
+            resident = (int64_t)cus * bpc1 * (L.waves == 1 ? 4 : 1);
+        }
+    }
+    const int S = shallow ? 1 : ring_slots(L.waves, L.chunks, op_gated(op));
     if (interleaved(op)) {
         // one group per resident group slot (at most one per row); a group's ring
         // slots past its last row skip their arithmetic

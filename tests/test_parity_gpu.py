@@ -177,6 +177,29 @@ def test_edge_hidden_sizes(H):
         check_lnq(x, sc, sh, qs, f"lnq H={H} qscale={qs}")
 
 
+# Row counts large enough that the interleaved ops take their one-slot ring (at
+# least three rows per resident row group), for one-, two- and four-wave rows with
+# and without a ragged last chunk.
+@pytest.mark.parametrize("op,T,H", [("ln", 30000, 520), ("ln", 30000, 1024),
+                                    ("ln", 7000, 3080), ("ln", 3600, 4104),
+                                    ("rgln", 30000, 1536), ("rgln", 6400, 2048),
+                                    ("lnq", 4000, 4096), ("lnq", 30000, 776)])
+def test_many_rows_per_group(op, T, H):
+    say(f"[parity] many rows {op} T={T} H={H}")
+    rng = np.random.default_rng(T + H)
+    x = synth.normal_bf16(rng, (1, T, H))
+    sc = synth.normal_bf16(rng, (1, H), 0.1)
+    sh = synth.normal_bf16(rng, (1, H), 0.1)
+    if op == "ln":
+        assert_bits_equal(run_ln(x, sc, sh), O.layernorm_modulate(x, sc, sh, EPS), f"ln {T}x{H}")
+    elif op == "rgln":
+        res = synth.normal_bf16(rng, (1, T, H))
+        g = synth.normal_bf16(rng, (1, H), 0.1)
+        check_rgln(res, x, g, sc, sh, f"rgln {T}x{H}")
+    else:
+        check_lnq(x, sc, sh, 0.0125, f"lnq {T}x{H}")
+
+
 @pytest.mark.parametrize("eps", [0.0, 1e-5, 1e-6, 0.25])
 def test_eps_values(eps):
     say(f"[parity] eps={eps}")

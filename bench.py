@@ -29,12 +29,17 @@ sys.path.insert(0, ROOT)
 
 PEAK_HBM_GBPS = 8000.0
 METRIC = "achieved HBM GB/s (% of MI355X peak) and rows/s for fused norm+modulate"
-KERNEL_SRC = os.path.join(ROOT, "diffusion_dit_adaln_amd", "csrc", "adaln_kernels.hip")
+# the sources of the fused kernel (its template, shared device helpers, parameters)
+KERNEL_SRCS = [os.path.join(ROOT, "diffusion_dit_adaln_amd", "csrc", f)
+               for f in ("adaln_kernels.hip", "adaln_device.hpp", "adaln_internal.hpp")]
 
 
 def kernel_src_sha() -> str:
-    with open(KERNEL_SRC, "rb") as fh:
-        return hashlib.sha256(fh.read()).hexdigest()[:16]
+    h = hashlib.sha256()
+    for path in KERNEL_SRCS:
+        with open(path, "rb") as fh:
+            h.update(fh.read())
+    return h.hexdigest()[:16]
 
 
 def load_counters(name: str):

@@ -396,7 +396,8 @@ const char* adaln_status_string(adaln_status status) {
         case ADALN_OK: return "success";
         case ADALN_ERR_NULL: return "a required pointer is NULL";
         case ADALN_ERR_SHAPE:
-            return "unsupported shape: need 8 <= H <= 8192, H % 8 == 0, B, T >= 0 (QK: head_dim 128)";
+            return "unsupported shape: sizes >= 0; row ops need 8 <= H <= 8192 and H % 8 == 0; "
+                   "QK-norm needs head_dim 128; the channel-first layout needs T, H % 8 == 0";
         case ADALN_ERR_ALIGN: return "a pointer is not 16-byte aligned";
         case ADALN_ERR_STRIDE: return "a batch stride is negative, not a multiple of 8, or in (0, H)";
         case ADALN_ERR_OVERLAP: return "an output overlaps an input or the other output";

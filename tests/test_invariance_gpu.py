@@ -16,7 +16,12 @@ EPS = 1e-6
 
 
 def _same(a, b):
+    if a.dtype == torch.uint8:
+        return torch.equal(a, b)
     return torch.equal(a.view(torch.int16), b.view(torch.int16))
+
+
+QSCALE = 0.0125
 
 
 @pytest.fixture(scope="module")
@@ -28,16 +33,23 @@ def stress():
     return st
 
 
-@pytest.mark.parametrize("op", ["ln", "rms"])
+# ln, rms; rgln: the residual-gate LayerNorm with res = x and gate = scale (the y
+# output); lnq: LayerNorm + FP8 quantisation (E4M3 codes)
+@pytest.mark.parametrize("op", ["ln", "rms", "rgln", "lnq"])
 def test_packed_sets_alone_and_single_rows(stress, op):
     st = stress
     R, H = st.x.shape
     S = len(st.offsets) - 1
     w = st.weight if op == "rms" else None
+    qs = torch.tensor([QSCALE], dtype=torch.float32, device="cuda")
 
     def run(x3, sc, sh):
         if op == "ln":
             return A.adaln_layernorm_modulate(x3, sc, sh, EPS)
+        if op == "rgln":
+            return A.adaln_residual_gate_layernorm_modulate(x3, x3, sc, sc, sh, EPS)[1]
+        if op == "lnq":
+            return A.adaln_layernorm_modulate_fp8_quant(x3, sc, sh, qs, EPS)
         return A.adaln_rmsnorm_scale_shift(x3, w, sc, sh, EPS)
 
     # (i) every row packed into one [1, R, H] batch with one shared vector
@@ -72,8 +84,13 @@ def test_packed_sets_alone_and_single_rows(stress, op):
     xr = xh.reshape(len(sample), 1, H)
     if op == "ln":
         want = O.layernorm_modulate(xr, sch, shh, EPS)
+    elif op == "rgln":
+        want = O.residual_gate_layernorm_modulate(xr, xr, sch, sch, shh, EPS)[1]
+    elif op == "lnq":
+        want = O.layernorm_modulate_fp8(xr, sch, shh, QSCALE, EPS)
     else:
         want = O.rmsnorm_scale_shift(xr, host(st.weight), sch, shh, EPS)
-    got = host(y_rows[torch.from_numpy(sample).cuda()])
+    picked = y_rows[torch.from_numpy(sample).cuda()]
+    got = picked.cpu().numpy() if op == "lnq" else host(picked)
     assert_bits_equal(got.reshape(want.shape), want, f"{op} sampled rows")
     assert set(np.unique(st.row_class[sample])) == {0, 1, 2}

@@ -1,9 +1,10 @@
 // adaln_kernels.hip -- gfx950 kernels of libadaln: LayerNorm / RMSNorm fused with
-// the adaLN modulate epilogue, optionally preceded by the residual-gate prologue.
+// the adaLN modulate epilogue, optionally preceded by the residual-gate prologue or
+// (LayerNorm) followed by a static FP8 quantisation of the output.
 //
 // One row is owned by one wave (H < 2048) or by one workgroup of two waves
-// (H < 4096) or four waves.  The row is read from HBM once with 16-byte loads and kept in
-// registers; the statistic is reduced in the fixed order of the numerics contract
+// (H < 4096) or four waves.  The row is read from HBM once with 16-byte loads and
+// kept in registers; the statistic is reduced in the fixed order of the numerics contract
 // (include/adaln.h), which depends on H only, so the bits of a row never depend on
 // the batch it is launched in or on the grid.  Sources, by page title and section:
 //  - kernels guide, "selection matrix / Norm + scale/shift": column ownership
@@ -50,12 +51,7 @@
 // gain from the interleaved assignment (more groups, shorter chains), the RMS ops
 // stream slightly faster over contiguous ranges.
 #ifndef ADALN_INTERLEAVE_LN
-#define ADALN_INTERLEAVE_LN 1
-#endif
-// Interleaved ops switch to a one-slot ring when each resident group would get at
-// least this many rows.
-#ifndef ADALN_SHALLOW_ROWS_PER_GROUP
-#define ADALN_SHALLOW_ROWS_PER_GROUP 3
+#define ADALN_INTERLEAVE_LN 1  // LayerNorm and LayerNorm + FP8
 #endif
 #ifndef ADALN_INTERLEAVE_RMS
 #define ADALN_INTERLEAVE_RMS 0
@@ -65,6 +61,12 @@
 #endif
 #ifndef ADALN_INTERLEAVE_RGLN
 #define ADALN_INTERLEAVE_RGLN 1
+#endif
+// Interleaved ops switch to a one-slot ring when each resident group would get at
+// least this many rows (measured on MI355X: more resident groups then beat a deeper
+// ring; with fewer rows per group the deeper ring is faster).
+#ifndef ADALN_SHALLOW_ROWS_PER_GROUP
+#define ADALN_SHALLOW_ROWS_PER_GROUP 3
 #endif
 
 namespace adaln {
@@ -218,7 +220,9 @@ constexpr int ring_slots(int W, int C, bool gated) {
 }
 
 // OP: Op; W: waves per row; C: chunks per lane; TAIL: the last chunk is partial;
-// WEIGHT: RMS weight present.  256 threads per workgroup.
+// WEIGHT: RMS weight present; IL: interleaved rows (per-row descriptors); SHALLOW:
+// a one-slot ring.  A workgroup is four independent one-wave groups (W == 1) or one
+// group of W waves.
 //
 // Per-lane constants of the current batch entry are kept as fp32 (no unpacking
 // per row) or, for wide rows on one wave, as packed bf16 pairs (every constant is

@@ -19,6 +19,7 @@ import ctypes
 import hashlib
 import json
 import os
+import re
 import sys
 import time
 
@@ -35,10 +36,15 @@ KERNEL_SRCS = [os.path.join(ROOT, "diffusion_dit_adaln_amd", "csrc", f)
 
 
 def kernel_src_sha() -> str:
+    """Hash of the fused kernel's code: its sources with comments and blank space
+    removed, so that a comment edit does not invalidate the counters."""
     h = hashlib.sha256()
     for path in KERNEL_SRCS:
-        with open(path, "rb") as fh:
-            h.update(fh.read())
+        with open(path) as fh:
+            text = fh.read()
+        text = re.sub(r"/\*.*?\*/", " ", text, flags=re.S)
+        text = re.sub(r"//[^\n]*", " ", text)
+        h.update(" ".join(text.split()).encode())
     return h.hexdigest()[:16]
 
 

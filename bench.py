@@ -295,8 +295,24 @@ def median3(f):
     return v[1]
 
 
-def cpu_baseline(wl, budget_s: float):
+def cpu_model() -> str:
+    try:
+        with open("/proc/cpuinfo") as fh:
+            for line in fh:
+                if line.startswith("model name"):
+                    return line.split(":", 1)[1].strip()
+    except OSError:
+        pass
+    return "unknown"
+
+
+def cpu_baseline(wl, budget_s: float, y_gpu=None):
+    """The C oracle, single-threaded, pinned to one core of this host, timed on the
+    whole workload for about budget_s seconds.  Its output is also compared with the
+    GPU's output of the same inputs (y_gpu, bf16 bits) when given."""
     from oracle import oracle as O
+    affinity = sorted(os.sched_getaffinity(0))
+    os.sched_setaffinity(0, {affinity[0]})
     fn = {"ln": lambda: O.layernorm_modulate(wl.x, wl.scale, wl.shift, wl.eps),
           "rms": lambda: O.rmsnorm_scale_shift(wl.x, wl.weight, wl.scale, wl.shift, wl.eps),
           "rg": lambda: O.residual_gate_rmsnorm_scale_shift(wl.res, wl.x, wl.gate, wl.weight,
@@ -305,7 +321,7 @@ def cpu_baseline(wl, budget_s: float):
                                                              wl.shift, wl.eps),
           "lnq": lambda: O.layernorm_modulate_fp8(wl.x, wl.scale, wl.shift, wl.qscale,
                                                   wl.eps)}[wl.op]
-    fn()  # warm (page in the library and the arrays)
+    first = fn()  # warm (page in the library and the arrays)
     reps = 0
     t0 = time.perf_counter()
     while True:
@@ -314,11 +330,28 @@ def cpu_baseline(wl, budget_s: float):
         el = time.perf_counter() - t0
         if el >= budget_s:
             break
-    return {"value": round(wl.algorithmic_bytes() * reps / el / 1e9, 4), "unit": "GB/s",
-            "cores": 1, "kind": "oracle",
-            "rows_per_s": round(wl.x.shape[0] * wl.x.shape[1] * reps / el, 1),
-            "sample": f"the whole workload ({wl.x.shape[0] * wl.x.shape[1]} rows) x {reps} "
-                      f"repetitions, single-threaded C oracle, {el:.1f} s"}
+    os.sched_setaffinity(0, set(affinity))
+    out = {"value": round(wl.algorithmic_bytes() * reps / el / 1e9, 4), "unit": "GB/s",
+           "cores": 1, "kind": "oracle",
+           "rows_per_s": round(wl.x.shape[0] * wl.x.shape[1] * reps / el, 1),
+           "sample": f"the whole workload ({wl.x.shape[0] * wl.x.shape[1]} rows) x {reps} "
+                     f"repetitions, single-threaded C oracle pinned to core {affinity[0]}, "
+                     f"{el:.1f} s",
+           "cpu_model": cpu_model(), "host_cores_available": len(affinity)}
+    if y_gpu is not None:
+        ref = first[-1] if isinstance(first, tuple) else first
+        out["gpu_output_equals_oracle"] = bool(np.array_equal(np.asarray(y_gpu), ref))
+    return out
+
+
+def inputs_sha256(wl) -> dict:
+    """SHA-256 (first 16 hex digits) of every input buffer of a workload."""
+    out = {}
+    for name in ("x", "res", "scale", "shift", "gate", "weight"):
+        a = getattr(wl, name, None)
+        if a is not None:
+            out[name] = hashlib.sha256(np.ascontiguousarray(a).tobytes()).hexdigest()[:16]
+    return out
 
 
 def describe(wl):
@@ -374,6 +407,10 @@ def main():
 
     t = time_steps(L.call, args.steps, args.warmup, args.timing)
     gbps = nbytes * args.steps / t / 1e9
+    # the output of buffer set 0 (every set holds the same inputs), as bits
+    y0 = L.sets[0]["y"]
+    y_gpu = (y0.cpu().numpy() if y0.dtype == torch.uint8
+             else y0.cpu().view(torch.int16).numpy().view(np.uint16))
     ms_per_step = t / args.steps * 1e3
     # average launch duration of the fused kernel: the same events, per launch
     avg_launch_s = t / args.steps
@@ -386,7 +423,8 @@ def main():
         "higher_is_better": True, "scaling": "weak", "vs_baseline": None, "dtype": "f32",
         "data": "synthetic",
         "config": {"workload": describe(wl), "io_dtype": "bf16", "rows": rows,
-                   "bytes_per_step": nbytes, "rotation_sets": L.nsets, "timing": args.timing},
+                   "bytes_per_step": nbytes, "rotation_sets": L.nsets, "timing": args.timing,
+                   "inputs_sha256": inputs_sha256(wl)},
         "pct_of_peak": round(100.0 * gbps / PEAK_HBM_GBPS, 2),
         "rows_per_s": round(rows * args.steps / t, 1),
         "roofline": {"bound": "hbm", "achieved": round(nbytes / avg_launch_s / 1e9, 2),
@@ -429,7 +467,7 @@ def main():
             torch.cuda.empty_cache()
         out["per_workload"] = per
     if not args.no_cpu:
-        cb = cpu_baseline(wl, args.cpu_seconds)
+        cb = cpu_baseline(wl, args.cpu_seconds, y_gpu=y_gpu)
         cb["cores"] = 1
         out["cpu_baseline"] = cb
     print(json.dumps(out), flush=True)

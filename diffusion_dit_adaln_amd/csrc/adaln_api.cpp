@@ -211,6 +211,9 @@ adaln_status validate_cf(const void* res, const void* update, const void* gate, 
     if (B < 0 || T < 0 || H < 0 || (T % 8) != 0 || (H % 8) != 0) return ADALN_ERR_SHAPE;
     if (B == 0 || T == 0 || H == 0) return ADALN_OK;
     if (B > INT64_MAX / T || B * T > INT64_MAX / 2 / H) return ADALN_ERR_SHAPE;
+    // one workgroup of 256 per 64x64 tile, and a grid holds fewer than 2^32 work-items
+    if (B > (int64_t(0xFFFFFFFF) / 256) / (((H + 63) / 64) * ((T + 63) / 64)))
+        return ADALN_ERR_SHAPE;
     *empty = false;
     if (!res || !update || !out) return ADALN_ERR_NULL;
     if (!aligned16(res) || !aligned16(update) || !aligned16(out)) return ADALN_ERR_ALIGN;

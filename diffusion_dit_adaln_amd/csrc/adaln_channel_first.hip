@@ -89,7 +89,8 @@ __global__ __launch_bounds__(256) void residual_gate_cf(CFParams p) {
 
 hipError_t launch_cf(const CFParams& p, hipStream_t stream) {
     const int64_t tiles = p.B * ((p.H + kTile - 1) / kTile) * ((p.T + kTile - 1) / kTile);
-    if (tiles > 0x7FFFFFFF) return hipErrorInvalidValue;
+    // a grid holds fewer than 2^32 work-items
+    if (tiles > int64_t(0xFFFFFFFF) / 256) return hipErrorInvalidValue;
     hipLaunchKernelGGL(residual_gate_cf, dim3((unsigned)tiles), dim3(256), 0, stream, p);
     return hipGetLastError();
 }

@@ -172,6 +172,12 @@ def test_channel_first_checks(lib):
     assert cf_check(lib, out=addr(1)) == OVERLAP         # over update
     assert cf_check(lib, T=4604) == SHAPE
     assert cf_check(lib, H=12) == SHAPE
+    # one 64x64 tile per workgroup of 256: at most 2^24 - 1 tiles in a grid
+    assert cf_check(lib, B=(1 << 24) - 1, T=8, H=8, gbs=0) == OK
+    assert cf_check(lib, B=1 << 24, T=8, H=8, gbs=0) == SHAPE
+    far = dict(res=addr(0), upd=addr(10), out=addr(20), gate=addr(30), gbs=0)  # 137 GB each
+    assert cf_check(lib, B=4854, **far) == OK            # 4854 * 48 * 72 tiles
+    assert cf_check(lib, B=4855, **far) == SHAPE
     assert cf_check(lib, B=0, res=None, upd=None, gate=None, out=None) == OK
     assert cf_check(lib, upd=None) == NULL
     assert cf_check(lib, gate=None) == NULL

@@ -159,8 +159,10 @@ adaln_status validate_qk(const void* q, const void* k, const void* q_weight, con
     if (head_dim != 128) return ADALN_ERR_SHAPE;
     if (tokens < 0 || heads_q < 0 || heads_k < 0) return ADALN_ERR_SHAPE;
     if (!(eps >= 0.0f) || !isfinite(eps)) return ADALN_ERR_VALUE;
+    // a token's row of heads is addressed with 32-bit byte offsets
+    const int64_t max_heads = (int64_t(1) << 23) - 8;
+    if (heads_q > max_heads || heads_k > max_heads) return ADALN_ERR_SHAPE;
     const int64_t lim = INT64_MAX / 4 / 128;
-    if (heads_q > lim || heads_k > lim) return ADALN_ERR_SHAPE;
     if (tokens != 0 && (heads_q + heads_k > lim / tokens)) return ADALN_ERR_SHAPE;
     if (tokens == 0 || heads_q + heads_k == 0) return ADALN_OK;
     *empty = false;

@@ -56,8 +56,9 @@ struct QKParams {
     uint16_t* k_out;           // [tokens, heads_k, 128]
     int64_t tokens, heads_q, heads_k, q_tstride, k_tstride;
     float eps;
-    // set by launch_qk
-    int64_t q_tasks, tasks_per_token, tasks, waves, sg_div, sg_mod;
+    // set by launch_qk: a task is eight heads of Q or of K of one token; waves is a
+    // multiple of tasks_per_token, and wave w takes the tasks w, w + waves, ...
+    int64_t q_tasks, tasks_per_token, waves;
 };
 hipError_t launch_qk(const QKParams& p, hipStream_t stream);
 

@@ -4,21 +4,24 @@
 // one kernel does the Q/K RMS reduction and the RoPE from an fp32 cos/sin cache,
 // head_dim 128, Q/K read through the packed QKV projection's strided views).
 //
-// A head vector (128 bf16, 256 bytes) is owned by 16 lanes, 8 columns each, so a
-// wave processes four heads at a time.  The statistic follows the library's fixed
-// order for H = 128: each lane squares its 8 columns in order, the 16 partials are
-// folded by the butterfly at distances 1, 2, 4, 8 (the lanes past column 128 of the
-// 64-lane layout hold +0 and add nothing).  Then yn = bf16(x * rstd * (w + 0)) with
-// one rounding, and each pair (yn[2i], yn[2i+1]) is rotated by the token's
-// (cos_i, sin_i) in binary32 with every product and sum rounded, then rounded once
-// to bf16.
+// The statistic follows the library's fixed order for H = 128: 16 lanes of the
+// 64-lane layout own 8 columns each (lane t: columns 8t .. 8t+7), square them in
+// order, and fold the 16 partials by the butterfly at distances 1, 2, 4, 8 (lanes
+// past column 128 hold +0 and add nothing).  Here a head is owned by 8 lanes and
+// lane l plays the layout's lanes l and l + 8: it keeps their two partials apart,
+// folds both at distances 1, 2, 4 across the 8 lanes, and adds them in-lane for
+// distance 8, which is the same sum of the same operands.  Then
+// yn = bf16(x * rstd * (w + 0)) with one rounding, and each pair (yn[2i], yn[2i+1])
+// is rotated by the token's (cos_i, sin_i) in binary32 with every product and sum
+// rounded, then rounded once to bf16.
 //
-// Work: a task is four consecutive heads of Q or of K of one token.  Waves walk
-// the tasks interleaved (wave w takes tasks w, w + G, ...) with the next task's
-// loads issued before the current one's arithmetic ends (a ring of S slots); the
-// loads and stores of a pass are unconditional (descriptor ranges drop what lies
-// past the end, and a slot without a task skips its arithmetic), so each slot
-// waits only for its own data.
+// Work: a task is eight consecutive heads of Q or of K of one token, one head per
+// 8-lane group of a wave.  The number of waves is a multiple of the tasks per
+// token and wave w takes the tasks w, w + waves, ..., so a wave always meets the
+// same side and heads (its weights stay in registers) and steps a fixed number of
+// tokens.  The next task's loads are issued when the current one's stores leave;
+// a task past the last token gets empty descriptors (its loads read zero, its
+// stores are dropped), so every pass issues the same memory operations.
 #include <hip/hip_runtime.h>
 #include <stdint.h>
 
@@ -28,162 +31,163 @@
 namespace adaln {
 namespace {
 
-// Tasks in flight per wave (launch tuning; never changes the bits).  Measured on
-// MI355X: one task per wave, with seven waves per SIMD covering the latency, beats
-// deeper rings (1: 4.72 TB/s, 2: 4.57, 3: 4.55, 4: 4.40 on [4608, 24+24, 128]).
 #ifndef ADALN_QK_SLOTS
-#define ADALN_QK_SLOTS 1
+#define ADALN_QK_SLOTS 1  // tasks in flight per wave (launch tuning; never the bits)
 #endif
 constexpr int kQKSlots = ADALN_QK_SLOTS;
-#ifndef ADALN_QK_OVERSUB
-#define ADALN_QK_OVERSUB 1  // waves per resident wave slot
-#endif
 
 __global__ __launch_bounds__(256) void qk_rmsnorm_rope(QKParams p) {
     constexpr int D = 128;
     const int lane = threadIdx.x & 63;
-    const int grp = lane >> 4;  // head within the task
-    const int l = lane & 15;    // lane within the head: columns 8l .. 8l+7
+    const int grp = lane >> 3;  // head within the task
+    const int l = lane & 7;     // columns 8l .. 8l+7 (chunk A) and 64+8l .. 64+8l+7 (B)
     const int64_t wave = (int64_t)blockIdx.x * 4 + __builtin_amdgcn_readfirstlane(threadIdx.x >> 6);
     if (wave >= p.waves) return;
-    const int64_t G = p.waves;
 
-    // weights of Q and K for this lane's 8 columns, (w + 0.0) applied
-    float wq[8], wk[8];
+    // the wave's side and heads (uniform)
+    const int64_t j = wave % p.tasks_per_token;
+    const bool is_q = j < p.q_tasks;
+    const int64_t head0 = 8 * (is_q ? j : j - p.q_tasks);
+    const int64_t heads = is_q ? p.heads_q : p.heads_k;
+    const uint16_t* in = is_q ? p.q : p.k;
+    const int64_t in_tstride = is_q ? p.q_tstride : p.k_tstride;
+    uint16_t* out = is_q ? p.q_out : p.k_out;
+    const uint16_t* wp = is_q ? p.q_weight : p.k_weight;
+    const int64_t tok_step = p.waves / p.tasks_per_token;
+
+    // (w + 0.0) of the lane's 16 columns
+    float w[16];
     {
         uint4 a = make_uint4(0x3F803F80u, 0x3F803F80u, 0x3F803F80u, 0x3F803F80u), b = a;  // 1.0
-        if (p.q_weight) a = ld16(p.q_weight + 8 * l);
-        if (p.k_weight) b = ld16(p.k_weight + 8 * l);
+        if (wp) {
+            a = ld16(wp + 8 * l);
+            b = ld16(wp + 64 + 8 * l);
+        }
 #pragma unroll
-        for (int j = 0; j < 4; ++j) {
-            wq[2 * j] = bf_lo(word(a, j)) + 0.0f;
-            wq[2 * j + 1] = bf_hi(word(a, j)) + 0.0f;
-            wk[2 * j] = bf_lo(word(b, j)) + 0.0f;
-            wk[2 * j + 1] = bf_hi(word(b, j)) + 0.0f;
+        for (int i = 0; i < 4; ++i) {
+            w[2 * i] = bf_lo(word(a, i)) + 0.0f;
+            w[2 * i + 1] = bf_hi(word(a, i)) + 0.0f;
+            w[8 + 2 * i] = bf_lo(word(b, i)) + 0.0f;
+            w[8 + 2 * i + 1] = bf_hi(word(b, i)) + 0.0f;
         }
     }
 
-    // task id = token * tasks_per_token + j; tasks j < q_tasks are Q heads 4j..4j+3,
-    // the rest K heads.  A slot tracks (token, j) of its task; stepping S*G tasks
-    // ahead adds the host's quotient and remainder of S*G by tasks_per_token, so
-    // the loop divides nothing.  All uniform over the wave.
-    struct Task {
-        int64_t token;
-        bool is_q;
-        int64_t head0;
+    // the lane's byte offset in a token's row of heads (chunk B 128 bytes further);
+    // heads past the count land past the descriptor's range
+    const int off = (int)((head0 + grp) * D * 2) + 16 * l;
+    const int in_bytes = (int)(heads * D * 2);
+    auto in_rsrc = [&](int64_t t) {
+        return t < p.tokens ? make_rsrc(in + t * in_tstride, in_bytes) : make_rsrc(in, 0);
     };
-    auto task_at = [&](int64_t tok, int64_t j) {
-        const bool q = j < p.q_tasks;
-        return Task{tok, q, 4 * (q ? j : j - p.q_tasks)};
+    auto out_rsrc = [&](int64_t t) {
+        return t < p.tokens ? make_rsrc(out + t * heads * D, in_bytes) : make_rsrc(out, 0);
     };
-    // descriptors: the task's input heads, its output heads, the token's cache row;
-    // a task past the end gets empty ones (its token and head then do not matter)
-    auto in_rsrc = [&](int64_t id, const Task& t) {
-        if (id >= p.tasks) return make_rsrc(p.q, 0);
-        const uint16_t* base = t.is_q ? p.q + t.token * p.q_tstride : p.k + t.token * p.k_tstride;
-        return make_rsrc(base, (t.is_q ? p.heads_q : p.heads_k) * D * 2);
+    auto cs_rsrc = [&](int64_t t) {
+        return t < p.tokens ? make_rsrc(p.cos_sin + t * D, D * 4) : make_rsrc(p.cos_sin, 0);
     };
-    auto out_rsrc = [&](int64_t id, const Task& t) {
-        if (id >= p.tasks) return make_rsrc(p.q_out, 0);
-        const int64_t h = t.is_q ? p.heads_q : p.heads_k;
-        uint16_t* base = (t.is_q ? p.q_out : p.k_out) + t.token * h * D;
-        return make_rsrc(base, h * D * 2);
-    };
-    auto cs_rsrc = [&](int64_t id, const Task& t) {
-        if (id >= p.tasks) return make_rsrc(p.cos_sin, 0);
-        return make_rsrc(p.cos_sin + t.token * D, D * 4);
-    };
-    // the lane's offset inside its head's row (heads past the count land out of range)
-    auto head_off = [&](const Task& t) { return (int)((t.head0 + grp) * D * 2) + 16 * l; };
 
     struct Slot {
-        uint4 x, c, s;
+        uint4 xa, xb, ca, cb, sa, sb;
     };
-    auto load_task = [&](int64_t id, const Task& t, Slot& sl) {
-        sl.x = ld16_stream(in_rsrc(id, t), head_off(t));
-        const rsrc_t rc = cs_rsrc(id, t);
-        sl.c = ld16_stream(rc, 16 * l);           // cos[4l .. 4l+3]
-        sl.s = ld16_stream(rc, D * 2 + 16 * l);   // sin[4l .. 4l+3]
+    auto load_task = [&](int64_t t, Slot& sl) {
+        const rsrc_t ri = in_rsrc(t);
+        sl.xa = ld16_stream(ri, off);
+        sl.xb = ld16_stream(ri, off + 128);
+        const rsrc_t rc = cs_rsrc(t);
+        sl.ca = ld16_stream(rc, 16 * l);        // cos of pairs 4l .. 4l+3
+        sl.cb = ld16_stream(rc, 128 + 16 * l);  // cos of pairs 32+4l .. 32+4l+3
+        sl.sa = ld16_stream(rc, 256 + 16 * l);  // sin, likewise
+        sl.sb = ld16_stream(rc, 384 + 16 * l);
     };
 
     const rsrc_t r_none = make_rsrc(p.q_out, 0);
     constexpr int S = kQKSlots;
     Slot ring[S];
-    int64_t tok[S], jj[S];
+    const int64_t tok0 = wave / p.tasks_per_token;
 #pragma unroll
     for (int k = 0; k < S; ++k) {
-        const int64_t id = wave + k * G;
-        tok[k] = id / p.tasks_per_token;
-        jj[k] = id - tok[k] * p.tasks_per_token;
-        if (k > 0) st16_stream(r_none, kOutOfRange, make_uint4(0u, 0u, 0u, 0u));
-        load_task(id, task_at(tok[k], jj[k]), ring[k]);
+        if (k > 0) {  // stand-ins for the previous slot's stores (dropped)
+            st16_stream(r_none, kOutOfRange, make_uint4(0u, 0u, 0u, 0u));
+            st16_stream(r_none, kOutOfRange - 16, make_uint4(0u, 0u, 0u, 0u));
+        }
+        load_task(tok0 + k * tok_step, ring[k]);
     }
 
-    for (int64_t id0 = wave; id0 < p.tasks; id0 += S * G) {
+    // rotate one 8-column chunk: x (bf16 pairs), its 4 cos and 4 sin, weights w8
+    auto chunk = [&](const uint4& xv, const uint4& cv, const uint4& sv, const float* w8,
+                     float rstd) {
+        const float c4[4] = {__uint_as_float(cv.x), __uint_as_float(cv.y),
+                             __uint_as_float(cv.z), __uint_as_float(cv.w)};
+        const float s4[4] = {__uint_as_float(sv.x), __uint_as_float(sv.y),
+                             __uint_as_float(sv.z), __uint_as_float(sv.w)};
+        u32 o[4];
+#pragma unroll
+        for (int i = 0; i < 4; ++i) {
+            const float n0 = bf_lo(word(xv, i)) * rstd, n1 = bf_hi(word(xv, i)) * rstd;
+            const float a = round_bf16(n0 * w8[2 * i]), b = round_bf16(n1 * w8[2 * i + 1]);
+            const float ac = a * c4[i], bs = b * s4[i], bc = b * c4[i], as = a * s4[i];
+            const float o1 = ac - bs;
+            const float o2 = bc + as;
+            o[i] = pack_bf16(o1, o2);
+        }
+        return make_uint4(o[0], o[1], o[2], o[3]);
+    };
+
+    for (int64_t t0 = tok0; t0 < p.tokens; t0 += S * tok_step) {
 #pragma unroll
         for (int k = 0; k < S; ++k) {
-            const int64_t id = id0 + k * G;
+            const int64_t t = t0 + k * tok_step;
             Slot& sl = ring[k];
-            const Task t = task_at(tok[k], jj[k]);
-
             // the arithmetic only for a real task (uniform branch, no memory operation
-            // inside); the store below is issued either way
-            u32 out[4] = {0u, 0u, 0u, 0u};
-            if (id < p.tasks) {
-            float x[8];
+            // inside); the stores below are issued either way
+            uint4 oa = make_uint4(0u, 0u, 0u, 0u), ob = oa;
+            if (t < p.tokens) {
+                // ordered squares of the two chunks, each chunk's partial folded at
+                // distances 1, 2, 4 over the head's 8 lanes, then the two added
+                float sa = 0.0f, sb = 0.0f;
 #pragma unroll
-            for (int j = 0; j < 4; ++j) {
-                x[2 * j] = bf_lo(word(sl.x, j));
-                x[2 * j + 1] = bf_hi(word(sl.x, j));
-            }
-            // ordered per-lane sum of squares, butterfly over the head's 16 lanes
-            float sum = 0.0f;
+                for (int i = 0; i < 4; ++i) {
+                    const float a0 = bf_lo(word(sl.xa, i)), a1 = bf_hi(word(sl.xa, i));
+                    const float q0 = a0 * a0;
+                    sa = sa + q0;
+                    const float q1 = a1 * a1;
+                    sa = sa + q1;
+                }
 #pragma unroll
-            for (int v = 0; v < 8; ++v) {
-                const float q = x[v] * x[v];
-                sum = sum + q;
+                for (int i = 0; i < 4; ++i) {
+                    const float b0 = bf_lo(word(sl.xb, i)), b1 = bf_hi(word(sl.xb, i));
+                    const float q0 = b0 * b0;
+                    sb = sb + q0;
+                    const float q1 = b1 * b1;
+                    sb = sb + q1;
+                }
+                sa = sa + dpp<DPP_XOR1>(sa);
+                sb = sb + dpp<DPP_XOR1>(sb);
+                sa = sa + dpp<DPP_XOR2>(sa);
+                sb = sb + dpp<DPP_XOR2>(sb);
+                sa = sa + dpp<DPP_HALF_MIRROR>(sa);
+                sb = sb + dpp<DPP_HALF_MIRROR>(sb);
+                const float sum = sa + sb;
+                const float rstd = finalize(sum / (float)D, p.eps);
+                oa = chunk(sl.xa, sl.ca, sl.sa, w, rstd);
+                ob = chunk(sl.xb, sl.cb, sl.sb, w + 8, rstd);
             }
-            sum = sum + dpp<DPP_XOR1>(sum);
-            sum = sum + dpp<DPP_XOR2>(sum);
-            sum = sum + dpp<DPP_HALF_MIRROR>(sum);
-            sum = sum + dpp<DPP_MIRROR>(sum);
-            const float rstd = finalize(sum / (float)D, p.eps);
-
-            const float c4[4] = {__uint_as_float(sl.c.x), __uint_as_float(sl.c.y),
-                                 __uint_as_float(sl.c.z), __uint_as_float(sl.c.w)};
-            const float s4[4] = {__uint_as_float(sl.s.x), __uint_as_float(sl.s.y),
-                                 __uint_as_float(sl.s.z), __uint_as_float(sl.s.w)};
-#pragma unroll
-            for (int j = 0; j < 4; ++j) {
-                const float w0 = t.is_q ? wq[2 * j] : wk[2 * j];
-                const float w1 = t.is_q ? wq[2 * j + 1] : wk[2 * j + 1];
-                const float n0 = x[2 * j] * rstd, n1 = x[2 * j + 1] * rstd;
-                const float a = round_bf16(n0 * w0), b = round_bf16(n1 * w1);  // yn pair
-                const float ac = a * c4[j], bs = b * s4[j], bc = b * c4[j], as = a * s4[j];
-                const float o1 = ac - bs;
-                const float o2 = bc + as;
-                out[j] = pack_bf16(o1, o2);
-            }
-            }  // id < tasks
-            st16_stream(out_rsrc(id, t), head_off(t), make_uint4(out[0], out[1], out[2], out[3]));
-
-            // the slot's task S*G ahead
-            tok[k] += p.sg_div;
-            jj[k] += p.sg_mod;
-            if (jj[k] >= p.tasks_per_token) {
-                jj[k] -= p.tasks_per_token;
-                tok[k] += 1;
-            }
-            load_task(id + S * G, task_at(tok[k], jj[k]), sl);
+            const rsrc_t ro = out_rsrc(t);
+            st16_stream(ro, off, oa);
+            st16_stream(ro, off + 128, ob);
+            load_task(t + S * tok_step, sl);
         }
     }
-    // never true (tasks > 0): keeps the ring's last loads inside the loop
-    if (p.tasks < 0) {
+    // never true (tokens > 0): keeps the ring's last loads inside the loop
+    if (p.tokens < 0) {
 #pragma unroll
         for (int k = 0; k < S; ++k) {
-            st16_stream(r_none, kOutOfRange, ring[k].x);
-            st16_stream(r_none, kOutOfRange, ring[k].c);
-            st16_stream(r_none, kOutOfRange, ring[k].s);
+            st16_stream(r_none, kOutOfRange, ring[k].xa);
+            st16_stream(r_none, kOutOfRange, ring[k].xb);
+            st16_stream(r_none, kOutOfRange, ring[k].ca);
+            st16_stream(r_none, kOutOfRange, ring[k].cb);
+            st16_stream(r_none, kOutOfRange, ring[k].sa);
+            st16_stream(r_none, kOutOfRange, ring[k].sb);
         }
     }
 }
@@ -192,19 +196,20 @@ __global__ __launch_bounds__(256) void qk_rmsnorm_rope(QKParams p) {
 
 hipError_t launch_qk(const QKParams& p_in, hipStream_t stream) {
     QKParams p = p_in;
-    p.q_tasks = (p.heads_q + 3) / 4;
-    p.tasks_per_token = p.q_tasks + (p.heads_k + 3) / 4;
-    p.tasks = p.tokens * p.tasks_per_token;
-    // resident waves, one per task at most
+    p.q_tasks = (p.heads_q + 7) / 8;
+    p.tasks_per_token = p.q_tasks + (p.heads_k + 7) / 8;
+    const int64_t tasks = p.tokens * p.tasks_per_token;
     int blocks_per_cu = 0, cus = 0;
     if (!occupancy(reinterpret_cast<const void*>(qk_rmsnorm_rope), 256, &blocks_per_cu, &cus))
         return hipErrorInvalidDeviceFunction;
-    const int64_t slots = (int64_t)blocks_per_cu * cus * 4 * ADALN_QK_OVERSUB;
-    p.waves = p.tasks < slots ? p.tasks : slots;
-    const int64_t sg = (int64_t)kQKSlots * p.waves;
-    p.sg_div = sg / p.tasks_per_token;
-    p.sg_mod = sg % p.tasks_per_token;
+    // as many waves as fit at once (at most one per task), a multiple of the tasks
+    // per token; at least one wave per task of a token
+    const int64_t slots = (int64_t)blocks_per_cu * cus * 4;
+    const int64_t fit = tasks < slots ? tasks : slots;
+    p.waves = fit / p.tasks_per_token * p.tasks_per_token;
+    if (p.waves < p.tasks_per_token) p.waves = p.tasks_per_token;
     const int64_t blocks = (p.waves + 3) / 4;
+    if (blocks > 0x7FFFFFFF) return hipErrorInvalidValue;
     hipLaunchKernelGGL(qk_rmsnorm_rope, dim3((unsigned)blocks), dim3(256), 0, stream, p);
     return hipGetLastError();
 }

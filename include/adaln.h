@@ -168,8 +168,9 @@ adaln_status adaln_layernorm_modulate_fp8_quant(const adaln_bf16* x, const adaln
  * contiguous, token stride >= heads_q*128 and % 8 == 0 when tokens > 1); K likewise;
  * cos_sin fp32 [tokens, 128] contiguous (cos of the 64 pairs, then their sin);
  * q_out [tokens, heads_q, 128] and k_out [tokens, heads_k, 128] contiguous; weights
- * [128] bf16 or NULL (one).  head_dim other than 128 is ADALN_ERR_SHAPE; heads_q or
- * heads_k may be 0 (that tensor's pointers are then unused). */
+ * [128] bf16 or NULL (one).  head_dim other than 128, or more than 2^23 - 8 heads
+ * on a side, is ADALN_ERR_SHAPE; heads_q or heads_k may be 0 (that tensor's pointers
+ * are then unused). */
 adaln_status adaln_qk_rmsnorm_rope(const adaln_bf16* q, const adaln_bf16* k,
                                    const adaln_bf16* q_weight, const adaln_bf16* k_weight,
                                    const float* cos_sin, adaln_bf16* q_out, adaln_bf16* k_out,

@@ -150,6 +150,11 @@ def test_qk_checks(lib):
     assert qk_check(lib, kts=3 * 3072 + 4) == STRIDE     # not % 8
     assert qk_check(lib, T=1, qts=0, kts=0) == OK        # stride unused for one token
     assert qk_check(lib, eps=float("nan")) == VALUE
+    # a token's heads are addressed with 32-bit byte offsets: at most 2^23 - 8 heads
+    big = (1 << 23) - 8
+    assert qk_check(lib, T=1, hq=big, hk=0, k=None, ko=None, qts=0) == OK
+    assert qk_check(lib, T=1, hq=big + 1, hk=0, k=None, ko=None, qts=0) == SHAPE
+    assert qk_check(lib, T=1, hq=0, hk=big + 1, q=None, qo=None, kts=0) == SHAPE
     assert qk_check(lib, qo=addr(0)) == OVERLAP          # output over the packed input
     assert qk_check(lib, ko=addr(4) + 16) == OVERLAP     # q_out and k_out overlap
     assert qk_check(lib, qo=addr(3) - 16) == OVERLAP     # runs into the cache

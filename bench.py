@@ -320,7 +320,10 @@ def cpu_baseline(wl, budget_s: float, y_gpu=None):
           "rgln": lambda: O.residual_gate_layernorm_modulate(wl.res, wl.x, wl.gate, wl.scale,
                                                              wl.shift, wl.eps),
           "lnq": lambda: O.layernorm_modulate_fp8(wl.x, wl.scale, wl.shift, wl.qscale,
-                                                  wl.eps)}[wl.op]
+                                                  wl.eps),
+          "qk": lambda: O.qk_rmsnorm_rope(wl.q, wl.k, wl.q_weight, wl.k_weight, wl.cos_sin,
+                                          wl.eps),
+          "cf": lambda: O.residual_gate_channel_first(wl.res, wl.update, wl.gate)}[wl.op]
     first = fn()  # warm (page in the library and the arrays)
     reps = 0
     t0 = time.perf_counter()
@@ -333,21 +336,41 @@ def cpu_baseline(wl, budget_s: float, y_gpu=None):
     os.sched_setaffinity(0, set(affinity))
     out = {"value": round(wl.algorithmic_bytes() * reps / el / 1e9, 4), "unit": "GB/s",
            "cores": 1, "kind": "oracle",
-           "rows_per_s": round(wl.x.shape[0] * wl.x.shape[1] * reps / el, 1),
-           "sample": f"the whole workload ({wl.x.shape[0] * wl.x.shape[1]} rows) x {reps} "
+           "rows_per_s": round(workload_rows(wl) * reps / el, 1),
+           "sample": f"the whole workload ({workload_rows(wl)} rows) x {reps} "
                      f"repetitions, single-threaded C oracle pinned to core {affinity[0]}, "
                      f"{el:.1f} s",
            "cpu_model": cpu_model(), "host_cores_available": len(affinity)}
     if y_gpu is not None:
-        ref = first[-1] if isinstance(first, tuple) else first
-        out["gpu_output_equals_oracle"] = bool(np.array_equal(np.asarray(y_gpu), ref))
+        # the fused ops' y (the last of r, y); QK's (q_out, k_out); channel-first's out
+        if wl.op == "qk":
+            ref = list(first)
+        else:
+            ref = [first[-1] if isinstance(first, tuple) else first]
+        out["gpu_output_equals_oracle"] = bool(
+            len(ref) == len(y_gpu) and all(np.array_equal(np.asarray(g), r)
+                                           for g, r in zip(y_gpu, ref)))
     return out
+
+
+KERNEL_OF = {"qk": "qk_rmsnorm_rope", "cf": "residual_gate_cf"}
+
+
+def workload_rows(wl) -> int:
+    """Rows of a workload: B*T for the fused ops, head vectors for QK (tokens x
+    (heads of Q + heads of K)), tokens (B*T) for the channel-first residual gate."""
+    if wl.op == "qk":
+        return wl.qkv.shape[0] * 2 * wl.qkv.shape[2]
+    if wl.op == "cf":
+        return wl.res.shape[0] * wl.res.shape[2]
+    return wl.x.shape[0] * wl.x.shape[1]
 
 
 def inputs_sha256(wl) -> dict:
     """SHA-256 (first 16 hex digits) of every input buffer of a workload."""
     out = {}
-    for name in ("x", "res", "scale", "shift", "gate", "weight"):
+    for name in ("x", "res", "scale", "shift", "gate", "weight", "qkv", "q_weight", "k_weight",
+                 "cos_sin", "update"):
         a = getattr(wl, name, None)
         if a is not None:
             out[name] = hashlib.sha256(np.ascontiguousarray(a).tobytes()).hexdigest()[:16]
@@ -355,6 +378,14 @@ def inputs_sha256(wl) -> dict:
 
 
 def describe(wl):
+    if wl.op == "qk":
+        T, _, Hd, D = wl.qkv.shape
+        return (f"qk_rmsnorm_rope bf16 q, k [{T},{Hd},{D}] as views of packed qkv "
+                f"[{T},3,{Hd},{D}], weights 1+0.02N, fp32 cos/sin cache, eps 1e-6")
+    if wl.op == "cf":
+        B, H, T = wl.res.shape
+        return (f"residual_gate_channel_first bf16 res/out [{B},{H},{T}], "
+                f"update [{B},{T},{H}], gate [{B},{H}]")
     B, T, H = wl.x.shape
     name = {"ln": "layernorm_modulate", "rms": "rmsnorm_scale_shift",
             "rg": "residual_gate_rmsnorm_scale_shift",
@@ -370,7 +401,8 @@ def main():
     ap.add_argument("--gpus", type=int, default=1)
     ap.add_argument("--steps", type=int, default=400)
     ap.add_argument("--warmup", type=int, default=40)
-    ap.add_argument("--config", default="1", choices=["0", "1", "2", "3a", "3b", "5", "6"])
+    ap.add_argument("--config", default="1",
+                    choices=["0", "1", "2", "3a", "3b", "5", "6", "7", "8"])
     ap.add_argument("--timing", default="graph", choices=["graph", "eager"])
     ap.add_argument("--rotate-mb", type=int, default=1024)
     ap.add_argument("--cpu-seconds", type=float, default=10.0)
@@ -401,16 +433,17 @@ def main():
                           "read_bytes": wl.algorithmic_bytes() // 2,
                           "write_bytes": wl.algorithmic_bytes() // 2}), flush=True)
         return
-    L = Launcher(wl, rotate)
+    L = launcher_for(wl, rotate)
     nbytes = wl.algorithmic_bytes()
-    rows = wl.x.shape[0] * wl.x.shape[1]
+    rows = workload_rows(wl)
 
     t = time_steps(L.call, args.steps, args.warmup, args.timing)
     gbps = nbytes * args.steps / t / 1e9
-    # the output of buffer set 0 (every set holds the same inputs), as bits
-    y0 = L.sets[0]["y"]
-    y_gpu = (y0.cpu().numpy() if y0.dtype == torch.uint8
-             else y0.cpu().view(torch.int16).numpy().view(np.uint16))
+    # the outputs of buffer set 0 (every set holds the same inputs), as bits
+    def bits(t):
+        return t.cpu().numpy() if t.dtype == torch.uint8 else t.cpu().view(torch.int16).numpy().view(np.uint16)
+    s0 = L.sets[0]
+    y_gpu = [bits(s0[k]) for k in ("y", "qo", "ko", "out") if k in s0]
     ms_per_step = t / args.steps * 1e3
     # average launch duration of the fused kernel: the same events, per launch
     avg_launch_s = t / args.steps
@@ -430,7 +463,7 @@ def main():
         "roofline": {"bound": "hbm", "achieved": round(nbytes / avg_launch_s / 1e9, 2),
                      "peak": PEAK_HBM_GBPS, "unit": "GB/s",
                      "frac": round(nbytes / avg_launch_s / 1e9 / PEAK_HBM_GBPS, 4),
-                     "traffic": traffic, "kernel": f"fused_norm_modulate ({wl.op})",
+                     "traffic": traffic, "kernel": KERNEL_OF.get(wl.op, f"fused_norm_modulate ({wl.op})"),
                      "avg_launch_us": round(avg_launch_s * 1e6, 3)},
     }
     del L
@@ -457,9 +490,7 @@ def main():
             cc = median3(lambda: copy_ceiling(nb2, rotate, steps, args.warmup))
             shape = list({"qk": lambda: w2.qkv.shape, "cf": lambda: w2.res.shape}.get(
                 w2.op, lambda: w2.x.shape)())
-            # rows: head vectors (qk), tokens (cf: B*T), else B*T
-            rows2 = {"qk": shape[0] * 2 * shape[2], "cf": shape[0] * shape[2]}.get(
-                w2.op, shape[0] * shape[1])
+            rows2 = workload_rows(w2)
             per[w2.name] = {"op": w2.op, "shape": shape, "bytes": nb2, **res,
                             "rows_per_s": round(rows2 / res["graph"]["us_per_launch"] * 1e6, 1),
                             "copy_ceiling_GBps": round(cc, 2),

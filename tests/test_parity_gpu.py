@@ -177,6 +177,29 @@ def test_edge_hidden_sizes(H):
         check_lnq(x, sc, sh, qs, f"lnq H={H} qscale={qs}")
 
 
+def _all_rows(alphabet, H, stride=1):
+    a = synth.f32_to_bf16_bits(np.array(alphabet, np.float32))
+    idx = np.indices((len(a),) * H).reshape(H, -1).T[::stride]
+    return np.ascontiguousarray(a[idx])
+
+
+# Brute force over small alphabets: every row of 8 values from six letters
+# (1.68 M rows, the oracle's own brute-force pin), and every 27th row of 16 values
+# from {-1, 0, 1} (1.59 M rows: ties, cancellations, zero rows, one-hot rows).
+@pytest.mark.parametrize("H,alphabet,stride", [(8, [0.0, 0.5, -1.0, 2.0, -3.0, 0.0625], 1),
+                                               (16, [-1.0, 0.0, 1.0], 27)])
+def test_brute_force_rows(H, alphabet, stride):
+    x = _all_rows(alphabet, H, stride)[None]
+    say(f"[parity] brute force H={H} rows={x.shape[1]}")
+    rng = np.random.default_rng(H)
+    sc = synth.normal_bf16(rng, (1, H), 0.1)
+    sh = synth.normal_bf16(rng, (1, H), 0.1)
+    w = synth.normal_bf16(rng, (H,), 0.02, 1.0)
+    assert_bits_equal(run_ln(x, sc, sh), O.layernorm_modulate(x, sc, sh, EPS), f"ln H={H}")
+    assert_bits_equal(run_rms(x, w, sc, sh), O.rmsnorm_scale_shift(x, w, sc, sh, EPS),
+                      f"rms H={H}")
+
+
 # Row counts large enough that the interleaved ops take their one-slot ring (at
 # least three rows per resident row group), for one-, two- and four-wave rows with
 # and without a ragged last chunk.

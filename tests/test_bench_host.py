@@ -1,0 +1,90 @@
+"""Host-side logic of bench.py (CPU only): the one-GPU guard, workload sizes and
+algorithmic bytes, the kernel-source hash that keys the committed counters, and the
+counter summary being used only while that hash matches."""
+import os
+import subprocess
+import sys
+
+import numpy as np
+import pytest
+
+import bench
+
+ROOT = os.path.dirname(os.path.dirname(os.path.abspath(__file__)))
+
+
+def test_more_than_one_gpu_is_refused():
+    r = subprocess.run([sys.executable, os.path.join(ROOT, "bench.py"), "--gpus", "2"],
+                       capture_output=True, text=True, timeout=120)
+    assert r.returncode == 2
+    assert "one GPU" in r.stderr and r.stdout == ""
+
+
+@pytest.mark.parametrize("cfg,op,rows,nbytes", [
+    ("0", "ln", 128, 4 * 128 * 2048),
+    ("1", "rms", 4216, 4 * 4216 * 4096),
+    ("2", "rg", 2280, 8 * 2280 * 4096),
+    ("3a", "ln", 9216, 4 * 9216 * 3072),
+    ("3b", "ln", 4333, 4 * 4333 * 3072),
+    ("5", "rgln", 8192, 8 * 8192 * 3072),
+    ("6", "lnq", 9216, 3 * 9216 * 3072),
+    ("7", "qk", 4608 * 48, 8 * 4608 * 24 * 128 + 4 * 4608 * 128),
+    ("8", "cf", 9216, 6 * 2 * 3072 * 4608),
+])
+def test_workload_sizes(cfg, op, rows, nbytes):
+    wl = bench.workload(cfg)
+    assert wl.op == op
+    assert bench.workload_rows(wl) == rows
+    assert wl.algorithmic_bytes() == nbytes
+    assert bench.describe(wl)
+    sha = bench.inputs_sha256(wl)
+    assert sha and all(len(v) == 16 for v in sha.values())
+
+
+def test_headline_config_is_the_rms_workload():
+    wl = bench.workload("1")
+    assert wl.x.shape == (1, 4216, 4096) and wl.weight is not None
+    assert wl.algorithmic_bytes() == 69074944
+
+
+def test_inputs_are_seeded():
+    a = bench.inputs_sha256(bench.workload("2"))
+    b = bench.inputs_sha256(bench.workload("2"))
+    assert a == b
+
+
+def test_kernel_hash_ignores_comments_and_blank_space(tmp_path, monkeypatch):
+    src = tmp_path / "k.hip"
+    src.write_text("int f(int a) {\n  return a + 1; // one\n}\n/* block\n comment */\n")
+    monkeypatch.setattr(bench, "KERNEL_SRCS", [str(src)])
+    h0 = bench.kernel_src_sha()
+    src.write_text("int f(int a) {   return a + 1; // other words\n}\n\n\n")
+    assert bench.kernel_src_sha() == h0
+    src.write_text("int f(int a) { return a + 2; }\n")
+    assert bench.kernel_src_sha() != h0
+
+
+def test_counters_used_only_for_the_same_kernel_source(tmp_path, monkeypatch):
+    (tmp_path / "profiles").mkdir()
+    monkeypatch.setattr(bench, "ROOT", str(tmp_path))
+    assert bench.load_counters("w") is None                      # no summary
+    f = tmp_path / "profiles" / "counters_w.txt"
+    f.write_text(f"# note = ignored\nkernel_src_sha = {bench.kernel_src_sha()}\n"
+                 "traffic_bytes_per_dispatch = 12345\n")
+    assert bench.load_counters("w") == 12345.0
+    f.write_text("kernel_src_sha = 0000000000000000\ntraffic_bytes_per_dispatch = 12345\n")
+    assert bench.load_counters("w") is None                      # another source
+
+
+def test_cpu_baseline_on_a_small_workload():
+    wl = bench.workload("0")
+    out = bench.cpu_baseline(wl, 0.05)
+    assert out["kind"] == "oracle" and out["cores"] == 1 and out["value"] > 0
+    assert out["unit"] == "GB/s" and "pinned to core" in out["sample"]
+    # the comparison with a GPU output of the same inputs (here the oracle's own bits)
+    from oracle import oracle as O
+    y = O.layernorm_modulate(wl.x, wl.scale, wl.shift, wl.eps)
+    assert bench.cpu_baseline(wl, 0.01, y_gpu=[y])["gpu_output_equals_oracle"] is True
+    y2 = y.copy()
+    y2.flat[0] ^= 1
+    assert bench.cpu_baseline(wl, 0.01, y_gpu=[y2])["gpu_output_equals_oracle"] is False

@@ -409,6 +409,26 @@ def test_qk_shapes(T, heads):
         check_qk(qkv, wq, wk, cs, f"qk T={T} heads={heads} fewer k heads", hk=heads - 1)
 
 
+# Q and K head counts that give one to several eight-head tasks per side, an odd
+# number of tasks per token, one side absent, and token counts below and far above
+# one task per resident wave (waves then step over many tokens).
+@pytest.mark.parametrize("T,hq,hk", [(7, 24, 8), (600, 24, 8), (20000, 24, 8), (9000, 20, 12),
+                                     (5000, 33, 1), (3000, 0, 5), (3000, 7, 0), (1, 64, 64)])
+def test_qk_task_mapping(T, hq, hk):
+    say(f"[parity] qk tasks T={T} hq={hq} hk={hk}")
+    rng = np.random.default_rng(T + 7 * hq + hk)
+    q = synth.normal_bf16(rng, (T, hq, 128))
+    k = synth.normal_bf16(rng, (T, hk, 128))
+    wq = synth.normal_bf16(rng, (128,), 0.02, 1.0)
+    wk = synth.normal_bf16(rng, (128,), 0.02, 1.0)
+    cs = synth.rope_cache(T, 128)
+    qo, ko = A.adaln_qk_rmsnorm_rope(dev(q), dev(k), dev(wq), dev(wk), torch.from_numpy(cs).cuda(),
+                                     EPS)
+    qo0, ko0 = O.qk_rmsnorm_rope(q, k, wq, wk, cs, EPS)
+    assert_bits_equal(host(qo), qo0, "q")
+    assert_bits_equal(host(ko), ko0, "k")
+
+
 @pytest.mark.parametrize("eps", [0.0, 1e-5, 0.25])
 def test_qk_eps_and_special_rows(eps):
     say(f"[parity] qk eps={eps}")

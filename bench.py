@@ -71,12 +71,15 @@ def load_counters(name: str):
 # ---------------------------------------------------------------------------
 # workloads
 # ---------------------------------------------------------------------------
-def workload(cfg: str):
+HEADLINE = "rms_1x4216x4096"
+WORKLOAD_NAMES = ["ln_1x128x2048", "rms_1x4216x4096", "rg_rms_2x1140x4096", "ln_2x4608x3072",
+                  "ln_1x4333x3072", "rg_ln_2x4096x3072", "ln_fp8_2x4608x3072",
+                  "qk_rmsnorm_rope_4608x24x128", "rg_channel_first_2x3072x4608"]
+
+
+def workload(name: str):
     from diffusion_dit_adaln_amd import synth
-    return {"0": synth.config0, "1": synth.config1, "2": synth.config2,
-            "3a": lambda: synth.config3(site="a"), "3b": lambda: synth.config3(site="b"),
-            "5": synth.config5, "6": synth.config6, "7": synth.config7,
-            "8": synth.config8}[cfg]()
+    return synth.WORKLOADS[name]()
 
 
 class Launcher:
@@ -401,8 +404,8 @@ def main():
     ap.add_argument("--gpus", type=int, default=1)
     ap.add_argument("--steps", type=int, default=400)
     ap.add_argument("--warmup", type=int, default=40)
-    ap.add_argument("--config", default="1",
-                    choices=["0", "1", "2", "3a", "3b", "5", "6", "7", "8"])
+    ap.add_argument("--workload", default=HEADLINE, choices=WORKLOAD_NAMES,
+                    help="the workload of the timed line (default: the headline RMS one)")
     ap.add_argument("--timing", default="graph", choices=["graph", "eager"])
     ap.add_argument("--rotate-mb", type=int, default=1024)
     ap.add_argument("--cpu-seconds", type=float, default=10.0)
@@ -425,7 +428,7 @@ def main():
         sys.exit(2)
 
     rotate = args.rotate_mb << 20
-    wl = workload(args.config)
+    wl = workload(args.workload)
     if args.copy_only:
         g = copy_ceiling(wl.algorithmic_bytes(), rotate, args.steps, args.warmup, args.timing)
         # (the library's streaming copy kernel, diag_copy: known bytes for counter scaling)
@@ -476,8 +479,8 @@ def main():
             lambda: copy_ceiling(nbytes, rotate, steps, args.warmup, kind="torch")), 2)
         out["frac_of_copy_ceiling"] = round(gbps / out["copy_ceiling_GBps"], 4)
         per = {}
-        for cfg in ["0", "1", "2", "3a", "3b", "5", "6", "7", "8"]:
-            w2 = workload(cfg)
+        for name in WORKLOAD_NAMES:
+            w2 = workload(name)
             L2 = launcher_for(w2, rotate)
             nb2 = w2.algorithmic_bytes()
             res = {}

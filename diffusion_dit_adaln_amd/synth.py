@@ -6,7 +6,7 @@ CPU oracle both take their inputs from here.
 
 Recipe (shared by tests, the smoke check and the benchmark):
   * every tensor has its own numpy ``PCG64`` stream seeded by
-    ``SeedSequence([seed, config_id, tensor_id])``;
+    ``SeedSequence([seed, stream, tensor_id])`` (a stream number per workload);
   * values are drawn as float64 standard normals, multiplied by sigma (a standard
     deviation) and offset by mu in float64, cast to float32, then rounded to
     bfloat16 (nearest-even) by torch's dtype conversion;
@@ -30,9 +30,11 @@ TENSOR_IDS = {"x": 0, "scale": 1, "shift": 2, "gate": 3, "res": 4, "weight": 5, 
               "tokens": 7, "class": 8}
 
 
-def _rng(seed: int, config_id: int, tensor: str) -> np.random.Generator:
+def _rng(seed: int, stream: int, tensor: str) -> np.random.Generator:
+    """The generator of one tensor of one workload: stream numbers keep the workloads'
+    draws apart."""
     return np.random.Generator(np.random.PCG64(np.random.SeedSequence(
-        [seed, config_id, TENSOR_IDS[tensor]])))
+        [seed, stream, TENSOR_IDS[tensor]])))
 
 
 def f32_to_bf16_bits(a: np.ndarray) -> np.ndarray:
@@ -92,11 +94,11 @@ class Workload:
         return (8 if self.op in ("rg", "rgln") else 4) * n
 
 
-def _vecs(seed, cid, B, H, names, sigma=0.1):
-    return {n: normal_bf16(_rng(seed, cid, n), (B, H), sigma) for n in names}
+def _vecs(seed, stream, B, H, names, sigma=0.1):
+    return {n: normal_bf16(_rng(seed, stream, n), (B, H), sigma) for n in names}
 
 
-def config0(seed: int = 0) -> Workload:
+def ln_1x128x2048(seed: int = 0) -> Workload:
     """LayerNorm (no affine, eps 1e-6) + modulate, x [1,128,2048] ~ N(0,1),
     scale/shift [1,2048] ~ 0.1*N(0,1)."""
     B, T, H = 1, 128, 2048
@@ -105,7 +107,7 @@ def config0(seed: int = 0) -> Workload:
                     v["scale"], v["shift"])
 
 
-def config1(seed: int = 0) -> Workload:
+def rms_1x4216x4096(seed: int = 0) -> Workload:
     """RMSNorm (weight 1+0.02*N, eps 1e-6) + scale/shift, x [1,4216,4096] ~ N(0,1)
     with 0.1% of entries multiplied by 50; scale/shift [1,4096] ~ 0.1*N."""
     B, T, H = 1, 4216, 4096
@@ -115,7 +117,7 @@ def config1(seed: int = 0) -> Workload:
     return Workload("rms", "rms_1x4216x4096", x, v["scale"], v["shift"], weight=w)
 
 
-def config2(seed: int = 0) -> Workload:
+def rg_rms_2x1140x4096(seed: int = 0) -> Workload:
     """Residual-gate RMSNorm + scale/shift (CFG batch): res, x [2,1140,4096] ~ N(0,1);
     gate/scale/shift [2,4096] ~ 0.1*N; no weight."""
     B, T, H = 2, 1140, 4096
@@ -125,19 +127,25 @@ def config2(seed: int = 0) -> Workload:
                     res=normal_bf16(_rng(seed, 2, "res"), (B, T, H)))
 
 
-def config3(seed: int = 0, site: str = "a") -> Workload:
-    """FLUX.1-like LayerNorm + modulate: site a x [2,4608,3072] (4096 image + 512
-    text tokens, CFG batch), site b x [1,4333,3072]; scale/shift [B,3072] ~ 0.1*N."""
-    if site == "a":
-        B, T, H, cid = 2, 4608, 3072, 3
-    else:
-        B, T, H, cid = 1, 4333, 3072, 33
-    v = _vecs(seed, cid, B, H, ["scale", "shift"])
-    return Workload("ln", f"ln_{B}x{T}x{H}", normal_bf16(_rng(seed, cid, "x"), (B, T, H)),
+def _flux_ln(seed, B, T, H, stream):
+    v = _vecs(seed, stream, B, H, ["scale", "shift"])
+    return Workload("ln", f"ln_{B}x{T}x{H}", normal_bf16(_rng(seed, stream, "x"), (B, T, H)),
                     v["scale"], v["shift"])
 
 
-def config5(seed: int = 0) -> Workload:
+def ln_2x4608x3072(seed: int = 0) -> Workload:
+    """FLUX.1-like LayerNorm + modulate: x [2,4608,3072] (4096 image + 512 text
+    tokens, CFG batch) ~ N(0,1); scale/shift [2,3072] ~ 0.1*N."""
+    return _flux_ln(seed, 2, 4608, 3072, 3)
+
+
+def ln_1x4333x3072(seed: int = 0) -> Workload:
+    """FLUX.1-like LayerNorm + modulate at a ragged token count: x [1,4333,3072] ~
+    N(0,1); scale/shift [1,3072] ~ 0.1*N."""
+    return _flux_ln(seed, 1, 4333, 3072, 33)
+
+
+def rg_ln_2x4096x3072(seed: int = 0) -> Workload:
     """Residual-gate LayerNorm + modulate at the FLUX.1 dual-stream image-token site
     (hidden 3072, 4096 image tokens, CFG batch of 2): res, x [2,4096,3072] ~ N(0,1);
     gate/scale/shift [2,3072] ~ 0.1*N."""
@@ -148,7 +156,7 @@ def config5(seed: int = 0) -> Workload:
                     res=normal_bf16(_rng(seed, 5, "res"), (B, T, H)))
 
 
-def config6(seed: int = 0) -> Workload:
+def ln_fp8_2x4608x3072(seed: int = 0) -> Workload:
     """LayerNorm + modulate + static FP8 quantisation at the FLUX site shape
     x [2,4608,3072] ~ N(0,1); scale/shift [2,3072] ~ 0.1*N; static scale 0.0125
     (about amax/448 of the modulated activations)."""
@@ -194,7 +202,7 @@ class QKWorkload:
         return 8 * T * Hd * D + 4 * T * D
 
 
-def config7(seed: int = 0) -> QKWorkload:
+def qk_rmsnorm_rope_4608x24x128(seed: int = 0) -> QKWorkload:
     """Qwen-Image-like attention input (Qwen PR report: batch 1, head_dim 128, Q/K as
     views of the packed QKV projection): 4096 image + 512 text tokens, 24 heads of 128
     (hidden 3072); qkv ~ N(0,1); RMSNorm weights 1 + 0.02*N; RoPE cache of positions
@@ -221,7 +229,7 @@ class CFWorkload:
         return 6 * int(np.prod(self.res.shape))
 
 
-def config8(seed: int = 0) -> CFWorkload:
+def rg_channel_first_2x3072x4608(seed: int = 0) -> CFWorkload:
     """Channel-first residual gating at the FLUX site size: hidden 3072, 4608 tokens,
     CFG batch 2; res, update ~ N(0,1); gate ~ 0.1*N."""
     B, H, T = 2, 3072, 4608
@@ -231,11 +239,11 @@ def config8(seed: int = 0) -> CFWorkload:
                       normal_bf16(_rng(seed, 8, "gate"), (B, H), 0.1))
 
 
-def flux_chunk_views(seed: int, B: int, H: int, chunks: int, cid: int = 30):
+def flux_chunk_views(seed: int, B: int, H: int, chunks: int, stream: int = 30):
     """scale/shift as strided views of one [B, chunks*H] embedding, like
     ``emb.chunk(chunks, dim=1)`` in the FLUX.1 test snippet: (emb, shift, scale)
     with shift = part 0 and scale = part 1, batch stride chunks*H."""
-    emb = normal_bf16(_rng(seed, cid, "scale"), (B, chunks * H), 1.0)
+    emb = normal_bf16(_rng(seed, stream, "scale"), (B, chunks * H), 1.0)
     return emb, emb[:, 0:H], emb[:, H:2 * H]
 
 
@@ -253,17 +261,17 @@ class StressSets:
 CLASS_SIGMA = (1.0, 1e-3, 1e3)
 
 
-def config4(seed: int = 0, n_sets: int = 256, max_tokens: int = 4096, H: int = 3072,
-            cid: int = 4) -> StressSets:
+def ragged_sets(seed: int = 0, n_sets: int = 256, max_tokens: int = 4096, H: int = 3072,
+                stream: int = 4) -> StressSets:
     """256 packed row-sets, token counts uniform in [1, max_tokens], hidden 3072;
     each row is N(0,1), 1e-3*N(0,1) or 1e3*N(0,1) with equal probability."""
-    tr = _rng(seed, cid, "tokens")
+    tr = _rng(seed, stream, "tokens")
     counts = tr.integers(1, max_tokens + 1, size=n_sets)
     offsets = np.zeros(n_sets + 1, np.int64)
     offsets[1:] = np.cumsum(counts)
     R = int(offsets[-1])
-    cls = _rng(seed, cid, "class").integers(0, 3, size=R).astype(np.int8)
-    xr = _rng(seed, cid, "x")
+    cls = _rng(seed, stream, "class").integers(0, 3, size=R).astype(np.int8)
+    xr = _rng(seed, stream, "x")
     x = np.empty((R, H), np.uint16)
     step = max(1, (1 << 22) // H)
     sig = np.array(CLASS_SIGMA, np.float64)
@@ -271,8 +279,8 @@ def config4(seed: int = 0, n_sets: int = 256, max_tokens: int = 4096, H: int = 3
         hi = min(R, lo + step)
         v = xr.standard_normal((hi - lo, H)) * sig[cls[lo:hi]][:, None]
         x[lo:hi] = f32_to_bf16_bits(v.astype(np.float32))
-    v = _vecs(seed, cid, n_sets, H, ["scale", "shift"])
-    w = normal_bf16(_rng(seed, cid, "weight"), (H,), 0.02, 1.0)
+    v = _vecs(seed, stream, n_sets, H, ["scale", "shift"])
+    w = normal_bf16(_rng(seed, stream, "weight"), (H,), 0.02, 1.0)
     return StressSets(x, offsets, cls, v["scale"], v["shift"], w)
 
 
@@ -287,19 +295,19 @@ class StressSetsDevice:
     weight: "torch.Tensor"   # [H] bfloat16, 1 + 0.02*N
 
 
-def config4_device(seed: int = 0, n_sets: int = 256, max_tokens: int = 4096, H: int = 3072,
-                   device: str = "cuda", cid: int = 4) -> StressSetsDevice:
-    """Same recipe as config4 (set sizes and row classes from the numpy streams),
+def ragged_sets_device(seed: int = 0, n_sets: int = 256, max_tokens: int = 4096, H: int = 3072,
+                       device: str = "cuda", stream: int = 4) -> StressSetsDevice:
+    """Same recipe as ragged_sets (set sizes and row classes from the numpy streams),
     but the ~1.6e9 activations are drawn on the device with torch's seeded
     generator: float32 N(0,1) times the row's sigma, rounded to bfloat16."""
-    tr = _rng(seed, cid, "tokens")
+    tr = _rng(seed, stream, "tokens")
     counts = tr.integers(1, max_tokens + 1, size=n_sets)
     offsets = np.zeros(n_sets + 1, np.int64)
     offsets[1:] = np.cumsum(counts)
     R = int(offsets[-1])
-    cls = _rng(seed, cid, "class").integers(0, 3, size=R).astype(np.int8)
+    cls = _rng(seed, stream, "class").integers(0, 3, size=R).astype(np.int8)
     gen = torch.Generator(device=device)
-    gen.manual_seed(int(np.random.SeedSequence([seed, cid, TENSOR_IDS["x"]]).generate_state(1)[0]))
+    gen.manual_seed(int(np.random.SeedSequence([seed, stream, TENSOR_IDS["x"]]).generate_state(1)[0]))
     sig = torch.tensor(CLASS_SIGMA, dtype=torch.float32, device=device)[
         torch.from_numpy(cls.astype(np.int64)).to(device)]
     x = torch.empty((R, H), dtype=torch.bfloat16, device=device)
@@ -308,10 +316,24 @@ def config4_device(seed: int = 0, n_sets: int = 256, max_tokens: int = 4096, H: 
         hi = min(R, lo + step)
         v = torch.randn((hi - lo, H), generator=gen, device=device, dtype=torch.float32)
         x[lo:hi] = (v * sig[lo:hi, None]).to(torch.bfloat16)
-    v = _vecs(seed, cid, n_sets, H, ["scale", "shift"])
-    w = normal_bf16(_rng(seed, cid, "weight"), (H,), 0.02, 1.0)
+    v = _vecs(seed, stream, n_sets, H, ["scale", "shift"])
+    w = normal_bf16(_rng(seed, stream, "weight"), (H,), 0.02, 1.0)
 
     def to_dev(a):
         return torch.from_numpy(np.ascontiguousarray(a).view(np.int16)).view(torch.bfloat16).to(device)
 
     return StressSetsDevice(x, offsets, cls, to_dev(v["scale"]), to_dev(v["shift"]), to_dev(w))
+
+
+# the benchmark and parity workloads by name (bench.py --workload NAME)
+WORKLOADS = {
+    "ln_1x128x2048": ln_1x128x2048,
+    "rms_1x4216x4096": rms_1x4216x4096,
+    "rg_rms_2x1140x4096": rg_rms_2x1140x4096,
+    "ln_2x4608x3072": ln_2x4608x3072,
+    "ln_1x4333x3072": ln_1x4333x3072,
+    "rg_ln_2x4096x3072": rg_ln_2x4096x3072,
+    "ln_fp8_2x4608x3072": ln_fp8_2x4608x3072,
+    "qk_rmsnorm_rope_4608x24x128": qk_rmsnorm_rope_4608x24x128,
+    "rg_channel_first_2x3072x4608": rg_channel_first_2x3072x4608,
+}

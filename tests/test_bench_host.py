@@ -20,20 +20,20 @@ def test_more_than_one_gpu_is_refused():
     assert "one GPU" in r.stderr and r.stdout == ""
 
 
-@pytest.mark.parametrize("cfg,op,rows,nbytes", [
-    ("0", "ln", 128, 4 * 128 * 2048),
-    ("1", "rms", 4216, 4 * 4216 * 4096),
-    ("2", "rg", 2280, 8 * 2280 * 4096),
-    ("3a", "ln", 9216, 4 * 9216 * 3072),
-    ("3b", "ln", 4333, 4 * 4333 * 3072),
-    ("5", "rgln", 8192, 8 * 8192 * 3072),
-    ("6", "lnq", 9216, 3 * 9216 * 3072),
-    ("7", "qk", 4608 * 48, 8 * 4608 * 24 * 128 + 4 * 4608 * 128),
-    ("8", "cf", 9216, 6 * 2 * 3072 * 4608),
+@pytest.mark.parametrize("name,op,rows,nbytes", [
+    ("ln_1x128x2048", "ln", 128, 4 * 128 * 2048),
+    ("rms_1x4216x4096", "rms", 4216, 4 * 4216 * 4096),
+    ("rg_rms_2x1140x4096", "rg", 2280, 8 * 2280 * 4096),
+    ("ln_2x4608x3072", "ln", 9216, 4 * 9216 * 3072),
+    ("ln_1x4333x3072", "ln", 4333, 4 * 4333 * 3072),
+    ("rg_ln_2x4096x3072", "rgln", 8192, 8 * 8192 * 3072),
+    ("ln_fp8_2x4608x3072", "lnq", 9216, 3 * 9216 * 3072),
+    ("qk_rmsnorm_rope_4608x24x128", "qk", 4608 * 48, 8 * 4608 * 24 * 128 + 4 * 4608 * 128),
+    ("rg_channel_first_2x3072x4608", "cf", 9216, 6 * 2 * 3072 * 4608),
 ])
-def test_workload_sizes(cfg, op, rows, nbytes):
-    wl = bench.workload(cfg)
-    assert wl.op == op
+def test_workload_sizes(name, op, rows, nbytes):
+    wl = bench.workload(name)
+    assert wl.name == name and wl.op == op
     assert bench.workload_rows(wl) == rows
     assert wl.algorithmic_bytes() == nbytes
     assert bench.describe(wl)
@@ -42,14 +42,15 @@ def test_workload_sizes(cfg, op, rows, nbytes):
 
 
 def test_headline_config_is_the_rms_workload():
-    wl = bench.workload("1")
+    assert bench.HEADLINE in bench.WORKLOAD_NAMES
+    wl = bench.workload(bench.HEADLINE)
     assert wl.x.shape == (1, 4216, 4096) and wl.weight is not None
     assert wl.algorithmic_bytes() == 69074944
 
 
 def test_inputs_are_seeded():
-    a = bench.inputs_sha256(bench.workload("2"))
-    b = bench.inputs_sha256(bench.workload("2"))
+    a = bench.inputs_sha256(bench.workload("rg_rms_2x1140x4096"))
+    b = bench.inputs_sha256(bench.workload("rg_rms_2x1140x4096"))
     assert a == b
 
 
@@ -77,7 +78,7 @@ def test_counters_used_only_for_the_same_kernel_source(tmp_path, monkeypatch):
 
 
 def test_cpu_baseline_on_a_small_workload():
-    wl = bench.workload("0")
+    wl = bench.workload("ln_1x128x2048")
     out = bench.cpu_baseline(wl, 0.05)
     assert out["kind"] == "oracle" and out["cores"] == 1 and out["value"] > 0
     assert out["unit"] == "GB/s" and "pinned to core" in out["sample"]

@@ -27,7 +27,7 @@ QSCALE = 0.0125
 @pytest.fixture(scope="module")
 def stress():
     say("[invariance] drawing the stress workload on the device")
-    st = synth.config4_device(seed=0)
+    st = synth.ragged_sets_device(seed=0)
     torch.cuda.synchronize()
     say(f"[invariance] rows={st.x.shape[0]} sets={len(st.offsets) - 1}")
     return st

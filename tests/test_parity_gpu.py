@@ -89,18 +89,17 @@ def check_workload(wl, what):
 # --------------------------------------------------------------------------
 # the workloads at full size
 # --------------------------------------------------------------------------
-@pytest.mark.parametrize("cfg", ["0", "1", "2", "3a", "3b", "5", "6"])
-def test_workload_full_size(cfg):
-    wl = {"0": synth.config0, "1": synth.config1, "2": synth.config2,
-          "3a": lambda: synth.config3(site="a"), "3b": lambda: synth.config3(site="b"),
-          "5": synth.config5, "6": synth.config6}[cfg]()
-    check_workload(wl, f"config {cfg}")
+@pytest.mark.parametrize("name", ["ln_1x128x2048", "rms_1x4216x4096", "rg_rms_2x1140x4096",
+                                  "ln_2x4608x3072", "ln_1x4333x3072", "rg_ln_2x4096x3072",
+                                  "ln_fp8_2x4608x3072"])
+def test_workload_full_size(name):
+    check_workload(synth.WORKLOADS[name](), name)
 
 
 def test_rg_with_weight():
-    wl = synth.config2()
+    wl = synth.rg_rms_2x1140x4096()
     wl.weight = synth.normal_bf16(np.random.default_rng(5), (4096,), 0.02, 1.0)
-    check_workload(wl, "config 2 with weight")
+    check_workload(wl, "rg_rms_2x1140x4096 with weight")
 
 
 # --------------------------------------------------------------------------
@@ -389,7 +388,7 @@ def check_qk(qkv, wq, wk, cs, what, eps=EPS, hk=None):
 
 
 def test_qk_workload_full_size():
-    wl = synth.config7()
+    wl = synth.qk_rmsnorm_rope_4608x24x128()
     say(f"[parity] qk {wl.qkv.shape}")
     check_qk(wl.qkv, wl.q_weight, wl.k_weight, wl.cos_sin, "qk full size")
 
@@ -471,7 +470,7 @@ def test_qk_heads_alone_equal_heads_in_batch():
 # residual gating on the channel-first layout
 # --------------------------------------------------------------------------
 def test_channel_first_full_size():
-    wl = synth.config8()
+    wl = synth.rg_channel_first_2x3072x4608()
     say(f"[parity] channel-first {wl.res.shape}")
     got = A.adaln_residual_gate_channel_first(dev(wl.res), dev(wl.update), dev(wl.gate))
     assert_bits_equal(host(got), O.residual_gate_channel_first(wl.res, wl.update, wl.gate),

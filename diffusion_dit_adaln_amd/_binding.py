@@ -117,10 +117,29 @@ def _stream(stream):
     return ctypes.c_void_p(int(stream))
 
 
-def _act(t: torch.Tensor, name: str):
+def _act(t: torch.Tensor, name: str, shape=None):
     if t.dtype != torch.bfloat16 or t.dim() != 3 or not t.is_contiguous():
         raise ValueError(f"{name}: expected a contiguous bfloat16 [B,T,H] tensor")
+    if shape is not None and tuple(t.shape) != tuple(shape):
+        raise ValueError(f"{name}: expected shape {tuple(shape)}, got {tuple(t.shape)}")
     return t
+
+
+def _on(dev, *named):
+    """Every given tensor must live on the GPU `dev` (the library takes device
+    pointers only; a host pointer or another GPU's memory would be dereferenced by
+    the kernel)."""
+    if dev.type != "cuda":
+        raise ValueError(f"expected CUDA (HIP) tensors, got a tensor on {dev}")
+    for t, name in named:
+        if t is not None and (not isinstance(t, torch.Tensor) or t.device != dev):
+            raise ValueError(f"{name}: expected a tensor on {dev}")
+
+
+def _call(dev, fn, *args, stream=None):
+    """Call a library entry point with `dev` current (its stream argument last)."""
+    with torch.cuda.device(dev):
+        return fn(*args, _stream(stream))
 
 
 def _vec(v: torch.Tensor, B: int, H: int, name: str):
@@ -151,11 +170,12 @@ def adaln_layernorm_modulate(x, scale, shift, eps: float = 1e-6, out=None, strea
     lib = load_library()
     _act(x, "x")
     B, T, H = x.shape
+    _on(x.device, (scale, "scale"), (shift, "shift"), (out, "out"))
     sp, sbs = _vec(scale, B, H, "scale")
     hp, hbs = _vec(shift, B, H, "shift")
-    y = torch.empty_like(x) if out is None else _act(out, "out")
-    _check(lib.adaln_layernorm_modulate(x.data_ptr(), sp, hp, y.data_ptr(), B, T, H, sbs, hbs,
-                                        _eps(eps), _stream(stream)), "adaln_layernorm_modulate")
+    y = torch.empty_like(x) if out is None else _act(out, "out", x.shape)
+    _check(_call(x.device, lib.adaln_layernorm_modulate, x.data_ptr(), sp, hp, y.data_ptr(), B, T,
+                 H, sbs, hbs, _eps(eps), stream=stream), "adaln_layernorm_modulate")
     return y
 
 
@@ -167,11 +187,12 @@ def adaln_rmsnorm_scale_shift(x, weight, scale, shift, eps: float = 1e-6, out=No
     if weight is not None and (weight.dtype != torch.bfloat16 or weight.numel() != H
                                or not weight.is_contiguous()):
         raise ValueError("weight: expected a contiguous bfloat16 [H] tensor")
+    _on(x.device, (weight, "weight"), (scale, "scale"), (shift, "shift"), (out, "out"))
     sp, sbs = _vec(scale, B, H, "scale")
     hp, hbs = _vec(shift, B, H, "shift")
-    y = torch.empty_like(x) if out is None else _act(out, "out")
-    _check(lib.adaln_rmsnorm_scale_shift(x.data_ptr(), _ptr(weight), sp, hp, y.data_ptr(), B, T, H,
-                                         sbs, hbs, _eps(eps), _stream(stream)),
+    y = torch.empty_like(x) if out is None else _act(out, "out", x.shape)
+    _check(_call(x.device, lib.adaln_rmsnorm_scale_shift, x.data_ptr(), _ptr(weight), sp, hp,
+                 y.data_ptr(), B, T, H, sbs, hbs, _eps(eps), stream=stream),
            "adaln_rmsnorm_scale_shift")
     return y
 
@@ -188,14 +209,16 @@ def adaln_residual_gate_rmsnorm_scale_shift(res, x, gate, weight, scale, shift, 
     if weight is not None and (weight.dtype != torch.bfloat16 or weight.numel() != H
                                or not weight.is_contiguous()):
         raise ValueError("weight: expected a contiguous bfloat16 [H] tensor")
+    _on(x.device, (res, "res"), (gate, "gate"), (weight, "weight"), (scale, "scale"),
+        (shift, "shift"), (out, "out"), (r_out, "r_out"))
     gp, gbs = _vec(gate, B, H, "gate")
     sp, sbs = _vec(scale, B, H, "scale")
     hp, hbs = _vec(shift, B, H, "shift")
-    y = torch.empty_like(x) if out is None else _act(out, "out")
-    r = torch.empty_like(x) if r_out is None else _act(r_out, "r_out")
-    _check(lib.adaln_residual_gate_rmsnorm_scale_shift(
-        res.data_ptr(), x.data_ptr(), gp, _ptr(weight), sp, hp, r.data_ptr(), y.data_ptr(), B, T,
-        H, gbs, sbs, hbs, _eps(eps), _stream(stream)), "adaln_residual_gate_rmsnorm_scale_shift")
+    y = torch.empty_like(x) if out is None else _act(out, "out", x.shape)
+    r = torch.empty_like(x) if r_out is None else _act(r_out, "r_out", x.shape)
+    _check(_call(x.device, lib.adaln_residual_gate_rmsnorm_scale_shift, res.data_ptr(),
+                 x.data_ptr(), gp, _ptr(weight), sp, hp, r.data_ptr(), y.data_ptr(), B, T, H, gbs,
+                 sbs, hbs, _eps(eps), stream=stream), "adaln_residual_gate_rmsnorm_scale_shift")
     return r, y
 
 
@@ -208,14 +231,16 @@ def adaln_residual_gate_layernorm_modulate(res, x, gate, scale, shift, eps: floa
     if res.shape != x.shape:
         raise ValueError("res and x must have the same shape")
     B, T, H = x.shape
+    _on(x.device, (res, "res"), (gate, "gate"), (scale, "scale"), (shift, "shift"),
+        (out, "out"), (r_out, "r_out"))
     gp, gbs = _vec(gate, B, H, "gate")
     sp, sbs = _vec(scale, B, H, "scale")
     hp, hbs = _vec(shift, B, H, "shift")
-    y = torch.empty_like(x) if out is None else _act(out, "out")
-    r = torch.empty_like(x) if r_out is None else _act(r_out, "r_out")
-    _check(lib.adaln_residual_gate_layernorm_modulate(
-        res.data_ptr(), x.data_ptr(), gp, sp, hp, r.data_ptr(), y.data_ptr(), B, T, H, gbs, sbs,
-        hbs, _eps(eps), _stream(stream)), "adaln_residual_gate_layernorm_modulate")
+    y = torch.empty_like(x) if out is None else _act(out, "out", x.shape)
+    r = torch.empty_like(x) if r_out is None else _act(r_out, "r_out", x.shape)
+    _check(_call(x.device, lib.adaln_residual_gate_layernorm_modulate, res.data_ptr(),
+                 x.data_ptr(), gp, sp, hp, r.data_ptr(), y.data_ptr(), B, T, H, gbs, sbs, hbs,
+                 _eps(eps), stream=stream), "adaln_residual_gate_layernorm_modulate")
     return r, y
 
 
@@ -227,7 +252,8 @@ def adaln_layernorm_modulate_fp8_quant(x, scale, shift, qscale, eps: float = 1e-
     lib = load_library()
     _act(x, "x")
     B, T, H = x.shape
-    if qscale.dtype != torch.float32 or qscale.numel() != 1 or not qscale.is_cuda:
+    _on(x.device, (scale, "scale"), (shift, "shift"), (qscale, "qscale"), (out, "out"))
+    if qscale.dtype != torch.float32 or qscale.numel() != 1:
         raise ValueError("qscale: expected a one-element float32 device tensor")
     sp, sbs = _vec(scale, B, H, "scale")
     hp, hbs = _vec(shift, B, H, "shift")
@@ -237,9 +263,8 @@ def adaln_layernorm_modulate_fp8_quant(x, scale, shift, qscale, eps: float = 1e-
         if out.dtype != torch.uint8 or out.shape != x.shape or not out.is_contiguous():
             raise ValueError("out: expected a contiguous uint8 [B,T,H] tensor")
         q = out
-    _check(lib.adaln_layernorm_modulate_fp8_quant(x.data_ptr(), sp, hp, qscale.data_ptr(),
-                                                  q.data_ptr(), B, T, H, sbs, hbs, _eps(eps),
-                                                  _stream(stream)),
+    _check(_call(x.device, lib.adaln_layernorm_modulate_fp8_quant, x.data_ptr(), sp, hp,
+                 qscale.data_ptr(), q.data_ptr(), B, T, H, sbs, hbs, _eps(eps), stream=stream),
            "adaln_layernorm_modulate_fp8_quant")
     return q
 
@@ -268,14 +293,15 @@ def adaln_qk_rmsnorm_rope(q, k, q_weight, k_weight, cos_sin, eps: float = 1e-6, 
         if w is not None and (w.dtype != torch.bfloat16 or w.numel() != 128 or
                               not w.is_contiguous()):
             raise ValueError(f"{name}: expected a contiguous bfloat16 [128] tensor")
+    _on(q.device, (k, "k"), (q_weight, "q_weight"), (k_weight, "k_weight"),
+        (cos_sin, "cos_sin"), (q_out, "q_out"), (k_out, "k_out"))
     qo = torch.empty((T, q.size(1), 128), dtype=torch.bfloat16, device=q.device) \
-        if q_out is None else q_out
+        if q_out is None else _act(q_out, "q_out", (T, q.size(1), 128))
     ko = torch.empty((T, k.size(1), 128), dtype=torch.bfloat16, device=k.device) \
-        if k_out is None else k_out
-    _check(lib.adaln_qk_rmsnorm_rope(q.data_ptr(), k.data_ptr(), _ptr(q_weight), _ptr(k_weight),
-                                     cos_sin.data_ptr(), qo.data_ptr(), ko.data_ptr(), T,
-                                     q.size(1), k.size(1), 128, qts, kts, _eps(eps),
-                                     _stream(stream)), "adaln_qk_rmsnorm_rope")
+        if k_out is None else _act(k_out, "k_out", (T, k.size(1), 128))
+    _check(_call(q.device, lib.adaln_qk_rmsnorm_rope, q.data_ptr(), k.data_ptr(), _ptr(q_weight),
+                 _ptr(k_weight), cos_sin.data_ptr(), qo.data_ptr(), ko.data_ptr(), T, q.size(1),
+                 k.size(1), 128, qts, kts, _eps(eps), stream=stream), "adaln_qk_rmsnorm_rope")
     return qo, ko
 
 
@@ -290,12 +316,13 @@ def adaln_residual_gate_channel_first(res, update, gate, out=None, stream=None):
     if (update.dtype != torch.bfloat16 or tuple(update.shape) != (B, T, H)
             or not update.is_contiguous()):
         raise ValueError("update: expected a contiguous bfloat16 [B,T,H] tensor")
+    _on(res.device, (update, "update"), (gate, "gate"), (out, "out"))
     gp, gbs = _vec(gate, B, H, "gate")
     o = torch.empty_like(res) if out is None else out
     if o.shape != res.shape or o.dtype != torch.bfloat16 or not o.is_contiguous():
         raise ValueError("out: expected a contiguous bfloat16 [B,H,T] tensor")
-    _check(lib.adaln_residual_gate_channel_first(res.data_ptr(), update.data_ptr(), gp,
-                                                 o.data_ptr(), B, T, H, gbs, _stream(stream)),
+    _check(_call(res.device, lib.adaln_residual_gate_channel_first, res.data_ptr(),
+                 update.data_ptr(), gp, o.data_ptr(), B, T, H, gbs, stream=stream),
            "adaln_residual_gate_channel_first")
     return o
 
@@ -372,9 +399,10 @@ def adaln_diag_round_bf16(x: torch.Tensor, stream=None) -> torch.Tensor:
     lib = load_library()
     if x.dtype != torch.float32 or not x.is_contiguous():
         raise ValueError("expected a contiguous float32 tensor")
+    _on(x.device)
     out = torch.empty(x.shape, dtype=torch.bfloat16, device=x.device)
-    _check(lib.adaln_diag_round_bf16(x.data_ptr(), out.data_ptr(), x.numel(), _stream(stream)),
-           "adaln_diag_round_bf16")
+    _check(_call(x.device, lib.adaln_diag_round_bf16, x.data_ptr(), out.data_ptr(), x.numel(),
+                 stream=stream), "adaln_diag_round_bf16")
     return out
 
 
@@ -383,9 +411,10 @@ def adaln_diag_finalize(x: torch.Tensor, eps: float = 1e-6, stream=None) -> torc
     lib = load_library()
     if x.dtype != torch.float32 or not x.is_contiguous():
         raise ValueError("expected a contiguous float32 tensor")
+    _on(x.device)
     out = torch.empty_like(x)
-    _check(lib.adaln_diag_finalize(x.data_ptr(), out.data_ptr(), x.numel(), _eps(eps),
-                                   _stream(stream)), "adaln_diag_finalize")
+    _check(_call(x.device, lib.adaln_diag_finalize, x.data_ptr(), out.data_ptr(), x.numel(),
+                 _eps(eps), stream=stream), "adaln_diag_finalize")
     return out
 
 
@@ -394,11 +423,12 @@ def adaln_diag_stream_copy(src: torch.Tensor, dst: torch.Tensor, stream=None) ->
     lib = load_library()
     if not (src.is_contiguous() and dst.is_contiguous()):
         raise ValueError("expected contiguous tensors")
+    _on(src.device, (dst, "dst"))
     nbytes = src.numel() * src.element_size()
     if dst.numel() * dst.element_size() != nbytes:
         raise ValueError("src and dst sizes differ")
-    _check(lib.adaln_diag_stream_copy(src.data_ptr(), dst.data_ptr(), nbytes, _stream(stream)),
-           "adaln_diag_stream_copy")
+    _check(_call(src.device, lib.adaln_diag_stream_copy, src.data_ptr(), dst.data_ptr(), nbytes,
+                 stream=stream), "adaln_diag_stream_copy")
     return dst
 
 
@@ -407,7 +437,10 @@ def adaln_diag_quant_fp8(v: torch.Tensor, qscale: torch.Tensor, stream=None) -> 
     lib = load_library()
     if v.dtype != torch.float32 or not v.is_contiguous():
         raise ValueError("expected a contiguous float32 tensor")
+    _on(v.device, (qscale, "qscale"))
+    if qscale.dtype != torch.float32 or qscale.numel() != 1:
+        raise ValueError("qscale: expected a one-element float32 device tensor")
     out = torch.empty(v.shape, dtype=torch.uint8, device=v.device)
-    _check(lib.adaln_diag_quant_fp8(v.data_ptr(), out.data_ptr(), v.numel(), qscale.data_ptr(),
-                                    _stream(stream)), "adaln_diag_quant_fp8")
+    _check(_call(v.device, lib.adaln_diag_quant_fp8, v.data_ptr(), out.data_ptr(), v.numel(),
+                 qscale.data_ptr(), stream=stream), "adaln_diag_quant_fp8")
     return out

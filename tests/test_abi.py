@@ -305,9 +305,38 @@ def test_compute_entry_points_reject_before_launch(lib):
 
 
 def test_binding_raises_adaln_error(lib):
-    torch = pytest.importorskip("torch")
-    x = torch.zeros(1, 2, 12, dtype=torch.bfloat16)
-    v = torch.zeros(12, dtype=torch.bfloat16)
+    # a non-OK status from the library becomes AdalnError carrying the status
     with pytest.raises(A.AdalnError) as e:
-        A.adaln_layernorm_modulate(x, v, v, stream=0)
+        A.adaln_reduction_layout(12)
     assert e.value.status == SHAPE
+
+
+def test_binding_rejects_host_tensors():
+    """The Python binding passes device pointers only: host tensors are refused
+    before the library is called."""
+    import torch
+    import diffusion_dit_adaln_amd as A
+    x = torch.zeros((1, 4, 64), dtype=torch.bfloat16)
+    v = torch.zeros((1, 64), dtype=torch.bfloat16)
+    w = torch.zeros(64, dtype=torch.bfloat16)
+    qs = torch.ones(1, dtype=torch.float32)
+    calls = [
+        lambda: A.adaln_layernorm_modulate(x, v, v),
+        lambda: A.adaln_rmsnorm_scale_shift(x, w, v, v),
+        lambda: A.adaln_residual_gate_rmsnorm_scale_shift(x, x, v, w, v, v),
+        lambda: A.adaln_residual_gate_layernorm_modulate(x, x, v, v, v),
+        lambda: A.adaln_layernorm_modulate_fp8_quant(x, v, v, qs),
+        lambda: A.adaln_qk_rmsnorm_rope(torch.zeros((2, 3, 128), dtype=torch.bfloat16),
+                                        torch.zeros((2, 3, 128), dtype=torch.bfloat16), None,
+                                        None, torch.zeros((2, 128), dtype=torch.float32)),
+        lambda: A.adaln_residual_gate_channel_first(torch.zeros((1, 8, 8), dtype=torch.bfloat16),
+                                                    torch.zeros((1, 8, 8), dtype=torch.bfloat16),
+                                                    torch.zeros((1, 8), dtype=torch.bfloat16)),
+        lambda: A.adaln_diag_round_bf16(torch.zeros(8)),
+        lambda: A.adaln_diag_finalize(torch.zeros(8)),
+        lambda: A.adaln_diag_stream_copy(torch.zeros(8), torch.zeros(8)),
+        lambda: A.adaln_diag_quant_fp8(torch.zeros(8), qs),
+    ]
+    for i, call in enumerate(calls):
+        with pytest.raises(ValueError, match="CUDA"):
+            call()

@@ -605,3 +605,26 @@ def test_device_finalize_all_nonnegative_stats():
     v = s + np.float32(1e-6)
     want = np.float32(1.0) / np.sqrt(v)
     assert np.array_equal(got.view(np.uint32), want.view(np.uint32))
+
+
+def test_binding_rejects_wrong_outputs():
+    """Outputs of the wrong shape, or outside the inputs' device, are refused before
+    any launch (the library cannot see a buffer's size)."""
+    say("[parity] binding output checks")
+    x = torch.zeros((1, 4, 64), dtype=torch.bfloat16, device="cuda")
+    v = torch.zeros((1, 64), dtype=torch.bfloat16, device="cuda")
+    small = torch.empty((1, 3, 64), dtype=torch.bfloat16, device="cuda")
+    with pytest.raises(ValueError, match="shape"):
+        A.adaln_layernorm_modulate(x, v, v, out=small)
+    with pytest.raises(ValueError, match="shape"):
+        A.adaln_residual_gate_layernorm_modulate(x, x, v, v, v, r_out=small)
+    with pytest.raises(ValueError):
+        A.adaln_layernorm_modulate(x, v, v, out=torch.empty((1, 4, 64), dtype=torch.bfloat16))
+    with pytest.raises(ValueError):
+        A.adaln_layernorm_modulate(x, v.cpu(), v)
+    q = torch.zeros((2, 3, 128), dtype=torch.bfloat16, device="cuda")
+    cs = torch.zeros((2, 128), dtype=torch.float32, device="cuda")
+    with pytest.raises(ValueError, match="shape"):
+        A.adaln_qk_rmsnorm_rope(q, q, None, None, cs,
+                                q_out=torch.empty((2, 2, 128), dtype=torch.bfloat16, device="cuda"))
+    torch.cuda.synchronize()

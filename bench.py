@@ -266,6 +266,30 @@ def time_steps(launch, steps: int, warmup: int, mode: str):
     return start.elapsed_time(end) / 1e3
 
 
+def single_launch_median(launch, n: int, warmup: int) -> float:
+    """Median seconds of single launches, each bracketed by its own pair of HIP
+    events on the launch stream (eager launches; a cross-check of the per-launch
+    average with the kernel durations rocprofv3 reports)."""
+    import torch
+    stream = torch.cuda.Stream()
+    handle = stream.cuda_stream
+    with torch.cuda.stream(stream):
+        for i in range(warmup):
+            launch(i, handle)
+    torch.cuda.synchronize()
+    ev = [(torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True))
+          for _ in range(n)]
+    with torch.cuda.stream(stream):
+        for i, (a, b) in enumerate(ev):
+            a.record(stream)
+            st = launch(warmup + i, handle)
+            b.record(stream)
+            if st:
+                raise RuntimeError(f"launch failed with status {st}")
+    torch.cuda.synchronize()
+    return float(np.median([a.elapsed_time(b) for a, b in ev])) / 1e3
+
+
 def copy_ceiling(nbytes_rw: int, rotate_bytes: int, steps: int, warmup: int, mode="graph",
                  kind="stream"):
     """GB/s of a plain device copy moving the same bytes (read n/2, write n/2):
@@ -469,6 +493,10 @@ def main():
                      "traffic": traffic, "kernel": KERNEL_OF.get(wl.op, f"fused_norm_modulate ({wl.op})"),
                      "avg_launch_us": round(avg_launch_s * 1e6, 3)},
     }
+    # per-launch cross-check: median of single launches between their own events
+    med = single_launch_median(L.call, 200, args.warmup)
+    out["roofline"]["single_launch_median_us"] = round(med * 1e6, 3)
+    out["roofline"]["single_launch_median_GBps"] = round(nbytes / med / 1e9, 2)
     del L
     torch.cuda.empty_cache()
     if not args.no_extras:

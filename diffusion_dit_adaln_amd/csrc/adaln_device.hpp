@@ -107,10 +107,35 @@ constexpr int DPP_XOR2 = 0x4E;
 constexpr int DPP_HALF_MIRROR = 0x141;
 constexpr int DPP_MIRROR = 0x140;
 
+// Every lane's source lies inside its own row, so bound_ctrl changes no value; it
+// lets the compiler fold the move into the instruction that consumes it.
 template <int CTRL>
 __device__ __forceinline__ float dpp(float v) {
     return __builtin_bit_cast(
-        float, __builtin_amdgcn_mov_dpp(__builtin_bit_cast(int, v), CTRL, 0xF, 0xF, false));
+        float, __builtin_amdgcn_mov_dpp(__builtin_bit_cast(int, v), CTRL, 0xF, 0xF, true));
+}
+// DPP into the lanes of the banks (groups of 4 lanes of a 16-lane row) set in
+// BANKS; the other lanes keep v.
+template <int CTRL, int BANKS>
+__device__ __forceinline__ float dpp_banks(float v) {
+    const int i = __builtin_bit_cast(int, v);
+    return __builtin_bit_cast(float, __builtin_amdgcn_update_dpp(i, i, CTRL, 0xF, BANKS, false));
+}
+// The butterfly partners at distance K (1, 2, 4, 8) in their fixed order: lo is
+// the value of lane t & ~K, hi that of lane t | K, in every lane.
+template <int K>
+__device__ __forceinline__ float partner_lo(float v) {
+    if constexpr (K == 1) return dpp<0xA0>(v);             // quad_perm [0,0,2,2]
+    else if constexpr (K == 2) return dpp<0x44>(v);        // quad_perm [0,1,0,1]
+    else if constexpr (K == 4) return dpp_banks<0x114, 0xA>(v);  // row_shr:4 into banks 1, 3
+    else return dpp_banks<0x118, 0xC>(v);                  // row_shr:8 into banks 2, 3
+}
+template <int K>
+__device__ __forceinline__ float partner_hi(float v) {
+    if constexpr (K == 1) return dpp<0xF5>(v);             // quad_perm [1,1,3,3]
+    else if constexpr (K == 2) return dpp<0xEE>(v);        // quad_perm [2,3,2,3]
+    else if constexpr (K == 4) return dpp_banks<0x104, 0x5>(v);  // row_shl:4 into banks 0, 2
+    else return dpp_banks<0x108, 0x3>(v);                  // row_shl:8 into banks 0, 1
 }
 __device__ __forceinline__ float readlane(float v, int lane) {
     return __builtin_bit_cast(float, __builtin_amdgcn_readlane(__builtin_bit_cast(int, v), lane));

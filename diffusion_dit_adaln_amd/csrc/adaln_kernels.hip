@@ -131,15 +131,13 @@ __device__ __forceinline__ Welford welford_level(const Welford& me, int lane) {
     return combine(lo, hi);
 }
 
-// The same level when both partners hold NA elements.
+// The same level when both partners hold NA elements: the partners are read in
+// their fixed order directly (lo from lane t & ~K, hi from lane t | K).
 template <int K, int CTRL, int NA>
-__device__ __forceinline__ void welford_level_equal(float& mean, float& m2, int lane) {
-    const float om = dpp<CTRL>(mean);
-    const float o2 = dpp<CTRL>(m2);
-    const bool upper = (lane & K) != 0;
-    const float lo = upper ? om : mean;
-    const float hi = upper ? mean : om;
-    combine_equal<NA>(lo, hi, m2 + o2, mean, m2);
+__device__ __forceinline__ void welford_level_equal(float& mean, float& m2) {
+    const float lo = partner_lo<K>(mean);
+    const float hi = partner_hi<K>(mean);
+    combine_equal<NA>(lo, hi, m2 + dpp<CTRL>(m2), mean, m2);
 }
 
 __device__ __forceinline__ Welford readlane(const Welford& w, int lane) {
@@ -172,11 +170,11 @@ __device__ __forceinline__ Welford wave_welford(Welford w, int lane) {
 
 // Wave butterfly when every lane holds N elements.
 template <int N>
-__device__ __forceinline__ void wave_welford_equal(float& mean, float& m2, int lane) {
-    welford_level_equal<1, DPP_XOR1, N>(mean, m2, lane);
-    welford_level_equal<2, DPP_XOR2, 2 * N>(mean, m2, lane);
-    welford_level_equal<4, DPP_HALF_MIRROR, 4 * N>(mean, m2, lane);
-    welford_level_equal<8, DPP_MIRROR, 8 * N>(mean, m2, lane);
+__device__ __forceinline__ void wave_welford_equal(float& mean, float& m2) {
+    welford_level_equal<1, DPP_XOR1, N>(mean, m2);
+    welford_level_equal<2, DPP_XOR2, 2 * N>(mean, m2);
+    welford_level_equal<4, DPP_HALF_MIRROR, 4 * N>(mean, m2);
+    welford_level_equal<8, DPP_MIRROR, 8 * N>(mean, m2);
     float ma, qa, mb, qb;
     combine_equal<16 * N>(readlane(mean, 0), readlane(mean, 16),
                           readlane(m2, 0) + readlane(m2, 16), ma, qa);
@@ -463,7 +461,7 @@ __global__ __launch_bounds__(256) void fused_norm_modulate(Params p) {
             }
             if (!TAIL) {
                 constexpr int N = 8 * C;
-                wave_welford_equal<N>(wm, w2, lane);
+                wave_welford_equal<N>(wm, w2);
                 if (W > 1) {
                     if (lane == 0) {
                         xwave[par][wave][0] = wm;

@@ -419,6 +419,9 @@ adaln_status adaln_diag_round_bf16(const float* in, adaln_bf16* out, int64_t n, 
     if (n == 0) return ADALN_OK;
     if (!in || !out) return ADALN_ERR_NULL;
     if (((uintptr_t)in & 3u) || ((uintptr_t)out & 1u)) return ADALN_ERR_ALIGN;
+    if (overlaps(Span{(uintptr_t)out, (uintptr_t)out + (uintptr_t)(2 * n)},
+                 Span{(uintptr_t)in, (uintptr_t)in + (uintptr_t)(4 * n)}))
+        return ADALN_ERR_OVERLAP;
     return adaln::launch_diag_round(in, out, n, (hipStream_t)hip_stream) == hipSuccess
                ? ADALN_OK
                : ADALN_ERR_LAUNCH;
@@ -431,6 +434,11 @@ adaln_status adaln_diag_finalize(const float* in, float* out, int64_t n, float e
     if (n == 0) return ADALN_OK;
     if (!in || !out) return ADALN_ERR_NULL;
     if (((uintptr_t)in & 3u) || ((uintptr_t)out & 3u)) return ADALN_ERR_ALIGN;
+    // elementwise: in place is fine, a shifted overlap is not
+    if ((const void*)in != (const void*)out &&
+        overlaps(Span{(uintptr_t)out, (uintptr_t)out + (uintptr_t)(4 * n)},
+                 Span{(uintptr_t)in, (uintptr_t)in + (uintptr_t)(4 * n)}))
+        return ADALN_ERR_OVERLAP;
     return adaln::launch_diag_finalize(in, out, n, eps, (hipStream_t)hip_stream) == hipSuccess
                ? ADALN_OK
                : ADALN_ERR_LAUNCH;

@@ -252,7 +252,8 @@ int adaln_abi_version(void);
  * tests can check them exhaustively against host IEEE arithmetic.
  *  - adaln_diag_round_bf16: out[i] = bf16(in[i]) (nearest-even).
  *  - adaln_diag_finalize:   out[i] = RN(1 / RN(sqrt(RN(in[i] + eps)))).
- * n >= 0 elements of device memory, 4-byte aligned; ADALN_ERR_* as above. */
+ * n >= 0 elements of device memory, 4-byte aligned; ADALN_ERR_* as above.  out may
+ * not overlap in (ADALN_ERR_OVERLAP), except that finalize may run in place. */
 adaln_status adaln_diag_round_bf16(const float* in, adaln_bf16* out, int64_t n, void* hip_stream);
 adaln_status adaln_diag_finalize(const float* in, float* out, int64_t n, float eps,
                                  void* hip_stream);
@@ -260,7 +261,7 @@ adaln_status adaln_diag_finalize(const float* in, float* out, int64_t n, float e
 /* Diagnostic: the FP8 kernel's quantisation step on binary32 inputs,
  * out[i] = E4M3(clamp(RN(in[i] * RN(1 / *qscale)), -448, 448)).  n >= 0 and
  * n % 4 == 0 (ADALN_ERR_SHAPE); in 16-byte aligned, out and qscale 4-byte aligned;
- * device memory. */
+ * device memory; out may not overlap in or *qscale (ADALN_ERR_OVERLAP). */
 adaln_status adaln_diag_quant_fp8(const float* in, uint8_t* out, int64_t n, const float* qscale,
                                   void* hip_stream);
 

@@ -302,6 +302,9 @@ def test_compute_entry_points_reject_before_launch(lib):
     assert lib.adaln_diag_stream_copy(addr(0), addr(0) + 16, 32, None) == OVERLAP
     assert lib.adaln_diag_stream_copy(None, None, 0, None) == OK
     assert lib.adaln_diag_finalize(addr(0), addr(1), 4, -1.0, None) == VALUE
+    assert lib.adaln_diag_round_bf16(addr(0), addr(0) + 4, 8, None) == OVERLAP
+    assert lib.adaln_diag_finalize(addr(0), addr(0) + 4, 8, 1e-6, None) == OVERLAP
+    assert lib.adaln_diag_quant_fp8(addr(0), addr(0) + 16, 8, addr(1), None) == OVERLAP
 
 
 def test_binding_raises_adaln_error(lib):

@@ -12,7 +12,7 @@ import os
 import torch
 
 _PKG = os.path.dirname(os.path.abspath(__file__))
-ABI_VERSION = 6
+ABI_VERSION = 7
 
 STATUS_NAMES = {0: "ADALN_OK", 1: "ADALN_ERR_NULL", 2: "ADALN_ERR_SHAPE", 3: "ADALN_ERR_ALIGN",
                 4: "ADALN_ERR_STRIDE", 5: "ADALN_ERR_OVERLAP", 6: "ADALN_ERR_VALUE",
@@ -28,7 +28,8 @@ EXPORTS = ("adaln_layernorm_modulate", "adaln_rmsnorm_scale_shift",
            "adaln_check_residual_gate_layernorm_modulate",
            "adaln_check_layernorm_modulate_fp8_quant", "adaln_reduction_layout",
            "adaln_status_string", "adaln_abi_version", "adaln_diag_round_bf16",
-           "adaln_diag_finalize", "adaln_diag_quant_fp8", "adaln_diag_stream_copy")
+           "adaln_diag_finalize", "adaln_diag_quant_fp8", "adaln_diag_stream_copy",
+           "adaln_diag_launch_plan")
 
 
 class AdalnError(RuntimeError):
@@ -79,6 +80,7 @@ def load_library():
         "adaln_diag_finalize": [P, P, I, F, P],
         "adaln_diag_stream_copy": [P, P, I, P],
         "adaln_diag_quant_fp8": [P, P, I, P, P],
+        "adaln_diag_launch_plan": [S, I, I, I, I, ctypes.POINTER(I)],
     }
     for name, args in sig.items():
         fn = getattr(lib, name)
@@ -384,6 +386,21 @@ def adaln_reduction_layout(H: int):
     _check(lib.adaln_reduction_layout(H, ctypes.byref(w), ctypes.byref(p), ctypes.byref(c)),
            "adaln_reduction_layout")
     return w.value, p.value, c.value
+
+
+OPS = {"ln": 0, "rms": 1, "rg": 2, "rgln": 3, "lnq": 4}
+PLAN_FIELDS = ("shallow", "slots", "groups", "group_stride", "step", "span", "blocks",
+               "block_threads")
+
+
+def adaln_diag_launch_plan(op: str, rows: int, H: int, resident: int,
+                           resident_shallow: int = 0) -> dict:
+    """The fused kernel's row-group plan for one launch (host only; see the header)."""
+    lib = load_library()
+    out = (ctypes.c_int64 * 8)()
+    _check(lib.adaln_diag_launch_plan(OPS[op], rows, H, resident, resident_shallow, out),
+           "adaln_diag_launch_plan")
+    return dict(zip(PLAN_FIELDS, list(out)))
 
 
 def adaln_status_string(status: int) -> str:

@@ -414,6 +414,26 @@ const char* adaln_status_string(adaln_status status) {
 
 int adaln_abi_version(void) { return ADALN_ABI_VERSION; }
 
+adaln_status adaln_diag_launch_plan(int op, int64_t rows, int64_t H, int64_t resident,
+                                    int64_t resident_shallow, int64_t* out) {
+    if (!out) return ADALN_ERR_NULL;
+    if (op < adaln::OP_LN || op > adaln::OP_LNQ) return ADALN_ERR_VALUE;
+    if (rows < 1 || H < 8 || H > kMaxH || (H % 8) != 0) return ADALN_ERR_SHAPE;
+    if (rows > INT64_MAX / (2 * H)) return ADALN_ERR_SHAPE;
+    if (resident < 1 || resident_shallow < 0) return ADALN_ERR_VALUE;
+    const adaln::Plan pl =
+        adaln::plan_launch(static_cast<adaln::Op>(op), rows, H, resident, resident_shallow);
+    out[0] = pl.shallow ? 1 : 0;
+    out[1] = pl.slots;
+    out[2] = pl.groups;
+    out[3] = pl.group_stride;
+    out[4] = pl.step;
+    out[5] = pl.span;
+    out[6] = pl.blocks;
+    out[7] = pl.block_threads;
+    return ADALN_OK;
+}
+
 adaln_status adaln_diag_round_bf16(const float* in, adaln_bf16* out, int64_t n, void* hip_stream) {
     if (n < 0) return ADALN_ERR_SHAPE;
     if (n == 0) return ADALN_OK;

@@ -76,6 +76,19 @@ hipError_t launch_cf(const CFParams& p, hipStream_t stream);
 // and the CU count (cached per kernel and device, thread-safe).
 bool occupancy(const void* fn, int block, int* blocks_per_cu, int* cus);
 
+// How a launch of the fused kernel splits `rows` rows over row groups, given how
+// many groups fit on the device at once for the deep-ring kernel (resident) and
+// for the one-slot ring (resident_shallow; 0 if it is not available).  Group g
+// takes the rows g*group_stride + i*step below min(g*group_stride + span, rows).
+struct Plan {
+    bool shallow;          // the one-slot ring kernel
+    int slots;             // ring depth S
+    int64_t groups, group_stride, step, span;
+    int64_t blocks;        // workgroups launched
+    int block_threads;     // threads per workgroup
+};
+Plan plan_launch(Op op, int64_t rows, int64_t H, int64_t resident, int64_t resident_shallow);
+
 // Launch the fused kernel for `op`; returns the HIP error of the launch.
 hipError_t launch(Op op, const Params& p, hipStream_t stream);
 

@@ -768,6 +768,47 @@ Layout layout_of(int64_t H) {
     return L;
 }
 
+Plan plan_launch(Op op, int64_t rows, int64_t H, int64_t resident, int64_t resident_shallow) {
+    const Layout L = layout_of(H);
+    Plan pl{};
+    pl.block_threads = L.waves == 1 ? 256 : 64 * L.waves;
+    // Interleaved ops with many rows per group: the one-slot ring (more resident
+    // groups, the latency covered by the other groups) streams faster; with few
+    // rows per group the deeper ring does (tuning; the bits never depend on it).
+    pl.shallow = interleaved(op) && resident_shallow > 0 &&
+                 rows >= ADALN_SHALLOW_ROWS_PER_GROUP * resident;
+    if (pl.shallow) resident = resident_shallow;
+    const int S = pl.shallow ? 1 : ring_slots(L.waves, L.chunks, op_gated(op));
+    pl.slots = S;
+    if (interleaved(op)) {
+        // one group per resident group slot (at most one per row); a group's ring
+        // slots past its last row skip their arithmetic
+        pl.groups = rows < resident ? rows : resident;
+        pl.group_stride = 1;
+        pl.step = pl.groups;
+        pl.span = rows;
+    } else {
+        // `per` contiguous rows per group, a multiple of S so that only the last
+        // group can end with idle ring slots; the group's descriptors address its
+        // rows with 32-bit byte offsets and the last pass reaches S rows past its
+        // range, so (per + S) rows stay below 2^31 bytes
+        const int64_t slots = resident * (L.waves == 1   ? ADALN_GROUP_OVERSUBSCRIBE_W1
+                                          : L.waves == 2 ? ADALN_GROUP_OVERSUBSCRIBE_W2
+                                                         : ADALN_GROUP_OVERSUBSCRIBE_W4);
+        const int64_t groups0 = rows < slots ? rows : slots;
+        int64_t per = (rows + groups0 - 1) / groups0;
+        per = (per + S - 1) / S * S;
+        const int64_t max_per = ((int64_t(0x7FFFFFFF) - 64) / (2 * H) - S) / S * S;
+        if (per > max_per) per = max_per;
+        pl.groups = (rows + per - 1) / per;
+        pl.group_stride = per;
+        pl.step = 1;
+        pl.span = per;
+    }
+    pl.blocks = L.waves == 1 ? (pl.groups + 3) / 4 : pl.groups;
+    return pl;
+}
+
 hipError_t launch(Op op, const Params& p_in, hipStream_t stream) {
     const Layout L = layout_of(p_in.H);
     const bool weight = p_in.weight != nullptr;
@@ -779,60 +820,32 @@ hipError_t launch(Op op, const Params& p_in, hipStream_t stream) {
                : op == OP_LNQ  ? pick<OP_LNQ>(L, false, shallow)
                                : nullptr;
     };
-    KernelFn fn = pick_op(false);
-    if (!fn) return hipErrorInvalidValue;
+    KernelFn deep = pick_op(false);
+    if (!deep) return hipErrorInvalidValue;
     // one-wave rows: four independent waves per workgroup; else one row group per
     // workgroup of W waves
     const int block = L.waves == 1 ? 256 : 64 * L.waves;
+    const int groups_per_block = L.waves == 1 ? 4 : 1;
     int blocks_per_cu = 0, cus = 0;
-    if (!occupancy(reinterpret_cast<const void*>(fn), block, &blocks_per_cu, &cus)) {
+    if (!occupancy(reinterpret_cast<const void*>(deep), block, &blocks_per_cu, &cus)) {
         (void)hipGetLastError();
         return hipErrorInvalidDeviceFunction;
     }
+    const int64_t resident = (int64_t)cus * blocks_per_cu * groups_per_block;
+    int64_t resident_shallow = 0;
+    KernelFn shallow = interleaved(op) ? pick_op(true) : nullptr;
+    int bpc1 = 0;
+    if (shallow && occupancy(reinterpret_cast<const void*>(shallow), block, &bpc1, &cus))
+        resident_shallow = (int64_t)cus * bpc1 * groups_per_block;
+    const Plan pl = plan_launch(op, p_in.rows, p_in.H, resident, resident_shallow);
     Params p = p_in;
-    int64_t resident = (int64_t)cus * blocks_per_cu * (L.waves == 1 ? 4 : 1);
-    // Interleaved ops with many rows per group: the one-slot ring (more resident
-    // groups, the latency covered by the other groups) streams faster; with few
-    // rows per group the deeper ring does (tuning; the bits never depend on it).
-    bool shallow = false;
-    if (interleaved(op) && p.rows >= ADALN_SHALLOW_ROWS_PER_GROUP * resident) {
-        KernelFn f1 = pick_op(true);
-        int bpc1 = 0;
-        if (f1 && occupancy(reinterpret_cast<const void*>(f1), block, &bpc1, &cus)) {
-            fn = f1;
-            shallow = true;
-            resident = (int64_t)cus * bpc1 * (L.waves == 1 ? 4 : 1);
-        }
-    }
-    const int S = shallow ? 1 : ring_slots(L.waves, L.chunks, op_gated(op));
-    if (interleaved(op)) {
-        // one group per resident group slot (at most one per row); a group's ring
-        // slots past its last row skip their arithmetic
-        p.groups = p.rows < resident ? p.rows : resident;
-        p.group_stride = 1;
-        p.step = p.groups;
-        p.span = p.rows;
-    } else {
-        // `per` contiguous rows per group, a multiple of S so that only the last
-        // group can end with idle ring slots; the group's descriptors address its
-        // rows with 32-bit byte offsets and the last pass reaches S rows past its
-        // range, so (per + S) rows stay below 2^31 bytes
-        const int64_t slots = resident * (L.waves == 1   ? ADALN_GROUP_OVERSUBSCRIBE_W1
-                                          : L.waves == 2 ? ADALN_GROUP_OVERSUBSCRIBE_W2
-                                                         : ADALN_GROUP_OVERSUBSCRIBE_W4);
-        const int64_t groups0 = p.rows < slots ? p.rows : slots;
-        int64_t per = (p.rows + groups0 - 1) / groups0;
-        per = (per + S - 1) / S * S;
-        const int64_t max_per = ((int64_t(0x7FFFFFFF) - 64) / (2 * p.H) - S) / S * S;
-        if (per > max_per) per = max_per;
-        p.groups = (p.rows + per - 1) / per;
-        p.group_stride = per;
-        p.step = 1;
-        p.span = per;
-    }
-    const int64_t groups = p.groups;
-    const int64_t blocks = L.waves == 1 ? (groups + 3) / 4 : groups;
-    hipLaunchKernelGGL(fn, dim3((unsigned)blocks), dim3(block), 0, stream, p);
+    p.groups = pl.groups;
+    p.group_stride = pl.group_stride;
+    p.step = pl.step;
+    p.span = pl.span;
+    if (pl.blocks > 0x7FFFFFFF) return hipErrorInvalidValue;
+    hipLaunchKernelGGL(pl.shallow ? shallow : deep, dim3((unsigned)pl.blocks), dim3(block), 0,
+                       stream, p);
     return hipGetLastError();
 }
 

@@ -90,11 +90,12 @@
 extern "C" {
 #endif
 
-#define ADALN_ABI_VERSION 6 /* 2: two waves per row for 2048 <= H < 4096;
+#define ADALN_ABI_VERSION 7 /* 2: two waves per row for 2048 <= H < 4096;
                               3: residual-gate LayerNorm, stream copy;
                               4: LayerNorm + modulate + FP8 quantisation;
                               5: per-head QK RMSNorm + RoPE;
-                              6: channel-first residual gating */
+                              6: channel-first residual gating;
+                              7: launch-plan diagnostic */
 
 typedef uint16_t adaln_bf16; /* raw bfloat16 bits */
 
@@ -264,6 +265,18 @@ adaln_status adaln_diag_finalize(const float* in, float* out, int64_t n, float e
  * device memory; out may not overlap in or *qscale (ADALN_ERR_OVERLAP). */
 adaln_status adaln_diag_quant_fp8(const float* in, uint8_t* out, int64_t n, const float* qscale,
                                   void* hip_stream);
+
+/* Diagnostic: the row-group plan of one launch of the fused kernel, computed on
+ * the host with no device work, for `resident` row groups fitting on the device at
+ * once with the deep ring and `resident_shallow` with the one-slot ring (0: not
+ * available).  op: 0 LayerNorm+modulate, 1 RMSNorm+scale/shift, 2 residual gate +
+ * RMSNorm, 3 residual gate + LayerNorm, 4 LayerNorm+modulate+FP8.  rows = B*T >= 1,
+ * H as for the entry points.  out[8] receives {one-slot ring (0/1), ring slots,
+ * groups, group stride, step, span, workgroups, threads per workgroup}: group g takes
+ * the rows g*stride + i*step below min(g*stride + span, rows).  ADALN_ERR_VALUE for
+ * an unknown op or a resident count below 1 (below 0 for resident_shallow). */
+adaln_status adaln_diag_launch_plan(int op, int64_t rows, int64_t H, int64_t resident,
+                                    int64_t resident_shallow, int64_t* out);
 
 /* Measurement aid: copy `bytes` bytes of device memory from src to dst with the
  * fused kernels' access style (16-byte non-temporal loads and stores), so that the

@@ -33,14 +33,14 @@ def declared_symbols():
 
 def test_header_symbols_are_exported(lib):
     names = declared_symbols()
-    assert len(names) == 21, names
+    assert len(names) == 22, names
     assert set(names) == set(_binding.EXPORTS)
     for n in names:
         assert hasattr(lib, n), n
 
 
 def test_abi_version_and_status_strings(lib):
-    assert A.adaln_abi_version() == A.ABI_VERSION == 6
+    assert A.adaln_abi_version() == A.ABI_VERSION == 7
     for s in range(8):
         assert len(A.adaln_status_string(s)) > 5
     assert A.adaln_status_string(99) == "unknown status"

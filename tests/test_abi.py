@@ -1,11 +1,9 @@
 """The C-ABI library loads, exports every symbol include/adaln.h declares, agrees
 with the oracle on the reduction layout, and rejects bad arguments before any GPU
 work (no compute call is made here, so these run without a GPU)."""
-import ctypes
 import os
 import re
 
-import numpy as np
 import pytest
 
 import diffusion_dit_adaln_amd as A

@@ -11,7 +11,8 @@
 // forms g = bf16(gate * update) and writes it to LDS as rows of tokens (16-byte
 // writes).  Phase 2 reads res along tokens (16-byte loads, eight lanes cover one
 // 128-byte hidden row), picks g for its (hidden, 8 tokens) from LDS and stores the
-// sum along tokens.  The LDS tile is unpadded; a 16-byte column chunk is stored at
+// sum along tokens (with T % 8 != 0 the token rows are not 16-byte aligned and
+// phase 2 moves single elements instead).  The LDS tile is unpadded; a 16-byte column chunk is stored at
 // chunk (hidden/8) XOR (token/8 mod 8), so the phase-2 reads of one instruction
 // (8 hidden rows x 8 token groups) fall in 32 distinct banks.
 #include <hip/hip_runtime.h>
@@ -25,6 +26,10 @@ namespace {
 
 constexpr int kTile = 64;
 
+// RAGGED: T % 8 != 0, so a token row of res/out is not 16-byte aligned; phase 2
+// then moves one element per access (lane tc of a hidden row takes the tokens
+// 8j + tc, so each access of the 8 lanes covers 8 consecutive tokens).
+template <bool RAGGED>
 __global__ __launch_bounds__(256) void residual_gate_cf(CFParams p) {
     const int tid = threadIdx.x;
     const int64_t tiles_h = (p.H + kTile - 1) / kTile;
@@ -62,6 +67,29 @@ __global__ __launch_bounds__(256) void residual_gate_cf(CFParams p) {
 
     // phase 2: residual rows (hidden), 8 lanes x 16 bytes per 64-token row
     const uint16_t* g16 = reinterpret_cast<const uint16_t*>(&g_lds[0][0]);
+    if (RAGGED) {
+#pragma unroll
+        for (int it = 0; it < 2; ++it) {
+            const int hl = (tid >> 3) + 32 * it;  // local hidden
+            const int tc = tid & 7;
+            const int64_t h = h0 + hl;
+            if (h >= p.H) continue;
+#pragma unroll
+            for (int j = 0; j < 8; ++j) {
+                const int tl = 8 * j + tc;  // local token
+                const int64_t t = t0 + tl;
+                if (t >= p.T) continue;
+                const int64_t off = (b * p.H + h) * p.T + t;
+                const float r = __uint_as_float((u32)__builtin_nontemporal_load(p.res + off) << 16);
+                // g of token tl at hidden hl: row tl, chunk (hl/8) ^ (tl/8 mod 8), slot hl%8
+                const int col = (((hl >> 3) ^ j) << 3) | (hl & 7);
+                const float g = __uint_as_float((u32)g16[tl * kTile + col] << 16);
+                const float s = r + g;
+                __builtin_nontemporal_store((uint16_t)(pack_bf16(s, 0.0f) & 0xFFFFu), p.out + off);
+            }
+        }
+        return;
+    }
 #pragma unroll
     for (int it = 0; it < 2; ++it) {
         const int hl = (tid >> 3) + 32 * it;  // local hidden
@@ -91,7 +119,10 @@ hipError_t launch_cf(const CFParams& p, hipStream_t stream) {
     const int64_t tiles = p.B * ((p.H + kTile - 1) / kTile) * ((p.T + kTile - 1) / kTile);
     // a grid holds fewer than 2^32 work-items
     if (tiles > int64_t(0xFFFFFFFF) / 256) return hipErrorInvalidValue;
-    hipLaunchKernelGGL(residual_gate_cf, dim3((unsigned)tiles), dim3(256), 0, stream, p);
+    if (p.T % 8 == 0)
+        hipLaunchKernelGGL(residual_gate_cf<false>, dim3((unsigned)tiles), dim3(256), 0, stream, p);
+    else
+        hipLaunchKernelGGL(residual_gate_cf<true>, dim3((unsigned)tiles), dim3(256), 0, stream, p);
     return hipGetLastError();
 }
 

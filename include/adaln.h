@@ -185,7 +185,7 @@ adaln_status adaln_qk_rmsnorm_rope(const adaln_bf16* q, const adaln_bf16* k,
  * with no .contiguous() copy):
  *   out[b][h][t] = bf16(res[b][h][t] + bf16(gate[b][h] * update[b][t][h]))
  * res, out: contiguous [B, H, T]; update: contiguous [B, T, H]; gate row b at
- * gate + b*gate_bstride (0 shares one vector; else >= H and % 8 == 0).  T % 8 == 0,
+ * gate + b*gate_bstride (0 shares one vector; else >= H and % 8 == 0).  Any T >= 0;
  * H % 8 == 0 and B*ceil(H/64)*ceil(T/64) <= 2^24 - 1 (one workgroup per 64x64 tile;
  * ADALN_ERR_SHAPE otherwise); pointers 16-byte aligned.  out may be
  * res itself (in-place update); any other overlap is ADALN_ERR_OVERLAP. */

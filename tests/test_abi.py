@@ -173,7 +173,7 @@ def test_channel_first_checks(lib):
     assert cf_check(lib, out=addr(0)) == OK              # in place
     assert cf_check(lib, out=addr(0) + 16) == OVERLAP    # partial overlap with res
     assert cf_check(lib, out=addr(1)) == OVERLAP         # over update
-    assert cf_check(lib, T=4604) == SHAPE
+    assert cf_check(lib, T=4333) == OK                   # ragged token count
     assert cf_check(lib, H=12) == SHAPE
     # one 64x64 tile per workgroup of 256: at most 2^24 - 1 tiles in a grid
     assert cf_check(lib, B=(1 << 24) - 1, T=8, H=8, gbs=0) == OK

@@ -24,7 +24,7 @@ def test_graph_replays_match_eager():
     qs = torch.tensor([0.0125], dtype=torch.float32, device="cuda")
     qkv = dev(synth.normal_bf16(rng, (64, 3, 8, 128)))
     cs = torch.from_numpy(synth.rope_cache(64, 128)).cuda()
-    Tc = 304                              # the channel-first layout needs T % 8 == 0
+    Tc = 300                              # a ragged token count for the channel-first op
     res_cf = dev(synth.normal_bf16(rng, (B, H, Tc)))
     upd_cf = dev(synth.normal_bf16(rng, (B, Tc, H)))
 

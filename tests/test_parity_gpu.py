@@ -478,7 +478,10 @@ def test_channel_first_full_size():
 
 
 @pytest.mark.parametrize("B,H,T", [(1, 8, 8), (2, 72, 40), (3, 136, 200), (1, 64, 64),
-                                   (2, 3072, 72), (1, 520, 4104)])
+                                   (2, 3072, 72), (1, 520, 4104),
+                                   # ragged token counts: rows of res/out not 16-byte aligned
+                                   (1, 8, 1), (2, 72, 7), (3, 136, 65), (2, 64, 63),
+                                   (1, 520, 129), (1, 3072, 4333)])
 def test_channel_first_shapes(B, H, T):
     say(f"[parity] channel-first B={B} H={H} T={T}")
     rng = np.random.default_rng(B * 7 + H + T)

@@ -479,7 +479,9 @@ def test_channel_first_full_size():
 
 @pytest.mark.parametrize("B,H,T", [(1, 8, 8), (2, 72, 40), (3, 136, 200), (1, 64, 64),
                                    (2, 3072, 72), (1, 520, 4104),
-                                   # ragged token counts: rows of res/out not 16-byte aligned
+                                   # token counts with rows of res/out 8-, 4- or 2-byte aligned
+                                   (2, 72, 12), (1, 136, 100), (1, 520, 4332), (2, 64, 6),
+                                   (3, 8, 98), (1, 3072, 4334),
                                    (1, 8, 1), (2, 72, 7), (3, 136, 65), (2, 64, 63),
                                    (1, 520, 129), (1, 3072, 4333)])
 def test_channel_first_shapes(B, H, T):

@@ -351,6 +351,23 @@ def cpu_baseline(wl, budget_s: float, y_gpu=None):
           "qk": lambda: O.qk_rmsnorm_rope(wl.q, wl.k, wl.q_weight, wl.k_weight, wl.cos_sin,
                                           wl.eps),
           "cf": lambda: O.residual_gate_channel_first(wl.res, wl.update, wl.gate)}[wl.op]
+    # the same oracle call on a slice of rows [lo, hi) of the flattened B*T rows
+    # (fused ops, one batch entry: B == 1), for the all-cores run below
+    fn_rows = None
+    if wl.op in ("ln", "rms", "rg", "rgln", "lnq") and wl.x.shape[0] == 1:
+        def fn_rows(lo, hi):
+            sl = slice(lo, hi)
+            xs = wl.x[:, sl]
+            rs = wl.res[:, sl] if wl.res is not None else None
+            return {"ln": lambda: O.layernorm_modulate(xs, wl.scale, wl.shift, wl.eps),
+                    "rms": lambda: O.rmsnorm_scale_shift(xs, wl.weight, wl.scale, wl.shift,
+                                                         wl.eps),
+                    "rg": lambda: O.residual_gate_rmsnorm_scale_shift(
+                        rs, xs, wl.gate, wl.weight, wl.scale, wl.shift, wl.eps),
+                    "rgln": lambda: O.residual_gate_layernorm_modulate(
+                        rs, xs, wl.gate, wl.scale, wl.shift, wl.eps),
+                    "lnq": lambda: O.layernorm_modulate_fp8(xs, wl.scale, wl.shift, wl.qscale,
+                                                            wl.eps)}[wl.op]()
     first = fn()  # warm (page in the library and the arrays)
     reps = 0
     t0 = time.perf_counter()
@@ -361,6 +378,7 @@ def cpu_baseline(wl, budget_s: float, y_gpu=None):
         if el >= budget_s:
             break
     os.sched_setaffinity(0, set(affinity))
+    par = cpu_all_cores(wl, fn_rows, budget_s / 2, len(affinity), first)
     out = {"value": round(wl.algorithmic_bytes() * reps / el / 1e9, 4), "unit": "GB/s",
            "cores": 1, "kind": "oracle",
            "rows_per_s": round(workload_rows(wl) * reps / el, 1),
@@ -368,6 +386,8 @@ def cpu_baseline(wl, budget_s: float, y_gpu=None):
                      f"repetitions, single-threaded C oracle pinned to core {affinity[0]}, "
                      f"{el:.1f} s",
            "cpu_model": cpu_model(), "host_cores_available": len(affinity)}
+    if par is not None:
+        out["all_cores"] = par
     if y_gpu is not None:
         # the fused ops' y (the last of r, y); QK's (q_out, k_out); channel-first's out
         if wl.op == "qk":
@@ -391,6 +411,37 @@ def workload_rows(wl) -> int:
     if wl.op == "cf":
         return wl.res.shape[0] * wl.res.shape[2]
     return wl.x.shape[0] * wl.x.shape[1]
+
+
+def cpu_all_cores(wl, fn_rows, budget_s: float, cores: int, single):
+    """The same oracle, rows split evenly over `cores` threads (the C oracle holds no
+    shared state and ctypes releases the GIL), timed for about budget_s seconds; its
+    output must equal the single-threaded one bit for bit.  None when not applicable."""
+    if fn_rows is None or cores < 2:
+        return None
+    from concurrent.futures import ThreadPoolExecutor
+    rows = wl.x.shape[1]
+    cuts = [rows * i // cores for i in range(cores + 1)]
+    parts = [(cuts[i], cuts[i + 1]) for i in range(cores) if cuts[i + 1] > cuts[i]]
+
+    def last(r):
+        return r[-1] if isinstance(r, tuple) else r
+
+    with ThreadPoolExecutor(len(parts)) as pool:
+        got = list(pool.map(lambda lh: last(fn_rows(*lh)), parts))
+        same = bool(np.array_equal(np.concatenate(got, axis=1), last(single)))
+        reps = 0
+        t0 = time.perf_counter()
+        while True:
+            list(pool.map(lambda lh: fn_rows(*lh), parts))
+            reps += 1
+            el = time.perf_counter() - t0
+            if el >= budget_s:
+                break
+    return {"value": round(wl.algorithmic_bytes() * reps / el / 1e9, 4), "unit": "GB/s",
+            "cores": len(parts), "equals_single_core": same,
+            "sample": f"the whole workload x {reps}, rows split over {len(parts)} threads, "
+                      f"{el:.1f} s"}
 
 
 def inputs_sha256(wl) -> dict:

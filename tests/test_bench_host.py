@@ -81,6 +81,9 @@ def test_cpu_baseline_on_a_small_workload():
     out = bench.cpu_baseline(wl, 0.05)
     assert out["kind"] == "oracle" and out["cores"] == 1 and out["value"] > 0
     assert out["unit"] == "GB/s" and "pinned to core" in out["sample"]
+    if len(__import__("os").sched_getaffinity(0)) > 1:
+        par = out["all_cores"]
+        assert par["cores"] > 1 and par["equals_single_core"] is True and par["value"] > 0
     # the comparison with a GPU output of the same inputs (here the oracle's own bits)
     from oracle import oracle as O
     y = O.layernorm_modulate(wl.x, wl.scale, wl.shift, wl.eps)

@@ -86,6 +86,15 @@ __device__ __forceinline__ void st8_stream(rsrc_t r, int off, u32 lo, u32 hi) {
 __device__ __forceinline__ float clamp448(float v) {
     return __builtin_elementwise_minimum(__builtin_elementwise_maximum(v, -448.0f), 448.0f);
 }
+// The same with the clamp as one median of three: exact for every input except a
+// NaN (which the median does not keep), so only for values known not to be NaN.
+__device__ __forceinline__ u32 quant4_no_nan(float a, float b, float c, float d) {
+    const u32 lo = __builtin_amdgcn_cvt_pk_fp8_f32(__builtin_amdgcn_fmed3f(a, -448.0f, 448.0f),
+                                                   __builtin_amdgcn_fmed3f(b, -448.0f, 448.0f), 0,
+                                                   false);
+    return __builtin_amdgcn_cvt_pk_fp8_f32(__builtin_amdgcn_fmed3f(c, -448.0f, 448.0f),
+                                           __builtin_amdgcn_fmed3f(d, -448.0f, 448.0f), lo, true);
+}
 __device__ __forceinline__ u32 quant4(float a, float b, float c, float d) {
     const u32 lo = __builtin_amdgcn_cvt_pk_fp8_f32(clamp448(a), clamp448(b), 0, false);
     return __builtin_amdgcn_cvt_pk_fp8_f32(clamp448(c), clamp448(d), lo, true);

@@ -362,9 +362,23 @@ __global__ __launch_bounds__(256) void fused_norm_modulate(Params p) {
         else st16_stream(r, off, make_uint4(w[0], w[1], w[2], w[3]));
     };
 
+    // LN+FP8: whether every modulation constant of this lane is finite; with finite
+    // row statistics too, no output can be NaN and the clamp can be one median
+    auto consts_finite = [&]() {
+        bool fin = true;
+#pragma unroll
+        for (int c = 0; c < C; ++c)
+#pragma unroll
+            for (int v = 0; v < 8; ++v)
+                fin = fin && __builtin_isfinite(K_a(c, v)) && __builtin_isfinite(K_h(c, v));
+        return fin;
+    };
     int64_t b = r_begin / p.T;
     int64_t t_in = r_begin - b * p.T;
     load_consts(b);
+    // and a finite, non-zero 1/scale (0 * inf and inf * 0 are the other NaN sources)
+    const bool inv_ok = FP8 && __builtin_isfinite(inv_qscale) && inv_qscale != 0.0f;
+    bool fast_q = inv_ok && consts_finite();
 
     // A ring of S row slots: slot k holds the group's row row0 + k*G; after a row is
     // finished its slot is refilled with the group's row S ahead, so S rows' loads
@@ -441,7 +455,7 @@ __global__ __launch_bounds__(256) void fused_norm_modulate(Params p) {
         if (!IL || row < r_end) {
 
         // Statistic: ordered per-lane chain, butterfly, cross-wave pairs, finalize.
-        float mean = 0.0f, rstd;
+        float mean = 0.0f, rstd, m2_row = 0.0f;
         if (LNSTAT) {
             float wm = 0.0f, w2 = 0.0f;
 #pragma unroll
@@ -503,6 +517,7 @@ __global__ __launch_bounds__(256) void fused_norm_modulate(Params p) {
                 w2 = w.m2;
             }
             mean = wm;
+            m2_row = w2;
             rstd = finalize(w2 / (float)H, p.eps);
         } else {
             float s = 0.0f;
@@ -563,8 +578,14 @@ __global__ __launch_bounds__(256) void fused_norm_modulate(Params p) {
                 }
             }
             if (FP8) {
-                out[0] = quant4(qv[0], qv[1], qv[2], qv[3]);
-                out[1] = quant4(qv[4], qv[5], qv[6], qv[7]);
+                if (fast_q && __builtin_isfinite(mean) && __builtin_isfinite(m2_row) &&
+                    __builtin_isfinite(rstd)) {
+                    out[0] = quant4_no_nan(qv[0], qv[1], qv[2], qv[3]);
+                    out[1] = quant4_no_nan(qv[4], qv[5], qv[6], qv[7]);
+                } else {
+                    out[0] = quant4(qv[0], qv[1], qv[2], qv[3]);
+                    out[1] = quant4(qv[4], qv[5], qv[6], qv[7]);
+                }
             }
             if (!IL) store_out(ry, off_of(row, c, OES), out);
         }
@@ -591,6 +612,7 @@ __global__ __launch_bounds__(256) void fused_norm_modulate(Params p) {
                     t_in = 0;
                 }
                 load_consts(b);
+                if (FP8) fast_q = inv_ok && consts_finite();
             }
         }
     }

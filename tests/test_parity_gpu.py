@@ -284,6 +284,57 @@ def test_nonfinite_inputs_give_nan_in_the_same_places():
         assert_bits_equal(got[~gn], want[~wn], "finite outputs")
 
 
+@pytest.mark.parametrize("H", [1024, 3072, 4096, 3080, 520])
+def test_lnq_nonfinite_modulation_and_overflowing_rows(H):
+    """LN+FP8 where the output can be NaN for reasons other than the row: scale and
+    shift with NaN and infinities in some columns, a scale so large that yn*(1+scale)
+    overflows, rows whose squared deviations overflow, zero rows (0*inf); batch entry
+    0 has finite vectors, entry 1 the bad columns, so row groups cross between them."""
+    say(f"[parity] lnq non-finite modulation H={H}")
+    rng = np.random.default_rng(H + 11)
+    B, T = 2, 700
+    x = synth.normal_bf16(rng, (B, T, H))
+    big = synth.f32_to_bf16_bits(np.array([3.0e38, -3.0e38, 1.0e38], np.float32))
+    for b in range(B):
+        x[b, 5, : H // 2] = big[0]
+        x[b, 5, H // 2:] = big[1]            # squared deviations overflow
+        x[b, 9, :] = big[2]                  # constant huge row
+        x[b, 13, :] = 0                      # zero row: yn = 0
+        x[b, 17, 3] = 0x7F80                 # inf in a row
+    sc = synth.normal_bf16(rng, (B, H), 0.1)
+    sh = synth.normal_bf16(rng, (B, H), 0.1)
+    cols = rng.choice(H, 12, replace=False)
+    sc[1, cols[0]] = 0x7FC0                  # NaN scale
+    sc[1, cols[1]] = 0x7F80                  # +inf scale (a = inf)
+    sc[1, cols[2]] = 0xFF80                  # -inf scale
+    sc[1, cols[3]] = synth.f32_to_bf16_bits(np.array([1.0e37], np.float32))[0]
+    sh[1, cols[3]] = 0xFF80                  # p may overflow to inf, shift -inf
+    sh[1, cols[4]] = 0x7FC0                  # NaN shift
+    sh[1, cols[5]] = 0x7F80                  # +inf shift
+    sh[1, cols[6]] = 0xFF80                  # -inf shift
+    sc[1, cols[7]] = synth.f32_to_bf16_bits(np.array([3.0e38], np.float32))[0]
+    for qs in (0.0125, 1.0):
+        check_lnq(x, sc, sh, qs, f"lnq non-finite H={H} qscale={qs}")
+
+
+@pytest.mark.parametrize("qscale", [0.0, float("inf"), float("nan"), -0.5, 1e-38, 3.0e38])
+@pytest.mark.parametrize("eps", [0.0, 1e-6])
+def test_lnq_special_scales_and_zero_eps(qscale, eps):
+    """LN+FP8 with a quantisation scale of 0 (1/scale = inf), inf (0), NaN, negative,
+    tiny or huge, and eps 0 with constant rows (a zero variance gives rstd = inf)."""
+    say(f"[parity] lnq qscale={qscale} eps={eps}")
+    rng = np.random.default_rng(5)
+    B, T, H = 1, 40, 3072
+    x = synth.normal_bf16(rng, (B, T, H))
+    x[0, 3, :] = 0x3F80                      # constant row
+    x[0, 4, :] = 0                           # zero row
+    x[0, 5, 17] = 0x7F80                     # inf in a row
+    sc = synth.normal_bf16(rng, (B, H), 0.1)
+    sh = synth.normal_bf16(rng, (B, H), 0.1)
+    sh[0, :8] = 0                            # y = 0 where yn = 0
+    check_lnq(x, sc, sh, qscale, f"lnq qscale={qscale} eps={eps}", eps)
+
+
 # --------------------------------------------------------------------------
 # shapes: empty, single rows, shared vectors
 # --------------------------------------------------------------------------

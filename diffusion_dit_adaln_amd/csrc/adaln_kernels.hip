@@ -364,6 +364,7 @@ __global__ __launch_bounds__(256) void fused_norm_modulate(Params p) {
 
     // LN+FP8: whether every modulation constant of this lane is finite; with finite
     // row statistics too, no output can be NaN and the clamp can be one median
+    // (a wave-uniform answer: true only if it holds in every lane of the wave)
     auto consts_finite = [&]() {
         bool fin = true;
 #pragma unroll
@@ -371,7 +372,7 @@ __global__ __launch_bounds__(256) void fused_norm_modulate(Params p) {
 #pragma unroll
             for (int v = 0; v < 8; ++v)
                 fin = fin && __builtin_isfinite(K_a(c, v)) && __builtin_isfinite(K_h(c, v));
-        return fin;
+        return __builtin_amdgcn_ballot_w64(!fin) == 0;
     };
     int64_t b = r_begin / p.T;
     int64_t t_in = r_begin - b * p.T;
@@ -545,6 +546,12 @@ __global__ __launch_bounds__(256) void fused_norm_modulate(Params p) {
             rstd = finalize(s / (float)H, p.eps);
         }
 
+        // LN+FP8: the row statistics are the same in every lane; the one-median clamp
+        // is exact when no output of the row can be NaN (see consts_finite)
+        const bool fast_row =
+            FP8 && fast_q &&
+            __builtin_amdgcn_ballot_w64(!(__builtin_isfinite(mean) && __builtin_isfinite(m2_row) &&
+                                          __builtin_isfinite(rstd))) == 0;
         // Normalise from registers, modulate.
 #pragma unroll
         for (int c = 0; c < C; ++c) {
@@ -578,8 +585,7 @@ __global__ __launch_bounds__(256) void fused_norm_modulate(Params p) {
                 }
             }
             if (FP8) {
-                if (fast_q && __builtin_isfinite(mean) && __builtin_isfinite(m2_row) &&
-                    __builtin_isfinite(rstd)) {
+                if (fast_row) {
                     out[0] = quant4_no_nan(qv[0], qv[1], qv[2], qv[3]);
                     out[1] = quant4_no_nan(qv[4], qv[5], qv[6], qv[7]);
                 } else {

@@ -12,7 +12,7 @@ import os
 import torch
 
 _PKG = os.path.dirname(os.path.abspath(__file__))
-ABI_VERSION = 7
+ABI_VERSION = 8
 
 STATUS_NAMES = {0: "ADALN_OK", 1: "ADALN_ERR_NULL", 2: "ADALN_ERR_SHAPE", 3: "ADALN_ERR_ALIGN",
                 4: "ADALN_ERR_STRIDE", 5: "ADALN_ERR_OVERLAP", 6: "ADALN_ERR_VALUE",
@@ -77,10 +77,10 @@ def load_library():
         "adaln_check_residual_gate_layernorm_modulate": [P, P, P, P, P, P, P, I, I, I, I, I, I, F],
         "adaln_reduction_layout": [I, ctypes.POINTER(S), ctypes.POINTER(S), ctypes.POINTER(S)],
         "adaln_diag_round_bf16": [P, P, I, P],
-        "adaln_diag_finalize": [P, P, I, F, P],
+        "adaln_diag_finalize": [P, P, I, I, F, P],
         "adaln_diag_stream_copy": [P, P, I, P],
         "adaln_diag_quant_fp8": [P, P, I, P, P],
-        "adaln_diag_launch_plan": [S, I, I, I, I, ctypes.POINTER(I)],
+        "adaln_diag_launch_plan": [S, I, I, I, I, I, ctypes.POINTER(I)],
     }
     for name, args in sig.items():
         fn = getattr(lib, name)
@@ -389,16 +389,17 @@ def adaln_reduction_layout(H: int):
 
 
 OPS = {"ln": 0, "rms": 1, "rg": 2, "rgln": 3, "lnq": 4}
-PLAN_FIELDS = ("shallow", "slots", "groups", "group_stride", "step", "span", "blocks",
-               "block_threads")
+PLAN_FIELDS = ("shallow", "slots", "groups", "gpb", "blk_rows", "group_stride", "step", "span",
+               "blocks", "block_threads")
 
 
-def adaln_diag_launch_plan(op: str, rows: int, H: int, resident: int,
+def adaln_diag_launch_plan(op: str, rows: int, H: int, T: int, resident: int,
                            resident_shallow: int = 0) -> dict:
-    """The fused kernel's row-group plan for one launch (host only; see the header)."""
+    """The fused kernel's row-group plan for one launch of B = rows / T batch entries
+    (host only; see the header)."""
     lib = load_library()
-    out = (ctypes.c_int64 * 8)()
-    _check(lib.adaln_diag_launch_plan(OPS[op], rows, H, resident, resident_shallow, out),
+    out = (ctypes.c_int64 * len(PLAN_FIELDS))()
+    _check(lib.adaln_diag_launch_plan(OPS[op], rows, H, T, resident, resident_shallow, out),
            "adaln_diag_launch_plan")
     return dict(zip(PLAN_FIELDS, list(out)))
 
@@ -423,15 +424,17 @@ def adaln_diag_round_bf16(x: torch.Tensor, stream=None) -> torch.Tensor:
     return out
 
 
-def adaln_diag_finalize(x: torch.Tensor, eps: float = 1e-6, stream=None) -> torch.Tensor:
-    """Device rstd = RN(1/RN(sqrt(RN(x + eps)))) of a float32 tensor (the kernels' step)."""
+def adaln_diag_finalize(x: torch.Tensor, eps: float = 1e-6, H: int = 1,
+                        stream=None) -> torch.Tensor:
+    """Device rstd = RN(1/RN(sqrt(RN(RN(x / H) + eps)))) of a float32 tensor of row
+    statistics over H elements (the kernels' step)."""
     lib = load_library()
     if x.dtype != torch.float32 or not x.is_contiguous():
         raise ValueError("expected a contiguous float32 tensor")
     _on(x.device)
     out = torch.empty_like(x)
     _check(_call(x.device, lib.adaln_diag_finalize, x.data_ptr(), out.data_ptr(), x.numel(),
-                 _eps(eps), stream=stream), "adaln_diag_finalize")
+                 int(H), _eps(eps), stream=stream), "adaln_diag_finalize")
     return out
 
 

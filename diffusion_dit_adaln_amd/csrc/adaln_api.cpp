@@ -414,23 +414,26 @@ const char* adaln_status_string(adaln_status status) {
 
 int adaln_abi_version(void) { return ADALN_ABI_VERSION; }
 
-adaln_status adaln_diag_launch_plan(int op, int64_t rows, int64_t H, int64_t resident,
+adaln_status adaln_diag_launch_plan(int op, int64_t rows, int64_t H, int64_t T, int64_t resident,
                                     int64_t resident_shallow, int64_t* out) {
     if (!out) return ADALN_ERR_NULL;
     if (op < adaln::OP_LN || op > adaln::OP_LNQ) return ADALN_ERR_VALUE;
     if (rows < 1 || H < 8 || H > kMaxH || (H % 8) != 0) return ADALN_ERR_SHAPE;
     if (rows > INT64_MAX / (2 * H)) return ADALN_ERR_SHAPE;
+    if (T < 1 || T > rows || rows % T != 0) return ADALN_ERR_SHAPE;
     if (resident < 1 || resident_shallow < 0) return ADALN_ERR_VALUE;
     const adaln::Plan pl =
-        adaln::plan_launch(static_cast<adaln::Op>(op), rows, H, resident, resident_shallow);
+        adaln::plan_launch(static_cast<adaln::Op>(op), rows, H, T, resident, resident_shallow);
     out[0] = pl.shallow ? 1 : 0;
     out[1] = pl.slots;
     out[2] = pl.groups;
-    out[3] = pl.group_stride;
-    out[4] = pl.step;
-    out[5] = pl.span;
-    out[6] = pl.blocks;
-    out[7] = pl.block_threads;
+    out[3] = pl.gpb;
+    out[4] = pl.blk_rows;
+    out[5] = pl.group_stride;
+    out[6] = pl.step;
+    out[7] = pl.span;
+    out[8] = pl.blocks;
+    out[9] = pl.block_threads;
     return ADALN_OK;
 }
 
@@ -447,9 +450,9 @@ adaln_status adaln_diag_round_bf16(const float* in, adaln_bf16* out, int64_t n, 
                : ADALN_ERR_LAUNCH;
 }
 
-adaln_status adaln_diag_finalize(const float* in, float* out, int64_t n, float eps,
+adaln_status adaln_diag_finalize(const float* in, float* out, int64_t n, int64_t H, float eps,
                                  void* hip_stream) {
-    if (n < 0) return ADALN_ERR_SHAPE;
+    if (n < 0 || H < 1 || H > kMaxH) return ADALN_ERR_SHAPE;
     if (!(eps >= 0.0f) || !isfinite(eps)) return ADALN_ERR_VALUE;
     if (n == 0) return ADALN_OK;
     if (!in || !out) return ADALN_ERR_NULL;
@@ -459,7 +462,7 @@ adaln_status adaln_diag_finalize(const float* in, float* out, int64_t n, float e
         overlaps(Span{(uintptr_t)out, (uintptr_t)out + (uintptr_t)(4 * n)},
                  Span{(uintptr_t)in, (uintptr_t)in + (uintptr_t)(4 * n)}))
         return ADALN_ERR_OVERLAP;
-    return adaln::launch_diag_finalize(in, out, n, eps, (hipStream_t)hip_stream) == hipSuccess
+    return adaln::launch_diag_finalize(in, out, n, H, eps, (hipStream_t)hip_stream) == hipSuccess
                ? ADALN_OK
                : ADALN_ERR_LAUNCH;
 }

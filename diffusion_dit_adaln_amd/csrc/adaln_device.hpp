@@ -157,5 +157,47 @@ __device__ __forceinline__ float finalize(float stat, float eps) {
     return 1.0f / root;
 }
 
+// rstd = RN(1 / RN(sqrt(RN(RN(S / H) + eps)))) for a row's statistic S (sum of
+// squares or M2) over H elements, rH = RN(1 / H); the same bits as finalize(S / H,
+// eps).  When every active lane of the wave is in the range below, shorter exact
+// sequences replace the general divide and square root (one uniform branch; the
+// general path only when some lane is outside it):
+//  - S / H: q0 = RN(S * rH) is within 1.5 ulp of S / H, its remainder S - q0 * H is
+//    exact (a multiple of ulp(q0) below 2^14 ulp(q0)), and one correction
+//    RN(q0 + r * rH) gives RN(S / H) (checked exhaustively on the CPU for every
+//    significand of S and every H = 8, 16, ..., 8192; the steps scale with S by
+//    powers of two while S stays in [2^-64, 2^64]; for S = 0 every step is 0);
+//  - sqrt: the hardware root s, then the neighbour below or above it when the
+//    exact residual v - (s -/+ ulp) * s says the root lies beyond the midpoint
+//    (checked on the CPU for every v in [1, 4) with s off by up to one ulp either
+//    way; scales by powers of four for v in [2^-100, 2^100]);
+//  - 1 / s: one Newton step from the hardware reciprocal, y0 + y0 * (1 - s * y0),
+//    which rounds correctly from any faithful y0 except for a significand of all
+//    ones (checked on the CPU for every significand), so that case keeps the
+//    general divide.
+// POW2: H is a power of two (S * rH is then exact).
+template <bool POW2>
+__device__ __forceinline__ float row_rstd(float S, float H, float rH, float eps) {
+    // every step computed unconditionally, then one uniform test
+    float q = S * rH;
+    if (!POW2) {
+        const float r = __builtin_fmaf(-q, H, S);
+        q = __builtin_fmaf(r, rH, q);
+    }
+    const float v = q + eps;
+    const float s0 = __builtin_amdgcn_sqrtf(v);
+    const float lo = __uint_as_float(__float_as_uint(s0) - 1u);
+    const float hi = __uint_as_float(__float_as_uint(s0) + 1u);
+    const float t = __builtin_fmaf(-lo, s0, v) <= 0.0f ? lo : s0;
+    const float s = __builtin_fmaf(-hi, s0, v) > 0.0f ? hi : t;  // RN(sqrt(v))
+    const float y0 = __builtin_amdgcn_rcpf(s);
+    const float e = __builtin_fmaf(-s, y0, 1.0f);
+    const float y = __builtin_fmaf(e, y0, y0);  // RN(1 / s)
+    const bool ok = ((S == 0.0f) | ((S >= 0x1p-64f) & (S <= 0x1p64f))) & (v >= 0x1p-100f) &
+                    (v <= 0x1p100f) & ((__float_as_uint(s) & 0x7FFFFFu) != 0x7FFFFFu);
+    if (__builtin_expect(__builtin_amdgcn_ballot_w64(!ok) != 0, 0)) return finalize(S / H, eps);
+    return y;
+}
+
 }  // namespace
 }  // namespace adaln

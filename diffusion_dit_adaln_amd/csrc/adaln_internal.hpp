@@ -33,9 +33,13 @@ struct Params {
     int64_t gate_bs, scale_bs, shift_bs;
     float eps;
     int64_t groups;          // row groups: a wave (H < 2048) or a workgroup of 2 or 4 waves
-    int64_t group_stride;    // group g's first row is g * group_stride
+    // The rows fall into blocks of blk_rows rows (the last may be short), each with
+    // gpb groups: group g works in block g / gpb as its (g % gpb)-th group.
+    int64_t gpb;             // groups per block (< 2^31)
+    int64_t blk_rows;        // rows per block (T or rows)
+    int64_t group_stride;    // a group's first row is its block's first + (g % gpb) * group_stride
     int64_t step;            // rows between a group's consecutive rows
-    int64_t span;            // a group's rows lie below first row + span (and below rows)
+    int64_t span;            // a group's rows lie below first row + span (and its block's end)
 };
 
 // Reduction layout of H (the numerics contract): waves per row, lanes, chunks.
@@ -83,17 +87,18 @@ bool occupancy(const void* fn, int block, int* blocks_per_cu, int* cus);
 struct Plan {
     bool shallow;          // the one-slot ring kernel
     int slots;             // ring depth S
-    int64_t groups, group_stride, step, span;
+    int64_t groups, gpb, blk_rows, group_stride, step, span;
     int64_t blocks;        // workgroups launched
     int block_threads;     // threads per workgroup
 };
-Plan plan_launch(Op op, int64_t rows, int64_t H, int64_t resident, int64_t resident_shallow);
+Plan plan_launch(Op op, int64_t rows, int64_t H, int64_t T, int64_t resident,
+                 int64_t resident_shallow);
 
 // Launch the fused kernel for `op`; returns the HIP error of the launch.
 hipError_t launch(Op op, const Params& p, hipStream_t stream);
 
 hipError_t launch_diag_round(const float* in, uint16_t* out, int64_t n, hipStream_t stream);
-hipError_t launch_diag_finalize(const float* in, float* out, int64_t n, float eps,
+hipError_t launch_diag_finalize(const float* in, float* out, int64_t n, int64_t H, float eps,
                                 hipStream_t stream);
 hipError_t launch_diag_copy(const void* src, void* dst, int64_t n16, hipStream_t stream);
 hipError_t launch_diag_quant(const float* in, uint8_t* out, int64_t n, const float* qscale,

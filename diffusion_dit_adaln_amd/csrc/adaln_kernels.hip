@@ -243,13 +243,18 @@ __global__ __launch_bounds__(256) void fused_norm_modulate(Params p) {
     // a whole wave (W == 1) or workgroup (W > 1) leaves, before any barrier
     if (group >= p.groups) return;
     // Group g owns the rows r_begin, r_begin + step, ... below r_end: a contiguous
-    // range (step 1) or every G-th row (step G, the interleaved assignment).
-    const int64_t r_begin = group * p.group_stride;
-    const int64_t r_end = r_begin + p.span < p.rows ? r_begin + p.span : p.rows;
+    // range (step 1) or every gpb-th row of its block (the interleaved assignment).
+    const int64_t blk = p.gpb == p.groups ? 0 : (int64_t)((uint32_t)group / (uint32_t)p.gpb);
+    const int64_t blk_begin = blk * p.blk_rows;
+    const int64_t r_begin = blk_begin + (group - blk * p.gpb) * p.group_stride;
+    int64_t r_end = r_begin + p.span < p.rows ? r_begin + p.span : p.rows;
+    if (r_end > blk_begin + p.blk_rows) r_end = blk_begin + p.blk_rows;
     if (r_begin >= r_end) return;
     const int64_t step = IL ? p.step : 1;
     const int t = (W == 1) ? lane : wave * 64 + lane;  // lane index within the row
     const int64_t H = TAIL ? p.H : HFULL;
+    constexpr bool POW2H = !TAIL && (HFULL & (HFULL - 1)) == 0;
+    const float rH = 1.0f / (float)H;  // a constant unless the row is ragged
 
     __shared__ float xwave[2][4][3];  // cross-wave partials, double-buffered by row parity
 
@@ -365,16 +370,21 @@ __global__ __launch_bounds__(256) void fused_norm_modulate(Params p) {
     // LN+FP8: whether every modulation constant of this lane is finite; with finite
     // row statistics too, no output can be NaN and the clamp can be one median
     // (a wave-uniform answer: true only if it holds in every lane of the wave)
+    // (the NaN-propagating maximum of the magnitudes is finite exactly when every
+    // value is: a NaN stays NaN, an infinity stays infinite)
     auto consts_finite = [&]() {
-        bool fin = true;
+        float m = 0.0f;
 #pragma unroll
         for (int c = 0; c < C; ++c)
 #pragma unroll
             for (int v = 0; v < 8; ++v)
-                fin = fin && __builtin_isfinite(K_a(c, v)) && __builtin_isfinite(K_h(c, v));
-        return __builtin_amdgcn_ballot_w64(!fin) == 0;
+                m = __builtin_elementwise_maximum(
+                    m, __builtin_elementwise_maximum(__builtin_fabsf(K_a(c, v)),
+                                                     __builtin_fabsf(K_h(c, v))));
+        return __builtin_amdgcn_ballot_w64(!__builtin_isfinite(m)) == 0;
     };
-    int64_t b = r_begin / p.T;
+    // blocks of one batch entry each: the block is the batch entry
+    int64_t b = p.blk_rows == p.T ? blk : r_begin / p.T;
     int64_t t_in = r_begin - b * p.T;
     load_consts(b);
     // and a finite, non-zero 1/scale (0 * inf and inf * 0 are the other NaN sources)
@@ -519,7 +529,7 @@ __global__ __launch_bounds__(256) void fused_norm_modulate(Params p) {
             }
             mean = wm;
             m2_row = w2;
-            rstd = finalize(w2 / (float)H, p.eps);
+            rstd = row_rstd<POW2H>(w2, (float)H, rH, p.eps);
         } else {
             float s = 0.0f;
 #pragma unroll
@@ -543,6 +553,8 @@ __global__ __launch_bounds__(256) void fused_norm_modulate(Params p) {
                     s = a + bb;
                 }
             }
+            // (the general steps here: the shortcut's uniform test costs the RMS ops
+            // more latency than its instructions save)
             rstd = finalize(s / (float)H, p.eps);
         }
 
@@ -650,10 +662,11 @@ __global__ __launch_bounds__(256) void diag_round(const float* in, uint16_t* out
 }
 
 __global__ __launch_bounds__(256) void diag_finalize(const float* in, float* out, int64_t n,
-                                                     float eps) {
+                                                     float H, float eps) {
+    const float rH = 1.0f / H;
     for (int64_t i = (int64_t)blockIdx.x * blockDim.x + threadIdx.x; i < n;
          i += (int64_t)gridDim.x * blockDim.x)
-        out[i] = finalize(in[i], eps);
+        out[i] = row_rstd<false>(in[i], H, rH, eps);
 }
 
 // A plain streaming copy with the fused kernel's memory access style (16-byte
@@ -796,7 +809,8 @@ Layout layout_of(int64_t H) {
     return L;
 }
 
-Plan plan_launch(Op op, int64_t rows, int64_t H, int64_t resident, int64_t resident_shallow) {
+Plan plan_launch(Op op, int64_t rows, int64_t H, int64_t T, int64_t resident,
+                 int64_t resident_shallow) {
     const Layout L = layout_of(H);
     Plan pl{};
     pl.block_threads = L.waves == 1 ? 256 : 64 * L.waves;
@@ -810,11 +824,26 @@ Plan plan_launch(Op op, int64_t rows, int64_t H, int64_t resident, int64_t resid
     pl.slots = S;
     if (interleaved(op)) {
         // one group per resident group slot (at most one per row); a group's ring
-        // slots past its last row skip their arithmetic
-        pl.groups = rows < resident ? rows : resident;
+        // slots past its last row skip their arithmetic.  With several batch entries
+        // and enough groups, each entry gets its own share of the groups, so that a
+        // group never changes entry (its per-column constants are loaded once), as
+        // long as the split leaves at most 1/16 of the slots idle.
+        const int64_t G = rows < resident ? rows : resident;
+        const int64_t B = rows / T;
+        const int64_t per_entry = B > 1 ? (G / B < T ? G / B : T) : 0;
+        if (per_entry > 0 && 16 * (G - per_entry * B) <= G) {
+            pl.groups = per_entry * B;
+            pl.gpb = per_entry;
+            pl.blk_rows = T;
+            pl.span = T;
+        } else {
+            pl.groups = G;
+            pl.gpb = G;
+            pl.blk_rows = rows;
+            pl.span = rows;
+        }
         pl.group_stride = 1;
-        pl.step = pl.groups;
-        pl.span = rows;
+        pl.step = pl.gpb;
     } else {
         // `per` contiguous rows per group, a multiple of S so that only the last
         // group can end with idle ring slots; the group's descriptors address its
@@ -829,6 +858,8 @@ Plan plan_launch(Op op, int64_t rows, int64_t H, int64_t resident, int64_t resid
         const int64_t max_per = ((int64_t(0x7FFFFFFF) - 64) / (2 * H) - S) / S * S;
         if (per > max_per) per = max_per;
         pl.groups = (rows + per - 1) / per;
+        pl.gpb = pl.groups;
+        pl.blk_rows = rows;
         pl.group_stride = per;
         pl.step = 1;
         pl.span = per;
@@ -865,13 +896,15 @@ hipError_t launch(Op op, const Params& p_in, hipStream_t stream) {
     int bpc1 = 0;
     if (shallow && occupancy(reinterpret_cast<const void*>(shallow), block, &bpc1, &cus))
         resident_shallow = (int64_t)cus * bpc1 * groups_per_block;
-    const Plan pl = plan_launch(op, p_in.rows, p_in.H, resident, resident_shallow);
+    const Plan pl = plan_launch(op, p_in.rows, p_in.H, p_in.T, resident, resident_shallow);
     Params p = p_in;
     p.groups = pl.groups;
+    p.gpb = pl.gpb;
+    p.blk_rows = pl.blk_rows;
     p.group_stride = pl.group_stride;
     p.step = pl.step;
     p.span = pl.span;
-    if (pl.blocks > 0x7FFFFFFF) return hipErrorInvalidValue;
+    if (pl.blocks > 0x7FFFFFFF || pl.groups > 0x7FFFFFFF) return hipErrorInvalidValue;
     hipLaunchKernelGGL(pl.shallow ? shallow : deep, dim3((unsigned)pl.blocks), dim3(block), 0,
                        stream, p);
     return hipGetLastError();
@@ -883,11 +916,11 @@ hipError_t launch_diag_round(const float* in, uint16_t* out, int64_t n, hipStrea
     return hipGetLastError();
 }
 
-hipError_t launch_diag_finalize(const float* in, float* out, int64_t n, float eps,
+hipError_t launch_diag_finalize(const float* in, float* out, int64_t n, int64_t H, float eps,
                                 hipStream_t stream) {
     const int64_t blocks = n / 256 + 1 < 65536 ? n / 256 + 1 : 65536;
     hipLaunchKernelGGL(diag_finalize, dim3((unsigned)blocks), dim3(256), 0, stream, in, out, n,
-                       eps);
+                       (float)H, eps);
     return hipGetLastError();
 }
 

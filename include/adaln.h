@@ -90,12 +90,14 @@
 extern "C" {
 #endif
 
-#define ADALN_ABI_VERSION 7 /* 2: two waves per row for 2048 <= H < 4096;
+#define ADALN_ABI_VERSION 8 /* 2: two waves per row for 2048 <= H < 4096;
                               3: residual-gate LayerNorm, stream copy;
                               4: LayerNorm + modulate + FP8 quantisation;
                               5: per-head QK RMSNorm + RoPE;
                               6: channel-first residual gating;
-                              7: launch-plan diagnostic */
+                              7: launch-plan diagnostic;
+                              8: the plan takes T and gives row blocks; the finalize
+                                 diagnostic takes H */
 
 typedef uint16_t adaln_bf16; /* raw bfloat16 bits */
 
@@ -252,11 +254,14 @@ int adaln_abi_version(void);
 /* Diagnostics: run the exact device steps the kernels use, elementwise, so that
  * tests can check them exhaustively against host IEEE arithmetic.
  *  - adaln_diag_round_bf16: out[i] = bf16(in[i]) (nearest-even).
- *  - adaln_diag_finalize:   out[i] = RN(1 / RN(sqrt(RN(in[i] + eps)))).
+ *  - adaln_diag_finalize:   out[i] = RN(1 / RN(sqrt(RN(RN(in[i] / H) + eps)))), the
+ *    rstd of a row of H elements whose statistic (sum of squares or M2) is in[i],
+ *    by the kernels' own code (including its shortcuts for in-range waves);
+ *    1 <= H <= 8192 (else ADALN_ERR_SHAPE).
  * n >= 0 elements of device memory, 4-byte aligned; ADALN_ERR_* as above.  out may
  * not overlap in (ADALN_ERR_OVERLAP), except that finalize may run in place. */
 adaln_status adaln_diag_round_bf16(const float* in, adaln_bf16* out, int64_t n, void* hip_stream);
-adaln_status adaln_diag_finalize(const float* in, float* out, int64_t n, float eps,
+adaln_status adaln_diag_finalize(const float* in, float* out, int64_t n, int64_t H, float eps,
                                  void* hip_stream);
 
 /* Diagnostic: the FP8 kernel's quantisation step on binary32 inputs,
@@ -270,12 +275,15 @@ adaln_status adaln_diag_quant_fp8(const float* in, uint8_t* out, int64_t n, cons
  * the host with no device work, for `resident` row groups fitting on the device at
  * once with the deep ring and `resident_shallow` with the one-slot ring (0: not
  * available).  op: 0 LayerNorm+modulate, 1 RMSNorm+scale/shift, 2 residual gate +
- * RMSNorm, 3 residual gate + LayerNorm, 4 LayerNorm+modulate+FP8.  rows = B*T >= 1,
- * H as for the entry points.  out[8] receives {one-slot ring (0/1), ring slots,
- * groups, group stride, step, span, workgroups, threads per workgroup}: group g takes
- * the rows g*stride + i*step below min(g*stride + span, rows).  ADALN_ERR_VALUE for
- * an unknown op or a resident count below 1 (below 0 for resident_shallow). */
-adaln_status adaln_diag_launch_plan(int op, int64_t rows, int64_t H, int64_t resident,
+ * RMSNorm, 3 residual gate + LayerNorm, 4 LayerNorm+modulate+FP8.  rows = B*T >= 1
+ * with 1 <= T <= rows and rows % T == 0 (else ADALN_ERR_SHAPE), H as for the entry
+ * points.  out[10] receives {one-slot ring (0/1), ring slots, groups, groups per
+ * block, rows per block, group stride, step, span, workgroups, threads per
+ * workgroup}: with k = g / (groups per block) and first = k * (rows per block) +
+ * (g % groups per block) * stride, group g takes the rows first + i*step below
+ * min(first + span, (k + 1) * (rows per block), rows).  ADALN_ERR_VALUE for an
+ * unknown op or a resident count below 1 (below 0 for resident_shallow). */
+adaln_status adaln_diag_launch_plan(int op, int64_t rows, int64_t H, int64_t T, int64_t resident,
                                     int64_t resident_shallow, int64_t* out);
 
 /* Measurement aid: copy `bytes` bytes of device memory from src to dst with the

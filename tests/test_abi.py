@@ -38,7 +38,7 @@ def test_header_symbols_are_exported(lib):
 
 
 def test_abi_version_and_status_strings(lib):
-    assert A.adaln_abi_version() == A.ABI_VERSION == 7
+    assert A.adaln_abi_version() == A.ABI_VERSION == 8
     for s in range(8):
         assert len(A.adaln_status_string(s)) > 5
     assert A.adaln_status_string(99) == "unknown status"
@@ -299,9 +299,11 @@ def test_compute_entry_points_reject_before_launch(lib):
     assert lib.adaln_diag_stream_copy(None, addr(1), 32, None) == NULL
     assert lib.adaln_diag_stream_copy(addr(0), addr(0) + 16, 32, None) == OVERLAP
     assert lib.adaln_diag_stream_copy(None, None, 0, None) == OK
-    assert lib.adaln_diag_finalize(addr(0), addr(1), 4, -1.0, None) == VALUE
+    assert lib.adaln_diag_finalize(addr(0), addr(1), 4, 1, -1.0, None) == VALUE
+    for H in (0, -1, 8193):
+        assert lib.adaln_diag_finalize(addr(0), addr(1), 4, H, 1e-6, None) == SHAPE
     assert lib.adaln_diag_round_bf16(addr(0), addr(0) + 4, 8, None) == OVERLAP
-    assert lib.adaln_diag_finalize(addr(0), addr(0) + 4, 8, 1e-6, None) == OVERLAP
+    assert lib.adaln_diag_finalize(addr(0), addr(0) + 4, 8, 1, 1e-6, None) == OVERLAP
     assert lib.adaln_diag_quant_fp8(addr(0), addr(0) + 16, 8, addr(1), None) == OVERLAP
 
 

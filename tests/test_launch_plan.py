@@ -1,7 +1,8 @@
-"""The fused kernel's launch plan (host logic, CPU): for every op, hidden size and
-row count, the row groups of one launch cover every row exactly once, the grid and
-ring settings follow the documented rules, and a contiguous group's rows stay within
-32-bit byte offsets.  The plan is the library's own host function (through the
+"""The fused kernel's launch plan (host logic, CPU): for every op, hidden size, row
+count and batch split, the row groups of one launch cover every row exactly once, the
+grid and ring settings follow the documented rules, an interleaved group that is given
+to one batch entry stays in it, and a contiguous group's rows stay within 32-bit byte
+offsets.  The plan is the library's own host function (through the
 launch-plan diagnostic), fed with resident counts like the device's."""
 import numpy as np
 import pytest
@@ -10,30 +11,37 @@ import diffusion_dit_adaln_amd as A
 
 OPS = ["ln", "rms", "rg", "rgln", "lnq"]
 INTERLEAVED = {"ln", "rgln", "lnq"}
-RESIDENT = [(1024, 1536), (768, 0), (256, 512), (1, 1), (7, 0)]
+RESIDENT = [(1024, 1536), (768, 0), (256, 512), (1, 1), (7, 0), (2560, 2560)]
+# (rows, T): one batch entry, a few long ones, many short ones
+SHAPES = [(1, 1), (3, 1), (7, 7), (7, 1), (100, 100), (100, 25), (4216, 4216), (4216, 527),
+          (9216, 4608), (9216, 9216), (30001, 1579), (524287, 524287), (524288, 4096),
+          (524288, 64)]
 
 
 def rows_of(plan, rows):
-    """Every row each group visits, as the kernel walks them."""
+    """Every row each group visits, as the kernel walks them, and the group of each."""
     g = np.arange(plan["groups"], dtype=np.int64)
-    begin = g * plan["group_stride"]
-    end = np.minimum(begin + plan["span"], rows)
+    blk = g // plan["gpb"]
+    blk_begin = blk * plan["blk_rows"]
+    begin = blk_begin + (g - blk * plan["gpb"]) * plan["group_stride"]
+    end = np.minimum(np.minimum(begin + plan["span"], rows), blk_begin + plan["blk_rows"])
     counts = np.maximum(0, (end - begin + plan["step"] - 1) // plan["step"])
     out = np.repeat(begin, counts)
     first = np.repeat(np.cumsum(counts) - counts, counts)
     out += (np.arange(out.size) - first) * plan["step"]
-    return out
+    return out, np.repeat(g, counts)
 
 
 @pytest.mark.parametrize("op", OPS)
 @pytest.mark.parametrize("H", [8, 520, 1024, 2048, 3072, 4096, 4104, 8192])
-@pytest.mark.parametrize("rows", [1, 3, 7, 100, 4216, 9216, 30001, 524287])
+@pytest.mark.parametrize("shape", SHAPES)
 @pytest.mark.parametrize("res", RESIDENT)
-def test_every_row_exactly_once(op, H, rows, res):
+def test_every_row_exactly_once(op, H, shape, res):
+    rows, T = shape
     resident, resident_shallow = res
-    plan = A.adaln_diag_launch_plan(op, rows, H, resident, resident_shallow)
+    plan = A.adaln_diag_launch_plan(op, rows, H, T, resident, resident_shallow)
     w, _, _ = A.adaln_reduction_layout(H)
-    visited = rows_of(plan, rows)
+    visited, group = rows_of(plan, rows)
     assert visited.size == rows
     assert np.array_equal(np.sort(visited), np.arange(rows))
     assert plan["block_threads"] == (256 if w == 1 else 64 * w)
@@ -41,13 +49,26 @@ def test_every_row_exactly_once(op, H, rows, res):
     if op in INTERLEAVED:
         shallow = resident_shallow > 0 and rows >= 3 * resident
         assert plan["shallow"] == shallow
-        assert plan["groups"] == min(rows, resident_shallow if shallow else resident)
-        assert plan["group_stride"] == 1 and plan["step"] == plan["groups"]
+        G = min(rows, resident_shallow if shallow else resident)
+        B = rows // T
+        per_entry = min(G // B, T) if B > 1 else 0
+        assert plan["group_stride"] == 1 and plan["step"] == plan["gpb"]
+        if per_entry > 0 and 16 * (G - per_entry * B) <= G:
+            # each batch entry has its own groups, at most 1/16 of the slots idle
+            assert (plan["gpb"], plan["blk_rows"], plan["span"]) == (per_entry, T, T)
+            assert plan["groups"] == per_entry * B
+            entries = np.zeros(plan["groups"], dtype=np.int64) - 1
+            entries[group] = visited // T
+            assert np.array_equal(entries[group], visited // T), "a group changes entry"
+        else:
+            assert plan["groups"] == plan["gpb"] == G
+            assert plan["blk_rows"] == plan["span"] == rows
         if shallow:
             assert plan["slots"] == 1
     else:
         S = plan["slots"]
         assert plan["shallow"] == 0 and plan["step"] == 1
+        assert plan["gpb"] == plan["groups"] and plan["blk_rows"] == rows
         assert plan["span"] == plan["group_stride"] and plan["span"] % S == 0
         # the last pass reaches S rows past the span: still below 2^31 bytes
         assert (plan["span"] + S) * 2 * H <= 2**31 - 1
@@ -55,11 +76,22 @@ def test_every_row_exactly_once(op, H, rows, res):
         assert plan["groups"] == -(-rows // plan["span"])
 
 
+def test_interleaved_batch_entries_get_their_own_groups():
+    # the FLUX.1 LayerNorm site [2, 4608, 3072] on 2560 resident groups: 1280 per entry
+    plan = A.adaln_diag_launch_plan("lnq", 9216, 3072, 4608, 2560, 2560)
+    assert (plan["groups"], plan["gpb"], plan["blk_rows"], plan["step"]) == (2560, 1280, 4608, 1280)
+    # 2560 groups over 7 entries would leave 5 slots idle (< 1/16): split
+    assert A.adaln_diag_launch_plan("ln", 7 * 4608, 3072, 4608, 2560, 2560)["gpb"] == 365
+    # 2560 groups over 1000 entries would idle 560 slots: one interleave over all rows
+    plan = A.adaln_diag_launch_plan("ln", 1000 * 64, 3072, 64, 2560, 2560)
+    assert (plan["groups"], plan["gpb"], plan["blk_rows"]) == (2560, 2560, 64000)
+
+
 def test_contiguous_groups_capped_by_32_bit_offsets():
     # so many rows per group that the span would pass 2^31 bytes: the span is
     # capped and the group count grows instead
     rows, H = 3 * 10**8, 8192
-    plan = A.adaln_diag_launch_plan("rms", rows, H, 1024, 0)
+    plan = A.adaln_diag_launch_plan("rms", rows, H, rows, 1024, 0)
     S = plan["slots"]
     assert (plan["span"] + S) * 2 * H <= 2**31 - 1
     assert plan["groups"] * plan["span"] >= rows > (plan["groups"] - 1) * plan["span"]
@@ -67,8 +99,11 @@ def test_contiguous_groups_capped_by_32_bit_offsets():
 
 def test_plan_rejects_bad_arguments():
     with pytest.raises(A.AdalnError):
-        A.adaln_diag_launch_plan("ln", 0, 1024, 1024)
+        A.adaln_diag_launch_plan("ln", 0, 1024, 1, 1024)
     with pytest.raises(A.AdalnError):
-        A.adaln_diag_launch_plan("ln", 10, 12, 1024)
+        A.adaln_diag_launch_plan("ln", 10, 12, 10, 1024)
     with pytest.raises(A.AdalnError):
-        A.adaln_diag_launch_plan("ln", 10, 1024, 0)
+        A.adaln_diag_launch_plan("ln", 10, 1024, 10, 0)
+    for T in (0, 3, 11, -1):  # T must divide rows
+        with pytest.raises(A.AdalnError):
+            A.adaln_diag_launch_plan("ln", 10, 1024, T, 1024)

@@ -635,30 +635,35 @@ def test_device_bf16_rounding_all_fp32_patterns():
     torch.cuda.synchronize()
 
 
-def test_device_finalize_all_nonnegative_stats():
-    # stat in [+0, +inf]: rstd = RN(1/RN(sqrt(RN(stat + eps)))).  Reference: the
-    # fp32 add, then sqrt and divide in float64 rounded once to float32 (a double
-    # rounding through binary64 equals the single fp32 rounding for sqrt and
-    # divide, since 53 >= 2*24 + 2).
-    eps = torch.tensor(1e-6, dtype=torch.float32, device="cuda")
+@pytest.mark.parametrize("H,eps", [(1, 1e-6), (3072, 1e-6), (8168, 0.0), (520, 1e-5)])
+def test_device_finalize_all_nonnegative_stats(H, eps):
+    # stat S in [+0, +inf] over H elements: rstd = RN(1/RN(sqrt(RN(RN(S/H) + eps)))),
+    # by the kernels' own code, shortcuts included (waves with every lane in range
+    # take them; 3072 = 3 * 2^10, 8168 = 8 * 1021 and 520 = 8 * 65 are not powers of
+    # two; eps 0 reaches the smallest roots).  Reference: divide, sqrt and reciprocal
+    # in float64 rounded once to float32 (a double rounding through binary64 equals
+    # the single fp32 rounding for divide and sqrt, since 53 >= 2*24 + 2), the add
+    # in fp32.
+    e = torch.tensor(eps, dtype=torch.float32, device="cuda")
     top = 0x7F800000 + 1
     n_chunks = 16
     step = (top + n_chunks - 1) // n_chunks
     for k in range(n_chunks):
-        say(f"[diag] finalize chunk {k + 1}/{n_chunks}")
+        say(f"[diag] finalize H={H} eps={eps} chunk {k + 1}/{n_chunks}")
         lo, hi = k * step, min(top, (k + 1) * step)
         s = torch.arange(lo, hi, dtype=torch.int32, device="cuda").view(torch.float32)
-        got = A.adaln_diag_finalize(s, 1e-6)
-        v = s + eps
+        got = A.adaln_diag_finalize(s, eps, H=H)
+        v = (s.double() / H).float() + e
         root = v.double().sqrt().float()
         want = (1.0 / root.double()).float()
         assert torch.equal(got.view(torch.int32), want.view(torch.int32)), f"chunk {k}"
+        del s, got, v, root, want
     # host IEEE arithmetic on a sample, independent of torch's device math
-    rng = np.random.default_rng(1)
+    rng = np.random.default_rng(H)
     bits = rng.integers(0, 0x7F800000, size=1 << 22, dtype=np.uint32)
     s = bits.view(np.float32)
-    got = A.adaln_diag_finalize(torch.from_numpy(s.copy()).cuda(), 1e-6).cpu().numpy()
-    v = s + np.float32(1e-6)
+    got = A.adaln_diag_finalize(torch.from_numpy(s.copy()).cuda(), eps, H=H).cpu().numpy()
+    v = (s.astype(np.float64) / H).astype(np.float32) + np.float32(eps)
     want = np.float32(1.0) / np.sqrt(v)
     assert np.array_equal(got.view(np.uint32), want.view(np.uint32))
 

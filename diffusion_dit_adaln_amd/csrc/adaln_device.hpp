@@ -175,6 +175,8 @@ __device__ __forceinline__ float finalize(float stat, float eps) {
 //    which rounds correctly from any faithful y0 except for a significand of all
 //    ones (checked on the CPU for every significand), so that case keeps the
 //    general divide.
+// (The host checks are tests/test_rstd_steps.py; the device's own results are
+// compared over every non-negative S by the GPU finalize tests.)
 // POW2: H is a power of two (S * rH is then exact).
 template <bool POW2>
 __device__ __forceinline__ float row_rstd(float S, float H, float rH, float eps) {

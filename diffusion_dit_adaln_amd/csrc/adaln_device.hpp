@@ -146,6 +146,22 @@ __device__ __forceinline__ float partner_hi(float v) {
     else if constexpr (K == 4) return dpp_banks<0x104, 0x5>(v);  // row_shl:4 into banks 0, 2
     else return dpp_banks<0x108, 0x3>(v);                  // row_shl:8 into banks 0, 1
 }
+// Distances 16 and 32 when every 16-lane row (every 32-lane half) holds one value:
+// v_permlane16_swap exchanges the odd rows of its first operand with the even rows
+// of its second, v_permlane32_swap the upper half of the first with the lower half
+// of the second, so that from two copies of v every lane gets the value of the lower
+// row (half) of its pair in lo and of the upper one in hi.  The leading s_nop covers
+// the wait states the swap needs after a VALU write of its operands.
+__device__ __forceinline__ void pair16(float v, float& lo, float& hi) {
+    lo = v;
+    hi = v;
+    asm("s_nop 1\n\tv_permlane16_swap_b32 %0, %1" : "+v"(lo), "+v"(hi));
+}
+__device__ __forceinline__ void pair32(float v, float& lo, float& hi) {
+    lo = v;
+    hi = v;
+    asm("s_nop 1\n\tv_permlane32_swap_b32 %0, %1" : "+v"(lo), "+v"(hi));
+}
 __device__ __forceinline__ float readlane(float v, int lane) {
     return __builtin_bit_cast(float, __builtin_amdgcn_readlane(__builtin_bit_cast(int, v), lane));
 }

@@ -145,17 +145,18 @@ __device__ __forceinline__ Welford readlane(const Welford& w, int lane) {
 }
 
 // Butterfly over the 64 lanes of a wave (distances 1..32).  Distances 16 and 32
-// combine the four uniform rows of 16 lanes: ((r0 (+) r1) (+) (r2 (+) r3)).
+// combine the four uniform rows of 16 lanes: ((r0 (+) r1) (+) (r2 (+) r3)), every
+// lane ending with the wave's value.
 __device__ __forceinline__ float wave_sum(float s) {
     s = s + dpp<DPP_XOR1>(s);
     s = s + dpp<DPP_XOR2>(s);
     s = s + dpp<DPP_HALF_MIRROR>(s);
     s = s + dpp<DPP_MIRROR>(s);
-    const float r0 = readlane(s, 0), r1 = readlane(s, 16);
-    const float r2 = readlane(s, 32), r3 = readlane(s, 48);
-    const float a = r0 + r1;
-    const float b = r2 + r3;
-    return a + b;
+    float lo, hi;
+    pair16(s, lo, hi);
+    s = lo + hi;
+    pair32(s, lo, hi);
+    return lo + hi;
 }
 
 __device__ __forceinline__ Welford wave_welford(Welford w, int lane) {
@@ -175,12 +176,13 @@ __device__ __forceinline__ void wave_welford_equal(float& mean, float& m2) {
     welford_level_equal<2, DPP_XOR2, 2 * N>(mean, m2);
     welford_level_equal<4, DPP_HALF_MIRROR, 4 * N>(mean, m2);
     welford_level_equal<8, DPP_MIRROR, 8 * N>(mean, m2);
-    float ma, qa, mb, qb;
-    combine_equal<16 * N>(readlane(mean, 0), readlane(mean, 16),
-                          readlane(m2, 0) + readlane(m2, 16), ma, qa);
-    combine_equal<16 * N>(readlane(mean, 32), readlane(mean, 48),
-                          readlane(m2, 32) + readlane(m2, 48), mb, qb);
-    combine_equal<32 * N>(ma, mb, qa + qb, mean, m2);
+    float mlo, mhi, qlo, qhi;
+    pair16(mean, mlo, mhi);
+    pair16(m2, qlo, qhi);
+    combine_equal<16 * N>(mlo, mhi, qlo + qhi, mean, m2);
+    pair32(mean, mlo, mhi);
+    pair32(m2, qlo, qhi);
+    combine_equal<32 * N>(mlo, mhi, qlo + qhi, mean, m2);
 }
 
 

@@ -292,8 +292,8 @@ __global__ __launch_bounds__(256) void fused_norm_modulate(Params p) {
                 const float w0 = bf_lo(w) + 0.0f, w1 = bf_hi(w) + 0.0f;    // (w + 0.0): -0 -> +0
                 if (KF) {
                     const int e = c * 8 + 2 * j;
-                    ka[e] = bf_lo(a);
-                    ka[e + 1] = bf_hi(a);
+                    ka[e] = round_bf16(1.0f + bf_lo(s));  // the same values as a, unpacked
+                    ka[e + 1] = round_bf16(1.0f + bf_hi(s));
                     kh[e] = bf_lo(word(sh, j));
                     kh[e + 1] = bf_hi(word(sh, j));
                     kw[e] = w0;
@@ -381,8 +381,8 @@ __global__ __launch_bounds__(256) void fused_norm_modulate(Params p) {
 #pragma unroll
             for (int v = 0; v < 8; ++v)
                 m = __builtin_elementwise_maximum(
-                    m, __builtin_elementwise_maximum(__builtin_fabsf(K_a(c, v)),
-                                                     __builtin_fabsf(K_h(c, v))));
+                    __builtin_elementwise_maximum(m, __builtin_fabsf(K_a(c, v))),
+                    __builtin_fabsf(K_h(c, v)));
         return __builtin_amdgcn_ballot_w64(!__builtin_isfinite(m)) == 0;
     };
     // blocks of one batch entry each: the block is the batch entry

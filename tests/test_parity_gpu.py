@@ -222,6 +222,32 @@ def test_many_rows_per_group(op, T, H):
         check_lnq(x, sc, sh, 0.0125, f"lnq {T}x{H}")
 
 
+# Several batch entries with enough rows for the one-slot ring: the interleaved ops
+# then give each entry its own share of the row groups (rows per group uneven, e.g.
+# 1500 rows over 365 groups), up to the split that leaves exactly 1/16 of the groups
+# idle (300 entries of 40 rows), and past it one interleave over all rows whose groups
+# change entry (1000 entries of 12 rows).  Each entry has its own vectors.
+@pytest.mark.parametrize("op,B,T,H", [("ln", 7, 1500, 3072), ("lnq", 3, 3001, 2056),
+                                      ("rgln", 2, 5000, 1024), ("ln", 40, 300, 3072),
+                                      ("ln", 300, 40, 3072), ("ln", 1000, 12, 3072),
+                                      ("rgln", 5, 2000, 4096)])
+def test_batch_entries_split_over_groups(op, B, T, H):
+    say(f"[parity] batch split {op} B={B} T={T} H={H}")
+    rng = np.random.default_rng(B * 7919 + T + H)
+    x = synth.normal_bf16(rng, (B, T, H))
+    sc = synth.normal_bf16(rng, (B, H), 0.1)
+    sh = synth.normal_bf16(rng, (B, H), 0.1)
+    if op == "ln":
+        assert_bits_equal(run_ln(x, sc, sh), O.layernorm_modulate(x, sc, sh, EPS),
+                          f"ln {B}x{T}x{H}")
+    elif op == "rgln":
+        res = synth.normal_bf16(rng, (B, T, H))
+        g = synth.normal_bf16(rng, (B, H), 0.1)
+        check_rgln(res, x, g, sc, sh, f"rgln {B}x{T}x{H}")
+    else:
+        check_lnq(x, sc, sh, 0.0125, f"lnq {B}x{T}x{H}")
+
+
 @pytest.mark.parametrize("eps", [0.0, 1e-5, 1e-6, 0.25])
 def test_eps_values(eps):
     say(f"[parity] eps={eps}")

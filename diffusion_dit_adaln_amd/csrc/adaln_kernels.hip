@@ -370,10 +370,10 @@ __global__ __launch_bounds__(256) void fused_norm_modulate(Params p) {
     };
 
     // LN+FP8: whether every modulation constant of this lane is finite; with finite
-    // row statistics too, no output can be NaN and the clamp can be one median
-    // (a wave-uniform answer: true only if it holds in every lane of the wave)
-    // (the NaN-propagating maximum of the magnitudes is finite exactly when every
-    // value is: a NaN stays NaN, an infinity stays infinite)
+    // row statistics too, no output can be NaN and the clamp can be one median.  The
+    // answer is wave-uniform (true only if it holds in every lane of the wave).  The
+    // NaN-propagating maximum of the magnitudes is finite exactly when every value
+    // is: a NaN stays NaN, an infinity stays infinite.
     auto consts_finite = [&]() {
         float m = 0.0f;
 #pragma unroll

@@ -1,7 +1,8 @@
 // adaln_device.hpp -- device helpers shared by the kernels of libadaln (gfx950):
 // bf16 <-> binary32 conversions, raw buffer descriptors with non-temporal 16-byte
-// accesses, the E4M3 quantisation step, DPP cross-lane moves and the correctly
-// rounded finalize.  Not installed; not part of the ABI.
+// accesses, the E4M3 quantisation step, DPP and row-swap cross-lane moves, and the
+// correctly rounded finalize (general, and the exact shortcut for in-range waves).
+// Not installed; not part of the ABI.
 #pragma once
 
 #include <hip/hip_runtime.h>

@@ -16,12 +16,14 @@
 //  - FLUX PR report, motivation: LayerNorm by per-element Welford updates and a
 //    count-weighted combine; test snippet `_eager` for the modulate chain.
 // Built with -ffp-contract=off; fp32 sqrt and divide are the correctly rounded
-// expansions (__builtin_sqrtf and '/'; HIP's __fsqrt_rn is the approximate one).
+// expansions (__builtin_sqrtf and '/'; HIP's __fsqrt_rn is the approximate one),
+// or for the LayerNorm rstd the exact shortcut of row_rstd (the same bits).
 //
 // Execution: a persistent grid of row groups (a wave, or a workgroup of W waves),
 // at most as many as can be resident at once.  A group owns either a contiguous
 // range of rows or every G-th row (interleaved; then the groups together stream a
-// contiguous band of the tensor at any moment).  It keeps the per-column constants
+// contiguous band of the tensor at any moment; with several batch entries each
+// entry can get its own share of the groups, so that no group changes entry).  It keeps the per-column constants
 // of its current batch entry in registers (bf16(1 + scale), shift, weight, gate:
 // computed once per batch entry, not once per row) and keeps its next rows' loads
 // in flight (non-temporal 16-byte loads) while it reduces the current one, so HBM

@@ -421,7 +421,12 @@ adaln_status adaln_diag_launch_plan(int op, int64_t rows, int64_t H, int64_t T, 
     if (rows < 1 || H < 8 || H > kMaxH || (H % 8) != 0) return ADALN_ERR_SHAPE;
     if (rows > INT64_MAX / (2 * H)) return ADALN_ERR_SHAPE;
     if (T < 1 || T > rows || rows % T != 0) return ADALN_ERR_SHAPE;
-    if (resident < 1 || resident_shallow < 0) return ADALN_ERR_VALUE;
+    // resident counts of a real device are far below 2^31; the plan's products of
+    // them stay in range only below that
+    constexpr int64_t kMaxResident = 0x7FFFFFFF;
+    if (resident < 1 || resident > kMaxResident || resident_shallow < 0 ||
+        resident_shallow > kMaxResident)
+        return ADALN_ERR_VALUE;
     const adaln::Plan pl =
         adaln::plan_launch(static_cast<adaln::Op>(op), rows, H, T, resident, resident_shallow);
     out[0] = pl.shallow ? 1 : 0;

@@ -282,7 +282,8 @@ adaln_status adaln_diag_quant_fp8(const float* in, uint8_t* out, int64_t n, cons
  * workgroup}: with k = g / (groups per block) and first = k * (rows per block) +
  * (g % groups per block) * stride, group g takes the rows first + i*step below
  * min(first + span, (k + 1) * (rows per block), rows).  ADALN_ERR_VALUE for an
- * unknown op or a resident count below 1 (below 0 for resident_shallow). */
+ * unknown op or a resident count below 1 (below 0 for resident_shallow) or above
+ * 2^31 - 1. */
 adaln_status adaln_diag_launch_plan(int op, int64_t rows, int64_t H, int64_t T, int64_t resident,
                                     int64_t resident_shallow, int64_t* out);
 

@@ -104,6 +104,10 @@ def test_plan_rejects_bad_arguments():
         A.adaln_diag_launch_plan("ln", 10, 12, 10, 1024)
     with pytest.raises(A.AdalnError):
         A.adaln_diag_launch_plan("ln", 10, 1024, 10, 0)
+    with pytest.raises(A.AdalnError):
+        A.adaln_diag_launch_plan("ln", 10, 1024, 10, 2**31)
+    with pytest.raises(A.AdalnError):
+        A.adaln_diag_launch_plan("ln", 10, 1024, 10, 1024, 2**31)
     for T in (0, 3, 11, -1):  # T must divide rows
         with pytest.raises(A.AdalnError):
             A.adaln_diag_launch_plan("ln", 10, 1024, T, 1024)

@@ -474,6 +474,33 @@ def describe(wl):
     return f"{name} bf16 [{B},{T},{H}]{extra}, eps 1e-6"
 
 
+def sweep_rows(rotate: int, steps: int, warmup: int) -> None:
+    """One JSON line: per row count, the fused RMS kernel's and the streaming copy's
+    GB/s and microseconds per launch (graph replay), and the least-squares fit of the
+    kernel's time per launch to fixed + bytes / rate."""
+    from diffusion_dit_adaln_amd import synth
+    points = []
+    for T in (256, 512, 1024, 2048, 4216, 8192, 16384, 32768, 65536):
+        wl = synth.rms_rows(T)
+        L = launcher_for(wl, rotate)
+        nbytes = wl.algorithmic_bytes()
+        t = time_steps(L.call, steps, warmup, "graph") / steps
+        del L
+        c = copy_ceiling(nbytes, rotate, steps, warmup)
+        points.append({"rows": T, "bytes": nbytes, "GBps": round(nbytes / t / 1e9, 1),
+                       "us_per_launch": round(t * 1e6, 3), "copy_GBps": round(c, 1),
+                       "frac_of_copy": round(nbytes / t / 1e9 / c, 4)})
+        print(f"[sweep] rows {T}: {points[-1]['GBps']} GB/s, copy {points[-1]['copy_GBps']}",
+              file=sys.stderr, flush=True)
+    b = np.array([p["bytes"] for p in points], dtype=np.float64)
+    u = np.array([p["us_per_launch"] for p in points], dtype=np.float64)
+    slope, fixed = np.polyfit(b, u, 1)
+    print(json.dumps({"sweep": "rmsnorm_scale_shift bf16 [1,T,4096] weight, graph replay",
+                      "points": points,
+                      "fit": {"fixed_us": round(float(fixed), 3),
+                              "asymptotic_GBps": round(float(1e-3 / slope), 1)}}), flush=True)
+
+
 def main():
     ap = argparse.ArgumentParser(description=__doc__)
     ap.add_argument("--gpus", type=int, default=1)
@@ -487,6 +514,10 @@ def main():
     ap.add_argument("--no-cpu", action="store_true", help="skip the CPU oracle baseline")
     ap.add_argument("--no-extras", action="store_true",
                     help="only the headline workload (for profiler runs)")
+    ap.add_argument("--sweep-rows", action="store_true",
+                    help="instead of the benchmark line: the RMS op at H 4096 over a range of "
+                         "row counts beside the streaming copy of the same bytes, with a fit "
+                         "of time = fixed + bytes / rate")
     ap.add_argument("--copy-only", action="store_true",
                     help="only a plain device copy of the workload's byte count (counter "
                          "calibration for profiler runs)")
@@ -503,6 +534,9 @@ def main():
         sys.exit(2)
 
     rotate = args.rotate_mb << 20
+    if args.sweep_rows:
+        sweep_rows(rotate, args.steps, args.warmup)
+        return
     wl = workload(args.workload)
     if args.copy_only:
         g = copy_ceiling(wl.algorithmic_bytes(), rotate, args.steps, args.warmup, args.timing)

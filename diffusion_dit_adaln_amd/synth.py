@@ -117,6 +117,16 @@ def rms_1x4216x4096(seed: int = 0) -> Workload:
     return Workload("rms", "rms_1x4216x4096", x, v["scale"], v["shift"], weight=w)
 
 
+def rms_rows(T: int, seed: int = 0) -> Workload:
+    """The headline RMS workload's distributions with T rows of H = 4096 (for size
+    sweeps): x [1,T,4096] ~ N(0,1) with 0.1% of entries multiplied by 50."""
+    B, H = 1, 4096
+    v = _vecs(seed, 1, B, H, ["scale", "shift"])
+    w = normal_bf16(_rng(seed, 1, "weight"), (H,), 0.02, 1.0)
+    x = normal_bf16(_rng(seed, 1, "x"), (B, T, H), outlier_frac=0.001, outlier_factor=50.0)
+    return Workload("rms", f"rms_1x{T}x4096", x, v["scale"], v["shift"], weight=w)
+
+
 def rg_rms_2x1140x4096(seed: int = 0) -> Workload:
     """Residual-gate RMSNorm + scale/shift (CFG batch): res, x [2,1140,4096] ~ N(0,1);
     gate/scale/shift [2,4096] ~ 0.1*N; no weight."""

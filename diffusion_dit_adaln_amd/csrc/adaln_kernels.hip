@@ -70,6 +70,14 @@
 #ifndef ADALN_SHALLOW_ROWS_PER_GROUP
 #define ADALN_SHALLOW_ROWS_PER_GROUP 3
 #endif
+// The RMS op (no gate) with four-wave rows takes the one-slot ring when every
+// resident one-slot group gets at most this many rows (measured on MI355X at H
+// 4096: +3% at 1024 rows, +11% at 2048, +39% at 256 against the three-row ring,
+// which fills fewer groups; from a few thousand rows on the three-row ring is
+// faster, and with the gate the one-slot ring was slower).
+#ifndef ADALN_CONTIG_SHALLOW_MAX_ROWS_PER_GROUP
+#define ADALN_CONTIG_SHALLOW_MAX_ROWS_PER_GROUP 2
+#endif
 
 namespace adaln {
 namespace {
@@ -729,10 +737,11 @@ KernelFn pick_weight(bool weight) {
     }
 }
 
-// shallow: the one-slot ring, instantiated for the interleaved ops only
+// shallow: the one-slot ring, instantiated for the interleaved ops and for the
+// ungated contiguous ops' four-wave rows
 template <int OP, int W, int C>
 KernelFn pick_tail(bool tail, bool weight, bool shallow) {
-    if constexpr (interleaved(OP)) {
+    if constexpr (interleaved(OP) || (W == 4 && !op_gated(OP))) {
         if (shallow)
             return tail ? pick_weight<OP, W, C, true, true>(weight)
                         : pick_weight<OP, W, C, false, true>(weight);
@@ -820,9 +829,14 @@ Plan plan_launch(Op op, int64_t rows, int64_t H, int64_t T, int64_t resident,
     pl.block_threads = L.waves == 1 ? 256 : 64 * L.waves;
     // Interleaved ops with many rows per group: the one-slot ring (more resident
     // groups, the latency covered by the other groups) streams faster; with few
-    // rows per group the deeper ring does (tuning; the bits never depend on it).
-    pl.shallow = interleaved(op) && resident_shallow > 0 &&
-                 rows >= ADALN_SHALLOW_ROWS_PER_GROUP * resident;
+    // rows per group the deeper ring does.  Contiguous four-wave RMS rows: the other
+    // way round, the one-slot ring only for launches of one or two rows per group
+    // (with the gate it measured slower; tuning; the bits never depend on it).
+    pl.shallow = resident_shallow > 0 &&
+                 (interleaved(op) ? rows >= ADALN_SHALLOW_ROWS_PER_GROUP * resident
+                                  : L.waves == 4 && !op_gated(op) &&
+                                        rows <= ADALN_CONTIG_SHALLOW_MAX_ROWS_PER_GROUP *
+                                                    resident_shallow);
     if (pl.shallow) resident = resident_shallow;
     const int S = pl.shallow ? 1 : ring_slots(L.waves, L.chunks, op_gated(op));
     pl.slots = S;
@@ -896,7 +910,8 @@ hipError_t launch(Op op, const Params& p_in, hipStream_t stream) {
     }
     const int64_t resident = (int64_t)cus * blocks_per_cu * groups_per_block;
     int64_t resident_shallow = 0;
-    KernelFn shallow = interleaved(op) ? pick_op(true) : nullptr;
+    KernelFn shallow =
+        (interleaved(op) || (L.waves == 4 && !op_gated(op))) ? pick_op(true) : nullptr;
     int bpc1 = 0;
     if (shallow && occupancy(reinterpret_cast<const void*>(shallow), block, &bpc1, &cus))
         resident_shallow = (int64_t)cus * bpc1 * groups_per_block;

@@ -67,7 +67,12 @@ def test_every_row_exactly_once(op, H, shape, res):
             assert plan["slots"] == 1
     else:
         S = plan["slots"]
-        assert plan["shallow"] == 0 and plan["step"] == 1
+        # four-wave RMS rows take the one-slot ring for at most two rows per group
+        shallow = (op == "rms" and w == 4 and resident_shallow > 0
+                   and rows <= 2 * resident_shallow)
+        assert plan["shallow"] == shallow and plan["step"] == 1
+        if shallow:
+            assert S == 1
         assert plan["gpb"] == plan["groups"] and plan["blk_rows"] == rows
         assert plan["span"] == plan["group_stride"] and plan["span"] % S == 0
         # the last pass reaches S rows past the span: still below 2^31 bytes

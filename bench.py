@@ -474,14 +474,15 @@ def describe(wl):
     return f"{name} bf16 [{B},{T},{H}]{extra}, eps 1e-6"
 
 
-def sweep_rows(rotate: int, steps: int, warmup: int) -> None:
-    """One JSON line: per row count, the fused RMS kernel's and the streaming copy's
-    GB/s and microseconds per launch (graph replay), and the least-squares fit of the
-    kernel's time per launch to fixed + bytes / rate."""
+def sweep_rows(rotate: int, steps: int, warmup: int, op: str = "rms") -> None:
+    """One JSON line: per row count, the fused kernel's (RMS at H 4096 or LayerNorm at
+    H 3072) and the streaming copy's GB/s and microseconds per launch (graph replay),
+    and the least-squares fit of the kernel's time per launch to fixed + bytes / rate."""
     from diffusion_dit_adaln_amd import synth
+    make = synth.rms_rows if op == "rms" else synth.ln_rows
     points = []
     for T in (256, 512, 1024, 2048, 4216, 8192, 16384, 32768, 65536):
-        wl = synth.rms_rows(T)
+        wl = make(T)
         L = launcher_for(wl, rotate)
         nbytes = wl.algorithmic_bytes()
         t = time_steps(L.call, steps, warmup, "graph") / steps
@@ -495,7 +496,9 @@ def sweep_rows(rotate: int, steps: int, warmup: int) -> None:
     b = np.array([p["bytes"] for p in points], dtype=np.float64)
     u = np.array([p["us_per_launch"] for p in points], dtype=np.float64)
     slope, fixed = np.polyfit(b, u, 1)
-    print(json.dumps({"sweep": "rmsnorm_scale_shift bf16 [1,T,4096] weight, graph replay",
+    name = ("rmsnorm_scale_shift bf16 [1,T,4096] weight" if op == "rms"
+            else "layernorm_modulate bf16 [1,T,3072]")
+    print(json.dumps({"sweep": name + ", graph replay",
                       "points": points,
                       "fit": {"fixed_us": round(float(fixed), 3),
                               "asymptotic_GBps": round(float(1e-3 / slope), 1)}}), flush=True)
@@ -515,9 +518,11 @@ def main():
     ap.add_argument("--no-extras", action="store_true",
                     help="only the headline workload (for profiler runs)")
     ap.add_argument("--sweep-rows", action="store_true",
-                    help="instead of the benchmark line: the RMS op at H 4096 over a range of "
+                    help="instead of the benchmark line: one op (--sweep-op) over a range of "
                          "row counts beside the streaming copy of the same bytes, with a fit "
                          "of time = fixed + bytes / rate")
+    ap.add_argument("--sweep-op", default="rms", choices=["rms", "ln"],
+                    help="the op of --sweep-rows: RMS at H 4096 or LayerNorm at H 3072")
     ap.add_argument("--copy-only", action="store_true",
                     help="only a plain device copy of the workload's byte count (counter "
                          "calibration for profiler runs)")
@@ -535,7 +540,7 @@ def main():
 
     rotate = args.rotate_mb << 20
     if args.sweep_rows:
-        sweep_rows(rotate, args.steps, args.warmup)
+        sweep_rows(rotate, args.steps, args.warmup, args.sweep_op)
         return
     wl = workload(args.workload)
     if args.copy_only:

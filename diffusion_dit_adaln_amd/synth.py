@@ -127,6 +127,15 @@ def rms_rows(T: int, seed: int = 0) -> Workload:
     return Workload("rms", f"rms_1x{T}x4096", x, v["scale"], v["shift"], weight=w)
 
 
+def ln_rows(T: int, seed: int = 0) -> Workload:
+    """LayerNorm (no affine, eps 1e-6) + modulate with T rows of H = 3072 (the FLUX.1
+    site width, for size sweeps): x [1,T,3072] ~ N(0,1), scale/shift ~ 0.1*N."""
+    B, H = 1, 3072
+    v = _vecs(seed, 2, B, H, ["scale", "shift"])
+    return Workload("ln", f"ln_1x{T}x3072", normal_bf16(_rng(seed, 2, "x"), (B, T, H)),
+                    v["scale"], v["shift"])
+
+
 def rg_rms_2x1140x4096(seed: int = 0) -> Workload:
     """Residual-gate RMSNorm + scale/shift (CFG batch): res, x [2,1140,4096] ~ N(0,1);
     gate/scale/shift [2,4096] ~ 0.1*N; no weight."""

@@ -87,12 +87,15 @@ bool occupancy(const void* fn, int block, int* blocks_per_cu, int* cus);
 struct Plan {
     bool shallow;          // the one-slot ring kernel
     int slots;             // ring depth S
+    int ring;              // the kernel instantiation: 0 default depth, 1 or 2 slots
     int64_t groups, gpb, blk_rows, group_stride, step, span;
     int64_t blocks;        // workgroups launched
     int block_threads;     // threads per workgroup
 };
+// resident_two: resident groups of the two-slot ring kernel (0: not available);
+// cus: compute units (0: unknown; the two-slot choice needs it)
 Plan plan_launch(Op op, int64_t rows, int64_t H, int64_t T, int64_t resident,
-                 int64_t resident_shallow);
+                 int64_t resident_shallow, int64_t resident_two = 0, int64_t cus = 0);
 
 // Launch the fused kernel for `op`; returns the HIP error of the launch.
 hipError_t launch(Op op, const Params& p, hipStream_t stream);

@@ -230,14 +230,14 @@ constexpr int ring_slots(int W, int C, bool gated) {
 }
 
 // OP: Op; W: waves per row; C: chunks per lane; TAIL: the last chunk is partial;
-// WEIGHT: RMS weight present; IL: interleaved rows (per-row descriptors); SHALLOW:
-// a one-slot ring.  A workgroup is four independent one-wave groups (W == 1) or one
+// WEIGHT: RMS weight present; IL: interleaved rows (per-row descriptors); RING: the
+// ring depth when not 0 (one or two slots), else ring_slots.  A workgroup is four independent one-wave groups (W == 1) or one
 // group of W waves.
 //
 // Per-lane constants of the current batch entry are kept as fp32 (no unpacking
 // per row) or, for wide rows on one wave, as packed bf16 pairs (every constant is
 // a bf16 value); see consts_as_f32.
-template <int OP, int W, int C, bool TAIL, bool WEIGHT, bool IL, bool SHALLOW>
+template <int OP, int W, int C, bool TAIL, bool WEIGHT, bool IL, int RING>
 __global__ __launch_bounds__(256) void fused_norm_modulate(Params p) {
     constexpr int P = 64 * W;
     constexpr bool KF = consts_as_f32(W, C, OP, WEIGHT);
@@ -406,7 +406,7 @@ __global__ __launch_bounds__(256) void fused_norm_modulate(Params p) {
     // A ring of S row slots: slot k holds the group's row row0 + k*G; after a row is
     // finished its slot is refilled with the group's row S ahead, so S rows' loads
     // stay in flight.
-    constexpr int S = SHALLOW ? 1 : ring_slots(W, C, GATED);
+    constexpr int S = RING ? RING : ring_slots(W, C, GATED);
     uint4 xs[S][C], rs[S][C];
     // Prologue in the steady state's order: before slot k's loads, stand-ins for
     // slot k-1's stores (out of range: dropped), so that at the loop head the
@@ -726,52 +726,60 @@ __global__ __launch_bounds__(256) void diag_quant(const float4* __restrict__ in,
 // ---------------------------------------------------------------------------
 using KernelFn = void (*)(Params);
 
-template <int OP, int W, int C, bool TAIL, bool SHALLOW>
+template <int OP, int W, int C, bool TAIL, int RING>
 KernelFn pick_weight(bool weight) {
     constexpr bool IL = interleaved(OP);
     if constexpr (op_layernorm(OP)) {
-        return fused_norm_modulate<OP, W, C, TAIL, false, IL, SHALLOW>;  // no weight
+        return fused_norm_modulate<OP, W, C, TAIL, false, IL, RING>;  // no weight
     } else {
-        return weight ? fused_norm_modulate<OP, W, C, TAIL, true, IL, SHALLOW>
-                      : fused_norm_modulate<OP, W, C, TAIL, false, IL, SHALLOW>;
+        return weight ? fused_norm_modulate<OP, W, C, TAIL, true, IL, RING>
+                      : fused_norm_modulate<OP, W, C, TAIL, false, IL, RING>;
     }
 }
 
-// shallow: the one-slot ring, instantiated for the interleaved ops and for the
-// ungated contiguous ops' four-wave rows
+// ring 1 (the one-slot ring) is instantiated for the interleaved ops and for the
+// ungated contiguous ops' four-wave rows, ring 2 for the latter only; ring 0 is
+// the default depth
 template <int OP, int W, int C>
-KernelFn pick_tail(bool tail, bool weight, bool shallow) {
-    if constexpr (interleaved(OP) || (W == 4 && !op_gated(OP))) {
-        if (shallow)
-            return tail ? pick_weight<OP, W, C, true, true>(weight)
-                        : pick_weight<OP, W, C, false, true>(weight);
+KernelFn pick_tail(bool tail, bool weight, int ring) {
+    constexpr bool contig4 = !interleaved(OP) && W == 4 && !op_gated(OP);
+    if constexpr (interleaved(OP) || contig4) {
+        if (ring == 1)
+            return tail ? pick_weight<OP, W, C, true, 1>(weight)
+                        : pick_weight<OP, W, C, false, 1>(weight);
     }
-    return tail ? pick_weight<OP, W, C, true, false>(weight)
-                : pick_weight<OP, W, C, false, false>(weight);
+    if constexpr (contig4) {
+        if (ring == 2)
+            return tail ? pick_weight<OP, W, C, true, 2>(weight)
+                        : pick_weight<OP, W, C, false, 2>(weight);
+    }
+    if (ring != 0) return nullptr;
+    return tail ? pick_weight<OP, W, C, true, 0>(weight)
+                : pick_weight<OP, W, C, false, 0>(weight);
 }
 
 template <int OP>
-KernelFn pick(const Layout& L, bool weight, bool shallow) {
+KernelFn pick(const Layout& L, bool weight, int ring) {
     // H < 2048: one wave, C = 1..4; 2048 <= H < 4096: two waves, C = 2..4;
     // H >= 4096: four waves, C = 2..4.
     if (L.waves == 1) {
         switch (L.chunks) {
-            case 1: return pick_tail<OP, 1, 1>(L.ragged, weight, shallow);
-            case 2: return pick_tail<OP, 1, 2>(L.ragged, weight, shallow);
-            case 3: return pick_tail<OP, 1, 3>(L.ragged, weight, shallow);
-            case 4: return pick_tail<OP, 1, 4>(L.ragged, weight, shallow);
+            case 1: return pick_tail<OP, 1, 1>(L.ragged, weight, ring);
+            case 2: return pick_tail<OP, 1, 2>(L.ragged, weight, ring);
+            case 3: return pick_tail<OP, 1, 3>(L.ragged, weight, ring);
+            case 4: return pick_tail<OP, 1, 4>(L.ragged, weight, ring);
         }
     } else if (L.waves == 2) {
         switch (L.chunks) {
-            case 2: return pick_tail<OP, 2, 2>(L.ragged, weight, shallow);
-            case 3: return pick_tail<OP, 2, 3>(L.ragged, weight, shallow);
-            case 4: return pick_tail<OP, 2, 4>(L.ragged, weight, shallow);
+            case 2: return pick_tail<OP, 2, 2>(L.ragged, weight, ring);
+            case 3: return pick_tail<OP, 2, 3>(L.ragged, weight, ring);
+            case 4: return pick_tail<OP, 2, 4>(L.ragged, weight, ring);
         }
     } else {
         switch (L.chunks) {
-            case 2: return pick_tail<OP, 4, 2>(L.ragged, weight, shallow);
-            case 3: return pick_tail<OP, 4, 3>(L.ragged, weight, shallow);
-            case 4: return pick_tail<OP, 4, 4>(L.ragged, weight, shallow);
+            case 2: return pick_tail<OP, 4, 2>(L.ragged, weight, ring);
+            case 3: return pick_tail<OP, 4, 3>(L.ragged, weight, ring);
+            case 4: return pick_tail<OP, 4, 4>(L.ragged, weight, ring);
         }
     }
     return nullptr;
@@ -823,7 +831,7 @@ Layout layout_of(int64_t H) {
 }
 
 Plan plan_launch(Op op, int64_t rows, int64_t H, int64_t T, int64_t resident,
-                 int64_t resident_shallow) {
+                 int64_t resident_shallow, int64_t resident_two, int64_t cus) {
     const Layout L = layout_of(H);
     Plan pl{};
     pl.block_threads = L.waves == 1 ? 256 : 64 * L.waves;
@@ -840,6 +848,7 @@ Plan plan_launch(Op op, int64_t rows, int64_t H, int64_t T, int64_t resident,
     if (pl.shallow) resident = resident_shallow;
     const int S = pl.shallow ? 1 : ring_slots(L.waves, L.chunks, op_gated(op));
     pl.slots = S;
+    pl.ring = pl.shallow ? 1 : 0;
     if (interleaved(op)) {
         // one group per resident group slot (at most one per row); a group's ring
         // slots past its last row skip their arithmetic.  With several batch entries
@@ -867,14 +876,32 @@ Plan plan_launch(Op op, int64_t rows, int64_t H, int64_t T, int64_t resident,
         // group can end with idle ring slots; the group's descriptors address its
         // rows with 32-bit byte offsets and the last pass reaches S rows past its
         // range, so (per + S) rows stay below 2^31 bytes
-        const int64_t slots = resident * (L.waves == 1   ? ADALN_GROUP_OVERSUBSCRIBE_W1
-                                          : L.waves == 2 ? ADALN_GROUP_OVERSUBSCRIBE_W2
-                                                         : ADALN_GROUP_OVERSUBSCRIBE_W4);
-        const int64_t groups0 = rows < slots ? rows : slots;
-        int64_t per = (rows + groups0 - 1) / groups0;
-        per = (per + S - 1) / S * S;
-        const int64_t max_per = ((int64_t(0x7FFFFFFF) - 64) / (2 * H) - S) / S * S;
-        if (per > max_per) per = max_per;
+        const int over = L.waves == 1   ? ADALN_GROUP_OVERSUBSCRIBE_W1
+                         : L.waves == 2 ? ADALN_GROUP_OVERSUBSCRIBE_W2
+                                        : ADALN_GROUP_OVERSUBSCRIBE_W4;
+        auto per_of = [&](int64_t res, int s) {
+            const int64_t slots = res * over;
+            const int64_t groups0 = rows < slots ? rows : slots;
+            int64_t q = (rows + groups0 - 1) / groups0;
+            q = (q + s - 1) / s * s;
+            const int64_t max_q = ((int64_t(0x7FFFFFFF) - 64) / (2 * H) - s) / s * s;
+            return q < max_q ? q : max_q;
+        };
+        int64_t per = per_of(resident, S);
+        // Ungated four-wave rows: the two-row ring instead of the deeper one when it
+        // leaves the most loaded CU fewer rows (its groups spread over the CUs more
+        // evenly), weighing a two-row ring's row 3.5% dearer (measured at 65536 rows).
+        if (!pl.shallow && !interleaved(op) && L.waves == 4 && !op_gated(op) &&
+            resident_two > 0 && cus > 0 && S > 2) {
+            const int64_t per2 = per_of(resident_two, 2);
+            const int64_t g2 = (rows + per2 - 1) / per2, g = (rows + per - 1) / per;
+            const int64_t load2 = (g2 + cus - 1) / cus * per2, load = (g + cus - 1) / cus * per;
+            if (load2 * 1035 < load * 1000) {
+                per = per2;
+                pl.slots = 2;
+                pl.ring = 2;
+            }
+        }
         pl.groups = (rows + per - 1) / per;
         pl.gpb = pl.groups;
         pl.blk_rows = rows;
@@ -889,15 +916,15 @@ Plan plan_launch(Op op, int64_t rows, int64_t H, int64_t T, int64_t resident,
 hipError_t launch(Op op, const Params& p_in, hipStream_t stream) {
     const Layout L = layout_of(p_in.H);
     const bool weight = p_in.weight != nullptr;
-    auto pick_op = [&](bool shallow) -> KernelFn {
-        return op == OP_LN     ? pick<OP_LN>(L, false, shallow)
-               : op == OP_RMS  ? pick<OP_RMS>(L, weight, shallow)
-               : op == OP_RG   ? pick<OP_RG>(L, weight, shallow)
-               : op == OP_RGLN ? pick<OP_RGLN>(L, false, shallow)
-               : op == OP_LNQ  ? pick<OP_LNQ>(L, false, shallow)
+    auto pick_op = [&](int ring) -> KernelFn {
+        return op == OP_LN     ? pick<OP_LN>(L, false, ring)
+               : op == OP_RMS  ? pick<OP_RMS>(L, weight, ring)
+               : op == OP_RG   ? pick<OP_RG>(L, weight, ring)
+               : op == OP_RGLN ? pick<OP_RGLN>(L, false, ring)
+               : op == OP_LNQ  ? pick<OP_LNQ>(L, false, ring)
                                : nullptr;
     };
-    KernelFn deep = pick_op(false);
+    KernelFn deep = pick_op(0);
     if (!deep) return hipErrorInvalidValue;
     // one-wave rows: four independent waves per workgroup; else one row group per
     // workgroup of W waves
@@ -909,13 +936,15 @@ hipError_t launch(Op op, const Params& p_in, hipStream_t stream) {
         return hipErrorInvalidDeviceFunction;
     }
     const int64_t resident = (int64_t)cus * blocks_per_cu * groups_per_block;
-    int64_t resident_shallow = 0;
-    KernelFn shallow =
-        (interleaved(op) || (L.waves == 4 && !op_gated(op))) ? pick_op(true) : nullptr;
-    int bpc1 = 0;
+    int64_t resident_shallow = 0, resident_two = 0;
+    KernelFn shallow = pick_op(1), two = pick_op(2);  // null where not instantiated
+    int bpc1 = 0, bpc2 = 0;
     if (shallow && occupancy(reinterpret_cast<const void*>(shallow), block, &bpc1, &cus))
         resident_shallow = (int64_t)cus * bpc1 * groups_per_block;
-    const Plan pl = plan_launch(op, p_in.rows, p_in.H, p_in.T, resident, resident_shallow);
+    if (two && occupancy(reinterpret_cast<const void*>(two), block, &bpc2, &cus))
+        resident_two = (int64_t)cus * bpc2 * groups_per_block;
+    const Plan pl = plan_launch(op, p_in.rows, p_in.H, p_in.T, resident, resident_shallow,
+                                resident_two, cus);
     Params p = p_in;
     p.groups = pl.groups;
     p.gpb = pl.gpb;
@@ -924,8 +953,9 @@ hipError_t launch(Op op, const Params& p_in, hipStream_t stream) {
     p.step = pl.step;
     p.span = pl.span;
     if (pl.blocks > 0x7FFFFFFF || pl.groups > 0x7FFFFFFF) return hipErrorInvalidValue;
-    hipLaunchKernelGGL(pl.shallow ? shallow : deep, dim3((unsigned)pl.blocks), dim3(block), 0,
-                       stream, p);
+    KernelFn fn = pl.ring == 1 ? shallow : pl.ring == 2 ? two : deep;
+    if (!fn) return hipErrorInvalidValue;
+    hipLaunchKernelGGL(fn, dim3((unsigned)pl.blocks), dim3(block), 0, stream, p);
     return hipGetLastError();
 }
 

@@ -248,6 +248,22 @@ def test_batch_entries_split_over_groups(op, B, T, H):
         check_lnq(x, sc, sh, 0.0125, f"lnq {B}x{T}x{H}")
 
 
+# RMS row counts where the four-wave rows take the two-row ring (the groups then
+# spread more evenly over the CUs than with the three-row ring), with and without a
+# ragged last chunk and the weight.
+@pytest.mark.parametrize("T,H,weight", [(8192, 4096, True), (5120, 4096, False),
+                                        (4096, 4104, True), (10240, 4096, True)])
+def test_rms_two_row_ring_sizes(T, H, weight):
+    say(f"[parity] rms two-row ring T={T} H={H} weight={weight}")
+    rng = np.random.default_rng(T * 3 + H)
+    x = synth.normal_bf16(rng, (1, T, H))
+    w = synth.normal_bf16(rng, (H,), 0.02, 1.0) if weight else None
+    sc = synth.normal_bf16(rng, (1, H), 0.1)
+    sh = synth.normal_bf16(rng, (1, H), 0.1)
+    assert_bits_equal(run_rms(x, w, sc, sh), O.rmsnorm_scale_shift(x, w, sc, sh, EPS),
+                      f"rms {T}x{H}")
+
+
 @pytest.mark.parametrize("eps", [0.0, 1e-5, 1e-6, 0.25])
 def test_eps_values(eps):
     say(f"[parity] eps={eps}")

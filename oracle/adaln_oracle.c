@@ -277,12 +277,14 @@ static uint16_t gate_residual(uint16_t res, uint16_t upd, uint16_t gate) {
 /* ------------------------------------------------------------------------ */
 /* The format: 1 sign bit, 4 exponent bits with bias 7, 3 mantissa bits; exponent
  * field 0 holds the subnormals m * 2^-9; there is no infinity; S.1111.111 is NaN,
- * so the largest finite value is 1.75 * 2^8 = 448.  Rounding to nearest-even from
+ * so the largest finite value is 1.75 * 2^8 = 448.  The format has two NaN codes
+ * and no page says which one a conversion writes (nor does IEEE 754 interpret the
+ * sign of a NaN): this library writes 0xFF for every NaN.  Rounding to nearest-even from
  * the definition: the spacing of representable values around |v| is 2^(E-3) for
  * |v| in [2^E, 2^(E+1)) with E >= -6, and 2^-9 below 2^-6. */
 static uint8_t to_e4m3fn(float v) {
     uint8_t sign = signbit(v) ? 0x80 : 0x00;
-    if (isnan(v)) return sign | 0x7F;
+    if (isnan(v)) return 0xFF;
     double a = fabs((double)v);
     if (a == 0.0) return sign;
     int e2;
@@ -301,7 +303,7 @@ static uint8_t to_e4m3fn(float v) {
     } else {
         code = (int)r;  /* exponent field 0: m * 2^-9 */
     }
-    if (code >= 0x7F) return sign | 0x7F;  /* beyond 448: NaN (the caller clamps first) */
+    if (code >= 0x7F) return 0xFF;  /* beyond 448: NaN (the caller clamps first) */
     return sign | (uint8_t)code;
 }
 

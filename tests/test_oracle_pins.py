@@ -339,6 +339,18 @@ def assert_fp8_equal(got, want, what):
     assert np.array_equal(got[~gn], want[~wn]), what
 
 
+def test_e4m3fn_nan_code_is_0xff():
+    # the format's NaN is S.1111.111; this library writes 0xFF for every NaN (reading of
+    # the pages, which fix no NaN code), including NaNs of either sign and payload
+    bits = np.array([0x7FC00000, 0xFFC00000, 0x7F800001, 0xFF800001, 0x7FFFFFFF],
+                    np.uint32).view(np.float32)
+    assert np.all(O.to_e4m3fn(bits) == 0xFF)
+    y = np.array([0x7FC0, 0xFFC0, 0x7F81], np.uint16)   # bf16 NaNs through the quantiser
+    assert np.all(O.quant_fp8(y, 0.0125) == 0xFF)
+    # and torch's conversion agrees that these are NaN (positions), whatever its sign
+    assert np.all((torch_e4m3fn(bits) & 0x7F) == 0x7F)
+
+
 def test_e4m3fn_codes_round_trip():
     codes, vals = e4m3fn_values()
     assert float(vals.max()) == 448.0 and float(vals[vals > 0].min()) == 2.0 ** -9

@@ -2,15 +2,20 @@
 
 A step is one pass of the whole hot path (load, statistic, fold, finalize,
 normalise, modulate, store) over one batch: one launch of the fused kernel.  The
-default workload is RMSNorm + scale/shift on bf16 x [1, 4216, 4096] (ERNIE-Image
-site shape), the configuration the headline metric is quoted on.  Inputs are
-resident in HBM; the launches rotate over buffer sets totalling >= 1 GiB so
-every launch reads from HBM, not from the 256 MB Infinity Cache.
+metric names no single configuration, so the timed line is the largest of them that
+has a bandwidth target: LayerNorm + modulate on bf16 x [2, 4608, 3072] (the FLUX.1
+adaLN site with CFG batch 2).  Inputs are resident in HBM; the launches rotate over
+buffer sets totalling >= 1 GiB so every launch reads from HBM, not from the 256 MB
+Infinity Cache.
 
 Prints ONE JSON line: value = achieved HBM GB/s (algorithmic bytes: read x[,res],
-write y[,r]) over the timed steps, plus rows/s, the roofline of the fused
-kernel, the copy ceiling, the other workloads' figures, and the CPU oracle timed
-on this host as the baseline.
+write y[,r]) over the timed steps, plus rows/s and the roofline of the fused
+kernel; then, per configuration with the 80 %-of-peak target (RMSNorm [1,4216,4096],
+residual-gate RMSNorm [2,1140,4096], LayerNorm [2,4608,3072] and [1,4333,3072]), its
+own roofline object: events and kernel-trace time, fraction of the 8 TB/s peak,
+HBM traffic ratio, and fractions of the measured streaming ceilings (copy, read-only,
+write-only at the same bytes and at 1 GiB); the other workloads' figures; and the
+CPU oracle timed on this host as the baseline.
 """
 from __future__ import annotations
 
@@ -71,7 +76,11 @@ def load_counters(name: str):
 # ---------------------------------------------------------------------------
 # workloads
 # ---------------------------------------------------------------------------
-HEADLINE = "rms_1x4216x4096"
+HEADLINE = "ln_2x4608x3072"
+# the configurations of the metric that carry the 80 %-of-peak target
+TARGET_CONFIGS = ["rms_1x4216x4096", "rg_rms_2x1140x4096", "ln_2x4608x3072", "ln_1x4333x3072"]
+TARGET_FRAC = 0.80
+STREAM_PERS = (1, 2, 4, 8, 16)
 WORKLOAD_NAMES = ["ln_1x128x2048", "rms_1x4216x4096", "rg_rms_2x1140x4096", "ln_2x4608x3072",
                   "ln_1x4333x3072", "rg_ln_2x4096x3072", "ln_fp8_2x4608x3072",
                   "qk_rmsnorm_rope_4608x24x128", "rg_channel_first_2x3072x4608"]
@@ -317,6 +326,72 @@ def copy_ceiling(nbytes_rw: int, rotate_bytes: int, steps: int, warmup: int, mod
     return nbytes_rw * steps / t / 1e9
 
 
+def stream_rate(kind: str, nbytes: int, per: int, rotate_bytes: int, steps: int,
+                warmup: int) -> float:
+    """GB/s of the library's streaming kernel `kind` moving `nbytes` bytes in total:
+    copy reads nbytes/2 and writes nbytes/2 (a fused kernel's mix), read reads nbytes,
+    fill writes nbytes.  Buffer sets rotate over >= rotate_bytes, graph replay."""
+    import torch
+    import diffusion_dit_adaln_amd as A
+    lib = A.load_library()
+    kid = {"copy": 0, "read": 1, "fill": 2}[kind]
+    span = nbytes // 2 if kind == "copy" else nbytes
+    span -= span % 16
+    nsets = max(2, -(-rotate_bytes // nbytes))
+    src = ([torch.empty(span, dtype=torch.uint8, device="cuda").fill_(1) for _ in range(nsets)]
+           if kind != "fill" else [None] * nsets)
+    if kind == "read":
+        dst = [torch.empty(span, dtype=torch.uint8, device="cuda")] * nsets  # only the folds
+    else:
+        dst = [torch.empty(span, dtype=torch.uint8, device="cuda") for _ in range(nsets)]
+
+    def launch(i, h):
+        s_ = src[i % nsets]
+        return lib.adaln_diag_stream(kid, None if s_ is None else s_.data_ptr(),
+                                     dst[i % nsets].data_ptr(), span, per, h)
+
+    t = time_steps(launch, steps, warmup, "graph")
+    moved = 2 * span if kind == "copy" else span
+    del src, dst
+    torch.cuda.empty_cache()
+    return moved * steps / t / 1e9
+
+
+def ceilings_at(nbytes: int, rotate_bytes: int, steps: int, warmup: int, pers=STREAM_PERS):
+    """The measured streaming ceilings at one byte count: for copy, read-only and
+    write-only, the rate at each vector count per thread and the best of them."""
+    out = {}
+    for kind in ("copy", "read", "fill"):
+        rates = {str(p): round(stream_rate(kind, nbytes, p, rotate_bytes, steps, warmup), 1)
+                 for p in pers}
+        best = max(rates, key=lambda k: rates[k])
+        out[kind] = {"GBps": rates[best], "per_thread": int(best), "by_per_thread": rates}
+    return out
+
+
+def load_profile_table(name: str, key_col: int, val_col: int):
+    """{workload: value} from a committed profile summary whose rows are
+    'workload | ... | value' (columns by index), or {} when the summary is missing or
+    was taken on a different kernel source."""
+    path = os.path.join(ROOT, "profiles", name)
+    if not os.path.exists(path):
+        return {}
+    rows, sha = {}, None
+    with open(path) as fh:
+        for line in fh:
+            if line.startswith("#"):
+                if "kernel_src_sha" in line and "=" in line:
+                    sha = line.split("=", 1)[1].strip()
+                continue
+            parts = [c.strip() for c in line.split("|")]
+            if len(parts) > max(key_col, val_col):
+                try:
+                    rows[parts[key_col]] = float(parts[val_col])
+                except ValueError:
+                    pass
+    return rows if sha == kernel_src_sha() else {}
+
+
 def median3(f):
     v = sorted(f() for _ in range(3))
     return v[1]
@@ -504,28 +579,111 @@ def sweep_rows(rotate: int, steps: int, warmup: int, op: str = "rms") -> None:
                               "asymptotic_GBps": round(float(1e-3 / slope), 1)}}), flush=True)
 
 
+def time_workload(name: str, rotate: int, steps: int, warmup: int, modes=("graph", "eager")):
+    """Median-of-3 GB/s and microseconds per launch of one workload, per timing mode."""
+    import torch
+    w = workload(name)
+    L = launcher_for(w, rotate)
+    nb = w.algorithmic_bytes()
+    res = {}
+    for mode in modes:
+        t = median3(lambda: time_steps(L.call, steps, warmup, mode))
+        res[mode] = {"GBps": round(nb * steps / t / 1e9, 2),
+                     "us_per_launch": round(t / steps * 1e6, 3)}
+    del L
+    torch.cuda.empty_cache()
+    return w, nb, res
+
+
+def config_roofline(name: str, rotate: int, steps: int, warmup: int, ceil_1g: dict):
+    """The roofline object of one target configuration: the rate between HIP events
+    (graph replay, median of 3), the committed kernel-trace time and traffic ratio
+    (when taken on the current kernel source), and the fractions of the 8 TB/s peak
+    and of the measured streaming ceilings at the same bytes and at 1 GiB."""
+    w, nb, res = time_workload(name, rotate, steps, warmup)
+    gbps = res["graph"]["GBps"]
+    trace_ns = load_profile_table("kernel_trace_configs.txt", 0, 3).get(name)
+    ratio = load_profile_table("counters_all_workloads.txt", 0, 6).get(name)
+    ceil = ceilings_at(nb, rotate, steps, warmup)
+    out = {"workload": describe(w), "bytes": nb, "rows": workload_rows(w),
+           "bound": "hbm", "achieved": gbps, "peak": PEAK_HBM_GBPS, "unit": "GB/s",
+           "frac": round(gbps / PEAK_HBM_GBPS, 4),
+           "us_per_launch": res["graph"]["us_per_launch"], "eager": res["eager"],
+           "trace_us": None if trace_ns is None else round(trace_ns / 1e3, 3),
+           "trace_GBps": None if trace_ns is None else round(nb / trace_ns, 1),
+           "traffic_ratio": ratio,
+           "traffic": None if ratio is None else round(ratio * nb),
+           "ceiling": {k: {"GBps": v["GBps"], "per_thread": v["per_thread"]}
+                       for k, v in ceil.items()},
+           "frac_of_copy": round(gbps / ceil["copy"]["GBps"], 4),
+           "frac_of_copy_1GiB": round(gbps / ceil_1g["copy"]["GBps"], 4),
+           "meets_target": gbps >= TARGET_FRAC * PEAK_HBM_GBPS,
+           "copy_meets_target": ceil["copy"]["GBps"] >= TARGET_FRAC * PEAK_HBM_GBPS}
+    if trace_ns is not None:
+        out["trace_frac"] = round(nb / trace_ns / PEAK_HBM_GBPS, 4)
+    return out, ceil
+
+
+CF_SWEEP_TOKENS = (4608, 4336, 4333, 4334, 4332, 4335)
+
+
+def sweep_cf(rotate: int, steps: int, warmup: int) -> None:
+    """One JSON line: the channel-first residual gate at [2, 3072, T] for token counts
+    T with every residue of T mod 8 that matters (0: aligned rows; odd, 2 and 4 mod 8:
+    rows starting inside a 16-byte block), GB/s per launch in graph replay (median of
+    3) beside the best streaming copy of the same bytes."""
+    from diffusion_dit_adaln_amd import synth
+    points = []
+    for T in CF_SWEEP_TOKENS:
+        wl = synth.cf_tokens(T)
+        L = launcher_for(wl, rotate)
+        nb = wl.algorithmic_bytes()
+        t = median3(lambda: time_steps(L.call, steps, warmup, "graph")) / steps
+        del L
+        cc = max(stream_rate("copy", nb, p, rotate, steps, warmup) for p in (1, 4, 8))
+        points.append({"tokens": T, "T_mod_8": T % 8, "bytes": nb,
+                       "GBps": round(nb / t / 1e9, 1), "us_per_launch": round(t * 1e6, 3),
+                       "copy_GBps": round(cc, 1), "frac_of_copy": round(nb / t / 1e9 / cc, 4)})
+        print(f"[sweep-cf] T={T}: {points[-1]['GBps']} GB/s", file=sys.stderr, flush=True)
+    base = next(p["GBps"] for p in points if p["tokens"] == 4336)
+    for p in points:
+        p["rate_vs_T4336"] = round(p["GBps"] / base, 4)
+    print(json.dumps({"sweep": "residual_gate_channel_first bf16 res/out [2,3072,T], "
+                               "update [2,T,3072], graph replay", "points": points}), flush=True)
+
+
 def main():
     ap = argparse.ArgumentParser(description=__doc__)
     ap.add_argument("--gpus", type=int, default=1)
     ap.add_argument("--steps", type=int, default=400)
     ap.add_argument("--warmup", type=int, default=40)
     ap.add_argument("--workload", default=HEADLINE, choices=WORKLOAD_NAMES,
-                    help="the workload of the timed line (default: the headline RMS one)")
+                    help="the workload of the timed line (default: LayerNorm [2,4608,3072])")
     ap.add_argument("--timing", default="graph", choices=["graph", "eager"])
     ap.add_argument("--rotate-mb", type=int, default=1024)
     ap.add_argument("--cpu-seconds", type=float, default=10.0)
     ap.add_argument("--no-cpu", action="store_true", help="skip the CPU oracle baseline")
     ap.add_argument("--no-extras", action="store_true",
-                    help="only the headline workload (for profiler runs)")
+                    help="only the timed workload (for profiler runs)")
     ap.add_argument("--sweep-rows", action="store_true",
                     help="instead of the benchmark line: one op (--sweep-op) over a range of "
                          "row counts beside the streaming copy of the same bytes, with a fit "
                          "of time = fixed + bytes / rate")
     ap.add_argument("--sweep-op", default="rms", choices=["rms", "ln"],
                     help="the op of --sweep-rows: RMS at H 4096 or LayerNorm at H 3072")
+    ap.add_argument("--sweep-cf", action="store_true",
+                    help="instead of the benchmark line: the channel-first residual gate over "
+                         "token counts with aligned and unaligned residual rows")
+    ap.add_argument("--cf-tokens", type=int, default=0,
+                    help="with --workload rg_channel_first_2x3072x4608: use this token count "
+                         "instead (for profiler runs of the sweep's shapes)")
     ap.add_argument("--copy-only", action="store_true",
                     help="only a plain device copy of the workload's byte count (counter "
                          "calibration for profiler runs)")
+    ap.add_argument("--ceilings", action="store_true",
+                    help="instead of the benchmark line: the streaming ceilings (copy, "
+                         "read-only, write-only, 1..16 vectors per thread) at each target "
+                         "configuration's bytes and at 1 GiB")
     args = ap.parse_args()
 
     if args.gpus != 1 or int(os.environ.get("WORLD_SIZE", "1")) != 1:
@@ -542,10 +700,28 @@ def main():
     if args.sweep_rows:
         sweep_rows(rotate, args.steps, args.warmup, args.sweep_op)
         return
+    if args.sweep_cf:
+        sweep_cf(rotate, args.steps, args.warmup)
+        return
+    if args.ceilings:
+        table = {}
+        for name in TARGET_CONFIGS + ["1GiB"]:
+            nb = (1 << 30) if name == "1GiB" else workload(name).algorithmic_bytes()
+            table[name] = {"bytes": nb, **ceilings_at(nb, rotate, max(50, args.steps // 4),
+                                                      args.warmup)}
+            print(f"[ceilings] {name} done", file=sys.stderr, flush=True)
+        print(json.dumps({"ceilings": table}), flush=True)
+        return
     wl = workload(args.workload)
+    if args.cf_tokens:
+        if wl.op != "cf":
+            ap.error("--cf-tokens applies to the channel-first workload")
+        from diffusion_dit_adaln_amd import synth
+        wl = synth.cf_tokens(args.cf_tokens)
     if args.copy_only:
         g = copy_ceiling(wl.algorithmic_bytes(), rotate, args.steps, args.warmup, args.timing)
-        # (the library's streaming copy kernel, diag_copy: known bytes for counter scaling)
+        # (the library's streaming copy kernel, 8 vectors per thread: known bytes for
+        # counter scaling)
         print(json.dumps({"copy_GBps": round(g, 2), "bytes_per_copy": wl.algorithmic_bytes(),
                           "read_bytes": wl.algorithmic_bytes() // 2,
                           "write_bytes": wl.algorithmic_bytes() // 2}), flush=True)
@@ -556,17 +732,21 @@ def main():
 
     t = time_steps(L.call, args.steps, args.warmup, args.timing)
     gbps = nbytes * args.steps / t / 1e9
+
     # the outputs of buffer set 0 (every set holds the same inputs), as bits
     def bits(t):
-        return t.cpu().numpy() if t.dtype == torch.uint8 else t.cpu().view(torch.int16).numpy().view(np.uint16)
+        return t.cpu().numpy() if t.dtype == torch.uint8 else \
+            t.cpu().view(torch.int16).numpy().view(np.uint16)
     s0 = L.sets[0]
     y_gpu = [bits(s0[k]) for k in ("y", "qo", "ko", "out") if k in s0]
     ms_per_step = t / args.steps * 1e3
     # average launch duration of the fused kernel: the same events, per launch
     avg_launch_s = t / args.steps
 
-    name = wl.name
-    traffic = load_counters(name)
+    traffic = load_counters(wl.name)
+    if traffic is None:
+        ratio = load_profile_table("counters_all_workloads.txt", 0, 6).get(wl.name)
+        traffic = None if ratio is None else round(ratio * nbytes)
     out = {
         "metric": METRIC, "value": round(gbps, 2), "unit": "GB/s", "n_gpus": 1,
         "steps": args.steps, "warmup": args.warmup, "ms_per_step": round(ms_per_step, 5),
@@ -580,43 +760,48 @@ def main():
         "roofline": {"bound": "hbm", "achieved": round(nbytes / avg_launch_s / 1e9, 2),
                      "peak": PEAK_HBM_GBPS, "unit": "GB/s",
                      "frac": round(nbytes / avg_launch_s / 1e9 / PEAK_HBM_GBPS, 4),
-                     "traffic": traffic, "kernel": KERNEL_OF.get(wl.op, f"fused_norm_modulate ({wl.op})"),
+                     "traffic": traffic,
+                     "kernel": KERNEL_OF.get(wl.op, f"fused_norm_modulate ({wl.op})"),
                      "avg_launch_us": round(avg_launch_s * 1e6, 3)},
     }
     # per-launch cross-check: median of single launches between their own events
     med = single_launch_median(L.call, 200, args.warmup)
     out["roofline"]["single_launch_median_us"] = round(med * 1e6, 3)
     out["roofline"]["single_launch_median_GBps"] = round(nbytes / med / 1e9, 2)
+    trace_ns = load_profile_table("kernel_trace_configs.txt", 0, 3).get(wl.name)
+    if trace_ns is not None:
+        out["roofline"]["trace_us"] = round(trace_ns / 1e3, 3)
     del L
     torch.cuda.empty_cache()
     if not args.no_extras:
         steps = max(50, args.steps // 2)
-        out["copy_ceiling_GBps"] = round(median3(
-            lambda: copy_ceiling(nbytes, rotate, steps, args.warmup)), 2)
-        out["torch_copy_GBps"] = round(median3(
-            lambda: copy_ceiling(nbytes, rotate, steps, args.warmup, kind="torch")), 2)
-        out["frac_of_copy_ceiling"] = round(gbps / out["copy_ceiling_GBps"], 4)
+        ceil_1g = ceilings_at(1 << 30, rotate, steps // 2, args.warmup)
+        out["ceilings_1GiB"] = ceil_1g
+        per_config = {}
+        for name in TARGET_CONFIGS:
+            per_config[name], _ = config_roofline(name, rotate, steps, args.warmup, ceil_1g)
+            print(f"[bench] {name} done", file=sys.stderr, flush=True)
+        out["per_config"] = per_config
+        if wl.name in per_config:
+            pc = per_config[wl.name]
+            out["roofline"]["frac_of_copy"] = round(gbps / pc["ceiling"]["copy"]["GBps"], 4)
+            out["roofline"]["ceiling"] = pc["ceiling"]
+        out["configs_meeting_target"] = sum(1 for v in per_config.values() if v["meets_target"])
         per = {}
         for name in WORKLOAD_NAMES:
-            w2 = workload(name)
-            L2 = launcher_for(w2, rotate)
-            nb2 = w2.algorithmic_bytes()
-            res = {}
-            for mode in ("graph", "eager"):
-                t2 = median3(lambda: time_steps(L2.call, steps, args.warmup, mode))
-                res[mode] = {"GBps": round(nb2 * steps / t2 / 1e9, 2),
-                             "us_per_launch": round(t2 / steps * 1e6, 3)}
-            del L2
-            torch.cuda.empty_cache()
-            cc = median3(lambda: copy_ceiling(nb2, rotate, steps, args.warmup))
+            if name in TARGET_CONFIGS:
+                continue
+            w2, nb2, res = time_workload(name, rotate, steps, args.warmup)
+            cc = max(stream_rate("copy", nb2, p, rotate, steps, args.warmup) for p in (4, 8, 16))
             shape = list({"qk": lambda: w2.qkv.shape, "cf": lambda: w2.res.shape}.get(
                 w2.op, lambda: w2.x.shape)())
-            rows2 = workload_rows(w2)
             per[w2.name] = {"op": w2.op, "shape": shape, "bytes": nb2, **res,
-                            "rows_per_s": round(rows2 / res["graph"]["us_per_launch"] * 1e6, 1),
+                            "rows_per_s": round(workload_rows(w2) / res["graph"]["us_per_launch"]
+                                                * 1e6, 1),
+                            "frac_of_peak": round(res["graph"]["GBps"] / PEAK_HBM_GBPS, 4),
                             "copy_ceiling_GBps": round(cc, 2),
                             "frac_of_copy_ceiling": round(res["graph"]["GBps"] / cc, 4)}
-            torch.cuda.empty_cache()
+            print(f"[bench] {name} done", file=sys.stderr, flush=True)
         out["per_workload"] = per
     if not args.no_cpu:
         cb = cpu_baseline(wl, args.cpu_seconds, y_gpu=y_gpu)

@@ -20,6 +20,7 @@ from ._binding import (  # noqa: F401
     adaln_diag_launch_plan,
     adaln_diag_quant_fp8,
     adaln_diag_round_bf16,
+    adaln_diag_stream,
     adaln_diag_stream_copy,
     adaln_layernorm_modulate,
     adaln_layernorm_modulate_fp8_quant,

@@ -12,7 +12,7 @@ import os
 import torch
 
 _PKG = os.path.dirname(os.path.abspath(__file__))
-ABI_VERSION = 8
+ABI_VERSION = 9
 
 STATUS_NAMES = {0: "ADALN_OK", 1: "ADALN_ERR_NULL", 2: "ADALN_ERR_SHAPE", 3: "ADALN_ERR_ALIGN",
                 4: "ADALN_ERR_STRIDE", 5: "ADALN_ERR_OVERLAP", 6: "ADALN_ERR_VALUE",
@@ -29,7 +29,7 @@ EXPORTS = ("adaln_layernorm_modulate", "adaln_rmsnorm_scale_shift",
            "adaln_check_layernorm_modulate_fp8_quant", "adaln_reduction_layout",
            "adaln_status_string", "adaln_abi_version", "adaln_diag_round_bf16",
            "adaln_diag_finalize", "adaln_diag_quant_fp8", "adaln_diag_stream_copy",
-           "adaln_diag_launch_plan")
+           "adaln_diag_stream", "adaln_diag_launch_plan")
 
 
 class AdalnError(RuntimeError):
@@ -44,9 +44,8 @@ _lib = None
 
 
 def library_path() -> str:
-    """The in-tree libadaln.so, or the build named by $ADALN_LIBRARY (used to compare
-    launch-tuning builds; the numerics of every build are the same)."""
-    return os.environ.get("ADALN_LIBRARY") or os.path.join(_PKG, "libadaln.so")
+    """The in-tree libadaln.so (the only library the binding loads)."""
+    return os.path.join(_PKG, "libadaln.so")
 
 
 def load_library():
@@ -79,6 +78,7 @@ def load_library():
         "adaln_diag_round_bf16": [P, P, I, P],
         "adaln_diag_finalize": [P, P, I, I, F, P],
         "adaln_diag_stream_copy": [P, P, I, P],
+        "adaln_diag_stream": [S, P, P, I, S, P],
         "adaln_diag_quant_fp8": [P, P, I, P, P],
         "adaln_diag_launch_plan": [S, I, I, I, I, I, ctypes.POINTER(I)],
     }
@@ -450,6 +450,25 @@ def adaln_diag_stream_copy(src: torch.Tensor, dst: torch.Tensor, stream=None) ->
     _check(_call(src.device, lib.adaln_diag_stream_copy, src.data_ptr(), dst.data_ptr(), nbytes,
                  stream=stream), "adaln_diag_stream_copy")
     return dst
+
+
+STREAM_KINDS = {"copy": 0, "read": 1, "fill": 2}
+
+
+def adaln_diag_stream(kind: str, src, dst: torch.Tensor, vectors_per_thread: int = 8,
+                      stream=None) -> None:
+    """The library's streaming measurement kernel `kind` (copy, read or fill) over the
+    byte size of dst (contiguous; src the same size, or None for fill)."""
+    lib = load_library()
+    if not dst.is_contiguous() or (src is not None and not src.is_contiguous()):
+        raise ValueError("expected contiguous tensors")
+    _on(dst.device, (src, "src"))
+    nbytes = dst.numel() * dst.element_size()
+    if src is not None and src.numel() * src.element_size() != nbytes:
+        raise ValueError("src and dst sizes differ")
+    _check(_call(dst.device, lib.adaln_diag_stream, STREAM_KINDS[kind], _ptr(src),
+                 dst.data_ptr(), nbytes, int(vectors_per_thread), stream=stream),
+           "adaln_diag_stream")
 
 
 def adaln_diag_quant_fp8(v: torch.Tensor, qscale: torch.Tensor, stream=None) -> torch.Tensor:

@@ -15,7 +15,8 @@ from concurrent.futures import ThreadPoolExecutor
 PKG = os.path.dirname(os.path.abspath(__file__))
 CSRC = os.path.join(PKG, "csrc")
 SOURCES = [os.path.join(CSRC, "adaln_kernels.hip"), os.path.join(CSRC, "adaln_qknorm.hip"),
-           os.path.join(CSRC, "adaln_channel_first.hip"), os.path.join(CSRC, "adaln_api.cpp")]
+           os.path.join(CSRC, "adaln_channel_first.hip"),
+           os.path.join(CSRC, "adaln_stream.hip"), os.path.join(CSRC, "adaln_api.cpp")]
 OUT = os.path.join(PKG, "libadaln.so")
 
 # -ffp-contract=off: every fp32 add/mul rounds on its own (no FMA contraction).

@@ -213,9 +213,11 @@ adaln_status validate_cf(const void* res, const void* update, const void* gate, 
     if (B < 0 || T < 0 || H < 0 || (H % 8) != 0) return ADALN_ERR_SHAPE;
     if (B == 0 || T == 0 || H == 0) return ADALN_OK;
     if (B > INT64_MAX / T || B * T > INT64_MAX / 2 / H) return ADALN_ERR_SHAPE;
-    // one workgroup of 256 per 64x64 tile, and a grid holds fewer than 2^32 work-items
-    if (B > (int64_t(0xFFFFFFFF) / 256) / (((H + 63) / 64) * ((T + 63) / 64)))
-        return ADALN_ERR_SHAPE;
+    // one workgroup of 256 per tile (adaln::cf_tiles), and a grid holds fewer than 2^32
+    // work-items; the bound on B first keeps the tile count itself in range
+    const int64_t per_b = adaln::cf_tiles(1, H, T);
+    if (B > (int64_t(0xFFFFFFFF) / 256) / per_b) return ADALN_ERR_SHAPE;
+    if (adaln::cf_grid(adaln::cf_tiles(B, H, T)) > int64_t(0xFFFFFFFF) / 256) return ADALN_ERR_SHAPE;
     *empty = false;
     if (!res || !update || !out) return ADALN_ERR_NULL;
     if (!aligned16(res) || !aligned16(update) || !aligned16(out)) return ADALN_ERR_ALIGN;
@@ -402,7 +404,8 @@ const char* adaln_status_string(adaln_status status) {
         case ADALN_ERR_NULL: return "a required pointer is NULL";
         case ADALN_ERR_SHAPE:
             return "unsupported shape: sizes >= 0; row ops need 8 <= H <= 8192 and H % 8 == 0; "
-                   "QK-norm needs head_dim 128; the channel-first layout needs T, H % 8 == 0";
+                   "QK-norm needs head_dim 128; the channel-first op needs H % 8 == 0 (any T) "
+                   "and fewer than 2^24 tiles of 64x64";
         case ADALN_ERR_ALIGN: return "a pointer is not 16-byte aligned";
         case ADALN_ERR_STRIDE: return "a batch stride is negative, not a multiple of 8, or in (0, H)";
         case ADALN_ERR_OVERLAP: return "an output overlaps an input or the other output";
@@ -489,14 +492,27 @@ adaln_status adaln_diag_quant_fp8(const float* in, uint8_t* out, int64_t n, cons
 
 adaln_status adaln_diag_stream_copy(const void* src, void* dst, int64_t bytes,
                                     void* hip_stream) {
+    return adaln_diag_stream(0, src, dst, bytes, 8, hip_stream);
+}
+
+adaln_status adaln_diag_stream(int kind, const void* src, void* dst, int64_t bytes,
+                               int vectors_per_thread, void* hip_stream) {
+    if (kind < adaln::STREAM_COPY || kind > adaln::STREAM_FILL) return ADALN_ERR_VALUE;
+    const int per = vectors_per_thread;
+    if (per != 1 && per != 2 && per != 4 && per != 8 && per != 16) return ADALN_ERR_VALUE;
     if (bytes < 0 || (bytes % 16) != 0) return ADALN_ERR_SHAPE;
     if (bytes == 0) return ADALN_OK;
-    if (!src || !dst) return ADALN_ERR_NULL;
-    if (!aligned16(src) || !aligned16(dst)) return ADALN_ERR_ALIGN;
-    const Span a{(uintptr_t)src, (uintptr_t)src + (uintptr_t)bytes};
-    const Span b{(uintptr_t)dst, (uintptr_t)dst + (uintptr_t)bytes};
-    if (overlaps(a, b)) return ADALN_ERR_OVERLAP;
-    return adaln::launch_diag_copy(src, dst, bytes / 16, (hipStream_t)hip_stream) == hipSuccess
+    const bool reads = kind != adaln::STREAM_FILL;
+    if ((reads && !src) || !dst) return ADALN_ERR_NULL;
+    if ((reads && !aligned16(src)) || !aligned16(dst)) return ADALN_ERR_ALIGN;
+    // copy: dst receives `bytes`; read: the waves' folds, a prefix of dst
+    const int64_t n16 = bytes / 16;
+    const int64_t written = kind == adaln::STREAM_READ ? adaln::stream_sink_bytes(n16, per) : bytes;
+    if (written > bytes) return ADALN_ERR_SHAPE;
+    if (reads && overlaps(Span{(uintptr_t)src, (uintptr_t)src + (uintptr_t)bytes},
+                          Span{(uintptr_t)dst, (uintptr_t)dst + (uintptr_t)written}))
+        return ADALN_ERR_OVERLAP;
+    return adaln::launch_stream(kind, src, dst, n16, per, (hipStream_t)hip_stream) == hipSuccess
                ? ADALN_OK
                : ADALN_ERR_LAUNCH;
 }

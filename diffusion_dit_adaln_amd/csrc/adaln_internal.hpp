@@ -75,6 +75,16 @@ struct CFParams {
     int64_t B, T, H, gate_bs;
 };
 hipError_t launch_cf(const CFParams& p, hipStream_t stream);
+// Workgroups of the channel-first launch: one per tile of 64 hidden x 64 tokens
+// (T % 8 == 0) or of 64 hidden x the 64-token span of eight aligned 16-byte blocks
+// of each residual row (otherwise; a row's blocks start up to 7 tokens before the
+// tile's first token, so the tiles cover T + 7 tokens), rounded up to a multiple of
+// eight so that consecutive tiles land on one XCD.
+inline int64_t cf_tiles(int64_t B, int64_t H, int64_t T) {
+    const int64_t span = T % 8 == 0 ? T : T + 7;
+    return B * ((H + 63) / 64) * ((span + 63) / 64);
+}
+inline int64_t cf_grid(int64_t tiles) { return (tiles + 7) / 8 * 8; }
 
 // Resident workgroups of `block` threads per CU for a kernel on the current device,
 // and the CU count (cached per kernel and device, thread-safe).
@@ -103,7 +113,13 @@ hipError_t launch(Op op, const Params& p, hipStream_t stream);
 hipError_t launch_diag_round(const float* in, uint16_t* out, int64_t n, hipStream_t stream);
 hipError_t launch_diag_finalize(const float* in, float* out, int64_t n, int64_t H, float eps,
                                 hipStream_t stream);
-hipError_t launch_diag_copy(const void* src, void* dst, int64_t n16, hipStream_t stream);
+// Streaming measurement kernels (adaln_stream.hip): copy src to dst, read src (the
+// XOR fold of each wave's data lands in dst, stream_sink_bytes(n16, per) bytes),
+// or fill dst; per: 16-byte vectors per thread (1, 2, 4, 8 or 16).
+enum StreamKind : int { STREAM_COPY = 0, STREAM_READ = 1, STREAM_FILL = 2 };
+hipError_t launch_stream(int kind, const void* src, void* dst, int64_t n16, int per,
+                         hipStream_t stream);
+int64_t stream_sink_bytes(int64_t n16, int per);
 hipError_t launch_diag_quant(const float* in, uint8_t* out, int64_t n, const float* qscale,
                              hipStream_t stream);
 

@@ -681,33 +681,6 @@ __global__ __launch_bounds__(256) void diag_finalize(const float* in, float* out
         out[i] = row_rstd<false>(in[i], H, rH, eps);
 }
 
-// A plain streaming copy with the fused kernel's memory access style (16-byte
-// non-temporal loads and stores): the attainable read+write rate of the device,
-// the ceiling the fused kernel is compared with.  Each thread moves kCopyPer
-// 16-byte vectors, all loads issued before the first store.
-constexpr int kCopyPer = 8;
-__global__ __launch_bounds__(256) void diag_copy(const u32x4* __restrict__ src,
-                                                 u32x4* __restrict__ dst, int64_t n16) {
-    const int64_t base = (int64_t)blockIdx.x * 256 * kCopyPer + threadIdx.x;
-    uint4 v[kCopyPer];
-#pragma unroll
-    for (int k = 0; k < kCopyPer; ++k) {
-        const int64_t i = base + (int64_t)k * 256;
-        if (i < n16) {
-            const u32x4 t = __builtin_nontemporal_load(src + i);
-            v[k] = make_uint4(t.x, t.y, t.z, t.w);
-        }
-    }
-#pragma unroll
-    for (int k = 0; k < kCopyPer; ++k) {
-        const int64_t i = base + (int64_t)k * 256;
-        if (i < n16) {
-            const u32x4 t = {v[k].x, v[k].y, v[k].z, v[k].w};
-            __builtin_nontemporal_store(t, dst + i);
-        }
-    }
-}
-
 // The fused LNQ kernel's quantisation step on binary32 inputs: out = E4M3 of
 // clamp(in * RN(1/qscale)), four values per thread.
 __global__ __launch_bounds__(256) void diag_quant(const float4* __restrict__ in,
@@ -939,10 +912,20 @@ hipError_t launch(Op op, const Params& p_in, hipStream_t stream) {
     int64_t resident_shallow = 0, resident_two = 0;
     KernelFn shallow = pick_op(1), two = pick_op(2);  // null where not instantiated
     int bpc1 = 0, bpc2 = 0;
-    if (shallow && occupancy(reinterpret_cast<const void*>(shallow), block, &bpc1, &cus))
-        resident_shallow = (int64_t)cus * bpc1 * groups_per_block;
-    if (two && occupancy(reinterpret_cast<const void*>(two), block, &bpc2, &cus))
-        resident_two = (int64_t)cus * bpc2 * groups_per_block;
+    // an optional kernel whose query fails is not used; its error is cleared so that
+    // the launch below reports only its own
+    if (shallow) {
+        if (occupancy(reinterpret_cast<const void*>(shallow), block, &bpc1, &cus))
+            resident_shallow = (int64_t)cus * bpc1 * groups_per_block;
+        else
+            (void)hipGetLastError();
+    }
+    if (two) {
+        if (occupancy(reinterpret_cast<const void*>(two), block, &bpc2, &cus))
+            resident_two = (int64_t)cus * bpc2 * groups_per_block;
+        else
+            (void)hipGetLastError();
+    }
     const Plan pl = plan_launch(op, p_in.rows, p_in.H, p_in.T, resident, resident_shallow,
                                 resident_two, cus);
     Params p = p_in;
@@ -980,15 +963,6 @@ hipError_t launch_diag_quant(const float* in, uint8_t* out, int64_t n, const flo
     hipLaunchKernelGGL(diag_quant, dim3((unsigned)blocks), dim3(256), 0, stream,
                        reinterpret_cast<const float4*>(in), reinterpret_cast<u32*>(out), n4,
                        qscale);
-    return hipGetLastError();
-}
-
-hipError_t launch_diag_copy(const void* src, void* dst, int64_t n16, hipStream_t stream) {
-    const int64_t per_block = 256 * kCopyPer;
-    const int64_t blocks = (n16 + per_block - 1) / per_block;
-    if (blocks > 0x7FFFFFFF) return hipErrorInvalidValue;
-    hipLaunchKernelGGL(diag_copy, dim3((unsigned)blocks), dim3(256), 0, stream,
-                       static_cast<const u32x4*>(src), static_cast<u32x4*>(dst), n16);
     return hipGetLastError();
 }
 

@@ -208,8 +208,10 @@ hipError_t launch_qk(const QKParams& p_in, hipStream_t stream) {
     p.tasks_per_token = p.q_tasks + (p.heads_k + 7) / 8;
     const int64_t tasks = p.tokens * p.tasks_per_token;
     int blocks_per_cu = 0, cus = 0;
-    if (!occupancy(reinterpret_cast<const void*>(qk_rmsnorm_rope), 256, &blocks_per_cu, &cus))
+    if (!occupancy(reinterpret_cast<const void*>(qk_rmsnorm_rope), 256, &blocks_per_cu, &cus)) {
+        (void)hipGetLastError();  // the query's error is reported as this status only
         return hipErrorInvalidDeviceFunction;
+    }
     // as many waves as fit at once (at most one per task), a multiple of the tasks
     // per token; at least one wave per task of a token
     const int64_t slots = (int64_t)blocks_per_cu * cus * 4;

@@ -258,6 +258,16 @@ def rg_channel_first_2x3072x4608(seed: int = 0) -> CFWorkload:
                       normal_bf16(_rng(seed, 8, "gate"), (B, H), 0.1))
 
 
+def cf_tokens(T: int, seed: int = 0) -> CFWorkload:
+    """Channel-first residual gating at hidden 3072, CFG batch 2, with T tokens (the
+    token-count sweep: T % 8 decides whether the residual rows are 16-byte aligned)."""
+    B, H = 2, 3072
+    return CFWorkload(f"rg_channel_first_2x3072x{T}",
+                      normal_bf16(_rng(seed, 38, "res"), (B, H, T)),
+                      normal_bf16(_rng(seed, 38, "x"), (B, T, H)),
+                      normal_bf16(_rng(seed, 38, "gate"), (B, H), 0.1))
+
+
 def flux_chunk_views(seed: int, B: int, H: int, chunks: int, stream: int = 30):
     """scale/shift as strided views of one [B, chunks*H] embedding, like
     ``emb.chunk(chunks, dim=1)`` in the FLUX.1 test snippet: (emb, shift, scale)
@@ -342,6 +352,27 @@ def ragged_sets_device(seed: int = 0, n_sets: int = 256, max_tokens: int = 4096,
         return torch.from_numpy(np.ascontiguousarray(a).view(np.int16)).view(torch.bfloat16).to(device)
 
     return StressSetsDevice(x, offsets, cls, to_dev(v["scale"]), to_dev(v["shift"]), to_dev(w))
+
+
+def ragged_residual_device(st: StressSetsDevice, seed: int = 0, stream: int = 4,
+                           device: str = "cuda"):
+    """The residual stream and per-set gates for the gated ops on the stress sets:
+    res [R, H] bfloat16 N(0,1) drawn on the device with its own seeded generator,
+    gate [S, H] bfloat16 0.1*N(0,1)."""
+    R, H = st.x.shape
+    S = len(st.offsets) - 1
+    gen = torch.Generator(device=device)
+    gen.manual_seed(int(np.random.SeedSequence([seed, stream, TENSOR_IDS["res"]])
+                        .generate_state(1)[0]))
+    res = torch.empty((R, H), dtype=torch.bfloat16, device=device)
+    step = 1 << 16
+    for lo in range(0, R, step):
+        hi = min(R, lo + step)
+        res[lo:hi] = torch.randn((hi - lo, H), generator=gen, device=device,
+                                 dtype=torch.float32).to(torch.bfloat16)
+    g = _vecs(seed, stream, S, H, ["gate"])["gate"]
+    gate = torch.from_numpy(np.ascontiguousarray(g).view(np.int16)).view(torch.bfloat16).to(device)
+    return res, gate
 
 
 # the benchmark and parity workloads by name (bench.py --workload NAME)

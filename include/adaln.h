@@ -90,14 +90,15 @@
 extern "C" {
 #endif
 
-#define ADALN_ABI_VERSION 8 /* 2: two waves per row for 2048 <= H < 4096;
+#define ADALN_ABI_VERSION 9 /* 2: two waves per row for 2048 <= H < 4096;
                               3: residual-gate LayerNorm, stream copy;
                               4: LayerNorm + modulate + FP8 quantisation;
                               5: per-head QK RMSNorm + RoPE;
                               6: channel-first residual gating;
                               7: launch-plan diagnostic;
                               8: the plan takes T and gives row blocks; the finalize
-                                 diagnostic takes H */
+                                 diagnostic takes H;
+                              9: streaming read / fill / copy measurement kernels */
 
 typedef uint16_t adaln_bf16; /* raw bfloat16 bits */
 
@@ -188,8 +189,9 @@ adaln_status adaln_qk_rmsnorm_rope(const adaln_bf16* q, const adaln_bf16* k,
  *   out[b][h][t] = bf16(res[b][h][t] + bf16(gate[b][h] * update[b][t][h]))
  * res, out: contiguous [B, H, T]; update: contiguous [B, T, H]; gate row b at
  * gate + b*gate_bstride (0 shares one vector; else >= H and % 8 == 0).  Any T >= 0;
- * H % 8 == 0 and B*ceil(H/64)*ceil(T/64) <= 2^24 - 1 (one workgroup per 64x64 tile;
- * ADALN_ERR_SHAPE otherwise); pointers 16-byte aligned.  out may be
+ * H % 8 == 0; one workgroup of 256 per tile of 64 hidden rows and 64 tokens (with
+ * T % 8 != 0 the tiles cover T + 7 tokens), at most 2^24 - 8 tiles
+ * (ADALN_ERR_SHAPE otherwise); pointers 16-byte aligned.  out may be
  * res itself (in-place update); any other overlap is ADALN_ERR_OVERLAP. */
 adaln_status adaln_residual_gate_channel_first(const adaln_bf16* res, const adaln_bf16* update,
                                                const adaln_bf16* gate, adaln_bf16* out, int64_t B,
@@ -291,8 +293,23 @@ adaln_status adaln_diag_launch_plan(int op, int64_t rows, int64_t H, int64_t T, 
  * fused kernels' access style (16-byte non-temporal loads and stores), so that the
  * attainable streaming rate of the device can be timed beside the fused kernels.
  * bytes >= 0 and % 16 == 0 (else ADALN_ERR_SHAPE); both pointers 16-byte aligned
- * (ADALN_ERR_ALIGN); the ranges may not overlap (ADALN_ERR_OVERLAP). */
+ * (ADALN_ERR_ALIGN); the ranges may not overlap (ADALN_ERR_OVERLAP).  The same as
+ * adaln_diag_stream(0, src, dst, bytes, 8, hip_stream). */
 adaln_status adaln_diag_stream_copy(const void* src, void* dst, int64_t bytes, void* hip_stream);
+
+/* Measurement aid: the streaming kernels behind the measured ceilings, with
+ * vectors_per_thread (1, 2, 4, 8 or 16; else ADALN_ERR_VALUE) 16-byte vectors in
+ * flight per thread, one-shot grids of 256 threads.
+ *  kind 0 (copy): dst[0, bytes) = src[0, bytes);
+ *  kind 1 (read): reads src[0, bytes) and writes 4 bytes per 1024*vectors_per_thread
+ *                 bytes read (a fold of the data, so that no load is dropped) to the
+ *                 start of dst, which must hold `bytes` bytes;
+ *  kind 2 (fill): writes a fixed pattern to dst[0, bytes); src is unused.
+ * bytes >= 0 and % 16 == 0 (ADALN_ERR_SHAPE); pointers used are non-NULL and
+ * 16-byte aligned; the bytes written may not overlap src (ADALN_ERR_OVERLAP);
+ * kind outside 0..2 is ADALN_ERR_VALUE.  Device memory of the current device. */
+adaln_status adaln_diag_stream(int kind, const void* src, void* dst, int64_t bytes,
+                               int vectors_per_thread, void* hip_stream);
 
 #ifdef __cplusplus
 }

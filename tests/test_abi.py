@@ -31,14 +31,14 @@ def declared_symbols():
 
 def test_header_symbols_are_exported(lib):
     names = declared_symbols()
-    assert len(names) == 22, names
+    assert len(names) == 23, names
     assert set(names) == set(_binding.EXPORTS)
     for n in names:
         assert hasattr(lib, n), n
 
 
 def test_abi_version_and_status_strings(lib):
-    assert A.adaln_abi_version() == A.ABI_VERSION == 8
+    assert A.adaln_abi_version() == A.ABI_VERSION == 9
     for s in range(8):
         assert len(A.adaln_status_string(s)) > 5
     assert A.adaln_status_string(99) == "unknown status"
@@ -175,9 +175,14 @@ def test_channel_first_checks(lib):
     assert cf_check(lib, out=addr(1)) == OVERLAP         # over update
     assert cf_check(lib, T=4333) == OK                   # ragged token count
     assert cf_check(lib, H=12) == SHAPE
-    # one 64x64 tile per workgroup of 256: at most 2^24 - 1 tiles in a grid
-    assert cf_check(lib, B=(1 << 24) - 1, T=8, H=8, gbs=0) == OK
-    assert cf_check(lib, B=1 << 24, T=8, H=8, gbs=0) == SHAPE
+    # one tile per workgroup of 256, the grid rounded up to a multiple of eight
+    # workgroups, fewer than 2^32 work-items: at most 2^24 - 8 tiles
+    assert cf_check(lib, B=(1 << 24) - 8, T=8, H=8, gbs=0) == OK
+    assert cf_check(lib, B=(1 << 24) - 7, T=8, H=8, gbs=0) == SHAPE
+    # a ragged T: the tiles cover T + 7 tokens (48 * 68 tiles per batch entry here)
+    far_r = dict(res=addr(0), upd=addr(10), out=addr(20), gate=addr(30), gbs=0, T=4333)
+    assert cf_check(lib, B=5140, **far_r) == OK
+    assert cf_check(lib, B=5141, **far_r) == SHAPE
     far = dict(res=addr(0), upd=addr(10), out=addr(20), gate=addr(30), gbs=0)  # 137 GB each
     assert cf_check(lib, B=4854, **far) == OK            # 4854 * 48 * 72 tiles
     assert cf_check(lib, B=4855, **far) == SHAPE
@@ -299,6 +304,24 @@ def test_compute_entry_points_reject_before_launch(lib):
     assert lib.adaln_diag_stream_copy(None, addr(1), 32, None) == NULL
     assert lib.adaln_diag_stream_copy(addr(0), addr(0) + 16, 32, None) == OVERLAP
     assert lib.adaln_diag_stream_copy(None, None, 0, None) == OK
+    for kind in (0, 1, 2):
+        assert lib.adaln_diag_stream(kind, addr(0), addr(1), 24, 8, None) == SHAPE
+        assert lib.adaln_diag_stream(kind, addr(0), addr(1), 32, 3, None) == VALUE
+        assert lib.adaln_diag_stream(kind, addr(0), addr(1) + 8, 32, 8, None) == ALIGN
+        assert lib.adaln_diag_stream(kind, addr(0), None, 32, 8, None) == NULL
+        assert lib.adaln_diag_stream(kind, None, None, 0, 8, None) == OK
+    assert lib.adaln_diag_stream(3, addr(0), addr(1), 32, 8, None) == VALUE
+    assert lib.adaln_diag_stream(-1, addr(0), addr(1), 32, 8, None) == VALUE
+    assert lib.adaln_diag_stream(0, None, addr(1), 32, 8, None) == NULL
+    assert lib.adaln_diag_stream(1, None, addr(1), 32, 8, None) == NULL
+    assert lib.adaln_diag_stream(1, addr(0) + 8, addr(1), 32, 8, None) == ALIGN
+    # fill reads nothing: an unaligned src is not checked (the dst check still is)
+    assert lib.adaln_diag_stream(2, addr(0) + 8, addr(1) + 8, 32, 8, None) == ALIGN
+    assert lib.adaln_diag_stream(0, addr(0), addr(0) + 16, 64, 8, None) == OVERLAP
+    # read writes only its folds (16 bytes per 4096*per bytes read) at the start of
+    # dst: a dst starting inside src overlaps, one starting past the folds' reach of
+    # src's end does not matter here (it would launch)
+    assert lib.adaln_diag_stream(1, addr(0), addr(0) + 16, 4096 * 8, 8, None) == OVERLAP
     assert lib.adaln_diag_finalize(addr(0), addr(1), 4, 1, -1.0, None) == VALUE
     for H in (0, -1, 8193):
         assert lib.adaln_diag_finalize(addr(0), addr(1), 4, H, 1e-6, None) == SHAPE

@@ -40,11 +40,29 @@ def test_workload_sizes(name, op, rows, nbytes):
     assert sha and all(len(v) == 16 for v in sha.values())
 
 
-def test_headline_config_is_the_rms_workload():
+def test_headline_config_is_the_largest_target_config():
+    # the metric names no configuration: the timed line is the largest configuration
+    # with the bandwidth target, the FLUX.1 LayerNorm site [2,4608,3072]
     assert bench.HEADLINE in bench.WORKLOAD_NAMES
     wl = bench.workload(bench.HEADLINE)
-    assert wl.x.shape == (1, 4216, 4096) and wl.weight is not None
-    assert wl.algorithmic_bytes() == 69074944
+    assert wl.x.shape == (2, 4608, 3072) and wl.op == "ln"
+    assert wl.algorithmic_bytes() == 113246208
+    sizes = {n: bench.workload(n).algorithmic_bytes() for n in bench.TARGET_CONFIGS}
+    assert max(sizes, key=sizes.get) == bench.HEADLINE
+    assert set(bench.TARGET_CONFIGS) == {"rms_1x4216x4096", "rg_rms_2x1140x4096",
+                                         "ln_2x4608x3072", "ln_1x4333x3072"}
+
+
+def test_profile_tables_used_only_for_the_same_kernel_source(tmp_path, monkeypatch):
+    (tmp_path / "profiles").mkdir()
+    monkeypatch.setattr(bench, "ROOT", str(tmp_path))
+    assert bench.load_profile_table("t.txt", 0, 3) == {}
+    f = tmp_path / "profiles" / "t.txt"
+    f.write_text(f"# a comment\n# kernel_src_sha = {bench.kernel_src_sha()}\n"
+                 "w1 | k | 10 | 15009.8 | x\nw2 | k | 10 | notanumber\n")
+    assert bench.load_profile_table("t.txt", 0, 3) == {"w1": 15009.8}
+    f.write_text("# kernel_src_sha = 0000000000000000\nw1 | k | 10 | 15009.8\n")
+    assert bench.load_profile_table("t.txt", 0, 3) == {}
 
 
 def test_inputs_are_seeded():

@@ -1,0 +1,152 @@
+"""Every output element is written exactly where it belongs and nowhere else.
+
+Each entry point writes into views of larger device buffers whose margins before
+and after the view hold random sentinel bits; after the call the margins must be
+unchanged and the view must equal the CPU oracle bit for bit.  The shapes cover
+ragged hidden sizes (partial last chunk), ragged row counts per group, the FP8
+8-byte stores, QK heads that do not fill a task of eight, and the channel-first
+kernel's narrow phase-2 accesses at ragged token counts, in place and out of place
+(kernels guide, "entry-point protocol": a kernel never degrades silently; an
+output written past its end would corrupt a neighbouring tensor).
+"""
+import zlib
+
+import numpy as np
+import pytest
+import torch
+
+import diffusion_dit_adaln_amd as A
+from diffusion_dit_adaln_amd import synth
+from oracle import oracle as O
+from tests.helpers import assert_bits_equal, dev, host, say
+
+pytestmark = pytest.mark.gpu
+EPS = 1e-6
+MARGIN = 8208  # elements (bf16) or bytes (uint8) on each side; a multiple of 16
+
+
+class Guarded:
+    """A device buffer of n + 2*MARGIN elements with random sentinel margins and the
+    middle n elements exposed as `view` (16-byte aligned)."""
+
+    def __init__(self, shape, dtype, rng):
+        n = int(np.prod(shape))
+        self.n = n
+        if dtype == torch.uint8:
+            bits = rng.integers(0, 256, size=n + 2 * MARGIN, dtype=np.uint8)
+            self.buf = torch.from_numpy(bits).cuda()
+        else:
+            bits = rng.integers(0, 1 << 16, size=n + 2 * MARGIN, dtype=np.uint16)
+            self.buf = torch.from_numpy(bits.view(np.int16)).view(torch.bfloat16).cuda()
+        self.before = self.buf[:MARGIN].clone()
+        self.after = self.buf[MARGIN + n:].clone()
+        self.view = self.buf[MARGIN:MARGIN + n].view(shape)
+        assert self.view.data_ptr() % 16 == 0
+
+    def check_margins(self, what):
+        torch.cuda.synchronize()
+        b = self.buf[:MARGIN].view(torch.uint8) if self.buf.dtype == torch.uint8 else \
+            self.buf[:MARGIN].view(torch.int16)
+        a = self.buf[MARGIN + self.n:]
+        a = a.view(torch.uint8) if a.dtype == torch.uint8 else a.view(torch.int16)
+        wb = self.before.view(torch.uint8) if self.before.dtype == torch.uint8 else \
+            self.before.view(torch.int16)
+        wa = self.after.view(torch.uint8) if self.after.dtype == torch.uint8 else \
+            self.after.view(torch.int16)
+        nb = int((b != wb).sum())
+        na = int((a != wa).sum())
+        assert nb == 0 and na == 0, f"{what}: {nb} elements before and {na} after the output " \
+                                    f"were written"
+
+
+FUSED_SHAPES = [(1, 1, 3072), (2, 37, 3072), (1, 300, 4096), (3, 11, 4104), (2, 9, 520),
+                (1, 5, 8192), (1, 129, 2048), (2, 3, 8)]
+
+
+@pytest.mark.parametrize("shape", FUSED_SHAPES)
+@pytest.mark.parametrize("op", ["ln", "rms", "rg", "rgln", "lnq"])
+def test_fused_outputs_stay_in_bounds(op, shape):
+    B, T, H = shape
+    say(f"[guard] {op} {shape}")
+    rng = np.random.default_rng(zlib.crc32(f"{op}{shape}".encode()))
+    x = synth.normal_bf16(rng, shape)
+    res = synth.normal_bf16(rng, shape)
+    g = synth.normal_bf16(rng, (B, H), 0.1)
+    sc = synth.normal_bf16(rng, (B, H), 0.1)
+    sh = synth.normal_bf16(rng, (B, H), 0.1)
+    w = synth.normal_bf16(rng, (H,), 0.02, 1.0)
+    if op == "lnq":
+        q = Guarded(shape, torch.uint8, rng)
+        qs = torch.tensor([0.0125], dtype=torch.float32, device="cuda")
+        A.adaln_layernorm_modulate_fp8_quant(dev(x), dev(sc), dev(sh), qs, EPS, out=q.view)
+        q.check_margins(f"{op} {shape} q")
+        want = O.layernorm_modulate_fp8(x, sc, sh, 0.0125, EPS)
+        assert np.array_equal(q.view.cpu().numpy(), want), f"{op} {shape}: codes differ"
+        return
+    y = Guarded(shape, torch.bfloat16, rng)
+    if op == "ln":
+        A.adaln_layernorm_modulate(dev(x), dev(sc), dev(sh), EPS, out=y.view)
+        want = [O.layernorm_modulate(x, sc, sh, EPS)]
+        got = [y]
+    elif op == "rms":
+        A.adaln_rmsnorm_scale_shift(dev(x), dev(w), dev(sc), dev(sh), EPS, out=y.view)
+        want = [O.rmsnorm_scale_shift(x, w, sc, sh, EPS)]
+        got = [y]
+    else:
+        r = Guarded(shape, torch.bfloat16, rng)
+        if op == "rg":
+            A.adaln_residual_gate_rmsnorm_scale_shift(dev(res), dev(x), dev(g), dev(w), dev(sc),
+                                                      dev(sh), EPS, out=y.view, r_out=r.view)
+            want = list(O.residual_gate_rmsnorm_scale_shift(res, x, g, w, sc, sh, EPS))
+        else:
+            A.adaln_residual_gate_layernorm_modulate(dev(res), dev(x), dev(g), dev(sc), dev(sh),
+                                                     EPS, out=y.view, r_out=r.view)
+            want = list(O.residual_gate_layernorm_modulate(res, x, g, sc, sh, EPS))
+        got = [r, y]
+    for gd, wt, nm in zip(got, want, ["r", "y"] if len(got) == 2 else ["y"]):
+        gd.check_margins(f"{op} {shape} {nm}")
+        assert_bits_equal(host(gd.view), wt, f"{op} {shape} {nm}")
+
+
+@pytest.mark.parametrize("tokens,heads_q,heads_k", [(1, 1, 1), (7, 5, 3), (33, 24, 24),
+                                                     (5, 13, 0), (4, 0, 9)])
+def test_qk_outputs_stay_in_bounds(tokens, heads_q, heads_k):
+    say(f"[guard] qk tokens={tokens} heads=({heads_q},{heads_k})")
+    rng = np.random.default_rng(tokens * 100 + heads_q * 10 + heads_k)
+    q = synth.normal_bf16(rng, (tokens, heads_q, 128))
+    k = synth.normal_bf16(rng, (tokens, heads_k, 128))
+    wq = synth.normal_bf16(rng, (128,), 0.02, 1.0)
+    wk = synth.normal_bf16(rng, (128,), 0.02, 1.0)
+    cs = synth.rope_cache(tokens, 128)
+    qo = Guarded((tokens, heads_q, 128), torch.bfloat16, rng)
+    ko = Guarded((tokens, heads_k, 128), torch.bfloat16, rng)
+    A.adaln_qk_rmsnorm_rope(dev(q), dev(k), dev(wq), dev(wk), torch.from_numpy(cs).cuda(), EPS,
+                            q_out=qo.view, k_out=ko.view)
+    qo.check_margins("qk q_out")
+    ko.check_margins("qk k_out")
+    q_ref, k_ref = O.qk_rmsnorm_rope(q, k, wq, wk, cs, EPS)
+    if heads_q:
+        assert_bits_equal(host(qo.view), q_ref, "qk q_out")
+    if heads_k:
+        assert_bits_equal(host(ko.view), k_ref, "qk k_out")
+
+
+@pytest.mark.parametrize("B,H,T", [(1, 64, 64), (2, 136, 40), (1, 72, 4333), (2, 64, 4334),
+                                   (1, 128, 4332), (2, 200, 1), (1, 8, 77), (3, 24, 129)])
+@pytest.mark.parametrize("in_place", [False, True])
+def test_channel_first_outputs_stay_in_bounds(B, H, T, in_place):
+    say(f"[guard] channel-first B={B} H={H} T={T} in_place={in_place}")
+    rng = np.random.default_rng(B * 1000 + H + T)
+    res = synth.normal_bf16(rng, (B, H, T))
+    upd = synth.normal_bf16(rng, (B, T, H))
+    g = synth.normal_bf16(rng, (B, H), 0.1)
+    want = O.residual_gate_channel_first(res, upd, g)
+    out = Guarded((B, H, T), torch.bfloat16, rng)
+    if in_place:
+        out.view.copy_(dev(res))
+        torch.cuda.synchronize()
+        A.adaln_residual_gate_channel_first(out.view, dev(upd), dev(g), out=out.view)
+    else:
+        A.adaln_residual_gate_channel_first(dev(res), dev(upd), dev(g), out=out.view)
+    out.check_margins(f"channel-first {B}x{H}x{T}")
+    assert_bits_equal(host(out.view), want, f"channel-first {B}x{H}x{T}")

@@ -33,64 +33,92 @@ def stress():
     return st
 
 
-# ln, rms; rgln: the residual-gate LayerNorm with res = x and gate = scale (the y
-# output); lnq: LayerNorm + FP8 quantisation (E4M3 codes)
-@pytest.mark.parametrize("op", ["ln", "rms", "rgln", "lnq"])
-def test_packed_sets_alone_and_single_rows(stress, op):
+@pytest.fixture(scope="module")
+def gated(stress):
+    say("[invariance] drawing the residual stream and gates on the device")
+    res, gate = synth.ragged_residual_device(stress, seed=0)
+    torch.cuda.synchronize()
+    return res, gate
+
+
+# ln, rms; rg: the residual-gate RMSNorm with its own residual stream and per-set
+# gates, checking both outputs (r and y); rgln: the residual-gate LayerNorm with
+# res = x and gate = scale (the y output); lnq: LayerNorm + FP8 quantisation (codes)
+@pytest.mark.parametrize("op", ["ln", "rms", "rg", "rgln", "lnq"])
+def test_packed_sets_alone_and_single_rows(stress, gated, op):
     st = stress
     R, H = st.x.shape
     S = len(st.offsets) - 1
-    w = st.weight if op == "rms" else None
+    w = st.weight if op in ("rms", "rg") else None
     qs = torch.tensor([QSCALE], dtype=torch.float32, device="cuda")
+    res_all, gate_all = gated
 
-    def run(x3, sc, sh):
+    def run(rows, sc, sh, g):
+        """Outputs (a tuple) for the rows `rows` (a slice or index tensor of the packed
+        rows) shaped [B, T, H] by `view`, with vectors sc, sh, g ([B,H] or [H])."""
+        x3, r3 = rows
         if op == "ln":
-            return A.adaln_layernorm_modulate(x3, sc, sh, EPS)
+            return (A.adaln_layernorm_modulate(x3, sc, sh, EPS),)
         if op == "rgln":
-            return A.adaln_residual_gate_layernorm_modulate(x3, x3, sc, sc, sh, EPS)[1]
+            return (A.adaln_residual_gate_layernorm_modulate(x3, x3, sc, sc, sh, EPS)[1],)
         if op == "lnq":
-            return A.adaln_layernorm_modulate_fp8_quant(x3, sc, sh, qs, EPS)
-        return A.adaln_rmsnorm_scale_shift(x3, w, sc, sh, EPS)
+            return (A.adaln_layernorm_modulate_fp8_quant(x3, sc, sh, qs, EPS),)
+        if op == "rg":
+            return A.adaln_residual_gate_rmsnorm_scale_shift(r3, x3, g, w, sc, sh, EPS)
+        return (A.adaln_rmsnorm_scale_shift(x3, w, sc, sh, EPS),)
+
+    def rows_view(lo, hi, shape):
+        return st.x[lo:hi].view(shape), res_all[lo:hi].view(shape)
+
+    def same_all(a, b):
+        return all(_same(u, v) for u, v in zip(a, b))
 
     # (i) every row packed into one [1, R, H] batch with one shared vector
     say(f"[invariance] {op}: packed batch of {R} rows")
-    y_packed = run(st.x.view(1, R, H), st.scale[0], st.shift[0])
-    # (ii) [R, 1, H]: each row carries its own set's vector (B = R, T = 1)
+    y_packed = run(rows_view(0, R, (1, R, H)), st.scale[0], st.shift[0], gate_all[0])
+    # (ii) [R, 1, H]: each row carries its own set's vectors (B = R, T = 1)
     set_of_row = torch.from_numpy(np.repeat(np.arange(S), np.diff(st.offsets))).cuda()
-    y_rows = run(st.x.view(R, 1, H), st.scale.index_select(0, set_of_row).contiguous(),
-                 st.shift.index_select(0, set_of_row).contiguous())
+    y_rows = run(rows_view(0, R, (R, 1, H)), st.scale.index_select(0, set_of_row).contiguous(),
+                 st.shift.index_select(0, set_of_row).contiguous(),
+                 gate_all.index_select(0, set_of_row).contiguous())
     torch.cuda.synchronize()
     say(f"[invariance] {op}: {S} sets alone")
     for s in range(S):
         lo, hi = int(st.offsets[s]), int(st.offsets[s + 1])
-        xs = st.x[lo:hi].view(1, hi - lo, H)
-        assert _same(run(xs, st.scale[0], st.shift[0])[0], y_packed[0, lo:hi]), f"set {s} (i)"
-        assert _same(run(xs, st.scale[s], st.shift[s])[0], y_rows[lo:hi, 0]), f"set {s} (ii)"
+        a = run(rows_view(lo, hi, (1, hi - lo, H)), st.scale[0], st.shift[0], gate_all[0])
+        assert same_all([t[0] for t in a], [t[0, lo:hi] for t in y_packed]), f"set {s} (i)"
+        a = run(rows_view(lo, hi, (1, hi - lo, H)), st.scale[s], st.shift[s], gate_all[s])
+        assert same_all([t[0] for t in a], [t[lo:hi, 0] for t in y_rows]), f"set {s} (ii)"
     # (iii) single rows alone
     rng = np.random.default_rng(3)
     rows = rng.choice(R, size=256, replace=False)
     say(f"[invariance] {op}: 256 single rows")
     for r in rows:
         s = int(np.searchsorted(st.offsets, r, side="right") - 1)
-        y1 = run(st.x[r:r + 1].view(1, 1, H), st.scale[s], st.shift[s])
-        assert _same(y1[0, 0], y_rows[r, 0]), f"row {r}"
+        a = run(rows_view(r, r + 1, (1, 1, H)), st.scale[s], st.shift[s], gate_all[s])
+        assert same_all([t[0, 0] for t in a], [t[r, 0] for t in y_rows]), f"row {r}"
     # sampled rows against the oracle, every class represented
     sample = np.sort(rng.choice(R, size=3000, replace=False))
     say(f"[invariance] {op}: 3000 sampled rows vs oracle")
-    xh = host(st.x[torch.from_numpy(sample).cuda()])[None]
+    idx = torch.from_numpy(sample).cuda()
+    xr = host(st.x[idx]).reshape(len(sample), 1, H)
     sets = np.searchsorted(st.offsets, sample, side="right") - 1
     sch = host(st.scale)[sets]
     shh = host(st.shift)[sets]
-    xr = xh.reshape(len(sample), 1, H)
     if op == "ln":
-        want = O.layernorm_modulate(xr, sch, shh, EPS)
+        want = [O.layernorm_modulate(xr, sch, shh, EPS)]
     elif op == "rgln":
-        want = O.residual_gate_layernorm_modulate(xr, xr, sch, sch, shh, EPS)[1]
+        want = [O.residual_gate_layernorm_modulate(xr, xr, sch, sch, shh, EPS)[1]]
     elif op == "lnq":
-        want = O.layernorm_modulate_fp8(xr, sch, shh, QSCALE, EPS)
+        want = [O.layernorm_modulate_fp8(xr, sch, shh, QSCALE, EPS)]
+    elif op == "rg":
+        rr = host(res_all[idx]).reshape(len(sample), 1, H)
+        want = list(O.residual_gate_rmsnorm_scale_shift(rr, xr, host(gate_all)[sets],
+                                                        host(st.weight), sch, shh, EPS))
     else:
-        want = O.rmsnorm_scale_shift(xr, host(st.weight), sch, shh, EPS)
-    picked = y_rows[torch.from_numpy(sample).cuda()]
-    got = picked.cpu().numpy() if op == "lnq" else host(picked)
-    assert_bits_equal(got.reshape(want.shape), want, f"{op} sampled rows")
+        want = [O.rmsnorm_scale_shift(xr, host(st.weight), sch, shh, EPS)]
+    for k, (t, wt) in enumerate(zip(y_rows, want)):
+        picked = t[idx]
+        got = picked.cpu().numpy() if op == "lnq" else host(picked)
+        assert_bits_equal(got.reshape(wt.shape), wt, f"{op} sampled rows, output {k}")
     assert set(np.unique(st.row_class[sample])) == {0, 1, 2}

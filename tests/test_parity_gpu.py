@@ -53,11 +53,11 @@ def run_lnq(x, sc, sh, qscale, eps=EPS):
 
 
 def assert_fp8_equal(got, want, what):
-    """E4M3 codes equal, NaN (S.1111.111) in the same places (any NaN code)."""
+    """E4M3 codes equal bit for bit, NaN codes (0xFF) included."""
     gn = (got & 0x7F) == 0x7F
     wn = (want & 0x7F) == 0x7F
     assert np.array_equal(gn, wn), what + ": NaN positions differ"
-    bad = np.flatnonzero(got[~gn] != want[~wn])
+    bad = np.flatnonzero(got != want)
     assert bad.size == 0, f"{what}: {bad.size} codes differ, first at {bad[:5]}"
 
 
@@ -323,7 +323,7 @@ def test_nonfinite_inputs_give_nan_in_the_same_places():
         gn = np.isnan(synth.bf16_bits_to_f32(got))
         wn = np.isnan(synth.bf16_bits_to_f32(want))
         assert np.array_equal(gn, wn)
-        assert_bits_equal(got[~gn], want[~wn], "finite outputs")
+        assert_bits_equal(got, want, "outputs, NaN bits (sign included) too")
 
 
 @pytest.mark.parametrize("H", [1024, 3072, 4096, 3080, 520])
@@ -541,7 +541,7 @@ def test_qk_eps_and_special_rows(eps):
         gn = np.isnan(synth.bf16_bits_to_f32(got))
         wn = np.isnan(synth.bf16_bits_to_f32(want))
         assert np.array_equal(gn, wn)
-        assert_bits_equal(got[~gn], want[~wn], f"qk eps={eps}")
+        assert_bits_equal(got, want, f"qk eps={eps} (NaN bits too)")
 
 
 def test_qk_heads_alone_equal_heads_in_batch():
@@ -617,6 +617,7 @@ def test_device_fp8_quant_all_fp32_patterns():
         wn = (want & 0x7F) == 0x7F
         assert torch.equal(gn, wn), f"chunk {k}: NaN positions"
         assert torch.equal(got[~gn], want[~wn]), f"chunk {k}"
+        assert bool((got[gn] == 0xFF).all()), f"chunk {k}: a NaN code other than 0xFF"
         del u, f, got, want, gn, wn
     torch.cuda.synchronize()
 
@@ -655,6 +656,43 @@ def test_stream_copy_is_exact():
     assert lib.adaln_diag_stream_copy(src.data_ptr(), src.data_ptr() + 16, 64, None) == 5
 
 
+@pytest.mark.parametrize("per", [1, 2, 4, 8, 16])
+def test_stream_kernels_do_what_they_say(per):
+    """The measured ceilings come from these kernels: the copy copies, the fill fills,
+    and the read folds every loaded word (its output is the XOR fold of the data of
+    each wave: 64 lanes x per vectors of 16 bytes, a wave covering 1024*per bytes in
+    the order the grid assigns them)."""
+    say(f"[diag] stream kernels per={per}")
+    g = torch.Generator(device="cuda")
+    g.manual_seed(per)
+    for n16 in (1, 255, 4096 * per + 17, 50000):
+        src = torch.randint(-(1 << 31), (1 << 31) - 1, (n16 * 4,), dtype=torch.int32,
+                            device="cuda", generator=g)
+        full = torch.full((n16 * 4 + 64,), 7, dtype=torch.int32, device="cuda")
+        dst = full[: n16 * 4]
+        A.adaln_diag_stream("copy", src, dst, per)
+        assert torch.equal(src, dst) and bool((full[n16 * 4:] == 7).all()), ("copy", n16)
+        full.fill_(7)
+        A.adaln_diag_stream("fill", None, dst, per)
+        assert bool((full[n16 * 4:] == 7).all()), ("fill past the end", n16)
+        pat = torch.tensor([0x3F803F80, 0x3F803F80 ^ 0x9E3779B9], dtype=torch.int64)
+        pat = ((pat + (1 << 31)) % (1 << 32) - (1 << 31)).to(torch.int32).cuda()
+        assert torch.equal(dst.view(-1, 2), pat.expand(n16 * 2, 2)), ("fill", n16)
+        full.fill_(7)
+        A.adaln_diag_stream("read", src, dst, per)
+        # expected folds: thread t of workgroup b reads vectors b*256*per + k*256 + t
+        v = src.view(-1, 4).cpu().numpy().astype(np.uint32)
+        words = np.bitwise_xor.reduce(v, axis=1)
+        blocks = -(-n16 // (256 * per))
+        pad = np.zeros(blocks * 256 * per, np.uint32)
+        pad[:n16] = words
+        per_thread = np.bitwise_xor.reduce(pad.reshape(blocks, per, 256), axis=1)
+        want = np.bitwise_xor.reduce(per_thread.reshape(blocks, 4, 64), axis=2).reshape(-1)
+        got = dst[: blocks * 4].cpu().numpy().astype(np.uint32)
+        assert np.array_equal(got, want), ("read", n16)
+        assert bool((dst[blocks * 4:] == 7).all()), ("read wrote past its folds", n16)
+
+
 # --------------------------------------------------------------------------
 # the device's rounding and finalize steps, exhaustively
 # --------------------------------------------------------------------------
@@ -673,7 +711,12 @@ def test_device_bf16_rounding_all_fp32_patterns():
         assert torch.equal(got[~nan], want[~nan]), f"chunk {k}"
         gw = got[nan].to(torch.int32) & 0xFFFF
         assert bool(((gw & 0x7F80) == 0x7F80).all() and ((gw & 0x7F) != 0).all())
-        del u, f, got, want, nan, gw
+        # a quiet NaN with the input's sign (the oracle writes 0x7FC0 | sign; the
+        # payload of a NaN is not part of the numerics, its sign and quietness are)
+        sign_in = (u[nan] >> 31).to(torch.int32)
+        assert bool(((gw >> 15) == sign_in).all()), f"chunk {k}: NaN sign"
+        assert bool(((gw & 0x0040) != 0).all()), f"chunk {k}: NaN not quiet"
+        del u, f, got, want, nan, gw, sign_in
     torch.cuda.synchronize()
 
 

@@ -35,9 +35,12 @@ sys.path.insert(0, ROOT)
 
 PEAK_HBM_GBPS = 8000.0
 METRIC = "achieved HBM GB/s (% of MI355X peak) and rows/s for fused norm+modulate"
-# the sources of the fused kernel (its template, shared device helpers, parameters)
+# the sources of the kernels whose profiles are committed (the fused template, the
+# QK and channel-first kernels, the streaming kernels, shared helpers, parameters)
 KERNEL_SRCS = [os.path.join(ROOT, "diffusion_dit_adaln_amd", "csrc", f)
-               for f in ("adaln_kernels.hip", "adaln_device.hpp", "adaln_internal.hpp")]
+               for f in ("adaln_kernels.hip", "adaln_qknorm.hip", "adaln_channel_first.hip",
+                         "adaln_stream.hip", "adaln_device.hpp", "adaln_fold.hpp",
+                         "adaln_internal.hpp")]
 
 
 def kernel_src_sha() -> str:
@@ -652,6 +655,27 @@ def sweep_cf(rotate: int, steps: int, warmup: int) -> None:
                                "update [2,T,3072], graph replay", "points": points}), flush=True)
 
 
+def all_workloads(rotate: int, steps: int, warmup: int, mode: str) -> None:
+    """For profiler runs: every workload (and the channel-first sweep's token counts)
+    launched `steps` times after `warmup`, then the library's streaming copy (8
+    vectors per thread) of the same byte count `steps` times; one JSON line per
+    workload, in this order, so that a trace or counter file can be split by it."""
+    import torch
+    from diffusion_dit_adaln_amd import synth
+    names = WORKLOAD_NAMES + [f"cf:{T}" for T in CF_SWEEP_TOKENS if T != 4608]
+    for name in names:
+        wl = synth.cf_tokens(int(name[3:])) if name.startswith("cf:") else workload(name)
+        L = launcher_for(wl, rotate)
+        nb = wl.algorithmic_bytes()
+        t = time_steps(L.call, steps, warmup, mode)
+        del L
+        torch.cuda.empty_cache()
+        c = copy_ceiling(nb, rotate, steps, warmup, mode)
+        print(json.dumps({"workload": wl.name, "op": wl.op, "bytes": nb,
+                          "GBps": round(nb * steps / t / 1e9, 2),
+                          "copy_GBps": round(c, 2)}), flush=True)
+
+
 def main():
     ap = argparse.ArgumentParser(description=__doc__)
     ap.add_argument("--gpus", type=int, default=1)
@@ -680,6 +704,9 @@ def main():
     ap.add_argument("--copy-only", action="store_true",
                     help="only a plain device copy of the workload's byte count (counter "
                          "calibration for profiler runs)")
+    ap.add_argument("--all-workloads", action="store_true",
+                    help="instead of the benchmark line: every workload and a same-bytes "
+                         "copy, --steps launches each (for profiler runs)")
     ap.add_argument("--ceilings", action="store_true",
                     help="instead of the benchmark line: the streaming ceilings (copy, "
                          "read-only, write-only, 1..16 vectors per thread) at each target "
@@ -699,6 +726,9 @@ def main():
     rotate = args.rotate_mb << 20
     if args.sweep_rows:
         sweep_rows(rotate, args.steps, args.warmup, args.sweep_op)
+        return
+    if args.all_workloads:
+        all_workloads(rotate, args.steps, args.warmup, args.timing)
         return
     if args.sweep_cf:
         sweep_cf(rotate, args.steps, args.warmup)

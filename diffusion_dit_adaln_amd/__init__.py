@@ -16,6 +16,7 @@ from ._binding import (  # noqa: F401
     adaln_check_residual_gate_layernorm_modulate,
     adaln_check_residual_gate_rmsnorm_scale_shift,
     adaln_check_rmsnorm_scale_shift,
+    adaln_diag_device_plan,
     adaln_diag_finalize,
     adaln_diag_launch_plan,
     adaln_diag_quant_fp8,

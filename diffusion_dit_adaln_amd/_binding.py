@@ -29,7 +29,7 @@ EXPORTS = ("adaln_layernorm_modulate", "adaln_rmsnorm_scale_shift",
            "adaln_check_layernorm_modulate_fp8_quant", "adaln_reduction_layout",
            "adaln_status_string", "adaln_abi_version", "adaln_diag_round_bf16",
            "adaln_diag_finalize", "adaln_diag_quant_fp8", "adaln_diag_stream_copy",
-           "adaln_diag_stream", "adaln_diag_launch_plan")
+           "adaln_diag_stream", "adaln_diag_launch_plan", "adaln_diag_device_plan")
 
 
 class AdalnError(RuntimeError):
@@ -80,7 +80,9 @@ def load_library():
         "adaln_diag_stream_copy": [P, P, I, P],
         "adaln_diag_stream": [S, P, P, I, S, P],
         "adaln_diag_quant_fp8": [P, P, I, P, P],
-        "adaln_diag_launch_plan": [S, I, I, I, I, I, ctypes.POINTER(I)],
+        "adaln_diag_launch_plan": [S, I, I, I, ctypes.POINTER(I), I, ctypes.POINTER(I)],
+        "adaln_diag_device_plan": [S, I, I, I, S, ctypes.POINTER(I), ctypes.POINTER(I),
+                                   ctypes.POINTER(I)],
     }
     for name, args in sig.items():
         fn = getattr(lib, name)
@@ -389,19 +391,38 @@ def adaln_reduction_layout(H: int):
 
 
 OPS = {"ln": 0, "rms": 1, "rg": 2, "rgln": 3, "lnq": 4}
-PLAN_FIELDS = ("shallow", "slots", "groups", "gpb", "blk_rows", "group_stride", "step", "span",
-               "blocks", "block_threads")
+PLAN_FIELDS = ("shallow", "slots", "ring", "groups", "gpb", "blk_rows", "group_stride", "step",
+               "span", "blocks", "block_threads")
 
 
-def adaln_diag_launch_plan(op: str, rows: int, H: int, T: int, resident: int,
-                           resident_shallow: int = 0) -> dict:
-    """The fused kernel's row-group plan for one launch of B = rows / T batch entries
-    (host only; see the header)."""
+def adaln_diag_launch_plan(op: str, rows: int, H: int, T: int, resident, cus: int = 0) -> dict:
+    """The fused launch's row-group plan for B = rows / T batch entries, given what fits
+    on the device at once (host only; see the header): resident = (groups with the
+    default ring, with the one-slot ring, with the two-row ring); a single number n
+    means (n, 0, 0)."""
     lib = load_library()
+    if isinstance(resident, int):
+        resident = (resident,)
+    res = (ctypes.c_int64 * 3)(*(list(resident) + [0] * (3 - len(resident))))
     out = (ctypes.c_int64 * len(PLAN_FIELDS))()
-    _check(lib.adaln_diag_launch_plan(OPS[op], rows, H, T, resident, resident_shallow, out),
+    _check(lib.adaln_diag_launch_plan(OPS[op], rows, H, T, res, cus, out),
            "adaln_diag_launch_plan")
     return dict(zip(PLAN_FIELDS, list(out)))
+
+
+def adaln_diag_device_plan(op: str, rows: int, H: int, T: int, weight: bool = False) -> dict:
+    """The plan a launch on the current device takes, with the resident counts and CU
+    count it was made from (keys "resident", "cus")."""
+    lib = load_library()
+    out = (ctypes.c_int64 * len(PLAN_FIELDS))()
+    res = (ctypes.c_int64 * 3)()
+    cus = ctypes.c_int64()
+    _check(lib.adaln_diag_device_plan(OPS[op], rows, H, T, int(bool(weight)), out, res,
+                                      ctypes.byref(cus)), "adaln_diag_device_plan")
+    d = dict(zip(PLAN_FIELDS, list(out)))
+    d["resident"] = tuple(res)
+    d["cus"] = cus.value
+    return d
 
 
 def adaln_status_string(status: int) -> str:

@@ -417,31 +417,65 @@ const char* adaln_status_string(adaln_status status) {
 
 int adaln_abi_version(void) { return ADALN_ABI_VERSION; }
 
-adaln_status adaln_diag_launch_plan(int op, int64_t rows, int64_t H, int64_t T, int64_t resident,
-                                    int64_t resident_shallow, int64_t* out) {
+}  // extern "C"
+
+namespace {
+
+// plan arguments shared by the two plan diagnostics
+adaln_status check_plan_args(int op, int64_t rows, int64_t H, int64_t T, const int64_t* out) {
     if (!out) return ADALN_ERR_NULL;
     if (op < adaln::OP_LN || op > adaln::OP_LNQ) return ADALN_ERR_VALUE;
     if (rows < 1 || H < 8 || H > kMaxH || (H % 8) != 0) return ADALN_ERR_SHAPE;
     if (rows > INT64_MAX / (2 * H)) return ADALN_ERR_SHAPE;
     if (T < 1 || T > rows || rows % T != 0) return ADALN_ERR_SHAPE;
+    return ADALN_OK;
+}
+
+void write_plan(const adaln::Plan& pl, int64_t* out) {
+    out[0] = pl.shallow ? 1 : 0;
+    out[1] = pl.slots;
+    out[2] = pl.ring;
+    out[3] = pl.groups;
+    out[4] = pl.gpb;
+    out[5] = pl.blk_rows;
+    out[6] = pl.group_stride;
+    out[7] = pl.step;
+    out[8] = pl.span;
+    out[9] = pl.blocks;
+    out[10] = pl.block_threads;
+}
+
+}  // namespace
+
+extern "C" {
+
+adaln_status adaln_diag_launch_plan(int op, int64_t rows, int64_t H, int64_t T,
+                                    const int64_t* resident, int64_t cus, int64_t* out) {
+    ADALN_TRY(check_plan_args(op, rows, H, T, out));
+    if (!resident) return ADALN_ERR_NULL;
     // resident counts of a real device are far below 2^31; the plan's products of
     // them stay in range only below that
     constexpr int64_t kMaxResident = 0x7FFFFFFF;
-    if (resident < 1 || resident > kMaxResident || resident_shallow < 0 ||
-        resident_shallow > kMaxResident)
-        return ADALN_ERR_VALUE;
-    const adaln::Plan pl =
-        adaln::plan_launch(static_cast<adaln::Op>(op), rows, H, T, resident, resident_shallow);
-    out[0] = pl.shallow ? 1 : 0;
-    out[1] = pl.slots;
-    out[2] = pl.groups;
-    out[3] = pl.gpb;
-    out[4] = pl.blk_rows;
-    out[5] = pl.group_stride;
-    out[6] = pl.step;
-    out[7] = pl.span;
-    out[8] = pl.blocks;
-    out[9] = pl.block_threads;
+    if (resident[0] < 1) return ADALN_ERR_VALUE;
+    for (int i = 0; i < 3; ++i)
+        if (resident[i] < 0 || resident[i] > kMaxResident) return ADALN_ERR_VALUE;
+    if (cus < 0 || cus > kMaxResident) return ADALN_ERR_VALUE;
+    write_plan(adaln::decide(static_cast<adaln::Op>(op), rows, H, T, resident, cus), out);
+    return ADALN_OK;
+}
+
+adaln_status adaln_diag_device_plan(int op, int64_t rows, int64_t H, int64_t T, int weight,
+                                    int64_t* out, int64_t* resident_out, int64_t* cus_out) {
+    ADALN_TRY(check_plan_args(op, rows, H, T, out));
+    adaln::Plan pl;
+    int64_t resident[3], cus = 0;
+    if (!adaln::device_plan(static_cast<adaln::Op>(op), rows, H, T, weight != 0, &pl, resident,
+                            &cus))
+        return ADALN_ERR_LAUNCH;
+    write_plan(pl, out);
+    if (resident_out)
+        for (int i = 0; i < 3; ++i) resident_out[i] = resident[i];
+    if (cus_out) *cus_out = cus;
     return ADALN_OK;
 }
 

@@ -75,14 +75,18 @@ struct CFParams {
     int64_t B, T, H, gate_bs;
 };
 hipError_t launch_cf(const CFParams& p, hipStream_t stream);
-// Workgroups of the channel-first launch: one per tile of 64 hidden x 64 tokens
-// (T % 8 == 0) or of 64 hidden x the 64-token span of eight aligned 16-byte blocks
-// of each residual row (otherwise; a row's blocks start up to 7 tokens before the
-// tile's first token, so the tiles cover T + 7 tokens), rounded up to a multiple of
-// eight so that consecutive tiles land on one XCD.
+// Workgroups of the channel-first launch: one per tile of 64 hidden x kCfTokens
+// tokens (T % 8 == 0) or of 64 hidden x the kCfTokens-token span of aligned 16-byte
+// blocks of each residual row (otherwise; a row's blocks start up to 7 tokens before
+// the tile's first token, so the tiles cover T + 7 tokens), rounded up to a multiple
+// of eight so that consecutive tiles land on one XCD.
+#ifndef ADALN_CF_TOKENS
+#define ADALN_CF_TOKENS 64  // tokens per tile (64, 128 or 256; launch tuning)
+#endif
+constexpr int64_t kCfTokens = ADALN_CF_TOKENS;
 inline int64_t cf_tiles(int64_t B, int64_t H, int64_t T) {
     const int64_t span = T % 8 == 0 ? T : T + 7;
-    return B * ((H + 63) / 64) * ((span + 63) / 64);
+    return B * ((H + 63) / 64) * ((span + kCfTokens - 1) / kCfTokens);
 }
 inline int64_t cf_grid(int64_t tiles) { return (tiles + 7) / 8 * 8; }
 
@@ -109,6 +113,15 @@ Plan plan_launch(Op op, int64_t rows, int64_t H, int64_t T, int64_t resident,
 
 // Launch the fused kernel for `op`; returns the HIP error of the launch.
 hipError_t launch(Op op, const Params& p, hipStream_t stream);
+
+// The plan of a launch from what fits on the device at once: resident[0..2] row
+// groups with the default ring, the one-slot ring and the two-row ring (0: not
+// available), and the CU count.
+Plan decide(Op op, int64_t rows, int64_t H, int64_t T, const int64_t resident[3], int64_t cus);
+// The same plan with the resident counts of the current device (occupancy queries,
+// cached); false when a query fails.
+bool device_plan(Op op, int64_t rows, int64_t H, int64_t T, bool weight, Plan* pl,
+                 int64_t resident[3], int64_t* cus);
 
 hipError_t launch_diag_round(const float* in, uint16_t* out, int64_t n, hipStream_t stream);
 hipError_t launch_diag_finalize(const float* in, float* out, int64_t n, int64_t H, float eps,

@@ -34,6 +34,7 @@
 #include <mutex>
 
 #include "adaln_device.hpp"
+#include "adaln_fold.hpp"
 #include "adaln_internal.hpp"
 
 // Launch tuning (never changes the numerics): for contiguous row ranges, groups per
@@ -79,6 +80,15 @@
 #define ADALN_CONTIG_SHALLOW_MAX_ROWS_PER_GROUP 2
 #endif
 
+// Wave priority by the rows a group has left (scheduling only; never changes the
+// numerics): 1 to raise it for groups with more rows left, and the rows per level.
+#ifndef ADALN_PRIO_BALANCE
+#define ADALN_PRIO_BALANCE 0
+#endif
+#ifndef ADALN_PRIO_ROWS
+#define ADALN_PRIO_ROWS 1
+#endif
+
 namespace adaln {
 namespace {
 
@@ -87,114 +97,6 @@ constexpr bool interleaved(int op) {
            (op == OP_RMS && ADALN_INTERLEAVE_RMS) || (op == OP_RG && ADALN_INTERLEAVE_RG) ||
            (op == OP_RGLN && ADALN_INTERLEAVE_RGLN);
 }
-
-// ---------------------------------------------------------------------------
-// statistics
-// ---------------------------------------------------------------------------
-struct Welford {
-    float n, mean, m2;
-};
-
-// Chan pairwise combine of (lo, hi) in that order; an empty side yields the other.
-// n = na + nb, delta = mean_b - mean_a, wb = RN(nb/n), mean = mean_a + delta*wb,
-// M2 = (M2a + M2b) + (delta*delta)*(na*wb).
-__device__ __forceinline__ Welford combine(const Welford& lo, const Welford& hi) {
-    const float n = lo.n + hi.n;
-    const float delta = hi.mean - lo.mean;
-    const float wb = hi.n / n;
-    const float step = delta * wb;
-    const float mean = lo.mean + step;
-    const float msum = lo.m2 + hi.m2;
-    const float dd = delta * delta;
-    const float nw = lo.n * wb;
-    const float corr = dd * nw;
-    const float m2 = msum + corr;
-    Welford o{n, mean, m2};
-    if (hi.n == 0.0f) o = lo;
-    if (lo.n == 0.0f) o = hi;
-    return o;
-}
-
-// The same combine when both sides hold NA > 0 elements (every level of a row
-// whose H fills all chunks): wb = RN(NA/2NA) = 1/2 and na*wb = NA/2 exactly, so
-// the two constants below give the bits of the general formula.  m2 enters as
-// the sum M2a + M2b, which fp32 addition makes independent of operand order.
-template <int NA>
-__device__ __forceinline__ void combine_equal(float lo_mean, float hi_mean, float m2_sum,
-                                              float& mean, float& m2) {
-    const float delta = hi_mean - lo_mean;
-    const float step = delta * 0.5f;
-    mean = lo_mean + step;
-    const float dd = delta * delta;
-    const float corr = dd * (0.5f * (float)NA);
-    m2 = m2_sum + corr;
-}
-
-// One in-row butterfly level at distance K (1, 2, 4 or 8) for Welford partials
-// with runtime counts (ragged rows).
-template <int K, int CTRL>
-__device__ __forceinline__ Welford welford_level(const Welford& me, int lane) {
-    Welford other{dpp<CTRL>(me.n), dpp<CTRL>(me.mean), dpp<CTRL>(me.m2)};
-    const bool upper = (lane & K) != 0;
-    Welford lo{upper ? other.n : me.n, upper ? other.mean : me.mean, upper ? other.m2 : me.m2};
-    Welford hi{upper ? me.n : other.n, upper ? me.mean : other.mean, upper ? me.m2 : other.m2};
-    return combine(lo, hi);
-}
-
-// The same level when both partners hold NA elements: the partners are read in
-// their fixed order directly (lo from lane t & ~K, hi from lane t | K).
-template <int K, int CTRL, int NA>
-__device__ __forceinline__ void welford_level_equal(float& mean, float& m2) {
-    const float lo = partner_lo<K>(mean);
-    const float hi = partner_hi<K>(mean);
-    combine_equal<NA>(lo, hi, m2 + dpp<CTRL>(m2), mean, m2);
-}
-
-__device__ __forceinline__ Welford readlane(const Welford& w, int lane) {
-    return Welford{readlane(w.n, lane), readlane(w.mean, lane), readlane(w.m2, lane)};
-}
-
-// Butterfly over the 64 lanes of a wave (distances 1..32).  Distances 16 and 32
-// combine the four uniform rows of 16 lanes: ((r0 (+) r1) (+) (r2 (+) r3)), every
-// lane ending with the wave's value.
-__device__ __forceinline__ float wave_sum(float s) {
-    s = s + dpp<DPP_XOR1>(s);
-    s = s + dpp<DPP_XOR2>(s);
-    s = s + dpp<DPP_HALF_MIRROR>(s);
-    s = s + dpp<DPP_MIRROR>(s);
-    float lo, hi;
-    pair16(s, lo, hi);
-    s = lo + hi;
-    pair32(s, lo, hi);
-    return lo + hi;
-}
-
-__device__ __forceinline__ Welford wave_welford(Welford w, int lane) {
-    w = welford_level<1, DPP_XOR1>(w, lane);
-    w = welford_level<2, DPP_XOR2>(w, lane);
-    w = welford_level<4, DPP_HALF_MIRROR>(w, lane);
-    w = welford_level<8, DPP_MIRROR>(w, lane);
-    const Welford a = combine(readlane(w, 0), readlane(w, 16));
-    const Welford b = combine(readlane(w, 32), readlane(w, 48));
-    return combine(a, b);
-}
-
-// Wave butterfly when every lane holds N elements.
-template <int N>
-__device__ __forceinline__ void wave_welford_equal(float& mean, float& m2) {
-    welford_level_equal<1, DPP_XOR1, N>(mean, m2);
-    welford_level_equal<2, DPP_XOR2, 2 * N>(mean, m2);
-    welford_level_equal<4, DPP_HALF_MIRROR, 4 * N>(mean, m2);
-    welford_level_equal<8, DPP_MIRROR, 8 * N>(mean, m2);
-    float mlo, mhi, qlo, qhi;
-    pair16(mean, mlo, mhi);
-    pair16(m2, qlo, qhi);
-    combine_equal<16 * N>(mlo, mhi, qlo + qhi, mean, m2);
-    pair32(mean, mlo, mhi);
-    pair32(m2, qlo, qhi);
-    combine_equal<32 * N>(mlo, mhi, qlo + qhi, mean, m2);
-}
-
 
 // ---------------------------------------------------------------------------
 // the fused row kernel
@@ -631,6 +533,17 @@ __global__ __launch_bounds__(256) void fused_norm_modulate(Params p) {
         load_row(row + S * step, xa, ra);
         ++seq;
         const int64_t next = row + step;
+        if (ADALN_PRIO_BALANCE) {
+            // the waves of a CU that were dispatched first otherwise keep the SIMDs and
+            // finish first, leaving the youngest to run on alone: a wave's priority is
+            // the number of rows it still has (at most 3), so the waves that are behind
+            // are served first (scheduling only)
+            const int64_t rem = next < r_end ? (r_end - next + step - 1) / step : 0;
+            if (rem >= ADALN_PRIO_ROWS * 3) __builtin_amdgcn_s_setprio(3);
+            else if (rem >= ADALN_PRIO_ROWS * 2) __builtin_amdgcn_s_setprio(2);
+            else if (rem >= ADALN_PRIO_ROWS) __builtin_amdgcn_s_setprio(1);
+            else __builtin_amdgcn_s_setprio(0);
+        }
         if (next < r_end) {  // uniform over the group
             t_in += step;
             if (t_in >= p.T) {
@@ -782,8 +695,7 @@ bool occupancy(const void* fn, int block, int* blocks_per_cu, int* cus) {
             return true;
         }
     int nb = 0, ncu = 0;
-    if (hipOccupancyMaxActiveBlocksPerMultiprocessor(&nb, fn, block,
-                                                     0) != hipSuccess)
+    if (hipOccupancyMaxActiveBlocksPerMultiprocessor(&nb, fn, block, 0) != hipSuccess)
         return false;
     if (hipDeviceGetAttribute(&ncu, hipDeviceAttributeMultiprocessorCount, dev) != hipSuccess)
         return false;
@@ -886,19 +798,28 @@ Plan plan_launch(Op op, int64_t rows, int64_t H, int64_t T, int64_t resident,
     return pl;
 }
 
-hipError_t launch(Op op, const Params& p_in, hipStream_t stream) {
-    const Layout L = layout_of(p_in.H);
-    const bool weight = p_in.weight != nullptr;
-    auto pick_op = [&](int ring) -> KernelFn {
-        return op == OP_LN     ? pick<OP_LN>(L, false, ring)
-               : op == OP_RMS  ? pick<OP_RMS>(L, weight, ring)
-               : op == OP_RG   ? pick<OP_RG>(L, weight, ring)
-               : op == OP_RGLN ? pick<OP_RGLN>(L, false, ring)
-               : op == OP_LNQ  ? pick<OP_LNQ>(L, false, ring)
-                               : nullptr;
-    };
-    KernelFn deep = pick_op(0);
-    if (!deep) return hipErrorInvalidValue;
+Plan decide(Op op, int64_t rows, int64_t H, int64_t T, const int64_t resident[3], int64_t cus) {
+    return plan_launch(op, rows, H, T, resident[0], resident[1], resident[2], cus);
+}
+
+namespace {
+
+KernelFn pick_op(Op op, const Layout& L, bool weight, int ring) {
+    return op == OP_LN     ? pick<OP_LN>(L, false, ring)
+           : op == OP_RMS  ? pick<OP_RMS>(L, weight, ring)
+           : op == OP_RG   ? pick<OP_RG>(L, weight, ring)
+           : op == OP_RGLN ? pick<OP_RGLN>(L, false, ring)
+           : op == OP_LNQ  ? pick<OP_LNQ>(L, false, ring)
+                           : nullptr;
+}
+
+}  // namespace
+
+bool device_plan(Op op, int64_t rows, int64_t H, int64_t T, bool weight, Plan* pl,
+                 int64_t resident[3], int64_t* cus_out) {
+    const Layout L = layout_of(H);
+    KernelFn deep = pick_op(op, L, weight, 0);
+    if (!deep) return false;
     // one-wave rows: four independent waves per workgroup; else one row group per
     // workgroup of W waves
     const int block = L.waves == 1 ? 256 : 64 * L.waves;
@@ -906,28 +827,40 @@ hipError_t launch(Op op, const Params& p_in, hipStream_t stream) {
     int blocks_per_cu = 0, cus = 0;
     if (!occupancy(reinterpret_cast<const void*>(deep), block, &blocks_per_cu, &cus)) {
         (void)hipGetLastError();
-        return hipErrorInvalidDeviceFunction;
+        return false;
     }
-    const int64_t resident = (int64_t)cus * blocks_per_cu * groups_per_block;
-    int64_t resident_shallow = 0, resident_two = 0;
-    KernelFn shallow = pick_op(1), two = pick_op(2);  // null where not instantiated
-    int bpc1 = 0, bpc2 = 0;
+    resident[0] = (int64_t)cus * blocks_per_cu * groups_per_block;
+    resident[1] = resident[2] = 0;
     // an optional kernel whose query fails is not used; its error is cleared so that
-    // the launch below reports only its own
+    // the launch reports only its own
+    KernelFn shallow = pick_op(op, L, weight, 1), two = pick_op(op, L, weight, 2);
+    int bpc = 0, c2 = 0;
     if (shallow) {
-        if (occupancy(reinterpret_cast<const void*>(shallow), block, &bpc1, &cus))
-            resident_shallow = (int64_t)cus * bpc1 * groups_per_block;
+        if (occupancy(reinterpret_cast<const void*>(shallow), block, &bpc, &c2))
+            resident[1] = (int64_t)c2 * bpc * groups_per_block;
         else
             (void)hipGetLastError();
     }
     if (two) {
-        if (occupancy(reinterpret_cast<const void*>(two), block, &bpc2, &cus))
-            resident_two = (int64_t)cus * bpc2 * groups_per_block;
+        if (occupancy(reinterpret_cast<const void*>(two), block, &bpc, &c2))
+            resident[2] = (int64_t)c2 * bpc * groups_per_block;
         else
             (void)hipGetLastError();
     }
-    const Plan pl = plan_launch(op, p_in.rows, p_in.H, p_in.T, resident, resident_shallow,
-                                resident_two, cus);
+    *cus_out = cus;
+    *pl = decide(op, rows, H, T, resident, cus);
+    return true;
+}
+
+hipError_t launch(Op op, const Params& p_in, hipStream_t stream) {
+    const bool weight = p_in.weight != nullptr;
+    Plan pl;
+    int64_t resident[3], cus = 0;
+    if (!device_plan(op, p_in.rows, p_in.H, p_in.T, weight, &pl, resident, &cus))
+        return hipErrorInvalidDeviceFunction;
+    if (pl.blocks > 0x7FFFFFFF || pl.groups > 0x7FFFFFFF) return hipErrorInvalidValue;
+    KernelFn fn = pick_op(op, layout_of(p_in.H), weight, pl.ring);
+    if (!fn) return hipErrorInvalidValue;
     Params p = p_in;
     p.groups = pl.groups;
     p.gpb = pl.gpb;
@@ -935,10 +868,7 @@ hipError_t launch(Op op, const Params& p_in, hipStream_t stream) {
     p.group_stride = pl.group_stride;
     p.step = pl.step;
     p.span = pl.span;
-    if (pl.blocks > 0x7FFFFFFF || pl.groups > 0x7FFFFFFF) return hipErrorInvalidValue;
-    KernelFn fn = pl.ring == 1 ? shallow : pl.ring == 2 ? two : deep;
-    if (!fn) return hipErrorInvalidValue;
-    hipLaunchKernelGGL(fn, dim3((unsigned)pl.blocks), dim3(block), 0, stream, p);
+    hipLaunchKernelGGL(fn, dim3((unsigned)pl.blocks), dim3(pl.block_threads), 0, stream, p);
     return hipGetLastError();
 }
 

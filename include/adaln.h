@@ -98,7 +98,10 @@ extern "C" {
                               7: launch-plan diagnostic;
                               8: the plan takes T and gives row blocks; the finalize
                                  diagnostic takes H;
-                              9: streaming read / fill / copy measurement kernels */
+                              9: streaming read / fill / copy measurement kernels;
+                                 the plan diagnostic takes every resident count and
+                                 the CU count and reports the ring; the device's own
+                                 plan */
 
 typedef uint16_t adaln_bf16; /* raw bfloat16 bits */
 
@@ -273,21 +276,32 @@ adaln_status adaln_diag_finalize(const float* in, float* out, int64_t n, int64_t
 adaln_status adaln_diag_quant_fp8(const float* in, uint8_t* out, int64_t n, const float* qscale,
                                   void* hip_stream);
 
-/* Diagnostic: the row-group plan of one launch of the fused kernel, computed on
- * the host with no device work, for `resident` row groups fitting on the device at
- * once with the deep ring and `resident_shallow` with the one-slot ring (0: not
- * available).  op: 0 LayerNorm+modulate, 1 RMSNorm+scale/shift, 2 residual gate +
- * RMSNorm, 3 residual gate + LayerNorm, 4 LayerNorm+modulate+FP8.  rows = B*T >= 1
- * with 1 <= T <= rows and rows % T == 0 (else ADALN_ERR_SHAPE), H as for the entry
- * points.  out[10] receives {one-slot ring (0/1), ring slots, groups, groups per
- * block, rows per block, group stride, step, span, workgroups, threads per
- * workgroup}: with k = g / (groups per block) and first = k * (rows per block) +
- * (g % groups per block) * stride, group g takes the rows first + i*step below
- * min(first + span, (k + 1) * (rows per block), rows).  ADALN_ERR_VALUE for an
- * unknown op or a resident count below 1 (below 0 for resident_shallow) or above
- * 2^31 - 1. */
-adaln_status adaln_diag_launch_plan(int op, int64_t rows, int64_t H, int64_t T, int64_t resident,
-                                    int64_t resident_shallow, int64_t* out);
+/* Diagnostic: the row-group plan of one launch of a fused entry point, computed on
+ * the host with no device work, for given counts of what fits on the device at once.
+ * op: 0 LayerNorm+modulate, 1 RMSNorm+scale/shift, 2 residual gate + RMSNorm,
+ * 3 residual gate + LayerNorm, 4 LayerNorm+modulate+FP8.  resident[3]: row groups
+ * resident at once with the default ring, with the one-slot ring and with the
+ * two-row ring (0: not available; resident[0] >= 1); cus: compute units (0: unknown;
+ * the two-row ring is chosen only with it).  rows = B*T >= 1 with 1 <= T <= rows and
+ * rows % T == 0 (else ADALN_ERR_SHAPE), H as for the entry points.  out[11]
+ * receives {one-slot ring (0/1), ring slots, ring kind (0 default depth, 1 one slot,
+ * 2 two rows), groups, groups per block, rows per block, group stride, step, span,
+ * workgroups, threads per workgroup}: with k = g / (groups per block) and first =
+ * k * (rows per block) + (g % groups per block) * stride, group g takes the rows
+ * first + i*step below min(first + span, (k + 1) * (rows per block), rows).
+ * ADALN_ERR_VALUE for an unknown op or a resident count or cus below 0 or above
+ * 2^31 - 1 (resident[0] below 1); ADALN_ERR_NULL for a NULL resident or out. */
+adaln_status adaln_diag_launch_plan(int op, int64_t rows, int64_t H, int64_t T,
+                                    const int64_t* resident, int64_t cus, int64_t* out);
+
+/* Diagnostic: the plan a launch takes on the current device, from the same
+ * occupancy queries (cached per kernel and device), with nothing launched; weight:
+ * nonzero when the RMS weight is given (ops 1 and 2; it selects the kernel whose
+ * occupancy is queried).  out[11] as above; resident_out[3] and *cus_out (each may be
+ * NULL) receive the counts it used.  ADALN_ERR_LAUNCH when the queries fail (for
+ * example no gfx950 device). */
+adaln_status adaln_diag_device_plan(int op, int64_t rows, int64_t H, int64_t T, int weight,
+                                    int64_t* out, int64_t* resident_out, int64_t* cus_out);
 
 /* Measurement aid: copy `bytes` bytes of device memory from src to dst with the
  * fused kernels' access style (16-byte non-temporal loads and stores), so that the

@@ -35,11 +35,12 @@ int main() {
             case 5: st = adaln_check_qk_rmsnorm_rope(ptr(), ptr(), ptr(), ptr(), (const float*)ptr(), (adaln_bf16*)ptr(), (adaln_bf16*)ptr(), T, B, H, s0, s1, pick(), eps); break;
             case 6: st = adaln_check_residual_gate_channel_first(ptr(), ptr(), ptr(), (adaln_bf16*)ptr(), B, H, T, s0); break;
             default: {
-                int64_t out[10];
-                st = adaln_diag_launch_plan((int)(rng() % 7) - 1, B, H, T, s0, s1, out);
+                int64_t out[11];
+                const int64_t res[3] = {s0, s1, s2};
+                st = adaln_diag_launch_plan((int)(rng() % 7) - 1, B, H, T, res, pick(), out);
                 if (st == ADALN_OK) {
-                    // groups cover rows: first and last group's ranges inside [0, rows)
-                    if (out[2] < 1 || out[3] < 1 || out[4] < 1) { std::printf("bad plan\n"); return 1; }
+                    // a plan has groups, groups per block and rows per block
+                    if (out[3] < 1 || out[4] < 1 || out[5] < 1) { std::printf("bad plan\n"); return 1; }
                 }
             }
         }
@@ -75,9 +76,13 @@ int main() {
             default: st = adaln_check_residual_gate_channel_first(r, x, g, y, B, T, H, s0); break;
         }
         if (st == ADALN_OK) ++acc2;
-        int64_t out[10];
-        if (B > 0 && T > 0 && B <= INT64_MAX / T)
-            (void)adaln_diag_launch_plan((int)(rng() % 5), B * T, H, T, 1 + (int64_t)(rng() % 8192), (int64_t)(rng() % 8192), out);
+        int64_t out[11];
+        if (B > 0 && T > 0 && B <= INT64_MAX / T) {
+            const int64_t res[3] = {1 + (int64_t)(rng() % 8192), (int64_t)(rng() % 8192),
+                                    (int64_t)(rng() % 8192)};
+            (void)adaln_diag_launch_plan((int)(rng() % 5), B * T, H, T, res,
+                                         (int64_t)(rng() % 512), out);
+        }
     }
     std::printf("structured accepted %ld\n", acc2);
     int w, l, c;

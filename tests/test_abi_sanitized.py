@@ -14,7 +14,8 @@ import pytest
 HERE = os.path.dirname(os.path.abspath(__file__))
 ROOT = os.path.dirname(HERE)
 CSRC = os.path.join(ROOT, "diffusion_dit_adaln_amd", "csrc")
-SOURCES = ["adaln_api.cpp", "adaln_kernels.hip", "adaln_qknorm.hip", "adaln_channel_first.hip"]
+SOURCES = ["adaln_api.cpp", "adaln_kernels.hip", "adaln_qknorm.hip", "adaln_channel_first.hip",
+           "adaln_stream.hip"]
 # sanitizers on the host side only, each right after -Xarch_host
 SAN = ["-Xarch_host", "-fsanitize=address", "-Xarch_host", "-fsanitize=undefined",
        "-Xarch_host", "-fno-sanitize-recover=all"]

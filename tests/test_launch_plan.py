@@ -1,9 +1,10 @@
-"""The fused kernel's launch plan (host logic, CPU): for every op, hidden size, row
-count and batch split, the row groups of one launch cover every row exactly once, the
-grid and ring settings follow the documented rules, an interleaved group that is given
-to one batch entry stays in it, and a contiguous group's rows stay within 32-bit byte
-offsets.  The plan is the library's own host function (through the
-launch-plan diagnostic), fed with resident counts like the device's."""
+"""The fused launch's plan (host logic, CPU): for every op, hidden size, row count,
+batch split and set of resident counts, the row groups of one launch cover every row
+exactly once; the grid and ring follow the documented rules; a group given to one
+batch entry stays in it; a contiguous group's rows stay within 32-bit byte offsets.
+The plan is the library's own host function (through the launch-plan diagnostic),
+fed with resident counts like a device's: row groups with the default ring, the
+one-slot ring and the two-row ring, and the CU count."""
 import numpy as np
 import pytest
 
@@ -11,11 +12,14 @@ import diffusion_dit_adaln_amd as A
 
 OPS = ["ln", "rms", "rg", "rgln", "lnq"]
 INTERLEAVED = {"ln", "rgln", "lnq"}
-RESIDENT = [(1024, 1536), (768, 0), (256, 512), (1, 1), (7, 0), (2560, 2560)]
+# (deep, one-slot, two-row, CUs)
+RESIDENT = [(1024, 1536, 1792, 256), (768, 0, 0, 256), (256, 512, 0, 64), (1, 1, 0, 1),
+            (7, 0, 0, 7), (2560, 2560, 0, 256), (1024, 1536, 1280, 256), (1024, 1536, 1792, 0),
+            (1024, 1536, 1280, 3)]
 # (rows, T): one batch entry, a few long ones, many short ones
 SHAPES = [(1, 1), (3, 1), (7, 7), (7, 1), (100, 100), (100, 25), (4216, 4216), (4216, 527),
           (9216, 4608), (9216, 9216), (30001, 1579), (524287, 524287), (524288, 4096),
-          (524288, 64)]
+          (524288, 64), (8192, 8192), (64 * 15, 15)]
 
 
 def rows_of(plan, rows):
@@ -33,24 +37,24 @@ def rows_of(plan, rows):
 
 
 @pytest.mark.parametrize("op", OPS)
-@pytest.mark.parametrize("H", [8, 520, 1024, 2048, 3072, 4096, 4104, 8192])
+@pytest.mark.parametrize("H", [8, 520, 1024, 2048, 3072, 4096, 4104, 6144, 8192])
 @pytest.mark.parametrize("shape", SHAPES)
 @pytest.mark.parametrize("res", RESIDENT)
 def test_every_row_exactly_once(op, H, shape, res):
     rows, T = shape
-    resident, resident_shallow = res
-    plan = A.adaln_diag_launch_plan(op, rows, H, T, resident, resident_shallow)
+    resident, resident_shallow, resident_two, cus = res
+    plan = A.adaln_diag_launch_plan(op, rows, H, T, res[:3], cus)
     w, _, _ = A.adaln_reduction_layout(H)
     visited, group = rows_of(plan, rows)
     assert visited.size == rows
     assert np.array_equal(np.sort(visited), np.arange(rows))
+    B = rows // T
     assert plan["block_threads"] == (256 if w == 1 else 64 * w)
     assert plan["blocks"] == ((plan["groups"] + 3) // 4 if w == 1 else plan["groups"])
     if op in INTERLEAVED:
         shallow = resident_shallow > 0 and rows >= 3 * resident
-        assert plan["shallow"] == shallow
+        assert plan["shallow"] == shallow and plan["ring"] == (1 if shallow else 0)
         G = min(rows, resident_shallow if shallow else resident)
-        B = rows // T
         per_entry = min(G // B, T) if B > 1 else 0
         assert plan["group_stride"] == 1 and plan["step"] == plan["gpb"]
         if per_entry > 0 and 16 * (G - per_entry * B) <= G:
@@ -72,7 +76,12 @@ def test_every_row_exactly_once(op, H, shape, res):
                    and rows <= 2 * resident_shallow)
         assert plan["shallow"] == shallow and plan["step"] == 1
         if shallow:
-            assert S == 1
+            assert S == 1 and plan["ring"] == 1
+        elif plan["ring"] == 2:
+            # the two-row ring: ungated four-wave rows, only with its resident count
+            assert op == "rms" and w == 4 and resident_two > 0 and cus > 0 and S == 2
+        else:
+            assert plan["ring"] == 0
         assert plan["gpb"] == plan["groups"] and plan["blk_rows"] == rows
         assert plan["span"] == plan["group_stride"] and plan["span"] % S == 0
         # the last pass reaches S rows past the span: still below 2^31 bytes
@@ -81,14 +90,31 @@ def test_every_row_exactly_once(op, H, shape, res):
         assert plan["groups"] == -(-rows // plan["span"])
 
 
+def test_two_row_ring_where_it_spreads_groups_more_evenly():
+    # four-wave RMS rows at 8192 rows on a device like MI355X (resident counts of the
+    # weighted kernels: 4, 6 and 5 groups per CU): the two-row ring leaves the most
+    # loaded CU fewer rows
+    res = (1024, 1536, 1280)
+    for H in (4096, 4104):
+        plan = A.adaln_diag_launch_plan("rms", 8192, H, 8192, res, 256)
+        assert plan["ring"] == 2 and plan["slots"] == 2 and not plan["shallow"]
+    # without its resident count or the CU count it is never chosen
+    assert A.adaln_diag_launch_plan("rms", 8192, 4096, 8192, (1024, 1536, 0), 256)["ring"] == 0
+    assert A.adaln_diag_launch_plan("rms", 8192, 4096, 8192, res, 0)["ring"] == 0
+    # with one more two-row group per CU the three-row ring spreads 8192 rows better
+    assert A.adaln_diag_launch_plan("rms", 8192, 4096, 8192, (1024, 1536, 1792), 256)["ring"] == 0
+    # never for the gated op
+    assert A.adaln_diag_launch_plan("rg", 8192, 4096, 8192, res, 256)["ring"] == 0
+
+
 def test_interleaved_batch_entries_get_their_own_groups():
     # the FLUX.1 LayerNorm site [2, 4608, 3072] on 2560 resident groups: 1280 per entry
-    plan = A.adaln_diag_launch_plan("lnq", 9216, 3072, 4608, 2560, 2560)
+    plan = A.adaln_diag_launch_plan("lnq", 9216, 3072, 4608, (2560, 2560), 256)
     assert (plan["groups"], plan["gpb"], plan["blk_rows"], plan["step"]) == (2560, 1280, 4608, 1280)
     # 2560 groups over 7 entries would leave 5 slots idle (< 1/16): split
-    assert A.adaln_diag_launch_plan("ln", 7 * 4608, 3072, 4608, 2560, 2560)["gpb"] == 365
+    assert A.adaln_diag_launch_plan("ln", 7 * 4608, 3072, 4608, (2560, 2560))["gpb"] == 365
     # 2560 groups over 1000 entries would idle 560 slots: one interleave over all rows
-    plan = A.adaln_diag_launch_plan("ln", 1000 * 64, 3072, 64, 2560, 2560)
+    plan = A.adaln_diag_launch_plan("ln", 1000 * 64, 3072, 64, (2560, 2560))
     assert (plan["groups"], plan["gpb"], plan["blk_rows"]) == (2560, 2560, 64000)
 
 
@@ -96,23 +122,21 @@ def test_contiguous_groups_capped_by_32_bit_offsets():
     # so many rows per group that the span would pass 2^31 bytes: the span is
     # capped and the group count grows instead
     rows, H = 3 * 10**8, 8192
-    plan = A.adaln_diag_launch_plan("rms", rows, H, rows, 1024, 0)
+    plan = A.adaln_diag_launch_plan("rms", rows, H, rows, (1024, 0, 0), 256)
     S = plan["slots"]
     assert (plan["span"] + S) * 2 * H <= 2**31 - 1
     assert plan["groups"] * plan["span"] >= rows > (plan["groups"] - 1) * plan["span"]
 
 
 def test_plan_rejects_bad_arguments():
-    with pytest.raises(A.AdalnError):
-        A.adaln_diag_launch_plan("ln", 0, 1024, 1, 1024)
-    with pytest.raises(A.AdalnError):
-        A.adaln_diag_launch_plan("ln", 10, 12, 10, 1024)
-    with pytest.raises(A.AdalnError):
-        A.adaln_diag_launch_plan("ln", 10, 1024, 10, 0)
-    with pytest.raises(A.AdalnError):
-        A.adaln_diag_launch_plan("ln", 10, 1024, 10, 2**31)
-    with pytest.raises(A.AdalnError):
-        A.adaln_diag_launch_plan("ln", 10, 1024, 10, 1024, 2**31)
+    bad = [("ln", 0, 1024, 1, (1024, 0, 0), 0), ("ln", 10, 12, 10, (1024, 0, 0), 0),
+           ("ln", 10, 1024, 10, (0, 0, 0), 0), ("ln", 10, 1024, 10, (2**31, 0, 0), 0),
+           ("ln", 10, 1024, 10, (1024, 2**31, 0), 0), ("ln", 10, 1024, 10, (1024, 0, -1), 0),
+           ("ln", 10, 1024, 10, (1024, 0, 2**31), 0), ("ln", 10, 1024, 10, (1024, 0, 0), -1),
+           ("ln", 10, 1024, 10, (1024, 0, 0), 2**31)]
+    for op, rows, H, T, res, cus in bad:
+        with pytest.raises(A.AdalnError):
+            A.adaln_diag_launch_plan(op, rows, H, T, res, cus)
     for T in (0, 3, 11, -1):  # T must divide rows
         with pytest.raises(A.AdalnError):
-            A.adaln_diag_launch_plan("ln", 10, 1024, T, 1024)
+            A.adaln_diag_launch_plan("ln", 10, 1024, T, (1024, 0, 0))

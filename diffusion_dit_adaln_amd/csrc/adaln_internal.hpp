@@ -75,18 +75,26 @@ struct CFParams {
     int64_t B, T, H, gate_bs;
 };
 hipError_t launch_cf(const CFParams& p, hipStream_t stream);
-// Workgroups of the channel-first launch: one per tile of 64 hidden x kCfTokens
-// tokens (T % 8 == 0) or of 64 hidden x the kCfTokens-token span of aligned 16-byte
-// blocks of each residual row (otherwise; a row's blocks start up to 7 tokens before
-// the tile's first token, so the tiles cover T + 7 tokens), rounded up to a multiple
-// of eight so that consecutive tiles land on one XCD.
+// Workgroups of the channel-first launch: one per tile of 64 hidden rows x kCfTokens
+// tokens of the residual rows.  A row's blocks start on a kCfAlign-element boundary
+// of the flat tensor, up to kCfAlign - 1 tokens before the tile's first token, so
+// unless every row starts on such a boundary (T % kCfAlign == 0) the tiles of a row
+// cover T + kCfAlign - 1 tokens.  The grid is rounded up to a multiple of eight so
+// that consecutive tiles land on one XCD.
 #ifndef ADALN_CF_TOKENS
-#define ADALN_CF_TOKENS 64  // tokens per tile (64, 128 or 256; launch tuning)
+#define ADALN_CF_TOKENS 64  // tokens per tile (64 or 128; launch tuning)
+#endif
+#ifndef ADALN_CF_ALIGN
+#define ADALN_CF_ALIGN 64  // block alignment in elements (64: 128-byte lines, or 8)
 #endif
 constexpr int64_t kCfTokens = ADALN_CF_TOKENS;
+constexpr int64_t kCfAlign = ADALN_CF_ALIGN;
+inline int64_t cf_tiles_t(int64_t T) {
+    const int64_t span = T % kCfAlign == 0 ? T : T + kCfAlign - 1;
+    return (span + kCfTokens - 1) / kCfTokens;
+}
 inline int64_t cf_tiles(int64_t B, int64_t H, int64_t T) {
-    const int64_t span = T % 8 == 0 ? T : T + 7;
-    return B * ((H + 63) / 64) * ((span + kCfTokens - 1) / kCfTokens);
+    return B * ((H + 63) / 64) * cf_tiles_t(T);
 }
 inline int64_t cf_grid(int64_t tiles) { return (tiles + 7) / 8 * 8; }
 

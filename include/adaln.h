@@ -192,9 +192,10 @@ adaln_status adaln_qk_rmsnorm_rope(const adaln_bf16* q, const adaln_bf16* k,
  *   out[b][h][t] = bf16(res[b][h][t] + bf16(gate[b][h] * update[b][t][h]))
  * res, out: contiguous [B, H, T]; update: contiguous [B, T, H]; gate row b at
  * gate + b*gate_bstride (0 shares one vector; else >= H and % 8 == 0).  Any T >= 0;
- * H % 8 == 0; one workgroup of 256 per tile of 64 hidden rows and 64 tokens (with
- * T % 8 != 0 the tiles cover T + 7 tokens), at most 2^24 - 8 tiles
- * (ADALN_ERR_SHAPE otherwise); pointers 16-byte aligned.  out may be
+ * H % 8 == 0; one workgroup of 256 per tile of 64 hidden rows and 64 tokens (each
+ * row's tiles start on a 128-byte line of the flat tensor, so with T % 64 != 0 they
+ * cover T + 63 tokens), at most 2^24 - 8 tiles (ADALN_ERR_SHAPE otherwise);
+ * pointers 16-byte aligned.  out may be
  * res itself (in-place update); any other overlap is ADALN_ERR_OVERLAP. */
 adaln_status adaln_residual_gate_channel_first(const adaln_bf16* res, const adaln_bf16* update,
                                                const adaln_bf16* gate, adaln_bf16* out, int64_t B,

@@ -177,12 +177,14 @@ def test_channel_first_checks(lib):
     assert cf_check(lib, H=12) == SHAPE
     # one tile per workgroup of 256, the grid rounded up to a multiple of eight
     # workgroups, fewer than 2^32 work-items: at most 2^24 - 8 tiles
-    assert cf_check(lib, B=(1 << 24) - 8, T=8, H=8, gbs=0) == OK
-    assert cf_check(lib, B=(1 << 24) - 7, T=8, H=8, gbs=0) == SHAPE
-    # a ragged T: the tiles cover T + 7 tokens (48 * 68 tiles per batch entry here)
+    assert cf_check(lib, B=(1 << 24) - 8, T=64, H=8, gbs=0) == OK
+    assert cf_check(lib, B=(1 << 24) - 7, T=64, H=8, gbs=0) == SHAPE
+    # T % 64 != 0: a row's tiles start on a 128-byte line and cover T + 63 tokens
+    assert cf_check(lib, B=(1 << 23) - 4, T=8, H=8, gbs=0) == OK      # two tiles each
+    assert cf_check(lib, B=(1 << 23) - 3, T=8, H=8, gbs=0) == SHAPE
     far_r = dict(res=addr(0), upd=addr(10), out=addr(20), gate=addr(30), gbs=0, T=4333)
-    assert cf_check(lib, B=5140, **far_r) == OK
-    assert cf_check(lib, B=5141, **far_r) == SHAPE
+    assert cf_check(lib, B=5065, **far_r) == OK          # 48 * 69 tiles per batch entry
+    assert cf_check(lib, B=5066, **far_r) == SHAPE
     far = dict(res=addr(0), upd=addr(10), out=addr(20), gate=addr(30), gbs=0)  # 137 GB each
     assert cf_check(lib, B=4854, **far) == OK            # 4854 * 48 * 72 tiles
     assert cf_check(lib, B=4855, **far) == SHAPE

@@ -80,15 +80,6 @@
 #define ADALN_CONTIG_SHALLOW_MAX_ROWS_PER_GROUP 2
 #endif
 
-// Wave priority by the rows a group has left (scheduling only; never changes the
-// numerics): 1 to raise it for groups with more rows left, and the rows per level.
-#ifndef ADALN_PRIO_BALANCE
-#define ADALN_PRIO_BALANCE 0
-#endif
-#ifndef ADALN_PRIO_ROWS
-#define ADALN_PRIO_ROWS 1
-#endif
-
 namespace adaln {
 namespace {
 
@@ -533,17 +524,6 @@ __global__ __launch_bounds__(256) void fused_norm_modulate(Params p) {
         load_row(row + S * step, xa, ra);
         ++seq;
         const int64_t next = row + step;
-        if (ADALN_PRIO_BALANCE) {
-            // the waves of a CU that were dispatched first otherwise keep the SIMDs and
-            // finish first, leaving the youngest to run on alone: a wave's priority is
-            // the number of rows it still has (at most 3), so the waves that are behind
-            // are served first (scheduling only)
-            const int64_t rem = next < r_end ? (r_end - next + step - 1) / step : 0;
-            if (rem >= ADALN_PRIO_ROWS * 3) __builtin_amdgcn_s_setprio(3);
-            else if (rem >= ADALN_PRIO_ROWS * 2) __builtin_amdgcn_s_setprio(2);
-            else if (rem >= ADALN_PRIO_ROWS) __builtin_amdgcn_s_setprio(1);
-            else __builtin_amdgcn_s_setprio(0);
-        }
         if (next < r_end) {  // uniform over the group
             t_in += step;
             if (t_in >= p.T) {

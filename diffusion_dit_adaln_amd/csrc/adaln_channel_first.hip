@@ -13,13 +13,18 @@
 // bytes per access.  A row's blocks start on a kCfAlign-element boundary of the flat
 // tensor: row (b, h) starts mis = ((b*H + h)*T) mod kCfAlign elements past one, and
 // in tile j it takes the blocks whose first token lies in
-// kCfTokens*j - mis .. kCfTokens*j - mis + kCfTokens - 1.  Every residual load and
-// output store is then a whole aligned 16-byte access, except the block that holds a
-// row's first or last token together with a neighbouring row's tokens (T % 8 != 0),
-// which is gathered and stored element by element.
+// kCfTokens*j - mis .. kCfTokens*j - mis + kCfTokens - 1, so the eight lanes of a row
+// cover whole 128-byte lines.  Every residual load is a whole aligned 16-byte access
+// (a block that also holds a neighbouring row's tokens, when T % 8 != 0, is loaded
+// whole and only this row's halfwords are used; only a block reaching past the end of
+// the tensor is gathered element by element), and so is every output store except
+// those of the blocks shared with a neighbouring row, which are stored element by
+// element.
 //
 // Order of work: the lane first issues its loads of `update` (two tokens x 8 hidden
-// values per item, 16-byte loads along hidden), then its residual blocks, so both
+// values per item, 16-byte loads along hidden; cached when the rows are not all
+// aligned, since a tile then reads kCfAlign update rows that the tile before it
+// also read, non-temporal otherwise), then its residual blocks, so both
 // streams are in flight together; it forms g = bf16(gate * update) as soon as the
 // update values arrive and writes them to LDS as rows of hidden, two tokens per
 // 32-bit word; after one barrier it adds, to each residual block, the eight gated
@@ -97,8 +102,10 @@ __global__ __launch_bounds__(256) void residual_gate_cf(CFParams p, u32 tiles, u
         const int64_t t0 = g0 + 2 * u;
         const bool ok = h_in && (kItems % 256 == 0 || tid + 256 * it < kItems);
         const bool ok0 = ok && t0 >= 0 && t0 < p.T, ok1 = ok && t0 + 1 >= 0 && t0 + 1 < p.T;
-        ua[it] = ld16_nt(ok0 ? p.update + (b * p.T + t0) * p.H + hg : p.update);
-        uc[it] = ld16_nt(ok1 ? p.update + (b * p.T + t0 + 1) * p.H + hg : p.update);
+        const uint16_t* a0 = ok0 ? p.update + (b * p.T + t0) * p.H + hg : p.update;
+        const uint16_t* a1 = ok1 ? p.update + (b * p.T + t0 + 1) * p.H + hg : p.update;
+        ua[it] = MIS ? ld16(a0) : ld16_nt(a0);
+        uc[it] = MIS ? ld16(a1) : ld16_nt(a1);
     }
 
     // residual blocks: hidden row hl = tid/8 + 32*it, block k = tid%8 + 8*m.  A block

@@ -3,7 +3,8 @@
 // loads and stores), timed beside them as ceilings.  Not on the path.
 //
 //  - copy: each thread loads PER 16-byte vectors, then stores them (loads first,
-//    so that PER vectors per thread are in flight);
+//    so that PER vectors per thread are in flight; the accesses of a whole block
+//    are unconditional, since a guarded load would be waited for before the next);
 //  - read: each thread loads PER vectors and folds them with XOR; lane 0 of each
 //    wave stores the wave's fold (4 bytes per 1024*PER bytes read), so no load
 //    can be removed;
@@ -23,15 +24,20 @@ __global__ __launch_bounds__(256) void stream_copy(const u32x4* __restrict__ src
                                                    u32x4* __restrict__ dst, int64_t n16) {
     const int64_t base = (int64_t)blockIdx.x * 256 * PER + threadIdx.x;
     u32x4 v[PER];
+    if ((int64_t)(blockIdx.x + 1) * 256 * PER <= n16) {
+        // a whole block: unconditional accesses, so every load is in flight before
+        // the first wait
 #pragma unroll
-    for (int k = 0; k < PER; ++k) {
-        const int64_t i = base + (int64_t)k * 256;
-        if (i < n16) v[k] = __builtin_nontemporal_load(src + i);
+        for (int k = 0; k < PER; ++k) v[k] = __builtin_nontemporal_load(src + base + k * 256);
+        __builtin_amdgcn_sched_barrier(0);  // every load issued before the first store
+#pragma unroll
+        for (int k = 0; k < PER; ++k) __builtin_nontemporal_store(v[k], dst + base + k * 256);
+        return;
     }
 #pragma unroll
     for (int k = 0; k < PER; ++k) {
         const int64_t i = base + (int64_t)k * 256;
-        if (i < n16) __builtin_nontemporal_store(v[k], dst + i);
+        if (i < n16) __builtin_nontemporal_store(__builtin_nontemporal_load(src + i), dst + i);
     }
 }
 
@@ -40,12 +46,21 @@ __global__ __launch_bounds__(256) void stream_read(const u32x4* __restrict__ src
                                                    u32* __restrict__ sink, int64_t n16) {
     const int64_t base = (int64_t)blockIdx.x * 256 * PER + threadIdx.x;
     u32 acc = 0;
+    if ((int64_t)(blockIdx.x + 1) * 256 * PER <= n16) {
+        u32x4 v[PER];
 #pragma unroll
-    for (int k = 0; k < PER; ++k) {
-        const int64_t i = base + (int64_t)k * 256;
-        if (i < n16) {
-            const u32x4 t = __builtin_nontemporal_load(src + i);
-            acc ^= t.x ^ t.y ^ t.z ^ t.w;
+        for (int k = 0; k < PER; ++k) v[k] = __builtin_nontemporal_load(src + base + k * 256);
+        __builtin_amdgcn_sched_barrier(0);  // every load issued before the first fold
+#pragma unroll
+        for (int k = 0; k < PER; ++k) acc ^= v[k].x ^ v[k].y ^ v[k].z ^ v[k].w;
+    } else {
+#pragma unroll
+        for (int k = 0; k < PER; ++k) {
+            const int64_t i = base + (int64_t)k * 256;
+            if (i < n16) {
+                const u32x4 t = __builtin_nontemporal_load(src + i);
+                acc ^= t.x ^ t.y ^ t.z ^ t.w;
+            }
         }
     }
     // fold over the wave (any order: XOR), lane 0 keeps the wave's value

@@ -260,7 +260,8 @@ def rg_channel_first_2x3072x4608(seed: int = 0) -> CFWorkload:
 
 def cf_tokens(T: int, seed: int = 0) -> CFWorkload:
     """Channel-first residual gating at hidden 3072, CFG batch 2, with T tokens (the
-    token-count sweep: T % 8 decides whether the residual rows are 16-byte aligned)."""
+    token-count sweep: T % 8 decides whether the residual rows are 16-byte aligned, and
+    T % 64 whether they start on 128-byte lines)."""
     B, H = 2, 3072
     return CFWorkload(f"rg_channel_first_2x3072x{T}",
                       normal_bf16(_rng(seed, 38, "res"), (B, H, T)),

@@ -79,6 +79,13 @@
 #ifndef ADALN_CONTIG_SHALLOW_MAX_ROWS_PER_GROUP
 #define ADALN_CONTIG_SHALLOW_MAX_ROWS_PER_GROUP 2
 #endif
+// The contiguous ops (RMS, residual-gate RMS) take the interleaved assignment with
+// the one-slot ring from this many elements (rows * H) per launch on (measured on
+// MI355X: +4% to +11% at 2^26 elements and above for one-, two- and four-wave rows,
+// mixed below, where contiguous ranges stay).
+#ifndef ADALN_CONTIG_INTERLEAVE_MIN_ELEMS
+#define ADALN_CONTIG_INTERLEAVE_MIN_ELEMS (int64_t(1) << 26)
+#endif
 
 namespace adaln {
 namespace {
@@ -592,9 +599,8 @@ __global__ __launch_bounds__(256) void diag_quant(const float4* __restrict__ in,
 // ---------------------------------------------------------------------------
 using KernelFn = void (*)(Params);
 
-template <int OP, int W, int C, bool TAIL, int RING>
+template <int OP, int W, int C, bool TAIL, int RING, bool IL = interleaved(OP)>
 KernelFn pick_weight(bool weight) {
-    constexpr bool IL = interleaved(OP);
     if constexpr (op_layernorm(OP)) {
         return fused_norm_modulate<OP, W, C, TAIL, false, IL, RING>;  // no weight
     } else {
@@ -604,11 +610,17 @@ KernelFn pick_weight(bool weight) {
 }
 
 // ring 1 (the one-slot ring) is instantiated for the interleaved ops and for the
-// ungated contiguous ops' four-wave rows, ring 2 for the latter only; ring 0 is
-// the default depth
+// ungated contiguous ops' four-wave rows, ring 2 for the latter only, ring 3 (the
+// one-slot ring on interleaved rows) for the contiguous ops' large launches; ring 0
+// is the default depth
 template <int OP, int W, int C>
 KernelFn pick_tail(bool tail, bool weight, int ring) {
     constexpr bool contig4 = !interleaved(OP) && W == 4 && !op_gated(OP);
+    if constexpr (!interleaved(OP)) {
+        if (ring == 3)
+            return tail ? pick_weight<OP, W, C, true, 1, true>(weight)
+                        : pick_weight<OP, W, C, false, 1, true>(weight);
+    }
     if constexpr (interleaved(OP) || contig4) {
         if (ring == 1)
             return tail ? pick_weight<OP, W, C, true, 1>(weight)
@@ -696,25 +708,31 @@ Layout layout_of(int64_t H) {
 }
 
 Plan plan_launch(Op op, int64_t rows, int64_t H, int64_t T, int64_t resident,
-                 int64_t resident_shallow, int64_t resident_two, int64_t cus) {
+                 int64_t resident_shallow, int64_t resident_two, int64_t resident_il,
+                 int64_t cus) {
     const Layout L = layout_of(H);
     Plan pl{};
     pl.block_threads = L.waves == 1 ? 256 : 64 * L.waves;
+    // large launches of the contiguous ops: interleaved rows, one-slot ring
+    const bool il_big = !interleaved(op) && resident_il > 0 &&
+                        rows >= (ADALN_CONTIG_INTERLEAVE_MIN_ELEMS + H - 1) / H;
+    const bool il = interleaved(op) || il_big;
     // Interleaved ops with many rows per group: the one-slot ring (more resident
     // groups, the latency covered by the other groups) streams faster; with few
     // rows per group the deeper ring does.  Contiguous four-wave RMS rows: the other
     // way round, the one-slot ring only for launches of one or two rows per group
     // (with the gate it measured slower; tuning; the bits never depend on it).
-    pl.shallow = resident_shallow > 0 &&
-                 (interleaved(op) ? rows >= ADALN_SHALLOW_ROWS_PER_GROUP * resident
-                                  : L.waves == 4 && !op_gated(op) &&
-                                        rows <= ADALN_CONTIG_SHALLOW_MAX_ROWS_PER_GROUP *
-                                                    resident_shallow);
-    if (pl.shallow) resident = resident_shallow;
+    pl.shallow = il_big ||
+                 (resident_shallow > 0 &&
+                  (interleaved(op) ? rows >= ADALN_SHALLOW_ROWS_PER_GROUP * resident
+                                   : L.waves == 4 && !op_gated(op) &&
+                                         rows <= ADALN_CONTIG_SHALLOW_MAX_ROWS_PER_GROUP *
+                                                     resident_shallow));
+    if (pl.shallow) resident = il_big ? resident_il : resident_shallow;
     const int S = pl.shallow ? 1 : ring_slots(L.waves, L.chunks, op_gated(op));
     pl.slots = S;
-    pl.ring = pl.shallow ? 1 : 0;
-    if (interleaved(op)) {
+    pl.ring = il_big ? 3 : pl.shallow ? 1 : 0;
+    if (il) {
         // one group per resident group slot (at most one per row); a group's ring
         // slots past its last row skip their arithmetic.  With several batch entries
         // and enough groups, each entry gets its own share of the groups, so that a
@@ -756,7 +774,7 @@ Plan plan_launch(Op op, int64_t rows, int64_t H, int64_t T, int64_t resident,
         // Ungated four-wave rows: the two-row ring instead of the deeper one when it
         // leaves the most loaded CU fewer rows (its groups spread over the CUs more
         // evenly), weighing a two-row ring's row 3.5% dearer (measured at 65536 rows).
-        if (!pl.shallow && !interleaved(op) && L.waves == 4 && !op_gated(op) &&
+        if (!pl.shallow && L.waves == 4 && !op_gated(op) &&
             resident_two > 0 && cus > 0 && S > 2) {
             const int64_t per2 = per_of(resident_two, 2);
             const int64_t g2 = (rows + per2 - 1) / per2, g = (rows + per - 1) / per;
@@ -778,8 +796,8 @@ Plan plan_launch(Op op, int64_t rows, int64_t H, int64_t T, int64_t resident,
     return pl;
 }
 
-Plan decide(Op op, int64_t rows, int64_t H, int64_t T, const int64_t resident[3], int64_t cus) {
-    return plan_launch(op, rows, H, T, resident[0], resident[1], resident[2], cus);
+Plan decide(Op op, int64_t rows, int64_t H, int64_t T, const int64_t resident[4], int64_t cus) {
+    return plan_launch(op, rows, H, T, resident[0], resident[1], resident[2], resident[3], cus);
 }
 
 namespace {
@@ -796,7 +814,7 @@ KernelFn pick_op(Op op, const Layout& L, bool weight, int ring) {
 }  // namespace
 
 bool device_plan(Op op, int64_t rows, int64_t H, int64_t T, bool weight, Plan* pl,
-                 int64_t resident[3], int64_t* cus_out) {
+                 int64_t resident[4], int64_t* cus_out) {
     const Layout L = layout_of(H);
     KernelFn deep = pick_op(op, L, weight, 0);
     if (!deep) return false;
@@ -810,20 +828,16 @@ bool device_plan(Op op, int64_t rows, int64_t H, int64_t T, bool weight, Plan* p
         return false;
     }
     resident[0] = (int64_t)cus * blocks_per_cu * groups_per_block;
-    resident[1] = resident[2] = 0;
-    // an optional kernel whose query fails is not used; its error is cleared so that
-    // the launch reports only its own
-    KernelFn shallow = pick_op(op, L, weight, 1), two = pick_op(op, L, weight, 2);
-    int bpc = 0, c2 = 0;
-    if (shallow) {
-        if (occupancy(reinterpret_cast<const void*>(shallow), block, &bpc, &c2))
-            resident[1] = (int64_t)c2 * bpc * groups_per_block;
-        else
-            (void)hipGetLastError();
-    }
-    if (two) {
-        if (occupancy(reinterpret_cast<const void*>(two), block, &bpc, &c2))
-            resident[2] = (int64_t)c2 * bpc * groups_per_block;
+    // the optional kernels (one-slot ring, two-row ring, interleaved one-slot ring):
+    // one whose query fails is not used, and its error is cleared so that the launch
+    // reports only its own
+    for (int ring = 1; ring <= 3; ++ring) {
+        resident[ring] = 0;
+        KernelFn fn = pick_op(op, L, weight, ring);
+        int bpc = 0, c2 = 0;
+        if (!fn) continue;
+        if (occupancy(reinterpret_cast<const void*>(fn), block, &bpc, &c2))
+            resident[ring] = (int64_t)c2 * bpc * groups_per_block;
         else
             (void)hipGetLastError();
     }
@@ -835,7 +849,7 @@ bool device_plan(Op op, int64_t rows, int64_t H, int64_t T, bool weight, Plan* p
 hipError_t launch(Op op, const Params& p_in, hipStream_t stream) {
     const bool weight = p_in.weight != nullptr;
     Plan pl;
-    int64_t resident[3], cus = 0;
+    int64_t resident[4], cus = 0;
     if (!device_plan(op, p_in.rows, p_in.H, p_in.T, weight, &pl, resident, &cus))
         return hipErrorInvalidDeviceFunction;
     if (pl.blocks > 0x7FFFFFFF || pl.groups > 0x7FFFFFFF) return hipErrorInvalidValue;

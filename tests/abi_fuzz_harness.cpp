@@ -36,7 +36,7 @@ int main() {
             case 6: st = adaln_check_residual_gate_channel_first(ptr(), ptr(), ptr(), (adaln_bf16*)ptr(), B, H, T, s0); break;
             default: {
                 int64_t out[11];
-                const int64_t res[3] = {s0, s1, s2};
+                const int64_t res[4] = {s0, s1, s2, pick()};
                 st = adaln_diag_launch_plan((int)(rng() % 7) - 1, B, H, T, res, pick(), out);
                 if (st == ADALN_OK) {
                     // a plan has groups, groups per block and rows per block
@@ -78,8 +78,8 @@ int main() {
         if (st == ADALN_OK) ++acc2;
         int64_t out[11];
         if (B > 0 && T > 0 && B <= INT64_MAX / T) {
-            const int64_t res[3] = {1 + (int64_t)(rng() % 8192), (int64_t)(rng() % 8192),
-                                    (int64_t)(rng() % 8192)};
+            const int64_t res[4] = {1 + (int64_t)(rng() % 8192), (int64_t)(rng() % 8192),
+                                    (int64_t)(rng() % 8192), (int64_t)(rng() % 8192)};
             (void)adaln_diag_launch_plan((int)(rng() % 5), B * T, H, T, res,
                                          (int64_t)(rng() % 512), out);
         }

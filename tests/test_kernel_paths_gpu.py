@@ -144,3 +144,44 @@ def test_device_plan_rings(op, rows, T, H, ring):
     plan = A.adaln_diag_device_plan(op, rows, H, T, op in ("rms", "rg"))
     assert plan["ring"] == ring, plan
     assert plan["resident"][0] >= 1 and plan["cus"] >= 1
+
+
+@pytest.mark.parametrize("op,B,T,H", [("rms", 1, 16384, 4096), ("rg", 2, 8192, 4096),
+                                      ("rms", 1, 21846, 3072), ("rg", 1, 65536, 1024)])
+def test_large_launches_take_interleaved_rows(op, B, T, H):
+    """From 2^26 elements per launch the RMS ops take the one-slot ring on interleaved
+    rows (asserted from the device plan first); sampled rows alone equal the rows in
+    the batch, and both equal the oracle."""
+    rows = B * T
+    weight = op == "rms"
+    plan = A.adaln_diag_device_plan(op, rows, H, T, weight)
+    assert plan["ring"] == 3 and plan["slots"] == 1 and plan["step"] == plan["gpb"], plan
+    say(f"[paths] interleaved large {op} B={B} T={T} H={H}")
+    gen = torch.Generator(device="cuda")
+    gen.manual_seed(rows + H)
+    x = torch.randn((B, T, H), generator=gen, device="cuda").to(torch.bfloat16)
+    res = torch.randn((B, T, H), generator=gen, device="cuda").to(torch.bfloat16)
+    rng = np.random.default_rng(H)
+    g = dev(synth.normal_bf16(rng, (B, H), 0.1))
+    w = dev(synth.normal_bf16(rng, (H,), 0.02, 1.0)) if weight else None
+    sc = dev(synth.normal_bf16(rng, (B, H), 0.1))
+    sh = dev(synth.normal_bf16(rng, (B, H), 0.1))
+    out = run(op, x, res, g, w, sc, sh)
+    hv = [None if t is None else host(t) for t in (g, w, sc, sh)]
+    for b in range(B):
+        ts = np.random.default_rng(b).choice(T, size=32, replace=False)
+        idx = torch.from_numpy(ts).cuda()
+        vb = [None if t is None else t[b:b + 1] for t in (g, sc, sh)]
+        for t in ts[:8]:  # alone
+            alone = run(op, x[b:b + 1, t:t + 1].contiguous(), res[b:b + 1, t:t + 1].contiguous(),
+                        vb[0], w, vb[1], vb[2])
+            for u, v in zip(out, alone):
+                assert torch.equal(u[b, t].view(torch.int16), v[0, 0].view(torch.int16)), (b, t)
+        xs, rs = host(x[b][idx])[None], host(res[b][idx])[None]
+        hb = [None if t is None else t[b:b + 1] for t in (hv[0], hv[2], hv[3])]
+        if op == "rms":
+            want = [O.rmsnorm_scale_shift(xs, hv[1], hb[1], hb[2], EPS)]
+        else:
+            want = list(O.residual_gate_rmsnorm_scale_shift(rs, xs, hb[0], hv[1], hb[1], hb[2], EPS))
+        for u, wt in zip(out, want):
+            assert_bits_equal(host(u[b][idx])[None], wt, f"{op} large, entry {b}")

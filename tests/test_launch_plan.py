@@ -4,7 +4,8 @@ exactly once; the grid and ring follow the documented rules; a group given to on
 batch entry stays in it; a contiguous group's rows stay within 32-bit byte offsets.
 The plan is the library's own host function (through the launch-plan diagnostic),
 fed with resident counts like a device's: row groups with the default ring, the
-one-slot ring and the two-row ring, and the CU count."""
+one-slot ring, the two-row ring and the one-slot ring on interleaved rows (the
+RMS ops' large launches), and the CU count."""
 import numpy as np
 import pytest
 
@@ -12,10 +13,11 @@ import diffusion_dit_adaln_amd as A
 
 OPS = ["ln", "rms", "rg", "rgln", "lnq"]
 INTERLEAVED = {"ln", "rgln", "lnq"}
-# (deep, one-slot, two-row, CUs)
-RESIDENT = [(1024, 1536, 1792, 256), (768, 0, 0, 256), (256, 512, 0, 64), (1, 1, 0, 1),
-            (7, 0, 0, 7), (2560, 2560, 0, 256), (1024, 1536, 1280, 256), (1024, 1536, 1792, 0),
-            (1024, 1536, 1280, 3)]
+# (deep, one-slot, two-row, interleaved one-slot, CUs)
+RESIDENT = [(1024, 1536, 1792, 1536, 256), (768, 0, 0, 0, 256), (256, 512, 0, 512, 64),
+            (1, 1, 0, 1, 1), (7, 0, 0, 0, 7), (2560, 2560, 0, 2560, 256),
+            (1024, 1536, 1280, 0, 256), (1024, 1536, 1792, 1536, 0), (1024, 1536, 1280, 1280, 3)]
+BIG = 1 << 26  # elements per launch from which the RMS ops interleave
 # (rows, T): one batch entry, a few long ones, many short ones
 SHAPES = [(1, 1), (3, 1), (7, 7), (7, 1), (100, 100), (100, 25), (4216, 4216), (4216, 527),
           (9216, 4608), (9216, 9216), (30001, 1579), (524287, 524287), (524288, 4096),
@@ -42,8 +44,8 @@ def rows_of(plan, rows):
 @pytest.mark.parametrize("res", RESIDENT)
 def test_every_row_exactly_once(op, H, shape, res):
     rows, T = shape
-    resident, resident_shallow, resident_two, cus = res
-    plan = A.adaln_diag_launch_plan(op, rows, H, T, res[:3], cus)
+    resident, resident_shallow, resident_two, resident_il, cus = res
+    plan = A.adaln_diag_launch_plan(op, rows, H, T, res[:4], cus)
     w, _, _ = A.adaln_reduction_layout(H)
     visited, group = rows_of(plan, rows)
     assert visited.size == rows
@@ -51,10 +53,13 @@ def test_every_row_exactly_once(op, H, shape, res):
     B = rows // T
     assert plan["block_threads"] == (256 if w == 1 else 64 * w)
     assert plan["blocks"] == ((plan["groups"] + 3) // 4 if w == 1 else plan["groups"])
-    if op in INTERLEAVED:
-        shallow = resident_shallow > 0 and rows >= 3 * resident
-        assert plan["shallow"] == shallow and plan["ring"] == (1 if shallow else 0)
-        G = min(rows, resident_shallow if shallow else resident)
+    # large launches of the RMS ops take the one-slot ring on interleaved rows
+    il_big = op not in INTERLEAVED and resident_il > 0 and rows >= -(-BIG // H)
+    if op in INTERLEAVED or il_big:
+        shallow = il_big or (resident_shallow > 0 and rows >= 3 * resident)
+        ring = 3 if il_big else 1 if shallow else 0
+        assert plan["shallow"] == shallow and plan["ring"] == ring
+        G = min(rows, resident_il if il_big else resident_shallow if shallow else resident)
         per_entry = min(G // B, T) if B > 1 else 0
         assert plan["group_stride"] == 1 and plan["step"] == plan["gpb"]
         if per_entry > 0 and 16 * (G - per_entry * B) <= G:
@@ -105,6 +110,27 @@ def test_two_row_ring_where_it_spreads_groups_more_evenly():
     assert A.adaln_diag_launch_plan("rms", 8192, 4096, 8192, (1024, 1536, 1792), 256)["ring"] == 0
     # never for the gated op
     assert A.adaln_diag_launch_plan("rg", 8192, 4096, 8192, res, 256)["ring"] == 0
+
+
+def test_large_rms_launches_take_interleaved_rows():
+    # from 2^26 elements per launch the RMS ops (with and without the gate) take the
+    # one-slot ring on interleaved rows, given that kernel's resident count
+    res = (1024, 1536, 1280, 1536)
+    for op in ("rms", "rg"):
+        for rows, H in ((16384, 4096), (8192, 8192), (21846, 3072), (65536, 1024)):
+            plan = A.adaln_diag_launch_plan(op, rows, H, rows, res, 256)
+            assert plan["ring"] == 3 and plan["slots"] == 1 and plan["shallow"]
+            assert plan["groups"] == 1536 and plan["step"] == 1536 and plan["group_stride"] == 1
+        # one row fewer: contiguous ranges
+        assert A.adaln_diag_launch_plan(op, 16383, 4096, 16383, res, 256)["ring"] != 3
+        assert A.adaln_diag_launch_plan(op, 21845, 3072, 21845, res, 256)["ring"] != 3
+        # without that kernel's resident count: never
+        assert A.adaln_diag_launch_plan(op, 65536, 4096, 65536, res[:3], 256)["ring"] != 3
+    # two batch entries: each entry its own share of the groups
+    plan = A.adaln_diag_launch_plan("rg", 2 * 8192, 4096, 8192, res, 256)
+    assert (plan["ring"], plan["groups"], plan["gpb"], plan["blk_rows"]) == (3, 1536, 768, 8192)
+    # the LayerNorm ops are interleaved at any size and never take ring 3
+    assert A.adaln_diag_launch_plan("ln", 65536, 4096, 65536, res, 256)["ring"] == 1
 
 
 def test_interleaved_batch_entries_get_their_own_groups():

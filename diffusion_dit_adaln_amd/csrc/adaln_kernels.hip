@@ -23,11 +23,13 @@
 // at most as many as can be resident at once.  A group owns either a contiguous
 // range of rows or every G-th row (interleaved; then the groups together stream a
 // contiguous band of the tensor at any moment; with several batch entries each
-// entry can get its own share of the groups, so that no group changes entry).  It keeps the per-column constants
-// of its current batch entry in registers (bf16(1 + scale), shift, weight, gate:
-// computed once per batch entry, not once per row) and keeps its next rows' loads
-// in flight (non-temporal 16-byte loads) while it reduces the current one, so HBM
-// traffic never waits on the reduction.
+// entry can get its own share of the groups, so that no group changes entry).  The
+// LayerNorm ops are interleaved; the RMS ops take contiguous ranges, and interleaved
+// rows with a one-slot ring from 2^26 elements per launch on.  A group keeps the
+// per-column constants of its current batch entry in registers (bf16(1 + scale),
+// shift, weight, gate: computed once per batch entry, not once per row) and keeps
+// its next rows' loads in flight (non-temporal 16-byte loads) while it reduces the
+// current one, so HBM traffic never waits on the reduction.
 #include <hip/hip_runtime.h>
 #include <stdint.h>
 
@@ -52,7 +54,8 @@
 // Row assignment per op (never changes the numerics): interleaved (group g takes
 // rows g, g + G, ...) or contiguous ranges.  Measured on MI355X: the LayerNorm ops
 // gain from the interleaved assignment (more groups, shorter chains), the RMS ops
-// stream slightly faster over contiguous ranges.
+// stream slightly faster over contiguous ranges below 2^26 elements per launch
+// (above, see ADALN_CONTIG_INTERLEAVE_MIN_ELEMS).
 #ifndef ADALN_INTERLEAVE_LN
 #define ADALN_INTERLEAVE_LN 1  // LayerNorm and LayerNorm + FP8
 #endif

@@ -147,7 +147,8 @@ def test_device_plan_rings(op, rows, T, H, ring):
 
 
 @pytest.mark.parametrize("op,B,T,H", [("rms", 1, 16384, 4096), ("rg", 2, 8192, 4096),
-                                      ("rms", 1, 21846, 3072), ("rg", 1, 65536, 1024)])
+                                      ("rms", 1, 21846, 3072), ("rg", 1, 65536, 1024),
+                                      ("rms", 1, 16353, 4104), ("rg", 1, 65028, 1032)])
 def test_large_launches_take_interleaved_rows(op, B, T, H):
     """From 2^26 elements per launch the RMS ops take the one-slot ring on interleaved
     rows (asserted from the device plan first); sampled rows alone equal the rows in

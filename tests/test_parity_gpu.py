@@ -577,6 +577,20 @@ def test_channel_first_full_size():
                       "channel-first full size")
 
 
+@pytest.mark.parametrize("T", [4336, 4333, 4334, 4335])
+def test_channel_first_full_size_misaligned_rows(T):
+    """The token sweep's workloads at full size: rows of res/out off the 128-byte lines
+    (T = 4336: 16-byte aligned; the others ragged), out of place and in place."""
+    wl = synth.cf_tokens(T)
+    say(f"[parity] channel-first {wl.res.shape}")
+    want = O.residual_gate_channel_first(wl.res, wl.update, wl.gate)
+    got = A.adaln_residual_gate_channel_first(dev(wl.res), dev(wl.update), dev(wl.gate))
+    assert_bits_equal(host(got), want, f"channel-first T={T}")
+    rd = dev(wl.res)
+    A.adaln_residual_gate_channel_first(rd, dev(wl.update), dev(wl.gate), out=rd)
+    assert_bits_equal(host(rd), want, f"channel-first T={T} in place")
+
+
 @pytest.mark.parametrize("B,H,T", [(1, 8, 8), (2, 72, 40), (3, 136, 200), (1, 64, 64),
                                    (2, 3072, 72), (1, 520, 4104),
                                    # token counts with rows of res/out 8-, 4- or 2-byte aligned

@@ -19,6 +19,7 @@ value, -0 included) and its sum as round(res + round(1 * x)) (x is a bf16 value)
 from concurrent.futures import ThreadPoolExecutor
 
 import numpy as np
+import pytest
 import torch
 
 from oracle import oracle as O
@@ -101,3 +102,22 @@ def test_sums_all_bf16_pairs():
         ref = _rb((_f64(a) + _f64(b)).astype(np.float32))
         return _same(got, ref)
     _run(check)
+
+
+# --------------------------------------------------------------------------
+# brute force over the two exhaustive row domains (tests/brute_domains.py)
+# --------------------------------------------------------------------------
+@pytest.mark.parametrize("name", ["h8", "h16"])
+def test_brute_force_full_domains(name):
+    """Every row of 8 values over {0, +-0.5, +-1, +-2, 3} and of 16 values over
+    {-1, 0, 1}: the oracle's LayerNorm and RMSNorm outputs lie within 2 bf16 ulp of
+    the float64 definition (with the LayerNorm floor of the mean's own error), and
+    its modulated outputs hash to the digests stored in tests/golden, which the GPU
+    test compares the device's outputs with.  Worker processes, no GPU."""
+    from tests import brute_domains as D
+
+    d_ln, d_rms, bad = D.oracle_digests(name, check=True)
+    assert bad == 0, f"{bad} norm outputs outside the float64 bound"
+    g = D.golden_digests()
+    assert (d_ln, d_rms) == (g[(name, "ln")], g[(name, "rms")])
+

@@ -212,6 +212,30 @@ def test_brute_force_rows(H, alphabet, stride):
                       f"rms H={H}")
 
 
+@pytest.mark.parametrize("name", ["h8", "h16"])
+def test_brute_force_full_domains(name):
+    """Every row of 8 values over {0, +-0.5, +-1, +-2, 3} (16.8 M rows) and of 16
+    values over {-1, 0, 1} (43 M rows): the device's LayerNorm+modulate and
+    RMSNorm+scale/shift outputs, in row order, hash to the oracle's digests stored in
+    tests/golden (written by a script that calls only the oracle; the CPU suite
+    recomputes them from the oracle and checks them against the float64 definition)."""
+    import hashlib
+
+    from tests import brute_domains as D
+
+    g = D.golden_digests()
+    H, _ = D.DOMAINS[name]
+    say(f"[parity] brute force {name}: {D.size(name)} rows of H={H}")
+    sc, sh, w = (dev(v) for v in D.vectors(H))
+    h_ln, h_rms = hashlib.sha256(), hashlib.sha256()
+    for lo, hi in D.chunks(name):
+        x = dev(D.rows(name, lo, hi)[None])
+        h_ln.update(host(A.adaln_layernorm_modulate(x, sc, sh, EPS)).tobytes())
+        h_rms.update(host(A.adaln_rmsnorm_scale_shift(x, w, sc, sh, EPS)).tobytes())
+    assert h_ln.hexdigest() == g[(name, "ln")], "LayerNorm+modulate differs from the oracle"
+    assert h_rms.hexdigest() == g[(name, "rms")], "RMSNorm+scale/shift differs from the oracle"
+
+
 # Row counts large enough that the interleaved ops take their one-slot ring (at
 # least three rows per resident row group), for one-, two- and four-wave rows with
 # and without a ragged last chunk.

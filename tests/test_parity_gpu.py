@@ -212,6 +212,42 @@ def test_brute_force_rows(H, alphabet, stride):
                       f"rms H={H}")
 
 
+@pytest.mark.parametrize("op", ["ln", "rms"])
+def test_norm_outputs_near_torch_eager(op):
+    """A loose cross-check against an implementation of another order (never a gate of
+    the numerics): with zero modulation the outputs are the norm outputs, and they lie
+    within 2 bf16 ulp of torch's own eager layer_norm / rms_norm computed in binary32 on
+    the device and rounded to bf16 (for LayerNorm plus the floor of the mean's own
+    error, as in the oracle's float64 pins)."""
+    import torch.nn.functional as Fn
+
+    from tests.test_oracle_pins import KAPPA, U32, ulp_bf16
+
+    wl = synth.WORKLOADS["ln_2x4608x3072" if op == "ln" else "rms_1x4216x4096"]()
+    B, T, H = wl.x.shape
+    say(f"[parity] {op} against torch eager {wl.x.shape}")
+    x = dev(wl.x)
+    z = torch.zeros((B, H), dtype=torch.bfloat16, device="cuda")
+    xf = x.float()
+    if op == "ln":
+        ours = A.adaln_layernorm_modulate(x, z, z, EPS)
+        ref = Fn.layer_norm(xf, (H,), eps=EPS).to(torch.bfloat16)
+        mu = xf.mean(dim=-1, keepdim=True)
+        sd = (xf - mu).pow(2).mean(dim=-1, keepdim=True).sqrt()
+        floor = (KAPPA * U32 * (mu.abs() + sd) / (sd + 1e-30)).double().cpu().numpy()
+    else:
+        w = dev(wl.weight)
+        ours = A.adaln_rmsnorm_scale_shift(x, w, z, z, EPS)
+        ref = Fn.rms_norm(xf, (H,), weight=w.float(), eps=EPS).to(torch.bfloat16)
+        floor = 0.0
+    a = synth.bf16_bits_to_f32(host(ours)).astype(np.float64)
+    b = synth.bf16_bits_to_f32(host(ref)).astype(np.float64)
+    tol = 2.0 * ulp_bf16(b) + floor
+    bad = np.abs(a - b) > tol
+    assert not bad.any(), (int(bad.sum()), float((np.abs(a - b) / tol).max()))
+    say(f"[parity] {op}: {float((a == b).mean()):.4f} of the outputs equal torch's bit for bit")
+
+
 @pytest.mark.parametrize("name", ["h8", "h16"])
 def test_brute_force_full_domains(name):
     """Every row of 8 values over {0, +-0.5, +-1, +-2, 3} (16.8 M rows) and of 16

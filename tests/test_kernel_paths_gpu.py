@@ -186,3 +186,34 @@ def test_large_launches_take_interleaved_rows(op, B, T, H):
             want = list(O.residual_gate_rmsnorm_scale_shift(rs, xs, hb[0], hv[1], hb[1], hb[2], EPS))
         for u, wt in zip(out, want):
             assert_bits_equal(host(u[b][idx])[None], wt, f"{op} large, entry {b}")
+
+
+@pytest.mark.parametrize("op,H", [("rms", 1024), ("rg", 1024), ("rg", 4096)])
+def test_large_launch_every_row_its_own_entry(op, H):
+    """The interleaved rows of a large RMS launch when every row is its own batch entry
+    ([R, 1, H], per-row vectors, so a group reloads its constants at every row): the
+    device plan takes ring 3 over one interleave of all rows, and sampled rows equal
+    the oracle with their own vectors."""
+    R = -(-(1 << 26) // H)
+    weight = op == "rms"
+    plan = A.adaln_diag_device_plan(op, R, H, 1, weight)
+    assert plan["ring"] == 3 and plan["gpb"] == plan["groups"], plan
+    say(f"[paths] interleaved large [R,1,H] {op} R={R} H={H}")
+    gen = torch.Generator(device="cuda")
+    gen.manual_seed(R + H)
+    x = torch.randn((R, 1, H), generator=gen, device="cuda").to(torch.bfloat16)
+    res = torch.randn((R, 1, H), generator=gen, device="cuda").to(torch.bfloat16)
+    vec = lambda: (0.1 * torch.randn((R, H), generator=gen, device="cuda")).to(torch.bfloat16)
+    g, sc, sh = vec(), vec(), vec()
+    w = dev(synth.normal_bf16(np.random.default_rng(H), (H,), 0.02, 1.0)) if weight else None
+    out = run(op, x, res, g, w, sc, sh)
+    wv = None if w is None else host(w)
+    for r in np.random.default_rng(R).choice(R, size=48, replace=False):
+        xs, rs = host(x[r:r + 1]), host(res[r:r + 1])
+        gs, ss, hs = host(g[r:r + 1]), host(sc[r:r + 1]), host(sh[r:r + 1])
+        if op == "rms":
+            want = [O.rmsnorm_scale_shift(xs, wv, ss, hs, EPS)]
+        else:
+            want = list(O.residual_gate_rmsnorm_scale_shift(rs, xs, gs, wv, ss, hs, EPS))
+        for u, wt in zip(out, want):
+            assert_bits_equal(host(u[r:r + 1]), wt, f"{op} [R,1,{H}] row {r}")

@@ -1,4 +1,4 @@
-"""Seeded random shapes for every fused op against the oracle, bit for bit (GPU).
+"""Seeded random shapes for every op against the oracle, bit for bit (GPU).
 
 Each case draws an op (LN, RMS with and without weight, residual-gate RMS with and
 without weight, residual-gate LN, LN+FP8), a hidden size (any multiple of 8 up to
@@ -116,3 +116,63 @@ def test_random_shape(seed):
     want = oracle(op, xs, rs, per_row(g), w, per_row(sc), per_row(sh), eps, qscale)
     for u, v in zip(got, want):
         assert_bits_equal(u.reshape(B * T, H)[rows][:, None], v, f"seed {seed} (sampled)")
+
+
+@pytest.mark.parametrize("seed", range(24))
+def test_random_qk(seed):
+    """QK-norm+RoPE: random token counts, Q and K head counts (either side may be
+    absent), packed-QKV strided views or contiguous tensors, weights present or not,
+    eps and scales."""
+    rng = np.random.default_rng(5000 + seed)
+    T = int(rng.integers(1, 9000))
+    hq, hk = int(rng.integers(0, 49)), int(rng.integers(0, 49))
+    if hq + hk == 0:
+        hq = 1
+    eps = float(rng.choice([1e-6, 1e-5, 0.25]))
+    sigma = float(rng.choice([1.0, 1e-3, 1e3]))
+    packed = bool(rng.integers(0, 2))
+    say(f"[random] qk seed={seed} T={T} hq={hq} hk={hk} packed={packed} eps={eps} sigma={sigma}")
+    if packed:
+        hmax = max(hq, hk)
+        qkv = synth.normal_bf16(rng, (T, 3, hmax, 128), sigma)
+        d = dev(qkv)
+        q, k = qkv[:, 0, :hq], qkv[:, 1, :hk]
+        qd, kd = d[:, 0, :hq], d[:, 1, :hk]
+    else:
+        q, k = synth.normal_bf16(rng, (T, hq, 128), sigma), synth.normal_bf16(rng, (T, hk, 128), sigma)
+        qd, kd = dev(q), dev(k)
+    wq = synth.normal_bf16(rng, (128,), 0.02, 1.0) if rng.integers(0, 2) else None
+    wk = synth.normal_bf16(rng, (128,), 0.02, 1.0) if rng.integers(0, 2) else None
+    ang = rng.uniform(-np.pi, np.pi, (T, 64))
+    cs = np.concatenate([np.cos(ang), np.sin(ang)], 1).astype(np.float32)
+    qo, ko = A.adaln_qk_rmsnorm_rope(qd, kd, None if wq is None else dev(wq),
+                                     None if wk is None else dev(wk), torch.from_numpy(cs).cuda(),
+                                     eps)
+    qo0, ko0 = O.qk_rmsnorm_rope(np.ascontiguousarray(q), np.ascontiguousarray(k), wq, wk, cs, eps)
+    assert_bits_equal(host(qo), qo0, f"seed {seed} q")
+    assert_bits_equal(host(ko), ko0, f"seed {seed} k")
+
+
+@pytest.mark.parametrize("seed", range(24))
+def test_random_channel_first(seed):
+    """Channel-first residual gate: random batch, hidden (multiple of 8) and token
+    counts (every residue mod 8 and mod 64), per-entry, shared or strided gates, out of
+    place and in place."""
+    rng = np.random.default_rng(7000 + seed)
+    B = int(rng.choice([1, 2, 3]))
+    H = 8 * int(rng.integers(1, 513))
+    T = int(rng.integers(1, max(2, (4 << 20) // (B * H))))
+    vk = str(rng.choice(["per_entry", "shared", "strided"]))
+    in_place = bool(rng.integers(0, 2))
+    say(f"[random] cf seed={seed} B={B} H={H} T={T} gate={vk} in_place={in_place}")
+    res = synth.normal_bf16(rng, (B, H, T))
+    upd = synth.normal_bf16(rng, (B, T, H))
+    (g, gd), = vectors(rng, B, H, vk, 1)
+    want = O.residual_gate_channel_first(res, upd, g)
+    rd = dev(res)
+    if in_place:
+        A.adaln_residual_gate_channel_first(rd, dev(upd), gd, out=rd)
+        got = rd
+    else:
+        got = A.adaln_residual_gate_channel_first(rd, dev(upd), gd)
+    assert_bits_equal(host(got), want, f"seed {seed}")

@@ -12,7 +12,7 @@ import os
 import torch
 
 _PKG = os.path.dirname(os.path.abspath(__file__))
-ABI_VERSION = 10
+ABI_VERSION = 11
 
 STATUS_NAMES = {0: "ADALN_OK", 1: "ADALN_ERR_NULL", 2: "ADALN_ERR_SHAPE", 3: "ADALN_ERR_ALIGN",
                 4: "ADALN_ERR_STRIDE", 5: "ADALN_ERR_OVERLAP", 6: "ADALN_ERR_VALUE",
@@ -398,13 +398,14 @@ PLAN_FIELDS = ("shallow", "slots", "ring", "groups", "gpb", "blk_rows", "group_s
 def adaln_diag_launch_plan(op: str, rows: int, H: int, T: int, resident, cus: int = 0) -> dict:
     """The fused launch's row-group plan for B = rows / T batch entries, given what fits
     on the device at once (host only; see the header): resident = (groups with the
-    default ring, with the one-slot ring, with the two-row ring, with the one-slot ring
-    on interleaved rows of the RMS ops); missing trailing counts are 0, so a single
-    number n means (n, 0, 0, 0)."""
+    default ring, with the one-slot ring, with the two-row ring); missing trailing
+    counts are 0, so a single number n means (n, 0, 0)."""
     lib = load_library()
     if isinstance(resident, int):
         resident = (resident,)
-    res = (ctypes.c_int64 * 4)(*(list(resident) + [0] * (4 - len(resident))))
+    if len(resident) > 3:
+        raise ValueError("at most three resident counts")
+    res = (ctypes.c_int64 * 3)(*(list(resident) + [0] * (3 - len(resident))))
     out = (ctypes.c_int64 * len(PLAN_FIELDS))()
     _check(lib.adaln_diag_launch_plan(OPS[op], rows, H, T, res, cus, out),
            "adaln_diag_launch_plan")
@@ -416,7 +417,7 @@ def adaln_diag_device_plan(op: str, rows: int, H: int, T: int, weight: bool = Fa
     count it was made from (keys "resident", "cus")."""
     lib = load_library()
     out = (ctypes.c_int64 * len(PLAN_FIELDS))()
-    res = (ctypes.c_int64 * 4)()
+    res = (ctypes.c_int64 * 3)()
     cus = ctypes.c_int64()
     _check(lib.adaln_diag_device_plan(OPS[op], rows, H, T, int(bool(weight)), out, res,
                                       ctypes.byref(cus)), "adaln_diag_device_plan")

@@ -457,10 +457,13 @@ adaln_status adaln_diag_launch_plan(int op, int64_t rows, int64_t H, int64_t T,
     // them stay in range only below that
     constexpr int64_t kMaxResident = 0x7FFFFFFF;
     if (resident[0] < 1) return ADALN_ERR_VALUE;
-    for (int i = 0; i < 4; ++i)
+    for (int i = 0; i < 3; ++i)
         if (resident[i] < 0 || resident[i] > kMaxResident) return ADALN_ERR_VALUE;
     if (cus < 0 || cus > kMaxResident) return ADALN_ERR_VALUE;
-    write_plan(adaln::decide(static_cast<adaln::Op>(op), rows, H, T, resident, cus), out);
+    const adaln::Plan pl = adaln::decide(static_cast<adaln::Op>(op), rows, H, T, resident, cus);
+    // a launch whose grid would pass 2^32 work-items is refused (rows past 2^55 bytes)
+    if (pl.blocks * pl.block_threads > int64_t(0xFFFFFFFF)) return ADALN_ERR_SHAPE;
+    write_plan(pl, out);
     return ADALN_OK;
 }
 
@@ -468,13 +471,13 @@ adaln_status adaln_diag_device_plan(int op, int64_t rows, int64_t H, int64_t T, 
                                     int64_t* out, int64_t* resident_out, int64_t* cus_out) {
     ADALN_TRY(check_plan_args(op, rows, H, T, out));
     adaln::Plan pl;
-    int64_t resident[4], cus = 0;
+    int64_t resident[3], cus = 0;
     if (!adaln::device_plan(static_cast<adaln::Op>(op), rows, H, T, weight != 0, &pl, resident,
                             &cus))
         return ADALN_ERR_LAUNCH;
     write_plan(pl, out);
     if (resident_out)
-        for (int i = 0; i < 4; ++i) resident_out[i] = resident[i];
+        for (int i = 0; i < 3; ++i) resident_out[i] = resident[i];
     if (cus_out) *cus_out = cus;
     return ADALN_OK;
 }

@@ -105,35 +105,34 @@ bool occupancy(const void* fn, int block, int* blocks_per_cu, int* cus);
 // How a launch of the fused kernel splits `rows` rows over row groups, given how
 // many groups fit on the device at once for the deep-ring kernel (resident) and
 // for the one-slot ring (resident_shallow; 0 if it is not available).  Group g
-// takes the rows g*group_stride + i*step below min(g*group_stride + span, rows).
+// takes the rows g*group_stride + i*step below min(g*group_stride + span, rows)
+// (within its block of rows: see Params).  Large launches take a one-shot grid
+// with more groups than fit at once.
 struct Plan {
-    bool shallow;          // a one-slot ring kernel (ring 1 or 3)
+    bool shallow;          // the one-slot ring kernel (ring 1)
     int slots;             // ring depth S
     int ring;              // the kernel instantiation: 0 default depth, 1 one slot,
-                           // 2 two rows, 3 one slot on interleaved rows (contiguous ops)
+                           // 2 two rows
     int64_t groups, gpb, blk_rows, group_stride, step, span;
     int64_t blocks;        // workgroups launched
     int block_threads;     // threads per workgroup
 };
-// resident_two: resident groups of the two-slot ring kernel, resident_il: of the
-// interleaved one-slot kernel of the contiguous ops (0: not available); cus: compute
-// units (0: unknown; the two-slot choice needs it)
+// resident_two: resident groups of the two-slot ring kernel (0: not available);
+// cus: compute units (0: unknown; the two-slot choice needs it)
 Plan plan_launch(Op op, int64_t rows, int64_t H, int64_t T, int64_t resident,
-                 int64_t resident_shallow, int64_t resident_two = 0, int64_t resident_il = 0,
-                 int64_t cus = 0);
+                 int64_t resident_shallow, int64_t resident_two = 0, int64_t cus = 0);
 
 // Launch the fused kernel for `op`; returns the HIP error of the launch.
 hipError_t launch(Op op, const Params& p, hipStream_t stream);
 
-// The plan of a launch from what fits on the device at once: resident[0..3] row
-// groups with the default ring, the one-slot ring, the two-row ring and the
-// interleaved one-slot ring of the contiguous ops (0: not available), and the CU
-// count.
-Plan decide(Op op, int64_t rows, int64_t H, int64_t T, const int64_t resident[4], int64_t cus);
+// The plan of a launch from what fits on the device at once: resident[0..2] row
+// groups with the default ring, the one-slot ring and the two-row ring (0: not
+// available), and the CU count.
+Plan decide(Op op, int64_t rows, int64_t H, int64_t T, const int64_t resident[3], int64_t cus);
 // The same plan with the resident counts of the current device (occupancy queries,
 // cached); false when a query fails.
 bool device_plan(Op op, int64_t rows, int64_t H, int64_t T, bool weight, Plan* pl,
-                 int64_t resident[4], int64_t* cus);
+                 int64_t resident[3], int64_t* cus);
 
 hipError_t launch_diag_round(const float* in, uint16_t* out, int64_t n, hipStream_t stream);
 hipError_t launch_diag_finalize(const float* in, float* out, int64_t n, int64_t H, float eps,

@@ -24,12 +24,14 @@
 // range of rows or every G-th row (interleaved; then the groups together stream a
 // contiguous band of the tensor at any moment; with several batch entries each
 // entry can get its own share of the groups, so that no group changes entry).  The
-// LayerNorm ops are interleaved; the RMS ops take contiguous ranges, and interleaved
-// rows with a one-slot ring from 2^26 elements per launch on.  A group keeps the
-// per-column constants of its current batch entry in registers (bf16(1 + scale),
-// shift, weight, gate: computed once per batch entry, not once per row) and keeps
-// its next rows' loads in flight (non-temporal 16-byte loads) while it reduces the
-// current one, so HBM traffic never waits on the reduction.
+// LayerNorm ops are interleaved; the RMS ops take contiguous ranges.  Launches of at
+// least 2^25 elements (all ops but LN+FP8) take a one-shot grid instead: every group
+// takes one ring's worth of consecutive rows and the hardware dispatches the groups
+// as slots free up, which keeps the rows in flight a compact band of the tensor.  A
+// group keeps the per-column constants of its current batch entry in registers
+// (bf16(1 + scale), shift, weight, gate: computed once per batch entry, not once per
+// row) and keeps its next rows' loads in flight (non-temporal 16-byte loads) while it
+// reduces the current one, so HBM traffic never waits on the reduction.
 #include <hip/hip_runtime.h>
 #include <stdint.h>
 
@@ -54,8 +56,7 @@
 // Row assignment per op (never changes the numerics): interleaved (group g takes
 // rows g, g + G, ...) or contiguous ranges.  Measured on MI355X: the LayerNorm ops
 // gain from the interleaved assignment (more groups, shorter chains), the RMS ops
-// stream slightly faster over contiguous ranges below 2^26 elements per launch
-// (above, see ADALN_CONTIG_INTERLEAVE_MIN_ELEMS).
+// stream slightly faster over contiguous ranges (below ADALN_ONESHOT_MIN_ELEMS).
 #ifndef ADALN_INTERLEAVE_LN
 #define ADALN_INTERLEAVE_LN 1  // LayerNorm and LayerNorm + FP8
 #endif
@@ -82,12 +83,13 @@
 #ifndef ADALN_CONTIG_SHALLOW_MAX_ROWS_PER_GROUP
 #define ADALN_CONTIG_SHALLOW_MAX_ROWS_PER_GROUP 2
 #endif
-// The contiguous ops (RMS, residual-gate RMS) take the interleaved assignment with
-// the one-slot ring from this many elements (rows * H) per launch on (measured on
-// MI355X: +4% to +11% at 2^26 elements and above for one-, two- and four-wave rows,
-// mixed below, where contiguous ranges stay).
-#ifndef ADALN_CONTIG_INTERLEAVE_MIN_ELEMS
-#define ADALN_CONTIG_INTERLEAVE_MIN_ELEMS (int64_t(1) << 26)
+// From this many elements (rows * H) per launch on, every op but LN+FP8 takes the
+// one-shot grid: one pass of the default ring per group, consecutive rows, as many
+// groups as that takes (measured on MI355X against the persistent grid: +0.7% to
+// +16% at 2^25 elements and above, for one-, two- and four-wave rows of every such
+// op; mixed or slower below; LN+FP8, bound by its arithmetic, 4-5% slower).
+#ifndef ADALN_ONESHOT_MIN_ELEMS
+#define ADALN_ONESHOT_MIN_ELEMS (int64_t(1) << 25)
 #endif
 
 namespace adaln {
@@ -602,8 +604,9 @@ __global__ __launch_bounds__(256) void diag_quant(const float4* __restrict__ in,
 // ---------------------------------------------------------------------------
 using KernelFn = void (*)(Params);
 
-template <int OP, int W, int C, bool TAIL, int RING, bool IL = interleaved(OP)>
+template <int OP, int W, int C, bool TAIL, int RING>
 KernelFn pick_weight(bool weight) {
+    constexpr bool IL = interleaved(OP);
     if constexpr (op_layernorm(OP)) {
         return fused_norm_modulate<OP, W, C, TAIL, false, IL, RING>;  // no weight
     } else {
@@ -613,17 +616,11 @@ KernelFn pick_weight(bool weight) {
 }
 
 // ring 1 (the one-slot ring) is instantiated for the interleaved ops and for the
-// ungated contiguous ops' four-wave rows, ring 2 for the latter only, ring 3 (the
-// one-slot ring on interleaved rows) for the contiguous ops' large launches; ring 0
-// is the default depth
+// ungated contiguous ops' four-wave rows, ring 2 for the latter only; ring 0 is the
+// default depth
 template <int OP, int W, int C>
 KernelFn pick_tail(bool tail, bool weight, int ring) {
     constexpr bool contig4 = !interleaved(OP) && W == 4 && !op_gated(OP);
-    if constexpr (!interleaved(OP)) {
-        if (ring == 3)
-            return tail ? pick_weight<OP, W, C, true, 1, true>(weight)
-                        : pick_weight<OP, W, C, false, 1, true>(weight);
-    }
     if constexpr (interleaved(OP) || contig4) {
         if (ring == 1)
             return tail ? pick_weight<OP, W, C, true, 1>(weight)
@@ -711,37 +708,62 @@ Layout layout_of(int64_t H) {
 }
 
 Plan plan_launch(Op op, int64_t rows, int64_t H, int64_t T, int64_t resident,
-                 int64_t resident_shallow, int64_t resident_two, int64_t resident_il,
-                 int64_t cus) {
+                 int64_t resident_shallow, int64_t resident_two, int64_t cus) {
     const Layout L = layout_of(H);
     Plan pl{};
     pl.block_threads = L.waves == 1 ? 256 : 64 * L.waves;
-    // large launches of the contiguous ops: interleaved rows, one-slot ring
-    const bool il_big = !interleaved(op) && resident_il > 0 &&
-                        rows >= (ADALN_CONTIG_INTERLEAVE_MIN_ELEMS + H - 1) / H;
-    const bool il = interleaved(op) || il_big;
+    // a grid holds fewer than 2^32 work-items
+    const int64_t max_groups =
+        int64_t(0xFFFFFFFF) / pl.block_threads * (L.waves == 1 ? 4 : 1);
+    // the most rows of a contiguous group with s ring slots: its descriptors address
+    // them with 32-bit byte offsets, and the last pass reaches s rows past its range,
+    // so (rows + s) rows stay below 2^31 bytes
+    auto max_rows = [&](int s) { return ((int64_t(0x7FFFFFFF) - 64) / (2 * H) - s) / s * s; };
+    // Large launches: the one-shot grid.  Group g takes the consecutive rows
+    // g*per .. g*per + per - 1, per = S (one pass of the default ring), unless the
+    // grid would then pass 2^32 work-items, when per grows by whole passes.  The
+    // interleaved ops' kernels address any row, so they take the same ranges.
+    if (op != OP_LNQ && rows >= (ADALN_ONESHOT_MIN_ELEMS + H - 1) / H) {
+        const int S = ring_slots(L.waves, L.chunks, op_gated(op));
+        const int64_t passes = ((rows + S - 1) / S + max_groups - 1) / max_groups;
+        int64_t per = passes * S;
+        // (only past 2^55 bytes of rows could a group need more than 32-bit offsets;
+        // the grid is then too large and the launch is refused)
+        if (!interleaved(op) && per > max_rows(S)) per = max_rows(S);
+        pl.shallow = false;
+        pl.slots = S;
+        pl.ring = 0;
+        pl.groups = (rows + per - 1) / per;
+        pl.gpb = pl.groups;
+        pl.blk_rows = rows;
+        pl.group_stride = per;
+        pl.step = 1;
+        pl.span = per;
+        pl.blocks = L.waves == 1 ? (pl.groups + 3) / 4 : pl.groups;
+        return pl;
+    }
     // Interleaved ops with many rows per group: the one-slot ring (more resident
     // groups, the latency covered by the other groups) streams faster; with few
     // rows per group the deeper ring does.  Contiguous four-wave RMS rows: the other
     // way round, the one-slot ring only for launches of one or two rows per group
     // (with the gate it measured slower; tuning; the bits never depend on it).
-    pl.shallow = il_big ||
-                 (resident_shallow > 0 &&
-                  (interleaved(op) ? rows >= ADALN_SHALLOW_ROWS_PER_GROUP * resident
-                                   : L.waves == 4 && !op_gated(op) &&
-                                         rows <= ADALN_CONTIG_SHALLOW_MAX_ROWS_PER_GROUP *
-                                                     resident_shallow));
-    if (pl.shallow) resident = il_big ? resident_il : resident_shallow;
+    pl.shallow = resident_shallow > 0 &&
+                 (interleaved(op) ? rows >= ADALN_SHALLOW_ROWS_PER_GROUP * resident
+                                  : L.waves == 4 && !op_gated(op) &&
+                                        rows <= ADALN_CONTIG_SHALLOW_MAX_ROWS_PER_GROUP *
+                                                    resident_shallow);
+    if (pl.shallow) resident = resident_shallow;
     const int S = pl.shallow ? 1 : ring_slots(L.waves, L.chunks, op_gated(op));
     pl.slots = S;
-    pl.ring = il_big ? 3 : pl.shallow ? 1 : 0;
-    if (il) {
+    pl.ring = pl.shallow ? 1 : 0;
+    if (interleaved(op)) {
         // one group per resident group slot (at most one per row); a group's ring
         // slots past its last row skip their arithmetic.  With several batch entries
         // and enough groups, each entry gets its own share of the groups, so that a
         // group never changes entry (its per-column constants are loaded once), as
         // long as the split leaves at most 1/16 of the slots idle.
-        const int64_t G = rows < resident ? rows : resident;
+        int64_t G = rows < resident ? rows : resident;
+        if (G > max_groups) G = max_groups;
         const int64_t B = rows / T;
         const int64_t per_entry = B > 1 ? (G / B < T ? G / B : T) : 0;
         if (per_entry > 0 && 16 * (G - per_entry * B) <= G) {
@@ -766,12 +788,12 @@ Plan plan_launch(Op op, int64_t rows, int64_t H, int64_t T, int64_t resident,
                          : L.waves == 2 ? ADALN_GROUP_OVERSUBSCRIBE_W2
                                         : ADALN_GROUP_OVERSUBSCRIBE_W4;
         auto per_of = [&](int64_t res, int s) {
-            const int64_t slots = res * over;
+            int64_t slots = res * over;
+            if (slots > max_groups) slots = max_groups;
             const int64_t groups0 = rows < slots ? rows : slots;
             int64_t q = (rows + groups0 - 1) / groups0;
             q = (q + s - 1) / s * s;
-            const int64_t max_q = ((int64_t(0x7FFFFFFF) - 64) / (2 * H) - s) / s * s;
-            return q < max_q ? q : max_q;
+            return q < max_rows(s) ? q : max_rows(s);
         };
         int64_t per = per_of(resident, S);
         // Ungated four-wave rows: the two-row ring instead of the deeper one when it
@@ -799,8 +821,8 @@ Plan plan_launch(Op op, int64_t rows, int64_t H, int64_t T, int64_t resident,
     return pl;
 }
 
-Plan decide(Op op, int64_t rows, int64_t H, int64_t T, const int64_t resident[4], int64_t cus) {
-    return plan_launch(op, rows, H, T, resident[0], resident[1], resident[2], resident[3], cus);
+Plan decide(Op op, int64_t rows, int64_t H, int64_t T, const int64_t resident[3], int64_t cus) {
+    return plan_launch(op, rows, H, T, resident[0], resident[1], resident[2], cus);
 }
 
 namespace {
@@ -817,7 +839,7 @@ KernelFn pick_op(Op op, const Layout& L, bool weight, int ring) {
 }  // namespace
 
 bool device_plan(Op op, int64_t rows, int64_t H, int64_t T, bool weight, Plan* pl,
-                 int64_t resident[4], int64_t* cus_out) {
+                 int64_t resident[3], int64_t* cus_out) {
     const Layout L = layout_of(H);
     KernelFn deep = pick_op(op, L, weight, 0);
     if (!deep) return false;
@@ -831,10 +853,9 @@ bool device_plan(Op op, int64_t rows, int64_t H, int64_t T, bool weight, Plan* p
         return false;
     }
     resident[0] = (int64_t)cus * blocks_per_cu * groups_per_block;
-    // the optional kernels (one-slot ring, two-row ring, interleaved one-slot ring):
-    // one whose query fails is not used, and its error is cleared so that the launch
-    // reports only its own
-    for (int ring = 1; ring <= 3; ++ring) {
+    // the optional kernels (one-slot ring, two-row ring): one whose query fails is not
+    // used, and its error is cleared so that the launch reports only its own
+    for (int ring = 1; ring <= 2; ++ring) {
         resident[ring] = 0;
         KernelFn fn = pick_op(op, L, weight, ring);
         int bpc = 0, c2 = 0;
@@ -852,10 +873,10 @@ bool device_plan(Op op, int64_t rows, int64_t H, int64_t T, bool weight, Plan* p
 hipError_t launch(Op op, const Params& p_in, hipStream_t stream) {
     const bool weight = p_in.weight != nullptr;
     Plan pl;
-    int64_t resident[4], cus = 0;
+    int64_t resident[3], cus = 0;
     if (!device_plan(op, p_in.rows, p_in.H, p_in.T, weight, &pl, resident, &cus))
         return hipErrorInvalidDeviceFunction;
-    if (pl.blocks > 0x7FFFFFFF || pl.groups > 0x7FFFFFFF) return hipErrorInvalidValue;
+    if (pl.blocks * pl.block_threads > int64_t(0xFFFFFFFF)) return hipErrorInvalidValue;
     KernelFn fn = pick_op(op, layout_of(p_in.H), weight, pl.ring);
     if (!fn) return hipErrorInvalidValue;
     Params p = p_in;

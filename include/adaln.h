@@ -90,7 +90,7 @@
 extern "C" {
 #endif
 
-#define ADALN_ABI_VERSION 10 /* 2: two waves per row for 2048 <= H < 4096;
+#define ADALN_ABI_VERSION 11 /* 2: two waves per row for 2048 <= H < 4096;
                               3: residual-gate LayerNorm, stream copy;
                               4: LayerNorm + modulate + FP8 quantisation;
                               5: per-head QK RMSNorm + RoPE;
@@ -104,7 +104,10 @@ extern "C" {
                                  plan;
                              10: the plan diagnostics take and report a fourth
                                  resident count, of the one-slot ring on interleaved
-                                 rows that large RMS launches take */
+                                 rows that large RMS launches take;
+                             11: large launches take a one-shot grid; the plan
+                                 diagnostics take and report three resident counts
+                                 again, ring kinds 0-2 */
 
 typedef uint16_t adaln_bf16; /* raw bfloat16 bits */
 
@@ -283,17 +286,22 @@ adaln_status adaln_diag_quant_fp8(const float* in, uint8_t* out, int64_t n, cons
 /* Diagnostic: the row-group plan of one launch of a fused entry point, computed on
  * the host with no device work, for given counts of what fits on the device at once.
  * op: 0 LayerNorm+modulate, 1 RMSNorm+scale/shift, 2 residual gate + RMSNorm,
- * 3 residual gate + LayerNorm, 4 LayerNorm+modulate+FP8.  resident[4]: row groups
- * resident at once with the default ring, with the one-slot ring, with the two-row
- * ring and with the one-slot ring on interleaved rows of ops 1 and 2 (0: not
- * available; resident[0] >= 1); cus: compute units (0: unknown; the two-row ring is
- * chosen only with it).  rows = B*T >= 1 with 1 <= T <= rows and rows % T == 0 (else
- * ADALN_ERR_SHAPE), H as for the entry points.  out[11] receives {one-slot ring
- * (0/1), ring slots, ring kind (0 default depth, 1 one slot, 2 two rows, 3 one slot
- * on interleaved rows), groups, groups per block, rows per block, group stride, step,
- * span, workgroups, threads per workgroup}: with k = g / (groups per block) and first =
+ * 3 residual gate + LayerNorm, 4 LayerNorm+modulate+FP8.  resident[3]: row groups
+ * resident at once with the default ring, with the one-slot ring and with the
+ * two-row ring (0: not available; resident[0] >= 1); cus: compute units (0: unknown;
+ * the two-row ring is chosen only with it).  rows = B*T >= 1 with 1 <= T <= rows and
+ * rows % T == 0 (else ADALN_ERR_SHAPE, also for a plan whose grid would pass 2^32
+ * work-items, which needs rows of more than 2^55 bytes), H as for the entry points.
+ * out[11] receives {one-slot ring (0/1), ring slots, ring kind (0 default depth,
+ * 1 one slot, 2 two rows), groups, groups per block, rows per block, group stride,
+ * step, span, workgroups, threads per workgroup}: with k = g / (groups per block) and
+ * first =
  * k * (rows per block) + (g % groups per block) * stride, group g takes the rows
- * first + i*step below min(first + span, (k + 1) * (rows per block), rows).
+ * first + i*step below min(first + span, (k + 1) * (rows per block), rows).  A launch
+ * of at least 2^25 elements (rows * H) of ops 0-3 takes a one-shot grid: the default
+ * ring, group g the rows g*span .. g*span + span - 1, span the ring depth (or a
+ * multiple of it when the grid would otherwise pass 2^32 work-items), and as many
+ * groups as that takes, whatever the resident counts.
  * ADALN_ERR_VALUE for an unknown op or a resident count or cus below 0 or above
  * 2^31 - 1 (resident[0] below 1); ADALN_ERR_NULL for a NULL resident or out. */
 adaln_status adaln_diag_launch_plan(int op, int64_t rows, int64_t H, int64_t T,
@@ -302,7 +310,7 @@ adaln_status adaln_diag_launch_plan(int op, int64_t rows, int64_t H, int64_t T,
 /* Diagnostic: the plan a launch takes on the current device, from the same
  * occupancy queries (cached per kernel and device), with nothing launched; weight:
  * nonzero when the RMS weight is given (ops 1 and 2; it selects the kernel whose
- * occupancy is queried).  out[11] as above; resident_out[4] and *cus_out (each may be
+ * occupancy is queried).  out[11] as above; resident_out[3] and *cus_out (each may be
  * NULL) receive the counts it used.  ADALN_ERR_LAUNCH when the queries fail (for
  * example no gfx950 device). */
 adaln_status adaln_diag_device_plan(int op, int64_t rows, int64_t H, int64_t T, int weight,

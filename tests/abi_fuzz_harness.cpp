@@ -36,11 +36,16 @@ int main() {
             case 6: st = adaln_check_residual_gate_channel_first(ptr(), ptr(), ptr(), (adaln_bf16*)ptr(), B, H, T, s0); break;
             default: {
                 int64_t out[11];
-                const int64_t res[4] = {s0, s1, s2, pick()};
+                const int64_t res[3] = {s0, s1, s2};
                 st = adaln_diag_launch_plan((int)(rng() % 7) - 1, B, H, T, res, pick(), out);
                 if (st == ADALN_OK) {
-                    // a plan has groups, groups per block and rows per block
-                    if (out[3] < 1 || out[4] < 1 || out[5] < 1) { std::printf("bad plan\n"); return 1; }
+                    // a plan has groups, groups per block and rows per block, and its
+                    // grid holds fewer than 2^32 work-items
+                    if (out[3] < 1 || out[4] < 1 || out[5] < 1 || out[9] < 1 ||
+                        out[9] > (int64_t)0xFFFFFFFF / out[10]) {
+                        std::printf("bad plan\n");
+                        return 1;
+                    }
                 }
             }
         }
@@ -78,8 +83,8 @@ int main() {
         if (st == ADALN_OK) ++acc2;
         int64_t out[11];
         if (B > 0 && T > 0 && B <= INT64_MAX / T) {
-            const int64_t res[4] = {1 + (int64_t)(rng() % 8192), (int64_t)(rng() % 8192),
-                                    (int64_t)(rng() % 8192), (int64_t)(rng() % 8192)};
+            const int64_t res[3] = {1 + (int64_t)(rng() % 8192), (int64_t)(rng() % 8192),
+                                    (int64_t)(rng() % 8192)};
             (void)adaln_diag_launch_plan((int)(rng() % 5), B * T, H, T, res,
                                          (int64_t)(rng() % 512), out);
         }

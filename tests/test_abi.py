@@ -38,7 +38,7 @@ def test_header_symbols_are_exported(lib):
 
 
 def test_abi_version_and_status_strings(lib):
-    assert A.adaln_abi_version() == A.ABI_VERSION == 10
+    assert A.adaln_abi_version() == A.ABI_VERSION == 11
     for s in range(8):
         assert len(A.adaln_status_string(s)) > 5
     assert A.adaln_status_string(99) == "unknown status"

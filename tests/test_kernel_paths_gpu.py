@@ -4,8 +4,8 @@ alone, against other plans of the same rows and against the oracle.
 The plan of a launch comes from the device's own occupancy (adaln_diag_device_plan),
 so each case first asserts which ring and assignment it exercises: the two-row ring
 for four-wave RMS rows at the row counts where it spreads the groups more evenly, the
-one-slot ring, and the interleaved and contiguous assignments with one or many batch
-entries.  The same rows run as one [1, R, H] batch, as [R, 1, H] (B = R batch
+one-slot ring, the interleaved and contiguous assignments with one or many batch
+entries, and the one-shot grid of large launches.  The same rows run as one [1, R, H] batch, as [R, 1, H] (B = R batch
 entries of one row each), as two entries and one at a time must give the same bits:
 batch invariance across plans as well as across launches (batch-invariance article,
 section 3)."""
@@ -146,18 +146,41 @@ def test_device_plan_rings(op, rows, T, H, ring):
     assert plan["resident"][0] >= 1 and plan["cus"] >= 1
 
 
-@pytest.mark.parametrize("op,B,T,H", [("rms", 1, 16384, 4096), ("rg", 2, 8192, 4096),
+def oracle_rows(op, xs, rs, g, w, sc, sh):
+    """The oracle's outputs (a list) of one op on [1, n, H] rows with [1, H] vectors."""
+    if op == "ln":
+        return [O.layernorm_modulate(xs, sc, sh, EPS)]
+    if op == "rms":
+        return [O.rmsnorm_scale_shift(xs, w, sc, sh, EPS)]
+    if op == "rg":
+        return list(O.residual_gate_rmsnorm_scale_shift(rs, xs, g, w, sc, sh, EPS))
+    return list(O.residual_gate_layernorm_modulate(rs, xs, g, sc, sh, EPS))
+
+
+def assert_one_shot(plan, rows):
+    S = plan["slots"]
+    assert plan["ring"] == 0 and not plan["shallow"], plan
+    assert (plan["span"], plan["group_stride"], plan["step"]) == (S, S, 1), plan
+    assert plan["groups"] == -(-rows // S) > plan["resident"][0], plan
+
+
+@pytest.mark.parametrize("op,B,T,H", [("rms", 1, 16384, 4096), ("rg", 2, 8191, 4096),
                                       ("rms", 1, 21846, 3072), ("rg", 1, 65536, 1024),
-                                      ("rms", 1, 16353, 4104), ("rg", 1, 65028, 1032)])
-def test_large_launches_take_interleaved_rows(op, B, T, H):
-    """From 2^26 elements per launch the RMS ops take the one-slot ring on interleaved
-    rows (asserted from the device plan first); sampled rows alone equal the rows in
-    the batch, and both equal the oracle."""
+                                      ("rms", 1, 16353, 4104), ("rg", 1, 65028, 1032),
+                                      ("ln", 1, 16384, 3072), ("rgln", 2, 8191, 3072),
+                                      ("ln", 1, 32768, 1032), ("rgln", 1, 8192, 4104),
+                                      ("ln", 3, 2731, 4096)])
+def test_large_launches_take_the_one_shot_grid(op, B, T, H):
+    """From 2^25 elements per launch every op but LN+FP8 takes the one-shot grid (one
+    pass of the default ring per group, consecutive rows; asserted from the device
+    plan first), with groups whose rows straddle two batch entries when T is not a
+    multiple of the ring depth; sampled rows alone equal the rows in the batch, and
+    both equal the oracle, the rows next to each entry boundary included."""
     rows = B * T
-    weight = op == "rms"
+    weight = op in ("rms", "rg")
     plan = A.adaln_diag_device_plan(op, rows, H, T, weight)
-    assert plan["ring"] == 3 and plan["slots"] == 1 and plan["step"] == plan["gpb"], plan
-    say(f"[paths] interleaved large {op} B={B} T={T} H={H}")
+    assert_one_shot(plan, rows)
+    say(f"[paths] one-shot {op} B={B} T={T} H={H}")
     gen = torch.Generator(device="cuda")
     gen.manual_seed(rows + H)
     x = torch.randn((B, T, H), generator=gen, device="cuda").to(torch.bfloat16)
@@ -170,7 +193,8 @@ def test_large_launches_take_interleaved_rows(op, B, T, H):
     out = run(op, x, res, g, w, sc, sh)
     hv = [None if t is None else host(t) for t in (g, w, sc, sh)]
     for b in range(B):
-        ts = np.random.default_rng(b).choice(T, size=32, replace=False)
+        ts = np.unique(np.concatenate([[0, 1, 2, T - 3, T - 2, T - 1],
+                                       np.random.default_rng(b).choice(T, size=32, replace=False)]))
         idx = torch.from_numpy(ts).cuda()
         vb = [None if t is None else t[b:b + 1] for t in (g, sc, sh)]
         for t in ts[:8]:  # alone
@@ -180,25 +204,22 @@ def test_large_launches_take_interleaved_rows(op, B, T, H):
                 assert torch.equal(u[b, t].view(torch.int16), v[0, 0].view(torch.int16)), (b, t)
         xs, rs = host(x[b][idx])[None], host(res[b][idx])[None]
         hb = [None if t is None else t[b:b + 1] for t in (hv[0], hv[2], hv[3])]
-        if op == "rms":
-            want = [O.rmsnorm_scale_shift(xs, hv[1], hb[1], hb[2], EPS)]
-        else:
-            want = list(O.residual_gate_rmsnorm_scale_shift(rs, xs, hb[0], hv[1], hb[1], hb[2], EPS))
+        want = oracle_rows(op, xs, rs, hb[0], hv[1], hb[1], hb[2])
         for u, wt in zip(out, want):
-            assert_bits_equal(host(u[b][idx])[None], wt, f"{op} large, entry {b}")
+            assert_bits_equal(host(u[b][idx])[None], wt, f"{op} one-shot, entry {b}")
 
 
-@pytest.mark.parametrize("op,H", [("rms", 1024), ("rg", 1024), ("rg", 4096)])
-def test_large_launch_every_row_its_own_entry(op, H):
-    """The interleaved rows of a large RMS launch when every row is its own batch entry
-    ([R, 1, H], per-row vectors, so a group reloads its constants at every row): the
-    device plan takes ring 3 over one interleave of all rows, and sampled rows equal
-    the oracle with their own vectors."""
-    R = -(-(1 << 26) // H)
-    weight = op == "rms"
+@pytest.mark.parametrize("op,H", [("rms", 1024), ("rg", 1024), ("rg", 4096), ("ln", 3072),
+                                  ("rgln", 1024)])
+def test_one_shot_every_row_its_own_entry(op, H):
+    """The one-shot grid when every row is its own batch entry ([R, 1, H], per-row
+    vectors, so a group reloads its constants at every row): sampled rows equal the
+    oracle with their own vectors."""
+    R = -(-(1 << 25) // H)
+    weight = op in ("rms", "rg")
     plan = A.adaln_diag_device_plan(op, R, H, 1, weight)
-    assert plan["ring"] == 3 and plan["gpb"] == plan["groups"], plan
-    say(f"[paths] interleaved large [R,1,H] {op} R={R} H={H}")
+    assert_one_shot(plan, R)
+    say(f"[paths] one-shot [R,1,H] {op} R={R} H={H}")
     gen = torch.Generator(device="cuda")
     gen.manual_seed(R + H)
     x = torch.randn((R, 1, H), generator=gen, device="cuda").to(torch.bfloat16)
@@ -211,9 +232,6 @@ def test_large_launch_every_row_its_own_entry(op, H):
     for r in np.random.default_rng(R).choice(R, size=48, replace=False):
         xs, rs = host(x[r:r + 1]), host(res[r:r + 1])
         gs, ss, hs = host(g[r:r + 1]), host(sc[r:r + 1]), host(sh[r:r + 1])
-        if op == "rms":
-            want = [O.rmsnorm_scale_shift(xs, wv, ss, hs, EPS)]
-        else:
-            want = list(O.residual_gate_rmsnorm_scale_shift(rs, xs, gs, wv, ss, hs, EPS))
+        want = oracle_rows(op, xs, rs, gs, wv, ss, hs)
         for u, wt in zip(out, want):
             assert_bits_equal(host(u[r:r + 1]), wt, f"{op} [R,1,{H}] row {r}")

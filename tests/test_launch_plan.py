@@ -4,8 +4,9 @@ exactly once; the grid and ring follow the documented rules; a group given to on
 batch entry stays in it; a contiguous group's rows stay within 32-bit byte offsets.
 The plan is the library's own host function (through the launch-plan diagnostic),
 fed with resident counts like a device's: row groups with the default ring, the
-one-slot ring, the two-row ring and the one-slot ring on interleaved rows (the
-RMS ops' large launches), and the CU count."""
+one-slot ring and the two-row ring, and the CU count.  Launches of at least 2^25
+elements (all ops but LN+FP8) take the one-shot grid: one pass of the default ring
+per group, consecutive rows, as many groups as that takes."""
 import numpy as np
 import pytest
 
@@ -13,15 +14,29 @@ import diffusion_dit_adaln_amd as A
 
 OPS = ["ln", "rms", "rg", "rgln", "lnq"]
 INTERLEAVED = {"ln", "rgln", "lnq"}
-# (deep, one-slot, two-row, interleaved one-slot, CUs)
-RESIDENT = [(1024, 1536, 1792, 1536, 256), (768, 0, 0, 0, 256), (256, 512, 0, 512, 64),
-            (1, 1, 0, 1, 1), (7, 0, 0, 0, 7), (2560, 2560, 0, 2560, 256),
-            (1024, 1536, 1280, 0, 256), (1024, 1536, 1792, 1536, 0), (1024, 1536, 1280, 1280, 3)]
-BIG = 1 << 26  # elements per launch from which the RMS ops interleave
+# (deep, one-slot, two-row, CUs)
+RESIDENT = [(1024, 1536, 1792, 256), (768, 0, 0, 256), (256, 512, 0, 64), (1, 1, 0, 1),
+            (7, 0, 0, 7), (2560, 2560, 0, 256), (1024, 1536, 1280, 256), (1024, 1536, 1792, 0),
+            (1024, 1536, 1280, 3)]
+ONESHOT = 1 << 25  # elements per launch from which the one-shot grid is taken
 # (rows, T): one batch entry, a few long ones, many short ones
 SHAPES = [(1, 1), (3, 1), (7, 7), (7, 1), (100, 100), (100, 25), (4216, 4216), (4216, 527),
           (9216, 4608), (9216, 9216), (30001, 1579), (524287, 524287), (524288, 4096),
           (524288, 64), (8192, 8192), (64 * 15, 15)]
+
+
+def default_slots(op, H):
+    """The default ring depth of a layout: two for two-wave rows without the gate,
+    else three up to 32 bf16 of activations per lane and two above."""
+    w, _, c = A.adaln_reduction_layout(H)
+    gated = op in ("rg", "rgln")
+    if w == 2 and not gated:
+        return 2
+    return 3 if c * 8 * (2 if gated else 1) <= 32 else 2
+
+
+def one_shot(op, rows, H):
+    return op != "lnq" and rows * H >= ONESHOT
 
 
 def rows_of(plan, rows):
@@ -44,8 +59,8 @@ def rows_of(plan, rows):
 @pytest.mark.parametrize("res", RESIDENT)
 def test_every_row_exactly_once(op, H, shape, res):
     rows, T = shape
-    resident, resident_shallow, resident_two, resident_il, cus = res
-    plan = A.adaln_diag_launch_plan(op, rows, H, T, res[:4], cus)
+    resident, resident_shallow, resident_two, cus = res
+    plan = A.adaln_diag_launch_plan(op, rows, H, T, res[:3], cus)
     w, _, _ = A.adaln_reduction_layout(H)
     visited, group = rows_of(plan, rows)
     assert visited.size == rows
@@ -53,13 +68,18 @@ def test_every_row_exactly_once(op, H, shape, res):
     B = rows // T
     assert plan["block_threads"] == (256 if w == 1 else 64 * w)
     assert plan["blocks"] == ((plan["groups"] + 3) // 4 if w == 1 else plan["groups"])
-    # large launches of the RMS ops take the one-slot ring on interleaved rows
-    il_big = op not in INTERLEAVED and resident_il > 0 and rows >= -(-BIG // H)
-    if op in INTERLEAVED or il_big:
-        shallow = il_big or (resident_shallow > 0 and rows >= 3 * resident)
-        ring = 3 if il_big else 1 if shallow else 0
-        assert plan["shallow"] == shallow and plan["ring"] == ring
-        G = min(rows, resident_il if il_big else resident_shallow if shallow else resident)
+    assert plan["blocks"] * plan["block_threads"] < 2**32
+    if one_shot(op, rows, H):
+        # one pass of the default ring per group, consecutive rows, any resident count
+        S = default_slots(op, H)
+        assert (plan["shallow"], plan["ring"], plan["slots"]) == (False, 0, S)
+        assert (plan["span"], plan["group_stride"], plan["step"]) == (S, S, 1)
+        assert plan["groups"] == plan["gpb"] == -(-rows // S) and plan["blk_rows"] == rows
+        assert (plan["span"] + S) * 2 * H <= 2**31 - 1
+    elif op in INTERLEAVED:
+        shallow = resident_shallow > 0 and rows >= 3 * resident
+        assert plan["shallow"] == shallow and plan["ring"] == (1 if shallow else 0)
+        G = min(rows, resident_shallow if shallow else resident)
         per_entry = min(G // B, T) if B > 1 else 0
         assert plan["group_stride"] == 1 and plan["step"] == plan["gpb"]
         if per_entry > 0 and 16 * (G - per_entry * B) <= G:
@@ -96,41 +116,64 @@ def test_every_row_exactly_once(op, H, shape, res):
 
 
 def test_two_row_ring_where_it_spreads_groups_more_evenly():
-    # four-wave RMS rows at 8192 rows on a device like MI355X (resident counts of the
-    # weighted kernels: 4, 6 and 5 groups per CU): the two-row ring leaves the most
-    # loaded CU fewer rows
+    # four-wave RMS rows at 8000 rows (just below the one-shot grid's 2^25 elements)
+    # on a device like MI355X (resident counts of the weighted kernels: 4, 6 and 5
+    # groups per CU): the two-row ring leaves the most loaded CU fewer rows
     res = (1024, 1536, 1280)
     for H in (4096, 4104):
-        plan = A.adaln_diag_launch_plan("rms", 8192, H, 8192, res, 256)
+        plan = A.adaln_diag_launch_plan("rms", 8000, H, 8000, res, 256)
         assert plan["ring"] == 2 and plan["slots"] == 2 and not plan["shallow"]
     # without its resident count or the CU count it is never chosen
-    assert A.adaln_diag_launch_plan("rms", 8192, 4096, 8192, (1024, 1536, 0), 256)["ring"] == 0
-    assert A.adaln_diag_launch_plan("rms", 8192, 4096, 8192, res, 0)["ring"] == 0
-    # with one more two-row group per CU the three-row ring spreads 8192 rows better
-    assert A.adaln_diag_launch_plan("rms", 8192, 4096, 8192, (1024, 1536, 1792), 256)["ring"] == 0
+    assert A.adaln_diag_launch_plan("rms", 8000, 4096, 8000, (1024, 1536, 0), 256)["ring"] == 0
+    assert A.adaln_diag_launch_plan("rms", 8000, 4096, 8000, res, 0)["ring"] == 0
+    # with one more two-row group per CU the three-row ring spreads 8000 rows better
+    assert A.adaln_diag_launch_plan("rms", 8000, 4096, 8000, (1024, 1536, 1792), 256)["ring"] == 0
     # never for the gated op
-    assert A.adaln_diag_launch_plan("rg", 8192, 4096, 8192, res, 256)["ring"] == 0
+    assert A.adaln_diag_launch_plan("rg", 8000, 4096, 8000, res, 256)["ring"] == 0
 
 
-def test_large_rms_launches_take_interleaved_rows():
-    # from 2^26 elements per launch the RMS ops (with and without the gate) take the
-    # one-slot ring on interleaved rows, given that kernel's resident count
-    res = (1024, 1536, 1280, 1536)
-    for op in ("rms", "rg"):
-        for rows, H in ((16384, 4096), (8192, 8192), (21846, 3072), (65536, 1024)):
+def test_large_launches_take_the_one_shot_grid():
+    # from 2^25 elements per launch every op but LN+FP8 takes one pass of its default
+    # ring per group, whatever fits on the device at once
+    res = (1024, 1536, 1280)
+    for op in ("ln", "rms", "rg", "rgln"):
+        for rows, H in ((8192, 4096), (4096, 8192), (10923, 3072), (32768, 1024), (16384, 2048)):
+            S = default_slots(op, H)
             plan = A.adaln_diag_launch_plan(op, rows, H, rows, res, 256)
-            assert plan["ring"] == 3 and plan["slots"] == 1 and plan["shallow"]
-            assert plan["groups"] == 1536 and plan["step"] == 1536 and plan["group_stride"] == 1
-        # one row fewer: contiguous ranges
-        assert A.adaln_diag_launch_plan(op, 16383, 4096, 16383, res, 256)["ring"] != 3
-        assert A.adaln_diag_launch_plan(op, 21845, 3072, 21845, res, 256)["ring"] != 3
-        # without that kernel's resident count: never
-        assert A.adaln_diag_launch_plan(op, 65536, 4096, 65536, res[:3], 256)["ring"] != 3
-    # two batch entries: each entry its own share of the groups
-    plan = A.adaln_diag_launch_plan("rg", 2 * 8192, 4096, 8192, res, 256)
-    assert (plan["ring"], plan["groups"], plan["gpb"], plan["blk_rows"]) == (3, 1536, 768, 8192)
-    # the LayerNorm ops are interleaved at any size and never take ring 3
-    assert A.adaln_diag_launch_plan("ln", 65536, 4096, 65536, res, 256)["ring"] == 1
+            assert (plan["ring"], plan["slots"], plan["span"], plan["step"]) == (0, S, S, 1)
+            assert plan["groups"] == -(-rows // S) > res[0]
+            # two batch entries: the same ranges over the flat rows
+            p2 = A.adaln_diag_launch_plan(op, 2 * rows, H, rows, res, 256)
+            assert (p2["gpb"], p2["blk_rows"], p2["span"]) == (-(-2 * rows // S), 2 * rows, S)
+        # one row fewer: the persistent grid (interleaved rows, or ranges of several
+        # passes), a few groups per resident slot at most
+        for rows, H in ((8191, 4096), (10922, 3072)):
+            plan = A.adaln_diag_launch_plan(op, rows, H, rows, res, 256)
+            S = default_slots(op, H)
+            assert plan["groups"] <= 3 * 1536
+            assert plan["step"] > 1 or plan["span"] > S
+    # LN+FP8, bound by its arithmetic, keeps the persistent grid at any size
+    plan = A.adaln_diag_launch_plan("lnq", 65536, 3072, 65536, res, 256)
+    assert plan["groups"] <= 1536 and plan["ring"] == 1
+
+
+def test_one_shot_grid_stays_below_2_32_work_items():
+    # so many rows that one pass per group would pass 2^32 work-items: each group
+    # takes whole passes more, and its rows stay within 32-bit byte offsets
+    for op, rows, H in (("rms", 3 * 10**8, 8192), ("ln", 2**33, 8), ("rg", 2**31, 1024),
+                        ("rgln", 5 * 10**8, 3072)):
+        plan = A.adaln_diag_launch_plan(op, rows, H, rows, (1024, 0, 0), 256)
+        S = plan["slots"]
+        assert S == default_slots(op, H) and plan["span"] % S == 0 and plan["span"] > S
+        assert plan["blocks"] * plan["block_threads"] <= 2**32 - 1
+        assert plan["groups"] * plan["span"] >= rows > (plan["groups"] - 1) * plan["span"]
+        assert (plan["span"] + S) * 2 * H <= 2**31 - 1
+        # one pass fewer per group would not fit
+        per = plan["span"] - S
+        w, _, _ = A.adaln_reduction_layout(H)
+        groups = -(-rows // per)
+        blocks = -(-groups // 4) if w == 1 else groups
+        assert blocks * plan["block_threads"] > 2**32 - 1
 
 
 def test_interleaved_batch_entries_get_their_own_groups():
@@ -138,23 +181,15 @@ def test_interleaved_batch_entries_get_their_own_groups():
     plan = A.adaln_diag_launch_plan("lnq", 9216, 3072, 4608, (2560, 2560), 256)
     assert (plan["groups"], plan["gpb"], plan["blk_rows"], plan["step"]) == (2560, 1280, 4608, 1280)
     # 2560 groups over 7 entries would leave 5 slots idle (< 1/16): split
-    assert A.adaln_diag_launch_plan("ln", 7 * 4608, 3072, 4608, (2560, 2560))["gpb"] == 365
+    assert A.adaln_diag_launch_plan("ln", 7 * 1024, 3072, 1024, (2560, 2560))["gpb"] == 365
     # 2560 groups over 1000 entries would idle 560 slots: one interleave over all rows
-    plan = A.adaln_diag_launch_plan("ln", 1000 * 64, 3072, 64, (2560, 2560))
-    assert (plan["groups"], plan["gpb"], plan["blk_rows"]) == (2560, 2560, 64000)
-
-
-def test_contiguous_groups_capped_by_32_bit_offsets():
-    # so many rows per group that the span would pass 2^31 bytes: the span is
-    # capped and the group count grows instead
-    rows, H = 3 * 10**8, 8192
-    plan = A.adaln_diag_launch_plan("rms", rows, H, rows, (1024, 0, 0), 256)
-    S = plan["slots"]
-    assert (plan["span"] + S) * 2 * H <= 2**31 - 1
-    assert plan["groups"] * plan["span"] >= rows > (plan["groups"] - 1) * plan["span"]
+    plan = A.adaln_diag_launch_plan("ln", 1000 * 8, 3072, 8, (2560, 2560))
+    assert (plan["groups"], plan["gpb"], plan["blk_rows"]) == (2560, 2560, 8000)
 
 
 def test_plan_rejects_bad_arguments():
+    with pytest.raises(ValueError):  # three resident counts at most
+        A.adaln_diag_launch_plan("ln", 10, 1024, 10, (1024, 0, 0, 0))
     bad = [("ln", 0, 1024, 1, (1024, 0, 0), 0), ("ln", 10, 12, 10, (1024, 0, 0), 0),
            ("ln", 10, 1024, 10, (0, 0, 0), 0), ("ln", 10, 1024, 10, (2**31, 0, 0), 0),
            ("ln", 10, 1024, 10, (1024, 2**31, 0), 0), ("ln", 10, 1024, 10, (1024, 0, -1), 0),

@@ -3,8 +3,9 @@
 Each case draws an op (LN, RMS with and without weight, residual-gate RMS with and
 without weight, residual-gate LN, LN+FP8), a hidden size (any multiple of 8 up to
 8192: one-, two- and four-wave rows, ragged last chunks), a batch split, a token
-count (up to 12 M elements per tensor, and just past 2^26 for the RMS ops, so that
-every ring and row assignment of the launch plan comes up), the form of the per-batch vectors (one per
+count (up to 12 M elements per tensor, and just past 2^25 for every op but LN+FP8,
+so that every ring and row assignment of the launch plan and the one-shot grid come
+up), the form of the per-batch vectors (one per
 entry, one shared by the batch, or strided views of a wider embedding), eps and the
 scale of the activations.  The case is printed before it runs."""
 import numpy as np
@@ -25,8 +26,8 @@ N_CASES = 63
 
 def draw(seed):
     """Three kinds of case, in turn over the ops: any hidden size up to 3 M elements;
-    two- and four-wave rows up to 12 M elements; and, for the RMS ops, launches just
-    past 2^26 elements (their interleaved rows)."""
+    two- and four-wave rows up to 12 M elements; and, for every op but LN+FP8,
+    launches just past 2^25 elements (the one-shot grid)."""
     rng = np.random.default_rng(seed)
     op = OPS[seed % len(OPS)]
     mode = (seed // len(OPS)) % 3
@@ -34,13 +35,13 @@ def draw(seed):
     if mode == 0:
         H = max(8, min(8192, int(8 * round(2 ** rng.uniform(0, 10)))))
         T = int(rng.integers(1, max(2, MAX_ELEMS // (B * H))))
-    elif mode == 1 or op not in ("rms", "rms_nw", "rg", "rg_nw"):
+    elif mode == 1 or op == "lnq":
         H = 8 * int(rng.integers(256, 1025))
         T = int(rng.integers(1, max(2, 4 * MAX_ELEMS // (B * H))))
     else:
         H = 8 * int(rng.integers(128, 1025))
-        B = int(rng.choice([1, 2]))
-        T = -(-((1 << 26) + int(rng.integers(0, 1 << 20))) // (B * H))
+        B = int(rng.choice([1, 2, 3]))
+        T = -(-((1 << 25) + int(rng.integers(0, 1 << 20))) // (B * H))
     vec = str(rng.choice(["per_entry", "shared", "strided"]))
     eps = float(rng.choice([1e-6, 1e-5, 0.0, 0.25]))
     sigma = float(rng.choice([1.0, 1e-3, 1e3]))

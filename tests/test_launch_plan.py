@@ -176,6 +176,18 @@ def test_one_shot_grid_stays_below_2_32_work_items():
         assert blocks * plan["block_threads"] > 2**32 - 1
 
 
+def test_persistent_grid_stays_below_2_32_work_items():
+    # LN+FP8 keeps the persistent grid at any size: even with resident counts no
+    # device has, its groups are capped so that the grid holds fewer than 2^32
+    # work-items, and every row is still covered
+    big = 2**31 - 1
+    for rows, H in ((2**26, 3072), (2**28, 1024), (2**25, 8192)):
+        plan = A.adaln_diag_launch_plan("lnq", rows, H, rows, (big, big, 0), 256)
+        assert plan["blocks"] * plan["block_threads"] <= 2**32 - 1
+        assert plan["step"] == plan["gpb"] == plan["groups"]
+        assert plan["groups"] * -(-rows // plan["groups"]) >= rows
+
+
 def test_interleaved_batch_entries_get_their_own_groups():
     # the FLUX.1 LayerNorm site [2, 4608, 3072] on 2560 resident groups: 1280 per entry
     plan = A.adaln_diag_launch_plan("lnq", 9216, 3072, 4608, (2560, 2560), 256)

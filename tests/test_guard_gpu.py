@@ -3,7 +3,8 @@
 Each entry point writes into views of larger device buffers whose margins before
 and after the view hold random sentinel bits; after the call the margins must be
 unchanged and the view must equal the CPU oracle bit for bit.  The shapes cover
-ragged hidden sizes (partial last chunk), ragged row counts per group, the FP8
+ragged hidden sizes (partial last chunk), ragged row counts per group (also in the
+one-shot grid of launches of 2^25 elements and more), the FP8
 8-byte stores, QK heads that do not fill a task of eight, and the channel-first
 kernel's narrow phase-2 accesses at ragged token counts, in place and out of place
 (kernels guide, "entry-point protocol": a kernel never degrades silently; an
@@ -61,6 +62,23 @@ class Guarded:
 
 FUSED_SHAPES = [(1, 1, 3072), (2, 37, 3072), (1, 300, 4096), (3, 11, 4104), (2, 9, 520),
                 (1, 5, 8192), (1, 129, 2048), (2, 3, 8)]
+
+
+# launches of at least 2^25 elements take the one-shot grid; the row counts leave the
+# last group a partial pass (four-wave rows of three-row rings, two-wave rows of
+# two-row rings, one-wave rows of three-row rings)
+ONESHOT_SHAPES = [(1, 8194, 4096), (1, 10923, 3072), (1, 32770, 1024)]
+
+
+@pytest.mark.parametrize("shape", ONESHOT_SHAPES)
+@pytest.mark.parametrize("op", ["ln", "rms", "rg", "rgln"])
+def test_one_shot_outputs_stay_in_bounds(op, shape):
+    B, T, H = shape
+    weight = op in ("rms", "rg")
+    plan = A.adaln_diag_device_plan(op, B * T, H, T, weight)
+    assert plan["step"] == 1 and plan["span"] == plan["slots"], plan
+    assert (B * T) % plan["slots"] != 0
+    test_fused_outputs_stay_in_bounds(op, shape)
 
 
 @pytest.mark.parametrize("shape", FUSED_SHAPES)
